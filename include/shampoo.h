@@ -1,0 +1,297 @@
+/*
+ * shampoo.h -- C ABI of the batched block preconditioner step of
+ * block-diagonal Shampoo, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources cited below (titles of the pages; sections as named there):
+ *   [DASH]  "DASH: Faster Shampoo via Batched Block Preconditioning and
+ *           Efficient Inverse-Root Solvers", source-linked AI summary.
+ *   [3DS]   "3D-Shampoo optimizer" README.
+ *   [NOTES] "Shampoo" notes (regret, Kronecker bound, scale, grafting).
+ *   [DIST]  "A Distributed Data-Parallel PyTorch Implementation of the
+ *           Distributed Shampoo Optimizer ..." (abstract).
+ *
+ * Conventions shared by every entry point:
+ *   - Layout: row-major.  A "stack" is a contiguous [n, B, B] array; matrix b
+ *     starts at element b*B*B.  Block tables are arrays of shampoo_block.
+ *   - Ownership: the caller owns every buffer.  No entry point allocates or
+ *     frees device memory; scratch comes in through an explicit workspace
+ *     whose size the matching *_workspace call reports.  Pointers named *_dev
+ *     and all stacks are device pointers; everything else is host memory.
+ *   - Streams: all device work is enqueued, in order, on the given stream.
+ *     No entry point synchronises the device except shampoo_check_flags.
+ *   - Errors: arguments are validated before the first launch, so a call
+ *     that returns an error has enqueued nothing.  No C++ exception crosses
+ *     the ABI.  shampoo_last_error() returns a thread-local message for the
+ *     last non-OK status of the calling thread.  A failed launch returns
+ *     SHAMPOO_E_HIP; faults that surface later are reported by the next
+ *     synchronising HIP call of the caller.
+ *   - Numerical failures are not errors: they set per-matrix flag bits
+ *     (SHAMPOO_FLAG_*) in a caller-provided int32 array, written with atomic
+ *     OR (the caller clears it).
+ */
+#ifndef SHAMPOO_H
+#define SHAMPOO_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum shampoo_status {
+  SHAMPOO_OK = 0,
+  SHAMPOO_E_INVALID = 1,     /* bad argument: null pointer, size, enum value */
+  SHAMPOO_E_UNSUPPORTED = 2, /* valid but not implemented combination */
+  SHAMPOO_E_WORKSPACE = 3,   /* workspace smaller than the *_workspace size */
+  SHAMPOO_E_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  SHAMPOO_E_NONFINITE = 5    /* shampoo_check_flags found a flagged matrix */
+} shampoo_status;
+
+typedef enum shampoo_dtype {
+  SHAMPOO_F32 = 0,
+  SHAMPOO_F16 = 1,
+  SHAMPOO_BF16 = 2,
+  SHAMPOO_F64 = 3
+} shampoo_dtype;
+
+/* Inverse-root solvers.  [NOTES] "Roots on idle CPUs, partial preconditioners
+ * for large layers, and grafting" (coupled Newton of Guo-Higham / Iannazzo);
+ * [DASH] "3. Inverse Root Methods" (Newton-DB); [DASH] "A.1/A.2 Chebyshev
+ * polynomials" (Chebyshev series summed by Clenshaw's recurrence). */
+typedef enum shampoo_method {
+  SHAMPOO_CN = 0,
+  SHAMPOO_NDB = 1,
+  SHAMPOO_CHEBYSHEV = 2
+} shampoo_method;
+
+/* [DASH] "3. Inverse Root Methods": Frobenius-norm scaling, or the largest
+ * Rayleigh quotient of a half-precision multi-start power iteration. */
+typedef enum shampoo_scaling {
+  SHAMPOO_SCALE_FROBENIUS = 0,
+  SHAMPOO_SCALE_POWER = 1
+} shampoo_scaling;
+
+/* Grafting.  [3DS] "Hyperparameters" (layer-wise onto SGD), "How to use"
+ * (lr 0.1, momentum 0.9); [DASH] "2. Preliminaries on Shampoo" (Adam). */
+typedef enum shampoo_graft {
+  SHAMPOO_GRAFT_SGD = 0,
+  SHAMPOO_GRAFT_MOMENTUM = 1,
+  SHAMPOO_GRAFT_ADAM = 2,
+  SHAMPOO_GRAFT_NONE = 3     /* W <- W - lr D, no rescaling */
+} shampoo_graft;
+
+/* Per-matrix flag bits. */
+#define SHAMPOO_FLAG_NONFINITE 1  /* a NaN or Inf in the output root */
+#define SHAMPOO_FLAG_ZERO_SCALE 2 /* scale s was 0 or not finite: output set to 0 */
+#define SHAMPOO_FLAG_PI_FALLBACK 4 /* power iteration gave no positive finite
+                                      quotient: Frobenius scale used instead */
+
+/* One row of a block table (32 bytes, plain old data).  [DASH] "4. Blocking
+ * Strategy"; [3DS] "Hyperparameters" (block_size, 0 = never split).
+ * param: parameter index; (brow, bcol): position in the parameter's block
+ * grid; (row0, col0): offset of the block's first element in the
+ * parameter's 2-D view; (rows, cols): valid extent (< B on ragged edges);
+ * B: side of the zero-padded stacked block. */
+typedef struct shampoo_block {
+  int32_t param, brow, bcol, row0, col0, rows, cols, B;
+} shampoo_block;
+
+/* A 2-D device matrix: element (r, c) at data[r * ld + c]. */
+typedef struct shampoo_matrix {
+  void* data;
+  int64_t rows, cols, ld;
+} shampoo_matrix;
+
+/* A parameter as seen by shampoo_step (device array of these).
+ * w: float32 weights [rows, ld]; g: gradient [rows, ld] in the step's g_dt;
+ * m: momentum buffer (MOMENTUM) or Adam first moment (ADAM), float32, else NULL;
+ * v: Adam second moment (ADAM), float32, else NULL;
+ * first_block: table index of the parameter's block (0, 0); its blocks are
+ * the next ceil(rows/B) * ceil(cols/B) table rows in row-major grid order. */
+typedef struct shampoo_param {
+  float* w;
+  const void* g;
+  float* m;
+  float* v;
+  int64_t rows, cols, ld;
+  int64_t first_block;
+} shampoo_param;
+
+/* Inverse-root options.
+ * method/scaling: shampoo_method / shampoo_scaling.
+ * compute: arithmetic of the solver chain.  SHAMPOO_F32: float32 MFMA;
+ *   SHAMPOO_F16: half-precision products with float32 accumulation and
+ *   float32 iterates ([DASH] "A.3 Numerical Precision"); SHAMPOO_F64:
+ *   float64 MFMA (iterates float64).
+ * iters: coupled-Newton iterations, or Newton-DB iterations of the first
+ *   call; iters2: Newton-DB iterations of the second call (p = 4 only).
+ * pi_vectors (1..32), pi_iters (>= 1): power-iteration start vectors and
+ *   products before the Rayleigh quotients; pi_start_dev: device float32
+ *   [pi_vectors, B] start vectors (required for SHAMPOO_SCALE_POWER).
+ * cheb_degree (>= 0), cheb_points (0 = 4 (degree + 1)): Chebyshev fit;
+ *   cheb_eps: the fit interval is [cheb_eps, 1 + cheb_eps].
+ * eps: added to the diagonal of each matrix's valid region before scaling
+ *   ([DASH] "2. Preliminaries on Shampoo"; added once, see [DASH] "B.1"). */
+typedef struct shampoo_root_opts {
+  int32_t method;
+  int32_t scaling;
+  int32_t compute;
+  int32_t iters;
+  int32_t iters2;
+  int32_t pi_vectors;
+  int32_t pi_iters;
+  int32_t cheb_degree;
+  int32_t cheb_points;
+  int32_t reserved0;
+  double eps;
+  double cheb_eps;
+  const float* pi_start_dev;
+} shampoo_root_opts;
+
+/* Arguments of one shampoo_step over one stack (one block size B). */
+typedef struct shampoo_step_args {
+  int32_t nparams;
+  int32_t B;
+  int64_t nblk;
+  const shampoo_param* params_dev;  /* device [nparams] */
+  const shampoo_block* table_dev;   /* device [nblk], as planned for B */
+  shampoo_dtype g_dt;               /* SHAMPOO_F32 or SHAMPOO_BF16 */
+  int32_t p;                        /* root order, 4 for Shampoo */
+  float* LR;                        /* device f32 [2 nblk, B, B]: L stack then R stack (state) */
+  float* roots;                     /* device f32 [2 nblk, B, B]: inverse roots (state) */
+  float beta2;                      /* statistics EMA; 1 = plain sum */
+  int32_t recompute_roots;          /* 0: reuse `roots` from an earlier step */
+  shampoo_root_opts root;
+  int32_t graft;                    /* shampoo_graft */
+  int32_t graft_blockwise;          /* 0: norms per parameter (layer-wise); 1: per block */
+  float lr;
+  float momentum;                   /* MOMENTUM */
+  float beta1, graft_beta2, graft_eps; /* ADAM */
+  int32_t t;                        /* 1-based step count (Adam bias correction) */
+  int32_t* flags_dev;               /* device int32 [2 nblk] or NULL */
+  float* dstack;                    /* device f32 [nblk, B, B] or NULL: receives D (ungrafted) */
+  void* ws;
+  size_t ws_bytes;
+} shampoo_step_args;
+
+/* Version string of the library. */
+const char* shampoo_version(void);
+
+/* Thread-local message of the calling thread's last non-OK status. */
+const char* shampoo_last_error(void);
+
+/* Block plan (host only, no device work).  [DASH] "4. Blocking Strategy";
+ * [3DS] "Hyperparameters".  shapes2d: host int64 [nparams, 2] (rows, cols)
+ * of the 2-D views; block_sizes: host int32 [nparams] (0 = one block of side
+ * max(rows, cols)).  Blocks are listed parameter by parameter, row-major over
+ * each block grid.  *nblk is the capacity of `out` on entry and the number of
+ * blocks on return; with out == NULL only the count is returned.
+ * Errors: E_INVALID for negative sizes or block sizes, or if the count
+ * exceeds the capacity (then *nblk holds the count needed). */
+shampoo_status shampoo_plan_blocks(const int64_t* shapes2d, const int32_t* block_sizes,
+                                   int32_t nparams, shampoo_block* out, int64_t* nblk);
+
+/* Pack parameter-layout matrices into a zero-padded block stack.  [DASH]
+ * "4. Blocking Strategy" (stacking blocks into 3-D tensors).
+ * mats_dev: device [nparams] shampoo_matrix indexed by table.param;
+ * table_dev: device [nblk]; stack: device [nblk, B, B] in dtype dt;
+ * stack_t: NULL, or device [nblk, B, B] receiving each block transposed.
+ * dt: SHAMPOO_F32, SHAMPOO_BF16, SHAMPOO_F16 or SHAMPOO_F64.
+ * Bit-exact copy; the padding is written as +0.  Errors: E_INVALID for null
+ * pointers, nblk < 0 or B < 1. */
+shampoo_status shampoo_pack_blocks(const shampoo_matrix* mats_dev, int32_t nparams,
+                                   const shampoo_block* table_dev, int64_t nblk, int32_t B,
+                                   shampoo_dtype dt, void* stack, void* stack_t,
+                                   hipStream_t stream);
+
+/* Inverse of shampoo_pack_blocks for float32 stacks: writes each block's
+ * valid region into the parameter-layout matrices mats_dev (float32). */
+shampoo_status shampoo_unpack_blocks(const float* stack, const shampoo_block* table_dev,
+                                     int64_t nblk, int32_t B, const shampoo_matrix* mats_dev,
+                                     int32_t nparams, hipStream_t stream);
+
+/* Statistics.  [DASH] "2. Preliminaries on Shampoo"; [NOTES] "The geometric
+ * mean of the two bounds is the Kronecker bound" (sums over steps):
+ *   L_b <- beta2 L_b + (1 - beta2) G_b G_b^T,  R_b <- beta2 R_b + (1 - beta2) G_b^T G_b,
+ * and L_b += G_b G_b^T, R_b += G_b^T G_b when beta2 == 1.
+ * gstack, gstack_t: device [nblk, B, B] block stack and its per-block
+ * transpose (as written by shampoo_pack_blocks) in g_dt (F32 or BF16);
+ * LR: device f32 [2 nblk, B, B], L_0..L_(nblk-1) then R_0..R_(nblk-1),
+ * updated in place; kept exactly symmetric.  B must be a multiple of 64. */
+shampoo_status shampoo_update_stats(const void* gstack, const void* gstack_t, shampoo_dtype g_dt,
+                                    int64_t nblk, int32_t B, float* LR, float beta2,
+                                    hipStream_t stream);
+
+/* Workspace bytes for shampoo_inverse_root with these arguments. */
+shampoo_status shampoo_inverse_root_workspace(int64_t n, int32_t B, int32_t p,
+                                              const shampoo_root_opts* opts, size_t* bytes);
+
+/* Batched inverse p-th roots of symmetric positive definite matrices.
+ * in: device [n, B, B] in io_dt (F32 or F64), symmetric; out: device
+ * [n, B, B] in io_dt, receives (A + eps I)^(-1/p) on each valid region and 0
+ * elsewhere (in may equal out).  valid_dev: device int32 [n] valid sizes
+ * (matrix b uses its leading valid[b] x valid[b] region; the rest is
+ * treated as padding) or NULL for all B.  scale_out_dev: device f32 [n]
+ * receiving the scale s of each matrix, or NULL.  flags_dev: device int32 [n]
+ * flag bits (OR-ed), or NULL.  Steps ([DASH] "3. Inverse Root Methods",
+ * "A.2"): A = in + eps I; s = ||A||_F, or (power) s = ||A||_F times the
+ * largest Rayleigh quotient of A/||A||_F; A_s = A/s with the padding set to
+ * the identity; X = solver(A_s); out = X s^(-1/p).
+ * Supported: CN with p in {1, 2, 4, 8}; NDB with p in {2, 4}; Chebyshev with
+ * p >= 1 (compute F32 or F64); power scaling with B <= 1024.  B must be a
+ * multiple of 64.  Errors: E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP. */
+shampoo_status shampoo_inverse_root(const void* in, void* out, shampoo_dtype io_dt, int64_t n,
+                                    int32_t B, int32_t p, const shampoo_root_opts* opts,
+                                    const int32_t* valid_dev, float* scale_out_dev,
+                                    int32_t* flags_dev, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/* Workspace bytes for shampoo_precondition: nblk * B * B * 4. */
+shampoo_status shampoo_precondition_workspace(int64_t nblk, int32_t B, size_t* bytes);
+
+/* Search direction per block.  [NOTES] "AdaGrad's regret argument goes
+ * through with the Kronecker preconditioner": S^(-1) vec(G) with
+ * S = L^(1/4) (x) R^(1/4), i.e. D_b = Lr_b G_b Rr_b.
+ * roots: device f32 [2 nblk, B, B] (inverse roots of L then of R, symmetric);
+ * gstack: device [nblk, B, B] in g_dt (F32 or BF16); dstack: device f32
+ * [nblk, B, B].  B must be a multiple of 64. */
+shampoo_status shampoo_precondition(const float* roots, const void* gstack, shampoo_dtype g_dt,
+                                    int64_t nblk, int32_t B, float* dstack, void* ws,
+                                    size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for shampoo_step with these arguments (ws fields ignored). */
+shampoo_status shampoo_step_workspace(const shampoo_step_args* args, size_t* bytes);
+
+/* One full preconditioner step over one stack: pack, statistics, inverse
+ * roots (unless recompute_roots == 0), preconditioning, grafting and the
+ * weight update ([3DS] "Hyperparameters"; [DASH] "2. Preliminaries on
+ * Shampoo"; [NOTES] "Grafting corrects Shampoo's eigenvalues").  Per
+ * parameter (or per block with graft_blockwise): D_g = (||Delta||_F /
+ * ||D||_F) D (0 when D = 0) with Delta = G (SGD, MOMENTUM) or the
+ * bias-corrected Adam direction; SGD/ADAM: W -= lr D_g; MOMENTUM:
+ * M = momentum M + D_g, W -= lr M; NONE: W -= lr D.  Norms are reduced in a
+ * fixed order, so two identical calls give identical bits. */
+shampoo_status shampoo_step(const shampoo_step_args* args, hipStream_t stream);
+
+/* Synchronises `stream`, then returns E_NONFINITE if any of the n flags is
+ * set, else OK. */
+shampoo_status shampoo_check_flags(const int32_t* flags_dev, int64_t n, hipStream_t stream);
+
+/* Optional timing of the batched products (for benchmarks).  While enabled
+ * with capacity > 0, shampoo_inverse_root records a HIP event pair on its
+ * stream around each of its batched-product launches, up to `capacity`
+ * launches; capacity 0 disables and releases the events (host objects, no
+ * device memory).  Process-wide state on the current device; not thread-safe.
+ * shampoo_timing_read waits for the recorded events and writes the duration
+ * in milliseconds of each recorded launch (at most `capacity` of them) to
+ * `ms`, their number to *count, and restarts the recording. */
+shampoo_status shampoo_timing_enable(int32_t capacity);
+shampoo_status shampoo_timing_read(float* ms, int32_t capacity, int32_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHAMPOO_H */

@@ -1,0 +1,374 @@
+// Batched square GEMM on CDNA4 matrix cores (gfx950), with the fused
+// epilogues the inverse-root chains need.
+//
+// For every matrix b of a batch of n x n matrices:
+//     acc  = A_b * op(B_b)
+//     C_b  = alpha * acc + beta * D_b + gamma * I   (D optional)
+//     C2_b = alpha2 * C_b + gamma2 * I              (second output, optional)
+// op(B) = B^T when B is read row-wise ("NT", B_KN = false) and op(B) = B when
+// B is read k-major ("NN", B_KN = true).
+//
+// NT serves the products of symmetric matrices (coupled Newton, Clenshaw,
+// statistics G G^T): there A * B = A * B^T.  `sym` mode computes only the
+// upper-triangular tiles of such a product and writes each twice (in place
+// and mirrored), which keeps the iterate exactly symmetric and skips the
+// lower tiles.  NN serves Newton-DB, whose coupled iterates must be
+// multiplied as they are, in the order of the recurrence: symmetrising its
+// products changes the first-order error map of the iteration from an
+// idempotent one into one with eigenvalue 1 - (r + 2 + 1/r)/4 for an
+// eigenvalue pair of ratio r^2, unstable once r^2 exceeds about 34.
+//
+// Layout: all operands row-major, side n a multiple of the tile, batch stride
+// `stride` elements.  LDS holds, for both operands, tile rows (m for A, j for
+// B) of 128 bytes of k plus 16 bytes of padding: a row pitch of 9 16-byte
+// bank groups, so the 16 lanes of a b128 fragment read hit distinct banks.
+// NT operands are copied row by row (16-byte global loads, coalesced per
+// 128-byte row segment); an NN B operand is loaded as VE x VE element blocks
+// (VE = elements per 16 bytes) along its rows and transposed in registers.
+//
+// Matrix-core mapping (16x16 family):
+//   f32: v_mfma_f32_16x16x4_f32     (lane supplies 1 value of k per operand)
+//   f64: v_mfma_f64_16x16x4_f64
+//   f16: v_mfma_f32_16x16x32_f16    (8 values; f32 operands rounded to half)
+//   bf16: v_mfma_f32_16x16x32_bf16
+// Lane l supplies row (l % 16) of its A fragment and column (l % 16) of its
+// B fragment for k-group (l / 16).  Result element v of lane l is column
+// l % 16 and row 4 (l / 16) + v (f32, f16, bf16) or row (l / 16) + 4 v (f64).
+// Logical k is assigned to (group, step) by a permutation applied
+// identically to A and B, chosen so that each lane reads 16 contiguous bytes
+// of its LDS row per fragment read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace shampoo {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef double doublex2 __attribute__((ext_vector_type(2)));
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum class Mma { F32, F64, F16, BF16 };
+
+template <Mma M> struct MmaTraits;
+
+template <> struct MmaTraits<Mma::F32> {
+  using lds_t = float;
+  using acc_t = float;
+  using accv_t = floatx4;
+  using frag_t = floatx4;  // one 16-byte LDS read
+  static constexpr int VE = 4;   // elements per 16 bytes
+  static constexpr int KV = 1;   // elements per lane per instruction
+  static constexpr int BK = 32;  // k per stage (128 bytes of LDS row)
+  static __device__ __forceinline__ int row(int grp, int v) { return 4 * grp + v; }
+  static __device__ __forceinline__ accv_t mma(const frag_t& a, const frag_t& b, int u, accv_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], c, 0, 0, 0);
+  }
+};
+
+template <> struct MmaTraits<Mma::F64> {
+  using lds_t = double;
+  using acc_t = double;
+  using accv_t = doublex4;
+  using frag_t = doublex2;
+  static constexpr int VE = 2;
+  static constexpr int KV = 1;
+  static constexpr int BK = 16;
+  static __device__ __forceinline__ int row(int grp, int v) { return grp + 4 * v; }
+  static __device__ __forceinline__ accv_t mma(const frag_t& a, const frag_t& b, int u, accv_t c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a[u], b[u], c, 0, 0, 0);
+  }
+};
+
+template <> struct MmaTraits<Mma::F16> {
+  using lds_t = _Float16;
+  using acc_t = float;
+  using accv_t = floatx4;
+  using frag_t = halfx8;
+  static constexpr int VE = 8;
+  static constexpr int KV = 8;
+  static constexpr int BK = 64;
+  static __device__ __forceinline__ int row(int grp, int v) { return 4 * grp + v; }
+  static __device__ __forceinline__ accv_t mma(const frag_t& a, const frag_t& b, int, accv_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct MmaTraits<Mma::BF16> {
+  using lds_t = __bf16;
+  using acc_t = float;
+  using accv_t = floatx4;
+  using frag_t = bf16x8;
+  static constexpr int VE = 8;
+  static constexpr int KV = 8;
+  static constexpr int BK = 64;
+  static __device__ __forceinline__ int row(int grp, int v) { return 4 * grp + v; }
+  static __device__ __forceinline__ accv_t mma(const frag_t& a, const frag_t& b, int, accv_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// One 16-byte LDS chunk (VE elements of the LDS type) staged through
+// registers from VE consecutive elements of the operand's global type.
+// ---------------------------------------------------------------------------
+template <typename TG, typename TL, int VE> struct Chunk;
+
+template <> struct Chunk<float, float, 4> {  // f32 -> f32
+  u32x4 w;
+  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void store(unsigned char* d) const { *reinterpret_cast<u32x4*>(d) = w; }
+  __device__ __forceinline__ float get(int e) const { return __uint_as_float(w[e]); }
+};
+
+template <> struct Chunk<__bf16, float, 4> {  // bf16 -> f32 (exact)
+  u32x2 w;
+  __device__ __forceinline__ void load(const __bf16* p) { w = *reinterpret_cast<const u32x2*>(p); }
+  __device__ __forceinline__ float get(int e) const {
+    const uint32_t x = w[e >> 1];
+    return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+  }
+  __device__ __forceinline__ void store(unsigned char* d) const {
+    u32x4 o;
+    o[0] = w[0] << 16;
+    o[1] = w[0] & 0xffff0000u;
+    o[2] = w[1] << 16;
+    o[3] = w[1] & 0xffff0000u;
+    *reinterpret_cast<u32x4*>(d) = o;
+  }
+};
+
+template <> struct Chunk<double, double, 2> {  // f64 -> f64
+  doublex2 w;
+  __device__ __forceinline__ void load(const double* p) { w = *reinterpret_cast<const doublex2*>(p); }
+  __device__ __forceinline__ void store(unsigned char* d) const { *reinterpret_cast<doublex2*>(d) = w; }
+  __device__ __forceinline__ double get(int e) const { return w[e]; }
+};
+
+template <> struct Chunk<float, _Float16, 8> {  // f32 -> f16, round to nearest even
+  floatx4 lo, hi;
+  __device__ __forceinline__ void load(const float* p) {
+    lo = *reinterpret_cast<const floatx4*>(p);
+    hi = *reinterpret_cast<const floatx4*>(p + 4);
+  }
+  __device__ __forceinline__ _Float16 get(int e) const { return (_Float16)(e < 4 ? lo[e] : hi[e - 4]); }
+  __device__ __forceinline__ void store(unsigned char* d) const {
+    halfx8 h;
+    h[0] = (_Float16)lo[0]; h[1] = (_Float16)lo[1]; h[2] = (_Float16)lo[2]; h[3] = (_Float16)lo[3];
+    h[4] = (_Float16)hi[0]; h[5] = (_Float16)hi[1]; h[6] = (_Float16)hi[2]; h[7] = (_Float16)hi[3];
+    *reinterpret_cast<halfx8*>(d) = h;
+  }
+};
+
+template <> struct Chunk<__bf16, __bf16, 8> {  // bf16 -> bf16
+  bf16x8 w;
+  __device__ __forceinline__ void load(const __bf16* p) { w = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void store(unsigned char* d) const { *reinterpret_cast<bf16x8*>(d) = w; }
+  __device__ __forceinline__ __bf16 get(int e) const { return w[e]; }
+};
+
+// VE x VE block of a k-major operand: rows k..k+VE-1, columns j..j+VE-1,
+// written transposed into LDS rows j..j+VE-1 at k.
+template <typename TG, typename TL, int VE> struct BlockKN {
+  Chunk<TG, TL, VE> r[VE];
+  __device__ __forceinline__ void load(const TG* p, int ld) {
+#pragma unroll
+    for (int i = 0; i < VE; ++i) r[i].load(p + (int64_t)i * ld);
+  }
+  __device__ __forceinline__ void store_t(unsigned char* d, int rowb) const {
+#pragma unroll
+    for (int c = 0; c < VE; ++c) {
+      TL t[VE];
+#pragma unroll
+      for (int i = 0; i < VE; ++i) t[i] = (TL)r[i].get(c);
+      *reinterpret_cast<u32x4*>(d + c * rowb) = *reinterpret_cast<const u32x4*>(t);
+    }
+  }
+};
+
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  const void* D;   // may be null (then beta is ignored)
+  void* C;
+  void* C2;        // may be null
+  int n;           // side of every matrix, a multiple of the tile
+  int tiles;       // tiles per matrix (n/T)^2, or (n/T)(n/T + 1)/2 in sym mode
+  int nt;          // n / T
+  int sym;         // compute upper tiles only and mirror (NT only)
+  int transC;      // write C transposed (no D, no C2, no sym)
+  int64_t stride;  // elements between consecutive matrices
+  int64_t total;   // batch * tiles (= grid size)
+  double alpha, beta, gamma, alpha2, gamma2;
+};
+
+// Workgroup id -> linear work index so that the consecutive work items of one
+// XCD are contiguous: the hardware deals workgroups to the 8 XCDs round-robin,
+// and each XCD has its own L2, so all tiles of a matrix should share an XCD.
+__device__ __forceinline__ int64_t xcd_remap(int64_t w, int64_t total) {
+  const int64_t q = total >> 3, r = total & 7;
+  const int64_t xcd = w & 7, local = w >> 3;
+  return xcd * q + (xcd < r ? xcd : r) + local;
+}
+
+template <typename TC> __device__ __forceinline__ void put(TC* p, double v);
+template <> __device__ __forceinline__ void put<float>(float* p, double v) { *p = (float)v; }
+template <> __device__ __forceinline__ void put<double>(double* p, double v) { *p = v; }
+
+template <Mma MM, int T, bool BKN, typename TA, typename TB, typename TC>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+  using Tr = MmaTraits<MM>;
+  using L = typename Tr::lds_t;
+  using acc_t = typename Tr::acc_t;
+  using accv_t = typename Tr::accv_t;
+  using frag_t = typename Tr::frag_t;
+  constexpr int BK = Tr::BK, VE = Tr::VE, KV = Tr::KV;
+  constexpr int ROWB = BK * (int)sizeof(L) + 16;  // 144 bytes
+  constexpr int WT = T / 2;                       // wave tile (2 x 2 waves)
+  constexpr int NB = WT / 16;                     // 16x16 blocks per wave side
+  constexpr int CH = T * 8 / 256;                 // 16-byte chunks per thread per row-wise operand
+  constexpr int NREAD = BK / (4 * VE);            // 16-byte fragment reads per stage
+  constexpr int KNB = (BK / VE) * (T / VE);       // VE x VE blocks of a k-major B tile
+  constexpr int KNQ = (KNB + 255) / 256;          // ... per thread
+  static_assert(BK * sizeof(L) == 128, "LDS row must hold 128 bytes of k");
+
+  __shared__ __attribute__((aligned(16))) unsigned char sA[T * ROWB];
+  __shared__ __attribute__((aligned(16))) unsigned char sB[T * ROWB];
+
+  const int64_t w = xcd_remap((int64_t)blockIdx.x, g.total);
+  const int64_t mat = w / g.tiles;
+  int t = (int)(w - mat * g.tiles);
+  int ti, tj;
+  if (g.sym) {
+    ti = 0;
+    int rowlen = g.nt;
+    while (t >= rowlen) { t -= rowlen; ++ti; --rowlen; }
+    tj = ti + t;
+  } else {
+    ti = t / g.nt;
+    tj = t - ti * g.nt;
+  }
+  const int n = g.n;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int i16 = lane & 15, grp = lane >> 4;
+
+  const TA* Ab = reinterpret_cast<const TA*>(g.A) + mat * g.stride + (int64_t)ti * T * n;
+  // NT: rows tj*T.. of B; NN: columns tj*T.. of B
+  const TB* Bb = reinterpret_cast<const TB*>(g.B) + mat * g.stride + (BKN ? (int64_t)tj * T : (int64_t)tj * T * n);
+
+  Chunk<TA, L, VE> ra[CH];
+  Chunk<TB, L, VE> rb[BKN ? 1 : CH];
+  BlockKN<TB, L, VE> kb[BKN ? KNQ : 1];
+
+  accv_t acc[NB][NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = (acc_t)0;
+
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int c = tid + 256 * q, row = c >> 3, cc = c & 7;
+      ra[q].load(Ab + (int64_t)row * n + k0 + cc * VE);
+      if constexpr (!BKN) rb[q].load(Bb + (int64_t)row * n + k0 + cc * VE);
+    }
+    if constexpr (BKN) {
+#pragma unroll
+      for (int q = 0; q < KNQ; ++q) {
+        const int blk = tid + 256 * q;
+        if (KNB % 256 == 0 || blk < KNB) {
+          const int jb = blk % (T / VE), kq = blk / (T / VE);
+          kb[q].load(Bb + (int64_t)(k0 + kq * VE) * n + jb * VE, n);
+        }
+      }
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int c = tid + 256 * q, row = c >> 3, cc = c & 7;
+      ra[q].store(sA + row * ROWB + cc * 16);
+      if constexpr (!BKN) rb[q].store(sB + row * ROWB + cc * 16);
+    }
+    if constexpr (BKN) {
+#pragma unroll
+      for (int q = 0; q < KNQ; ++q) {
+        const int blk = tid + 256 * q;
+        if (KNB % 256 == 0 || blk < KNB) {
+          const int jb = blk % (T / VE), kq = blk / (T / VE);
+          kb[q].store_t(sB + (jb * VE) * ROWB + kq * VE * (int)sizeof(L), ROWB);
+        }
+      }
+    }
+  };
+
+  gload(0);
+  for (int k0 = 0; k0 < n; k0 += BK) {
+    __syncthreads();
+    sstore();
+    __syncthreads();
+    if (k0 + BK < n) gload(k0 + BK);
+#pragma unroll
+    for (int r = 0; r < NREAD; ++r) {
+      frag_t a[NB], b[NB];
+      const int off = (r * 4 * VE + grp * VE) * (int)sizeof(L);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        a[i] = *reinterpret_cast<const frag_t*>(sA + (wm * WT + i * 16 + i16) * ROWB + off);
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        b[j] = *reinterpret_cast<const frag_t*>(sB + (wn * WT + j * 16 + i16) * ROWB + off);
+#pragma unroll
+      for (int u = 0; u < VE / KV; ++u)
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = Tr::mma(a[i], b[j], u, acc[i][j]);
+    }
+  }
+
+  // Epilogue.
+  TC* C = reinterpret_cast<TC*>(g.C) + mat * g.stride;
+  TC* C2 = g.C2 ? reinterpret_cast<TC*>(g.C2) + mat * g.stride : nullptr;
+  const TC* D = g.D ? reinterpret_cast<const TC*>(g.D) + mat * g.stride : nullptr;
+  const bool diag = g.sym && ti == tj;
+  const bool mirror = g.sym != 0;
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = wm * WT + i * 16 + Tr::row(grp, v);
+        const int col = wn * WT + j * 16 + i16;
+        if (diag && row > col) continue;
+        const int R = ti * T + row, Cc = tj * T + col;
+        double x = g.alpha * (double)acc[i][j][v];
+        if (D) x += g.beta * (double)D[(int64_t)R * n + Cc];
+        if (R == Cc) x += g.gamma;
+        if (g.transC) {
+          put<TC>(C + (int64_t)Cc * n + R, x);
+          continue;
+        }
+        put<TC>(C + (int64_t)R * n + Cc, x);
+        double x2 = 0.0;
+        if (C2) {
+          x2 = g.alpha2 * x + (R == Cc ? g.gamma2 : 0.0);
+          put<TC>(C2 + (int64_t)R * n + Cc, x2);
+        }
+        if (mirror && R != Cc) {
+          put<TC>(C + (int64_t)Cc * n + R, x);
+          if (C2) put<TC>(C2 + (int64_t)Cc * n + R, x2);
+        }
+      }
+}
+
+}  // namespace shampoo

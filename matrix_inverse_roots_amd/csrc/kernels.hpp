@@ -1,0 +1,462 @@
+// Bandwidth-bound kernels of the preconditioner step (gfx950, wave64).
+//
+// pack/unpack   parameter layout <-> zero-padded [nblk, B, B] block stacks
+//               ([DASH] "4. Blocking Strategy"), with an LDS tile transpose
+//               for the transposed stack the right-factor products read.
+// frob_norm     s = ||A + eps I||_F over each matrix's valid region
+//               ([DASH] "3. Inverse Root Methods", Matrix scaling).
+// prep          A_s = (A + eps I)/s with the padding set to the identity (or
+//               to zero for the power iteration), and up to three affine
+//               images alpha A_s + gamma I that seed the solver chains.
+// power_iter    half-precision multi-start power iteration on the Frobenius
+//               scaled matrix, largest Rayleigh quotient ([DASH] "3. Inverse
+//               Root Methods", Power-Iteration).
+// finalize      out = X s^(-1/p) on the valid region, 0 on the padding,
+//               non-finite flags.
+// graft_*       layer-wise (or block-wise) grafting norms and the weight
+//               update ([3DS] "Hyperparameters"; [DASH] "2. Preliminaries on
+//               Shampoo").
+//
+// All reductions run in a fixed order inside one workgroup (no float
+// atomics), so repeated calls give identical bits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm.hpp"
+#include "shampoo.h"
+
+namespace shampoo {
+
+// ---------------------------------------------------------------------------
+// reductions
+// ---------------------------------------------------------------------------
+template <typename T> __device__ __forceinline__ T wave_sum(T x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Sum over a 256-thread workgroup; every thread gets the result.
+template <typename T> __device__ __forceinline__ T block_sum256(T x, T* red /* [4] */) {
+  x = wave_sum(x);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// ---------------------------------------------------------------------------
+// pack / unpack: 64 x 64 element tiles, 256 threads
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ const void* desc_data(const shampoo_matrix& m) { return m.data; }
+__device__ __forceinline__ const void* desc_data(const shampoo_param& p) { return p.g; }
+
+// E: raw element type of the right width (the copy is bit-exact).
+// Desc: shampoo_matrix (data) or shampoo_param (gradient g).
+template <typename E, typename Desc>
+__global__ __launch_bounds__(256) void pack_kernel(const Desc* __restrict__ descs, int nparams,
+                                                   const shampoo_block* __restrict__ table, int B,
+                                                   int tiles_per_side, E* __restrict__ stack,
+                                                   E* __restrict__ stack_t) {
+  __shared__ E tile[64][65];
+  const int64_t b = blockIdx.y;
+  const int tt = blockIdx.x;
+  const int tr = tt / tiles_per_side, tc = tt - tr * tiles_per_side;
+  const shampoo_block blk = table[b];
+  if (blk.param < 0 || blk.param >= nparams) return;  // uniform per workgroup
+  const Desc m = descs[blk.param];
+  const E* src = reinterpret_cast<const E*>(desc_data(m));
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int64_t BB = (int64_t)B * B;
+#pragma unroll 4
+  for (int rr = ty; rr < 64; rr += 4) {
+    const int r = tr * 64 + rr, c = tc * 64 + tx;
+    E v = E(0);
+    if (r < blk.rows && c < blk.cols) v = src[(int64_t)(blk.row0 + r) * m.ld + blk.col0 + c];
+    if (r < B && c < B) stack[b * BB + (int64_t)r * B + c] = v;
+    tile[rr][tx] = v;
+  }
+  if (!stack_t) return;
+  __syncthreads();
+#pragma unroll 4
+  for (int cc = ty; cc < 64; cc += 4) {
+    const int c = tc * 64 + cc, r = tr * 64 + tx;
+    if (r < B && c < B) stack_t[b * BB + (int64_t)c * B + r] = tile[tx][cc];
+  }
+}
+
+__global__ __launch_bounds__(256) void unpack_kernel(const float* __restrict__ stack,
+                                                     const shampoo_block* __restrict__ table, int B,
+                                                     int tiles_per_side,
+                                                     const shampoo_matrix* __restrict__ mats, int nparams) {
+  const int64_t b = blockIdx.y;
+  const int tt = blockIdx.x;
+  const int tr = tt / tiles_per_side, tc = tt - tr * tiles_per_side;
+  const shampoo_block blk = table[b];
+  if (blk.param < 0 || blk.param >= nparams) return;
+  const shampoo_matrix m = mats[blk.param];
+  float* dst = reinterpret_cast<float*>(m.data);
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int rr = ty; rr < 64; rr += 4) {
+    const int r = tr * 64 + rr, c = tc * 64 + tx;
+    if (r < blk.rows && c < blk.cols)
+      dst[(int64_t)(blk.row0 + r) * m.ld + blk.col0 + c] = stack[b * (int64_t)B * B + (int64_t)r * B + c];
+  }
+}
+
+__global__ void valid_from_table_kernel(const shampoo_block* __restrict__ table, int64_t nblk,
+                                        int32_t* __restrict__ valid) {
+  const int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (b >= nblk) return;
+  valid[b] = table[b].rows;
+  valid[nblk + b] = table[b].cols;
+}
+
+// ---------------------------------------------------------------------------
+// Frobenius norm of A + eps I over the valid region; one workgroup per matrix
+// ---------------------------------------------------------------------------
+template <typename TI>
+__global__ __launch_bounds__(256) void frob_norm_kernel(const TI* __restrict__ in, int B,
+                                                        const int32_t* __restrict__ valid, double eps,
+                                                        double* __restrict__ s_out) {
+  __shared__ double red[4];
+  const int64_t b = blockIdx.x;
+  const int v = valid ? min(max(valid[b], 0), B) : B;
+  const TI* A = in + b * (int64_t)B * B;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double acc = 0.0;
+  for (int r = wave; r < v; r += 4) {
+    const TI* row = A + (int64_t)r * B;
+    for (int c = lane; c < v; c += 64) {
+      double x = (double)row[c];
+      if (c == r) x += eps;
+      acc += x * x;
+    }
+  }
+  acc = block_sum256(acc, red);
+  if (threadIdx.x == 0) s_out[b] = sqrt(acc);
+}
+
+// ---------------------------------------------------------------------------
+// prep: a = (A + eps I)/s on the valid region, delta_ij * pad_diag elsewhere;
+// out_q = alpha_q a + gamma_q I for up to three outputs.
+// ---------------------------------------------------------------------------
+struct PrepOut {
+  void* p;
+  double alpha, gamma;
+};
+
+template <typename TI, typename TS>
+__global__ __launch_bounds__(256) void prep_kernel(const TI* __restrict__ in, int B, int64_t nmat,
+                                                   const int32_t* __restrict__ valid, double eps,
+                                                   const double* __restrict__ s, double pad_diag,
+                                                   PrepOut o0, PrepOut o1, PrepOut o2) {
+  const int64_t BB = (int64_t)B * B;
+  const int64_t idx = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) * 4;
+  if (idx >= nmat * BB) return;
+  const int64_t b = idx / BB;
+  const int64_t e = idx - b * BB;
+  const int r = (int)(e / B);
+  const int c0 = (int)(e - (int64_t)r * B);
+  const int v = valid ? min(max(valid[b], 0), B) : B;
+  const double sb = s[b];
+  const double inv = (sb > 0.0 && sb < 1.0e300) ? 1.0 / sb : 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = c0 + q;
+    double a;
+    if (r < v && c < v) {
+      a = (double)in[idx + q];
+      if (r == c) a += eps;
+      a *= inv;
+    } else {
+      a = (r == c) ? pad_diag : 0.0;
+    }
+    const double d = (r == c) ? 1.0 : 0.0;
+    if (o0.p) reinterpret_cast<TS*>(o0.p)[idx + q] = (TS)(o0.alpha * a + o0.gamma * d);
+    if (o1.p) reinterpret_cast<TS*>(o1.p)[idx + q] = (TS)(o1.alpha * a + o1.gamma * d);
+    if (o2.p) reinterpret_cast<TS*>(o2.p)[idx + q] = (TS)(o2.alpha * a + o2.gamma * d);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Multi-start power iteration, one workgroup (4 waves) per matrix.
+// Af: Frobenius-scaled matrices (padding zero), storage type TS.
+// Each of `iters` rounds normalises the k vectors and multiplies by Af with
+// half-precision operands and float32 accumulation (MFMA 16x16x32 f16); a
+// final product gives the Rayleigh quotients of the last normalised vectors.
+// s_out[b] = sf[b] * max_j rq_j (lowest j on ties).
+// Dynamic LDS: Vh half [k16][B + 8], Wf float [k16][B + 4], 2 * k16 floats.
+// ---------------------------------------------------------------------------
+template <typename TS> struct HalfLoad8;
+template <> struct HalfLoad8<float> {
+  static __device__ __forceinline__ halfx8 load(const float* p) {
+    const floatx4 lo = *reinterpret_cast<const floatx4*>(p);
+    const floatx4 hi = *reinterpret_cast<const floatx4*>(p + 4);
+    halfx8 h;
+    h[0] = (_Float16)lo[0]; h[1] = (_Float16)lo[1]; h[2] = (_Float16)lo[2]; h[3] = (_Float16)lo[3];
+    h[4] = (_Float16)hi[0]; h[5] = (_Float16)hi[1]; h[6] = (_Float16)hi[2]; h[7] = (_Float16)hi[3];
+    return h;
+  }
+};
+template <> struct HalfLoad8<double> {
+  static __device__ __forceinline__ halfx8 load(const double* p) {
+    halfx8 h;
+#pragma unroll
+    for (int q = 0; q < 8; q += 2) {
+      const doublex2 d = *reinterpret_cast<const doublex2*>(p + q);
+      // double -> float -> half is a double rounding; the operands are
+      // Frobenius-scaled values whose float32 rounding error (2^-24
+      // relative) sits far below half precision's (2^-11).
+      h[q] = (_Float16)(float)d[0];
+      h[q + 1] = (_Float16)(float)d[1];
+    }
+    return h;
+  }
+};
+
+template <typename TS, int NVB>
+__global__ __launch_bounds__(256) void power_iter_kernel(const TS* __restrict__ Af, int B, int k,
+                                                         int iters, const float* __restrict__ v0,
+                                                         const double* __restrict__ sf,
+                                                         double* __restrict__ s_out,
+                                                         int32_t* __restrict__ flags) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int k16 = NVB * 16;
+  const int VP = B + 8;  // half pitch (elements)
+  const int WP = B + 4;  // float pitch
+  _Float16* Vh = reinterpret_cast<_Float16*>(smem);
+  float* Wf = reinterpret_cast<float*>(smem + (size_t)k16 * VP * 2);
+  float* rq = Wf + (size_t)k16 * WP;
+  const int64_t b = blockIdx.x;
+  const TS* A = Af + b * (int64_t)B * B;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, grp = lane >> 4;
+
+  for (int e = tid; e < k16 * B; e += 256) {
+    const int vv = e / B, i = e - vv * B;
+    Wf[vv * WP + i] = vv < k ? v0[(int64_t)vv * B + i] : 0.0f;
+  }
+
+  for (int it = 0; it <= iters; ++it) {
+    __syncthreads();
+    // normalise the columns of W into half-precision V
+    for (int vv = wave; vv < k16; vv += 4) {
+      float ss = 0.0f;
+      for (int i = lane; i < B; i += 64) {
+        const float x = Wf[vv * WP + i];
+        ss += x * x;
+      }
+      ss = wave_sum(ss);
+      const float nrm = sqrtf(ss);
+      const float inv = nrm > 0.0f ? 1.0f / nrm : 1.0f;
+      for (int i = lane; i < B; i += 64) Vh[vv * VP + i] = (_Float16)(Wf[vv * WP + i] * inv);
+    }
+    __syncthreads();
+    // W = A V
+    for (int rb = wave; rb < B / 16; rb += 4) {
+      floatx4 acc[NVB];
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) acc[vb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const TS* arow = A + (int64_t)(rb * 16 + i16) * B + 8 * grp;
+#pragma unroll 4
+      for (int kk = 0; kk < B; kk += 32) {
+        const halfx8 a = HalfLoad8<TS>::load(arow + kk);
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) {
+          const halfx8 bv = *reinterpret_cast<const halfx8*>(Vh + (vb * 16 + i16) * VP + kk + 8 * grp);
+          acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv, acc[vb], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Wf[(vb * 16 + i16) * WP + rb * 16 + 4 * grp + v] = acc[vb][v];
+    }
+  }
+  __syncthreads();
+  // Rayleigh quotients of the last normalised (half) vectors
+  for (int vv = wave; vv < k16; vv += 4) {
+    float num = 0.0f, den = 0.0f;
+    for (int i = lane; i < B; i += 64) {
+      const float x = (float)Vh[vv * VP + i];
+      num += x * Wf[vv * WP + i];
+      den += x * x;
+    }
+    num = wave_sum(num);
+    den = wave_sum(den);
+    if (lane == 0) rq[vv] = den > 0.0f ? num / den : 0.0f;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float best = rq[0];
+    for (int vv = 1; vv < k; ++vv)
+      if (rq[vv] > best) best = rq[vv];
+    const double sfb = sf[b];
+    const bool ok = best > 0.0f && best < 3.0e38f;
+    s_out[b] = ok ? sfb * (double)best : sfb;
+    if (!ok && flags) atomicOr(flags + b, SHAMPOO_FLAG_PI_FALLBACK);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// finalize: out = X s^(-1/p) on the valid region, 0 elsewhere
+// ---------------------------------------------------------------------------
+template <typename TS, typename TO>
+__global__ __launch_bounds__(256) void finalize_kernel(const TS* __restrict__ X, TO* __restrict__ out, int B,
+                                                       int64_t nmat, const int32_t* __restrict__ valid,
+                                                       const double* __restrict__ s, double inv_p,
+                                                       int sym_out, float* __restrict__ scale_out,
+                                                       int32_t* __restrict__ flags) {
+  const int64_t BB = (int64_t)B * B;
+  const int64_t idx = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) * 4;
+  if (idx >= nmat * BB) return;
+  const int64_t b = idx / BB;
+  const int64_t e = idx - b * BB;
+  const int r = (int)(e / B);
+  const int c0 = (int)(e - (int64_t)r * B);
+  const int v = valid ? min(max(valid[b], 0), B) : B;
+  const double sb = s[b];
+  const bool zero = !(sb > 0.0 && sb < 1.0e300);
+  const double f = zero ? 0.0 : pow(sb, -inv_p);
+  bool bad = false;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = c0 + q;
+    double x = 0.0;
+    if (r < v && c < v && !zero) {
+      x = (double)X[idx + q];
+      if (sym_out) x = 0.5 * (x + (double)X[b * BB + (int64_t)c * B + r]);
+      x *= f;
+      if (!isfinite(x)) bad = true;
+    }
+    out[idx + q] = (TO)x;
+  }
+  if (flags) {
+    if (bad) atomicOr(flags + b, SHAMPOO_FLAG_NONFINITE);
+    if (zero && e == 0) atomicOr(flags + b, SHAMPOO_FLAG_ZERO_SCALE);
+  }
+  if (scale_out && e == 0) scale_out[b] = (float)sb;
+}
+
+// ---------------------------------------------------------------------------
+// grafting.  Work item = (block, chunk of GRAFT_ROWS rows of the block).
+// ---------------------------------------------------------------------------
+constexpr int GRAFT_ROWS = 16;
+
+template <typename TG> __device__ __forceinline__ float gval(const void* g, int64_t i);
+template <> __device__ __forceinline__ float gval<float>(const void* g, int64_t i) {
+  return reinterpret_cast<const float*>(g)[i];
+}
+template <> __device__ __forceinline__ float gval<__bf16>(const void* g, int64_t i) {
+  const uint16_t u = reinterpret_cast<const uint16_t*>(g)[i];
+  return __uint_as_float((uint32_t)u << 16);
+}
+
+struct GraftArgs {
+  const shampoo_param* params;
+  int nparams;
+  const shampoo_block* table;
+  const float* dstack;
+  int B;
+  int nchunk;        // chunks per block
+  int graft;         // shampoo_graft
+  float lr, momentum, beta1, beta2, eps;
+  float bc1, bc2;    // 1 - beta1^t, 1 - beta2^t
+  double* partials;  // [nblk][nchunk][2]: sum D^2, sum Delta^2
+  float* scales;     // [nblk]: per-block D_g / D factor
+};
+
+template <typename TG>
+__global__ __launch_bounds__(256) void graft_partials_kernel(GraftArgs a) {
+  __shared__ double red[4];
+  const int64_t b = blockIdx.y;
+  const int ch = blockIdx.x;
+  const shampoo_block blk = a.table[b];
+  if (blk.param < 0 || blk.param >= a.nparams) return;
+  const shampoo_param P = a.params[blk.param];
+  const float* D = a.dstack + b * (int64_t)a.B * a.B;
+  double sd = 0.0, sg = 0.0;
+  const int r0 = ch * GRAFT_ROWS;
+  const int r1 = min(blk.rows, r0 + GRAFT_ROWS);
+  for (int r = r0; r < r1; ++r) {
+    const int64_t prow = (int64_t)(blk.row0 + r) * P.ld + blk.col0;
+    for (int c = threadIdx.x; c < blk.cols; c += 256) {
+      const float d = D[(int64_t)r * a.B + c];
+      sd += (double)d * d;
+      const float g = gval<TG>(P.g, prow + c);
+      float delta = g;
+      if (a.graft == SHAMPOO_GRAFT_ADAM && P.m && P.v) {
+        const float m = a.beta1 * P.m[prow + c] + (1.0f - a.beta1) * g;
+        const float v = a.beta2 * P.v[prow + c] + (1.0f - a.beta2) * g * g;
+        P.m[prow + c] = m;
+        P.v[prow + c] = v;
+        delta = (m / a.bc1) / (sqrtf(v / a.bc2) + a.eps);
+      }
+      sg += (double)delta * delta;
+    }
+  }
+  sd = block_sum256(sd, red);
+  sg = block_sum256(sg, red);
+  if (threadIdx.x == 0) {
+    a.partials[(b * a.nchunk + ch) * 2 + 0] = sd;
+    a.partials[(b * a.nchunk + ch) * 2 + 1] = sg;
+  }
+}
+
+// One thread per block: the scale of its norm group (its parameter, or the
+// block itself), reduced in a fixed order over the group's blocks and chunks.
+__global__ void graft_scale_kernel(GraftArgs a, int64_t nblk, int blockwise) {
+  const int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (b >= nblk) return;
+  int64_t first = b, count = 1;
+  if (!blockwise) {
+    const shampoo_block blk = a.table[b];
+    const shampoo_param P = a.params[blk.param];
+    first = P.first_block;
+    const int64_t bs = blk.B;  // planning block size (the stack side a.B may be larger)
+    count = ((P.rows + bs - 1) / bs) * ((P.cols + bs - 1) / bs);
+    if (first < 0) first = 0;
+    if (first + count > nblk) count = nblk - first;
+  }
+  double sd = 0.0, sg = 0.0;
+  for (int64_t q = first; q < first + count; ++q)
+    for (int ch = 0; ch < a.nchunk; ++ch) {
+      sd += a.partials[(q * a.nchunk + ch) * 2 + 0];
+      sg += a.partials[(q * a.nchunk + ch) * 2 + 1];
+    }
+  float sc;
+  if (a.graft == SHAMPOO_GRAFT_NONE) sc = 1.0f;
+  else sc = sd > 0.0 ? (float)(sqrt(sg) / sqrt(sd)) : 0.0f;
+  a.scales[b] = sc;
+}
+
+__global__ __launch_bounds__(256) void graft_update_kernel(GraftArgs a) {
+  const int64_t b = blockIdx.y;
+  const int ch = blockIdx.x;
+  const shampoo_block blk = a.table[b];
+  if (blk.param < 0 || blk.param >= a.nparams) return;
+  const shampoo_param P = a.params[blk.param];
+  const float* D = a.dstack + b * (int64_t)a.B * a.B;
+  const float sc = a.scales[b];
+  const int r0 = ch * GRAFT_ROWS;
+  const int r1 = min(blk.rows, r0 + GRAFT_ROWS);
+  for (int r = r0; r < r1; ++r) {
+    const int64_t prow = (int64_t)(blk.row0 + r) * P.ld + blk.col0;
+    for (int c = threadIdx.x; c < blk.cols; c += 256) {
+      const float dg = sc * D[(int64_t)r * a.B + c];
+      if (a.graft == SHAMPOO_GRAFT_MOMENTUM && P.m) {
+        const float m = a.momentum * P.m[prow + c] + dg;
+        P.m[prow + c] = m;
+        P.w[prow + c] -= a.lr * m;
+      } else {
+        P.w[prow + c] -= a.lr * dg;
+      }
+    }
+  }
+}
+
+}  // namespace shampoo

@@ -1,0 +1,913 @@
+// C ABI of the batched block preconditioner step (see include/shampoo.h).
+//
+// Host side: argument validation (before any launch), workspace carving,
+// the solver-chain planner and kernel launches.  No entry point allocates
+// device memory; every launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <type_traits>
+#include <vector>
+
+#include "gemm.hpp"
+#include "kernels.hpp"
+#include "shampoo.h"
+
+using namespace shampoo;
+
+namespace {
+
+thread_local std::string g_err;
+
+shampoo_status fail(shampoo_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+#define HIP_TRY(expr)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(SHAMPOO_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+#define LAUNCH_CHECK(what)                                                             \
+  do {                                                                                 \
+    hipError_t e_ = hipGetLastError();                                                 \
+    if (e_ != hipSuccess) return fail(SHAMPOO_E_HIP, "%s launch: %s", what, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+size_t dtype_size(int dt) {
+  switch (dt) {
+    case SHAMPOO_F32: return 4;
+    case SHAMPOO_F16: return 2;
+    case SHAMPOO_BF16: return 2;
+    case SHAMPOO_F64: return 8;
+    default: return 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM dispatch
+// ---------------------------------------------------------------------------
+struct GemmCall {
+  const void* A;
+  const void* B;
+  const void* D;
+  void* C;
+  void* C2;
+  double alpha = 1.0, beta = 0.0, gamma = 0.0, alpha2 = 0.0, gamma2 = 0.0;
+  bool sym = true;
+  bool transC = false;
+  bool nn = false;  // B read k-major: C = A B (no symmetry assumed)
+};
+
+template <Mma MM, typename TA, typename TB, typename TC>
+hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
+  const int T = (n % 128 == 0) ? 128 : 64;
+  GemmArgs g;
+  g.A = c.A;
+  g.B = c.B;
+  g.D = c.D;
+  g.C = c.C;
+  g.C2 = c.C2;
+  g.n = n;
+  g.nt = n / T;
+  g.sym = c.sym ? 1 : 0;
+  g.transC = c.transC ? 1 : 0;
+  g.tiles = c.sym ? g.nt * (g.nt + 1) / 2 : g.nt * g.nt;
+  g.stride = (int64_t)n * n;
+  g.total = batch * g.tiles;
+  g.alpha = c.alpha;
+  g.beta = c.beta;
+  g.gamma = c.gamma;
+  g.alpha2 = c.alpha2;
+  g.gamma2 = c.gamma2;
+  if (g.total == 0) return hipSuccess;
+  dim3 grid((unsigned)g.total);
+  if constexpr (std::is_same<TB, float>::value || std::is_same<TB, double>::value) {
+    if (c.nn) {
+      if (T == 128)
+        hipLaunchKernelGGL((gemm_kernel<MM, 128, true, TA, TB, TC>), grid, dim3(256), 0, st, g);
+      else
+        hipLaunchKernelGGL((gemm_kernel<MM, 64, true, TA, TB, TC>), grid, dim3(256), 0, st, g);
+      return hipGetLastError();
+    }
+  }
+  if (c.nn) return hipErrorInvalidValue;
+  if (T == 128)
+    hipLaunchKernelGGL((gemm_kernel<MM, 128, false, TA, TB, TC>), grid, dim3(256), 0, st, g);
+  else
+    hipLaunchKernelGGL((gemm_kernel<MM, 64, false, TA, TB, TC>), grid, dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+int64_t gemm_wgs(int n, int64_t batch, bool sym) {
+  const int T = (n % 128 == 0) ? 128 : 64;
+  const int64_t nt = n / T;
+  return batch * (sym ? nt * (nt + 1) / 2 : nt * nt);
+}
+
+// ---------------------------------------------------------------------------
+// Solver-chain planner.  Buffers are small integers handed out by a pool that
+// records its peak, so the workspace query and the execution run the very
+// same plan.
+// ---------------------------------------------------------------------------
+enum OpKind { OP_PREP, OP_GEMM, OP_FINAL };
+
+struct Op {
+  OpKind kind;
+  // PREP: up to three outputs (buffer, alpha, gamma)
+  int out[3] = {-1, -1, -1};
+  double oa[3] = {0, 0, 0}, og[3] = {0, 0, 0};
+  // GEMM: C = alpha A B^T + beta D + gamma I ; C2 = alpha2 C + gamma2 I
+  int a = -1, b = -1, d = -1, c = -1, c2 = -1;
+  bool nn = false;  // full product A B in the given order (else symmetric NT)
+  double alpha = 1, beta = 0, gamma = 0, alpha2 = 0, gamma2 = 0;
+  // FINAL: buffer a -> out
+};
+
+struct Plan {
+  std::vector<Op> ops;
+  int peak = 0;
+  int gemms = 0;
+  bool sym_out = false;  // finalize returns the symmetric part (X + X^T)/2
+  std::vector<bool> used;
+  int get() {
+    for (size_t i = 0; i < used.size(); ++i)
+      if (!used[i]) {
+        used[i] = true;
+        return (int)i;
+      }
+    used.push_back(true);
+    peak = (int)used.size() > peak ? (int)used.size() : peak;
+    return (int)used.size() - 1;
+  }
+  void put(int i) {
+    if (i >= 0) used[i] = false;
+  }
+  void prep(int o0, double a0, double g0, int o1 = -1, double a1 = 0, double g1 = 0, int o2 = -1,
+            double a2 = 0, double g2 = 0) {
+    Op op;
+    op.kind = OP_PREP;
+    op.out[0] = o0; op.oa[0] = a0; op.og[0] = g0;
+    op.out[1] = o1; op.oa[1] = a1; op.og[1] = g1;
+    op.out[2] = o2; op.oa[2] = a2; op.og[2] = g2;
+    ops.push_back(op);
+  }
+  void gemm(int a, int b, int c, double alpha, double gamma, int d = -1, double beta = 0, int c2 = -1,
+            double alpha2 = 0, double gamma2 = 0, bool nn = false) {
+    Op op;
+    op.kind = OP_GEMM;
+    op.a = a; op.b = b; op.c = c; op.d = d; op.c2 = c2;
+    op.alpha = alpha; op.beta = beta; op.gamma = gamma; op.alpha2 = alpha2; op.gamma2 = gamma2;
+    op.nn = nn;
+    ops.push_back(op);
+    ++gemms;
+  }
+  void final_(int x) {
+    Op op;
+    op.kind = OP_FINAL;
+    op.a = x;
+    ops.push_back(op);
+  }
+};
+
+// Coupled Newton ([NOTES] "Roots on idle CPUs ...": coupled iteration of
+// Guo-Higham / Iannazzo): X_0 = I, M_0 = A_s; T = ((p+1) I - M)/p;
+// X <- X T; M <- T^p M.  X_1 = T_1 comes from the prep pass; the last
+// iteration updates X only, and the one before it produces only the T the
+// last one needs.  T^p by repeated squaring (p a power of two).
+void plan_cn(Plan& P, int p, int iters) {
+  const double ap = -1.0 / p, gp = (p + 1.0) / p;
+  int M = P.get(), T = P.get(), X = P.get();
+  P.prep(M, 1.0, 0.0, T, ap, gp, X, ap, gp);
+  for (int k = 1; k <= iters; ++k) {
+    if (k >= 2) {
+      const int Xn = P.get();
+      P.gemm(X, T, Xn, 1.0, 0.0);
+      P.put(X);
+      X = Xn;
+    }
+    if (k == iters) break;
+    int Pw = T;
+    for (int q = 1; q < p; q *= 2) {
+      const int Pn = P.get();
+      P.gemm(Pw, Pw, Pn, 1.0, 0.0);
+      if (Pw != T) P.put(Pw);
+      Pw = Pn;
+    }
+    if (Pw != T) P.put(T);
+    const bool next_is_last = (k + 1 == iters);
+    if (next_is_last) {
+      const int Tn = P.get();
+      P.gemm(Pw, M, Tn, ap, gp);  // T_(k+1) = ((p+1) I - T^p M)/p directly
+      if (Pw == T) P.put(T); else P.put(Pw);
+      P.put(M);
+      M = -1;
+      T = Tn;
+    } else {
+      const int Mn = P.get(), Tn = P.get();
+      P.gemm(Pw, M, Mn, 1.0, 0.0, -1, 0.0, Tn, ap, gp);
+      if (Pw == T) P.put(T); else P.put(Pw);
+      P.put(M);
+      M = Mn;
+      T = Tn;
+    }
+  }
+  P.final_(X);
+}
+
+// One Newton-DB call ([DASH] "3. Inverse Root Methods", Newton-DB):
+// Y_0 = A, Z_0 = I; T = (3 I - Z Y)/2; Y <- Y T; Z <- T Z.  The first
+// iteration uses T_0 from the caller and Z_1 = T_0 (one product instead of
+// three); products whose results are not used afterwards are skipped.
+// On return *Yo / *Zo hold the requested final iterates and *Tn the seed
+// 1.5 I - 0.5 Y of a following call.
+void ndb_call(Plan& P, int Y, int T0, int iters, bool needY, bool needZ, bool wantTn, int* Yo, int* Zo,
+              int* Tn) {
+  int Z = -1;
+  *Tn = -1;
+  // k = 1
+  Z = T0;
+  if (iters == 1) {
+    if (needY || wantTn) {
+      const int Yn = P.get();
+      int t = -1;
+      if (wantTn) t = P.get();
+      P.gemm(Y, T0, Yn, 1.0, 0.0, -1, 0.0, t, -0.5, 1.5, true);
+      P.put(Y);
+      Y = Yn;
+      *Tn = t;
+    }
+  } else {
+    const int Yn = P.get();
+    P.gemm(Y, T0, Yn, 1.0, 0.0, -1, 0.0, -1, 0.0, 0.0, true);
+    P.put(Y);
+    Y = Yn;
+  }
+  for (int k = 2; k <= iters; ++k) {
+    const bool last = (k == iters);
+    const int T = P.get();
+    P.gemm(Z, Y, T, -0.5, 1.5, -1, 0.0, -1, 0.0, 0.0, true);
+    if (!last || needY || wantTn) {
+      const int Yn = P.get();
+      int t = -1;
+      if (last && wantTn) t = P.get();
+      P.gemm(Y, T, Yn, 1.0, 0.0, -1, 0.0, t, -0.5, 1.5, true);
+      P.put(Y);
+      Y = Yn;
+      if (t >= 0) *Tn = t;
+    }
+    if (!last || needZ) {
+      const int Zn = P.get();
+      P.gemm(T, Z, Zn, 1.0, 0.0, -1, 0.0, -1, 0.0, 0.0, true);
+      P.put(Z);
+      Z = Zn;
+    }
+    P.put(T);
+  }
+  if (!needY) {
+    P.put(Y);
+    Y = -1;
+  }
+  if (!needZ) {
+    P.put(Z);
+    Z = -1;
+  }
+  *Yo = Y;
+  *Zo = Z;
+}
+
+// The Newton-DB products are full products in the order of the recurrence
+// (see gemm.hpp: symmetrising them destabilises the coupled iteration); the
+// converged root is returned as its symmetric part, which is at least as
+// close as X itself to the symmetric exact root.
+void plan_ndb(Plan& P, int p, int iters1, int iters2) {
+  P.sym_out = true;
+  const int Y0 = P.get(), T0 = P.get();
+  P.prep(Y0, 1.0, 0.0, T0, -0.5, 1.5);
+  int Y, Z, Tn;
+  if (p == 2) {
+    ndb_call(P, Y0, T0, iters1, false, true, false, &Y, &Z, &Tn);
+    P.final_(Z);
+    return;
+  }
+  ndb_call(P, Y0, T0, iters1, true, false, true, &Y, &Z, &Tn);
+  int Y2, Z2, T2;
+  ndb_call(P, Y, Tn, iters2, false, true, false, &Y2, &Z2, &T2);
+  P.final_(Z2);
+}
+
+// Chebyshev series by Clenshaw's recurrence ([DASH] "A.2 Chebyshev
+// polynomials for matrices": initialise B_d and B_(d-1), stop at B_1;
+// d - 1 products).  S = 2 A_s - I; B_d = c_d I is kept implicit.
+void plan_cheb(Plan& P, const std::vector<double>& c) {
+  const int d = (int)c.size() - 1;
+  if (d == 0) {
+    const int X = P.get();
+    P.prep(X, 0.0, c[0]);
+    P.final_(X);
+    return;
+  }
+  if (d == 1) {
+    const int X = P.get();
+    P.prep(X, 2.0 * c[1], c[0] - c[1]);
+    P.final_(X);
+    return;
+  }
+  const int S = P.get();
+  int Bk1 = P.get();
+  int Bk2 = -1;  // -1 stands for B_d = c_d I
+  P.prep(S, 2.0, -1.0, Bk1, 4.0 * c[d], c[d - 1] - 2.0 * c[d]);
+  for (int k = d - 2; k >= 1; --k) {
+    const int N = P.get();
+    if (Bk2 < 0) P.gemm(S, Bk1, N, 2.0, c[k] - c[d]);
+    else P.gemm(S, Bk1, N, 2.0, c[k], Bk2, -1.0);
+    P.put(Bk2);
+    Bk2 = Bk1;
+    Bk1 = N;
+  }
+  const int X = P.get();
+  if (Bk2 < 0) P.gemm(S, Bk1, X, 1.0, c[0] - c[d]);
+  else P.gemm(S, Bk1, X, 1.0, c[0], Bk2, -1.0);
+  P.put(S);
+  P.put(Bk1);
+  P.put(Bk2);
+  P.final_(X);
+}
+
+// Chebyshev coefficients of x^(-1/p) on [eps, 1 + eps] ([DASH] "A.1/A.2"):
+// N first-kind nodes t_j = cos(theta_j), theta_j = pi (j + 1/2) / N, mapped
+// to x_j = (t_j + 1)/2 + eps; c_k = (2/N) sum_j f(x_j) cos(k theta_j), with
+// c_0 halved (the least-squares fit at the nodes).
+std::vector<double> cheb_coeffs(int p, int d, int N, double eps) {
+  std::vector<double> c(d + 1, 0.0);
+  std::vector<double> th(N), fx(N);
+  for (int j = 0; j < N; ++j) {
+    th[j] = M_PI * (j + 0.5) / N;
+    const double x = 0.5 * (std::cos(th[j]) + 1.0) + eps;
+    fx[j] = std::pow(x, -1.0 / p);
+  }
+  for (int k = 0; k <= d; ++k) {
+    double s = 0.0;
+    for (int j = 0; j < N; ++j) s += fx[j] * std::cos(k * th[j]);
+    c[k] = 2.0 * s / N;
+  }
+  c[0] *= 0.5;
+  return c;
+}
+
+bool pow2_in(int p, int maxp) {
+  for (int q = 1; q <= maxp; q *= 2)
+    if (q == p) return true;
+  return false;
+}
+
+shampoo_status check_root_args(int64_t n, int32_t B, int32_t p, const shampoo_root_opts* o) {
+  if (!o) return fail(SHAMPOO_E_INVALID, "opts is NULL");
+  if (n < 0) return fail(SHAMPOO_E_INVALID, "n = %lld < 0", (long long)n);
+  if (B < 64 || B % 64 != 0) return fail(SHAMPOO_E_UNSUPPORTED, "B = %d: must be a positive multiple of 64", B);
+  if (p < 1) return fail(SHAMPOO_E_INVALID, "p = %d < 1", p);
+  if (o->compute != SHAMPOO_F32 && o->compute != SHAMPOO_F16 && o->compute != SHAMPOO_F64)
+    return fail(SHAMPOO_E_UNSUPPORTED, "compute dtype %d not supported (F32, F16, F64)", o->compute);
+  if (!(o->eps >= 0.0) || !std::isfinite(o->eps)) return fail(SHAMPOO_E_INVALID, "eps must be finite and >= 0");
+  switch (o->method) {
+    case SHAMPOO_CN:
+      if (!pow2_in(p, 8)) return fail(SHAMPOO_E_UNSUPPORTED, "coupled Newton supports p in {1, 2, 4, 8}, got %d", p);
+      if (o->iters < 1) return fail(SHAMPOO_E_INVALID, "iters = %d < 1", o->iters);
+      break;
+    case SHAMPOO_NDB:
+      if (p != 2 && p != 4) return fail(SHAMPOO_E_UNSUPPORTED, "Newton-DB supports p in {2, 4}, got %d", p);
+      if (o->iters < 1) return fail(SHAMPOO_E_INVALID, "iters = %d < 1", o->iters);
+      if (p == 4 && o->iters2 < 1) return fail(SHAMPOO_E_INVALID, "iters2 = %d < 1", o->iters2);
+      break;
+    case SHAMPOO_CHEBYSHEV: {
+      if (o->cheb_degree < 0 || o->cheb_degree > 1000) return fail(SHAMPOO_E_INVALID, "cheb_degree = %d", o->cheb_degree);
+      const int N = o->cheb_points ? o->cheb_points : 4 * (o->cheb_degree + 1);
+      if (N <= o->cheb_degree) return fail(SHAMPOO_E_INVALID, "cheb_points = %d must exceed the degree", N);
+      if (!(o->cheb_eps >= 0.0) || !std::isfinite(o->cheb_eps)) return fail(SHAMPOO_E_INVALID, "cheb_eps must be finite and >= 0");
+      break;
+    }
+    default:
+      return fail(SHAMPOO_E_INVALID, "unknown method %d", o->method);
+  }
+  if (o->scaling != SHAMPOO_SCALE_FROBENIUS && o->scaling != SHAMPOO_SCALE_POWER)
+    return fail(SHAMPOO_E_INVALID, "unknown scaling %d", o->scaling);
+  if (o->scaling == SHAMPOO_SCALE_POWER) {
+    if (o->pi_vectors < 1 || o->pi_vectors > 32) return fail(SHAMPOO_E_INVALID, "pi_vectors = %d not in 1..32", o->pi_vectors);
+    if (o->pi_iters < 1) return fail(SHAMPOO_E_INVALID, "pi_iters = %d < 1", o->pi_iters);
+    const int k16 = (o->pi_vectors + 15) / 16 * 16;
+    if ((int64_t)k16 * B > 16384)
+      return fail(SHAMPOO_E_UNSUPPORTED, "power iteration needs ceil16(pi_vectors) * B <= 16384 (got %d * %d)", k16, B);
+  }
+  return SHAMPOO_OK;
+}
+
+Plan build_plan(int32_t p, const shampoo_root_opts* o) {
+  Plan P;
+  switch (o->method) {
+    case SHAMPOO_CN: plan_cn(P, p, o->iters); break;
+    case SHAMPOO_NDB: plan_ndb(P, p, o->iters, o->iters2); break;
+    default: {
+      const int N = o->cheb_points ? o->cheb_points : 4 * (o->cheb_degree + 1);
+      plan_cheb(P, cheb_coeffs(p, o->cheb_degree, N, o->cheb_eps));
+    }
+  }
+  return P;
+}
+
+size_t root_ws_bytes(int64_t n, int32_t B, const Plan& P, int compute) {
+  const size_t es = compute == SHAMPOO_F64 ? 8 : 4;
+  const int nbuf = P.peak > 1 ? P.peak : 1;  // the power iteration borrows one buffer
+  return 2 * align_up((size_t)n * 8) + (size_t)nbuf * align_up((size_t)n * B * B * es);
+}
+
+int64_t elementwise_grid(int64_t nelem) { return (nelem / 4 + 255) / 256; }
+
+// Benchmark timing of the batched products (shampoo_timing_enable).
+struct Timing {
+  std::vector<hipEvent_t> ev;  // 2 per launch
+  int cap = 0;
+  int used = 0;
+} g_timing;
+
+hipError_t timing_mark(int which, hipStream_t st) {
+  if (g_timing.cap == 0 || g_timing.used >= g_timing.cap) return hipSuccess;
+  return hipEventRecord(g_timing.ev[2 * g_timing.used + which], st);
+}
+
+void timing_advance() {
+  if (g_timing.cap && g_timing.used < g_timing.cap) ++g_timing.used;
+}
+
+template <typename TI, typename TS>
+hipError_t launch_prep(const void* in, int B, int64_t n, const int32_t* valid, double eps, const double* s,
+                       double pad_diag, const PrepOut& o0, const PrepOut& o1, const PrepOut& o2,
+                       hipStream_t st) {
+  const int64_t g = elementwise_grid(n * (int64_t)B * B);
+  hipLaunchKernelGGL((prep_kernel<TI, TS>), dim3((unsigned)g), dim3(256), 0, st, (const TI*)in, B, n, valid,
+                     eps, s, pad_diag, o0, o1, o2);
+  return hipGetLastError();
+}
+
+template <typename TI, typename TS, Mma MM>
+shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t p, const shampoo_root_opts* o,
+                        const Plan& P, const int32_t* valid, float* scale_out, int32_t* flags, void* ws,
+                        hipStream_t st) {
+  const int64_t BB = (int64_t)B * B;
+  unsigned char* w = (unsigned char*)ws;
+  double* sf = (double*)w;
+  double* s = (double*)(w + align_up((size_t)n * 8));
+  unsigned char* bufbase = w + 2 * align_up((size_t)n * 8);
+  const size_t bufstride = align_up((size_t)n * BB * sizeof(TS));
+  auto buf = [&](int i) -> TS* { return (TS*)(bufbase + (size_t)i * bufstride); };
+
+  hipLaunchKernelGGL((frob_norm_kernel<TI>), dim3((unsigned)n), dim3(256), 0, st, (const TI*)in, B, valid,
+                     o->eps, sf);
+  LAUNCH_CHECK("frob_norm");
+  const double* sc = sf;
+  if (o->scaling == SHAMPOO_SCALE_POWER) {
+    if (!o->pi_start_dev) return fail(SHAMPOO_E_INVALID, "power scaling needs pi_start_dev");
+    PrepOut a{buf(0), 1.0, 0.0}, none{nullptr, 0, 0};
+    HIP_TRY((launch_prep<TI, TS>(in, B, n, valid, o->eps, sf, 0.0, a, none, none, st)));
+    const int k16 = (o->pi_vectors + 15) / 16 * 16;
+    const size_t lds = (size_t)k16 * (B + 8) * 2 + (size_t)k16 * (B + 4) * 4 + (size_t)k16 * 4;
+    HIP_TRY(hipFuncSetAttribute(k16 == 16 ? (const void*)power_iter_kernel<TS, 1> : (const void*)power_iter_kernel<TS, 2>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    if (k16 == 16)
+      hipLaunchKernelGGL((power_iter_kernel<TS, 1>), dim3((unsigned)n), dim3(256), lds, st, buf(0), B,
+                         o->pi_vectors, o->pi_iters, o->pi_start_dev, sf, s, flags);
+    else
+      hipLaunchKernelGGL((power_iter_kernel<TS, 2>), dim3((unsigned)n), dim3(256), lds, st, buf(0), B,
+                         o->pi_vectors, o->pi_iters, o->pi_start_dev, sf, s, flags);
+    LAUNCH_CHECK("power_iter");
+    sc = s;
+  }
+  for (const Op& op : P.ops) {
+    if (op.kind == OP_PREP) {
+      PrepOut q[3];
+      for (int i = 0; i < 3; ++i) q[i] = PrepOut{op.out[i] >= 0 ? buf(op.out[i]) : nullptr, op.oa[i], op.og[i]};
+      HIP_TRY((launch_prep<TI, TS>(in, B, n, valid, o->eps, sc, 1.0, q[0], q[1], q[2], st)));
+    } else if (op.kind == OP_GEMM) {
+      GemmCall c;
+      c.A = buf(op.a);
+      c.B = buf(op.b);
+      c.D = op.d >= 0 ? buf(op.d) : nullptr;
+      c.C = buf(op.c);
+      c.C2 = op.c2 >= 0 ? buf(op.c2) : nullptr;
+      c.alpha = op.alpha; c.beta = op.beta; c.gamma = op.gamma; c.alpha2 = op.alpha2; c.gamma2 = op.gamma2;
+      c.sym = !op.nn;
+      c.nn = op.nn;
+      HIP_TRY(timing_mark(0, st));
+      HIP_TRY((gemm<MM, TS, TS, TS>(c, B, n, st)));
+      HIP_TRY(timing_mark(1, st));
+      timing_advance();
+    } else {
+      const int64_t g = elementwise_grid(n * BB);
+      hipLaunchKernelGGL((finalize_kernel<TS, TI>), dim3((unsigned)g), dim3(256), 0, st, buf(op.a), (TI*)out, B, n,
+                         valid, sc, 1.0 / p, P.sym_out ? 1 : 0, scale_out, flags);
+      LAUNCH_CHECK("finalize");
+    }
+  }
+  return SHAMPOO_OK;
+}
+
+shampoo_status inverse_root_impl(const void* in, void* out, shampoo_dtype io_dt, int64_t n, int32_t B, int32_t p,
+                                 const shampoo_root_opts* o, const int32_t* valid, float* scale_out,
+                                 int32_t* flags, void* ws, size_t ws_bytes, hipStream_t st) {
+  shampoo_status r = check_root_args(n, B, p, o);
+  if (r != SHAMPOO_OK) return r;
+  if (io_dt != SHAMPOO_F32 && io_dt != SHAMPOO_F64)
+    return fail(SHAMPOO_E_UNSUPPORTED, "io dtype %d not supported (F32, F64)", (int)io_dt);
+  if (n == 0) return SHAMPOO_OK;
+  if (!in || !out) return fail(SHAMPOO_E_INVALID, "in/out is NULL");
+  if (o->scaling == SHAMPOO_SCALE_POWER && !o->pi_start_dev)
+    return fail(SHAMPOO_E_INVALID, "power scaling needs pi_start_dev");
+  if (gemm_wgs(B, n, true) >= (int64_t)1 << 31 || n >= ((int64_t)1 << 31))
+    return fail(SHAMPOO_E_UNSUPPORTED, "batch too large for one launch");
+  const Plan P = build_plan(p, o);
+  const size_t need = root_ws_bytes(n, B, P, o->compute);
+  if (!ws || ws_bytes < need)
+    return fail(SHAMPOO_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  const bool in64 = io_dt == SHAMPOO_F64;
+  switch (o->compute) {
+    case SHAMPOO_F32:
+      return in64 ? run_root<double, float, Mma::F32>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, st)
+                  : run_root<float, float, Mma::F32>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, st);
+    case SHAMPOO_F16:
+      return in64 ? run_root<double, float, Mma::F16>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, st)
+                  : run_root<float, float, Mma::F16>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, st);
+    default:
+      return in64 ? run_root<double, double, Mma::F64>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, st)
+                  : run_root<float, double, Mma::F64>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, st);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// pack, statistics, preconditioning
+// ---------------------------------------------------------------------------
+template <typename E>
+hipError_t launch_pack(const shampoo_matrix* mats, int nparams, const shampoo_block* table, int64_t nblk, int B, void* stack,
+                       void* stack_t, hipStream_t st) {
+  const int tps = (B + 63) / 64;
+  dim3 grid((unsigned)(tps * tps), (unsigned)nblk);
+  hipLaunchKernelGGL((pack_kernel<E, shampoo_matrix>), grid, dim3(256), 0, st, mats, nparams, table, B, tps,
+                     (E*)stack, (E*)stack_t);
+  return hipGetLastError();
+}
+
+shampoo_status pack_impl(const shampoo_matrix* mats, int32_t nparams, const shampoo_block* table, int64_t nblk,
+                         int32_t B, shampoo_dtype dt, void* stack, void* stack_t, hipStream_t st) {
+  if (nblk < 0 || B < 1 || nparams < 0) return fail(SHAMPOO_E_INVALID, "bad sizes nblk=%lld B=%d", (long long)nblk, B);
+  if (nblk == 0) return SHAMPOO_OK;
+  if (!mats || !table || !stack) return fail(SHAMPOO_E_INVALID, "null pointer argument");
+  if (nblk > 65535) return fail(SHAMPOO_E_UNSUPPORTED, "nblk = %lld > 65535", (long long)nblk);
+  switch (dt) {
+    case SHAMPOO_F32: HIP_TRY(launch_pack<uint32_t>(mats, nparams, table, nblk, B, stack, stack_t, st)); break;
+    case SHAMPOO_F16:
+    case SHAMPOO_BF16: HIP_TRY(launch_pack<uint16_t>(mats, nparams, table, nblk, B, stack, stack_t, st)); break;
+    case SHAMPOO_F64: HIP_TRY(launch_pack<uint64_t>(mats, nparams, table, nblk, B, stack, stack_t, st)); break;
+    default: return fail(SHAMPOO_E_INVALID, "unknown dtype %d", (int)dt);
+  }
+  return SHAMPOO_OK;
+}
+
+shampoo_status stats_impl(const void* g, const void* gt, shampoo_dtype gdt, int64_t nblk, int32_t B, float* LR,
+                          float beta2, hipStream_t st) {
+  if (nblk < 0) return fail(SHAMPOO_E_INVALID, "nblk < 0");
+  if (B < 64 || B % 64 != 0) return fail(SHAMPOO_E_UNSUPPORTED, "B = %d: must be a positive multiple of 64", B);
+  if (!(beta2 >= 0.0f && beta2 <= 1.0f)) return fail(SHAMPOO_E_INVALID, "beta2 = %g not in [0, 1]", beta2);
+  if (gdt != SHAMPOO_F32 && gdt != SHAMPOO_BF16) return fail(SHAMPOO_E_UNSUPPORTED, "gradient dtype %d (F32, BF16)", (int)gdt);
+  if (nblk == 0) return SHAMPOO_OK;
+  if (!g || !gt || !LR) return fail(SHAMPOO_E_INVALID, "null pointer argument");
+  if (gemm_wgs(B, nblk, true) >= (int64_t)1 << 31) return fail(SHAMPOO_E_UNSUPPORTED, "batch too large");
+  const double a = beta2 == 1.0f ? 1.0 : 1.0 - (double)beta2;
+  const double b = beta2;
+  const size_t es = gdt == SHAMPOO_F32 ? 4 : 2;
+  (void)es;
+  GemmCall cl;
+  cl.A = g; cl.B = g; cl.D = LR; cl.C = LR; cl.C2 = nullptr; cl.alpha = a; cl.beta = b; cl.sym = true;
+  GemmCall cr = cl;
+  cr.A = gt; cr.B = gt; cr.D = LR + nblk * (int64_t)B * B; cr.C = (void*)cr.D;
+  if (gdt == SHAMPOO_F32) {
+    HIP_TRY((gemm<Mma::F32, float, float, float>(cl, B, nblk, st)));
+    HIP_TRY((gemm<Mma::F32, float, float, float>(cr, B, nblk, st)));
+  } else {
+    HIP_TRY((gemm<Mma::BF16, __bf16, __bf16, float>(cl, B, nblk, st)));
+    HIP_TRY((gemm<Mma::BF16, __bf16, __bf16, float>(cr, B, nblk, st)));
+  }
+  return SHAMPOO_OK;
+}
+
+shampoo_status precond_impl(const float* roots, const void* g, shampoo_dtype gdt, int64_t nblk, int32_t B,
+                            float* dstack, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (nblk < 0) return fail(SHAMPOO_E_INVALID, "nblk < 0");
+  if (B < 64 || B % 64 != 0) return fail(SHAMPOO_E_UNSUPPORTED, "B = %d: must be a positive multiple of 64", B);
+  if (gdt != SHAMPOO_F32 && gdt != SHAMPOO_BF16) return fail(SHAMPOO_E_UNSUPPORTED, "gradient dtype %d (F32, BF16)", (int)gdt);
+  if (nblk == 0) return SHAMPOO_OK;
+  if (!roots || !g || !dstack) return fail(SHAMPOO_E_INVALID, "null pointer argument");
+  const size_t need = (size_t)nblk * B * B * 4;
+  if (!ws || ws_bytes < need) return fail(SHAMPOO_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (gemm_wgs(B, nblk, false) >= (int64_t)1 << 31) return fail(SHAMPOO_E_UNSUPPORTED, "batch too large");
+  const float* Lr = roots;
+  const float* Rr = roots + nblk * (int64_t)B * B;
+  // E = G Rr, stored transposed; D = Lr E = Lr (E^T)^T.
+  GemmCall c1;
+  c1.A = g; c1.B = Rr; c1.D = nullptr; c1.C = ws; c1.C2 = nullptr; c1.sym = false; c1.transC = true;
+  if (gdt == SHAMPOO_F32) HIP_TRY((gemm<Mma::F32, float, float, float>(c1, B, nblk, st)));
+  else HIP_TRY((gemm<Mma::F32, __bf16, float, float>(c1, B, nblk, st)));
+  GemmCall c2;
+  c2.A = Lr; c2.B = ws; c2.D = nullptr; c2.C = dstack; c2.C2 = nullptr; c2.sym = false;
+  HIP_TRY((gemm<Mma::F32, float, float, float>(c2, B, nblk, st)));
+  return SHAMPOO_OK;
+}
+
+// ---------------------------------------------------------------------------
+// step
+// ---------------------------------------------------------------------------
+struct StepLayout {
+  size_t g, gt, valid, root, partials, scales, total;
+  size_t root_bytes;
+  int nchunk;
+};
+
+shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
+  if (!a) return fail(SHAMPOO_E_INVALID, "args is NULL");
+  if (a->nblk < 0 || a->nparams < 0) return fail(SHAMPOO_E_INVALID, "negative sizes");
+  if (a->B < 64 || a->B % 64 != 0) return fail(SHAMPOO_E_UNSUPPORTED, "B = %d: must be a positive multiple of 64", a->B);
+  if (a->g_dt != SHAMPOO_F32 && a->g_dt != SHAMPOO_BF16) return fail(SHAMPOO_E_UNSUPPORTED, "gradient dtype %d", (int)a->g_dt);
+  if (a->nblk > 65535) return fail(SHAMPOO_E_UNSUPPORTED, "nblk = %lld > 65535", (long long)a->nblk);
+  shampoo_status r = check_root_args(2 * a->nblk, a->B, a->p, &a->root);
+  if (r != SHAMPOO_OK) return r;
+  const Plan P = build_plan(a->p, &a->root);
+  const int64_t BB = (int64_t)a->B * a->B;
+  const size_t es = dtype_size(a->g_dt);
+  L->nchunk = (a->B + GRAFT_ROWS - 1) / GRAFT_ROWS;
+  L->root_bytes = root_ws_bytes(2 * a->nblk, a->B, P, a->root.compute);
+  size_t root = L->root_bytes;
+  const size_t ed = align_up((size_t)a->nblk * BB * 4);
+  if (root < 2 * ed) root = 2 * ed;  // E^T and D reuse the root workspace
+  size_t off = 0;
+  L->g = off; off += align_up((size_t)a->nblk * BB * es);
+  L->gt = off; off += align_up((size_t)a->nblk * BB * es);
+  L->valid = off; off += align_up((size_t)a->nblk * 2 * 4);
+  L->root = off; off += root;
+  L->partials = off; off += align_up((size_t)a->nblk * L->nchunk * 2 * 8);
+  L->scales = off; off += align_up((size_t)a->nblk * 4);
+  L->total = off;
+  return SHAMPOO_OK;
+}
+
+shampoo_status step_impl(const shampoo_step_args* a, hipStream_t st) {
+  StepLayout L;
+  shampoo_status r = step_layout(a, &L);
+  if (r != SHAMPOO_OK) return r;
+  if (a->nblk == 0) return SHAMPOO_OK;
+  if (!a->params_dev || !a->table_dev || !a->LR || !a->roots) return fail(SHAMPOO_E_INVALID, "null pointer argument");
+  if (a->graft < 0 || a->graft > SHAMPOO_GRAFT_NONE) return fail(SHAMPOO_E_INVALID, "unknown graft %d", a->graft);
+  if (a->graft == SHAMPOO_GRAFT_ADAM && (a->t < 1 || !(a->beta1 >= 0 && a->beta1 < 1) || !(a->graft_beta2 >= 0 && a->graft_beta2 < 1)))
+    return fail(SHAMPOO_E_INVALID, "Adam grafting needs t >= 1 and beta1, graft_beta2 in [0, 1)");
+  if (!a->ws || a->ws_bytes < L.total) return fail(SHAMPOO_E_WORKSPACE, "workspace %zu bytes < %zu needed", a->ws_bytes, L.total);
+  unsigned char* w = (unsigned char*)a->ws;
+  const int B = a->B;
+  const int64_t nblk = a->nblk;
+  const int64_t BB = (int64_t)B * B;
+  void* g = w + L.g;
+  void* gt = w + L.gt;
+  int32_t* valid = (int32_t*)(w + L.valid);
+  unsigned char* root = w + L.root;
+
+  // 1. pack G and G^T; valid sizes of the 2 nblk factors
+  {
+    const int tps = (B + 63) / 64;
+    dim3 grid((unsigned)(tps * tps), (unsigned)nblk);
+    if (a->g_dt == SHAMPOO_F32)
+      hipLaunchKernelGGL((pack_kernel<uint32_t, shampoo_param>), grid, dim3(256), 0, st, a->params_dev, a->nparams, a->table_dev,
+                         B, tps, (uint32_t*)g, (uint32_t*)gt);
+    else
+      hipLaunchKernelGGL((pack_kernel<uint16_t, shampoo_param>), grid, dim3(256), 0, st, a->params_dev, a->nparams, a->table_dev,
+                         B, tps, (uint16_t*)g, (uint16_t*)gt);
+    LAUNCH_CHECK("pack");
+    hipLaunchKernelGGL(valid_from_table_kernel, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, st, a->table_dev,
+                       nblk, valid);
+    LAUNCH_CHECK("valid");
+  }
+  // 2. statistics
+  r = stats_impl(g, gt, a->g_dt, nblk, B, a->LR, a->beta2, st);
+  if (r != SHAMPOO_OK) return r;
+  // 3. inverse roots of the 2 nblk factors
+  if (a->recompute_roots) {
+    r = inverse_root_impl(a->LR, a->roots, SHAMPOO_F32, 2 * nblk, B, a->p, &a->root, valid, nullptr, a->flags_dev,
+                          root, L.root_bytes, st);
+    if (r != SHAMPOO_OK) return r;
+  }
+  // 4. D = Lr G Rr
+  float* Et = (float*)root;
+  float* D = a->dstack ? a->dstack : (float*)(root + align_up((size_t)nblk * BB * 4));
+  r = precond_impl(a->roots, g, a->g_dt, nblk, B, D, Et, (size_t)nblk * BB * 4, st);
+  if (r != SHAMPOO_OK) return r;
+  // 5. grafting and update
+  GraftArgs ga;
+  ga.params = a->params_dev;
+  ga.nparams = a->nparams;
+  ga.table = a->table_dev;
+  ga.dstack = D;
+  ga.B = B;
+  ga.nchunk = L.nchunk;
+  ga.graft = a->graft;
+  ga.lr = a->lr;
+  ga.momentum = a->momentum;
+  ga.beta1 = a->beta1;
+  ga.beta2 = a->graft_beta2;
+  ga.eps = a->graft_eps;
+  ga.bc1 = a->graft == SHAMPOO_GRAFT_ADAM ? (float)(1.0 - std::pow((double)a->beta1, a->t)) : 1.0f;
+  ga.bc2 = a->graft == SHAMPOO_GRAFT_ADAM ? (float)(1.0 - std::pow((double)a->graft_beta2, a->t)) : 1.0f;
+  ga.partials = (double*)(w + L.partials);
+  ga.scales = (float*)(w + L.scales);
+  dim3 grid((unsigned)L.nchunk, (unsigned)nblk);
+  if (a->g_dt == SHAMPOO_F32) hipLaunchKernelGGL(graft_partials_kernel<float>, grid, dim3(256), 0, st, ga);
+  else hipLaunchKernelGGL(graft_partials_kernel<__bf16>, grid, dim3(256), 0, st, ga);
+  LAUNCH_CHECK("graft_partials");
+  hipLaunchKernelGGL(graft_scale_kernel, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, st, ga, nblk,
+                     a->graft_blockwise);
+  LAUNCH_CHECK("graft_scale");
+  hipLaunchKernelGGL(graft_update_kernel, grid, dim3(256), 0, st, ga);
+  LAUNCH_CHECK("graft_update");
+  return SHAMPOO_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// exported C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+const char* shampoo_version(void) { return "shampoo-mi355x 0.1.0 (gfx950)"; }
+
+const char* shampoo_last_error(void) { return g_err.c_str(); }
+
+shampoo_status shampoo_plan_blocks(const int64_t* shapes2d, const int32_t* block_sizes, int32_t nparams,
+                                   shampoo_block* out, int64_t* nblk) {
+  if (!nblk) return fail(SHAMPOO_E_INVALID, "nblk is NULL");
+  if (nparams < 0) return fail(SHAMPOO_E_INVALID, "nparams < 0");
+  if (nparams > 0 && (!shapes2d || !block_sizes)) return fail(SHAMPOO_E_INVALID, "null pointer argument");
+  int64_t count = 0;
+  for (int32_t p = 0; p < nparams; ++p) {
+    const int64_t m = shapes2d[2 * p], n = shapes2d[2 * p + 1];
+    const int64_t bs = block_sizes[p];
+    if (m < 0 || n < 0 || bs < 0) return fail(SHAMPOO_E_INVALID, "parameter %d: negative size", p);
+    if (m == 0 || n == 0) continue;
+    const int64_t B = bs == 0 ? (m > n ? m : n) : bs;
+    if (B > INT32_MAX || m > INT32_MAX || n > INT32_MAX) return fail(SHAMPOO_E_INVALID, "parameter %d too large", p);
+    count += ((m + B - 1) / B) * ((n + B - 1) / B);
+  }
+  if (!out) {
+    *nblk = count;
+    return SHAMPOO_OK;
+  }
+  if (count > *nblk) {
+    const int64_t cap = *nblk;
+    *nblk = count;
+    return fail(SHAMPOO_E_INVALID, "table capacity %lld < %lld blocks", (long long)cap, (long long)count);
+  }
+  int64_t i = 0;
+  for (int32_t p = 0; p < nparams; ++p) {
+    const int64_t m = shapes2d[2 * p], n = shapes2d[2 * p + 1];
+    if (m == 0 || n == 0) continue;
+    const int64_t B = block_sizes[p] == 0 ? (m > n ? m : n) : block_sizes[p];
+    const int64_t nbr = (m + B - 1) / B, nbc = (n + B - 1) / B;
+    for (int64_t br = 0; br < nbr; ++br)
+      for (int64_t bc = 0; bc < nbc; ++bc) {
+        shampoo_block b;
+        b.param = p;
+        b.brow = (int32_t)br;
+        b.bcol = (int32_t)bc;
+        b.row0 = (int32_t)(br * B);
+        b.col0 = (int32_t)(bc * B);
+        b.rows = (int32_t)((m - br * B) < B ? (m - br * B) : B);
+        b.cols = (int32_t)((n - bc * B) < B ? (n - bc * B) : B);
+        b.B = (int32_t)B;
+        out[i++] = b;
+      }
+  }
+  *nblk = count;
+  return SHAMPOO_OK;
+}
+
+shampoo_status shampoo_pack_blocks(const shampoo_matrix* mats_dev, int32_t nparams, const shampoo_block* table_dev,
+                                   int64_t nblk, int32_t B, shampoo_dtype dt, void* stack, void* stack_t,
+                                   hipStream_t stream) {
+  return pack_impl(mats_dev, nparams, table_dev, nblk, B, dt, stack, stack_t, stream);
+}
+
+shampoo_status shampoo_unpack_blocks(const float* stack, const shampoo_block* table_dev, int64_t nblk, int32_t B,
+                                     const shampoo_matrix* mats_dev, int32_t nparams, hipStream_t stream) {
+  if (nblk < 0 || B < 1 || nparams < 0) return fail(SHAMPOO_E_INVALID, "bad sizes");
+  if (nblk == 0) return SHAMPOO_OK;
+  if (!stack || !table_dev || !mats_dev) return fail(SHAMPOO_E_INVALID, "null pointer argument");
+  if (nblk > 65535) return fail(SHAMPOO_E_UNSUPPORTED, "nblk = %lld > 65535", (long long)nblk);
+  const int tps = (B + 63) / 64;
+  dim3 grid((unsigned)(tps * tps), (unsigned)nblk);
+  hipLaunchKernelGGL(unpack_kernel, grid, dim3(256), 0, stream, stack, table_dev, B, tps, mats_dev, nparams);
+  LAUNCH_CHECK("unpack");
+  return SHAMPOO_OK;
+}
+
+shampoo_status shampoo_update_stats(const void* gstack, const void* gstack_t, shampoo_dtype g_dt, int64_t nblk,
+                                    int32_t B, float* LR, float beta2, hipStream_t stream) {
+  return stats_impl(gstack, gstack_t, g_dt, nblk, B, LR, beta2, stream);
+}
+
+shampoo_status shampoo_inverse_root_workspace(int64_t n, int32_t B, int32_t p, const shampoo_root_opts* opts,
+                                              size_t* bytes) {
+  if (!bytes) return fail(SHAMPOO_E_INVALID, "bytes is NULL");
+  shampoo_status r = check_root_args(n, B, p, opts);
+  if (r != SHAMPOO_OK) return r;
+  *bytes = root_ws_bytes(n, B, build_plan(p, opts), opts->compute);
+  return SHAMPOO_OK;
+}
+
+shampoo_status shampoo_inverse_root(const void* in, void* out, shampoo_dtype io_dt, int64_t n, int32_t B, int32_t p,
+                                    const shampoo_root_opts* opts, const int32_t* valid_dev, float* scale_out_dev,
+                                    int32_t* flags_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return inverse_root_impl(in, out, io_dt, n, B, p, opts, valid_dev, scale_out_dev, flags_dev, ws, ws_bytes, stream);
+}
+
+shampoo_status shampoo_precondition_workspace(int64_t nblk, int32_t B, size_t* bytes) {
+  if (!bytes || nblk < 0 || B < 1) return fail(SHAMPOO_E_INVALID, "bad arguments");
+  *bytes = (size_t)nblk * B * B * 4;
+  return SHAMPOO_OK;
+}
+
+shampoo_status shampoo_precondition(const float* roots, const void* gstack, shampoo_dtype g_dt, int64_t nblk,
+                                    int32_t B, float* dstack, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return precond_impl(roots, gstack, g_dt, nblk, B, dstack, ws, ws_bytes, stream);
+}
+
+shampoo_status shampoo_step_workspace(const shampoo_step_args* args, size_t* bytes) {
+  if (!bytes) return fail(SHAMPOO_E_INVALID, "bytes is NULL");
+  StepLayout L;
+  shampoo_status r = step_layout(args, &L);
+  if (r != SHAMPOO_OK) return r;
+  *bytes = L.total;
+  return SHAMPOO_OK;
+}
+
+shampoo_status shampoo_step(const shampoo_step_args* args, hipStream_t stream) { return step_impl(args, stream); }
+
+shampoo_status shampoo_check_flags(const int32_t* flags_dev, int64_t n, hipStream_t stream) {
+  if (n < 0) return fail(SHAMPOO_E_INVALID, "n < 0");
+  if (n == 0) return SHAMPOO_OK;
+  if (!flags_dev) return fail(SHAMPOO_E_INVALID, "flags_dev is NULL");
+  int32_t host[4096];
+  bool any = false;
+  for (int64_t i = 0; i < n; i += 4096) {
+    const int64_t m = (n - i) < 4096 ? (n - i) : 4096;
+    HIP_TRY(hipMemcpyAsync(host, flags_dev + i, (size_t)m * 4, hipMemcpyDeviceToHost, stream));
+    HIP_TRY(hipStreamSynchronize(stream));
+    for (int64_t j = 0; j < m; ++j)
+      if (host[j]) any = true;
+  }
+  if (any) return fail(SHAMPOO_E_NONFINITE, "flagged matrices present");
+  return SHAMPOO_OK;
+}
+
+shampoo_status shampoo_timing_enable(int32_t capacity) {
+  if (capacity < 0 || capacity > (1 << 20)) return fail(SHAMPOO_E_INVALID, "capacity %d", capacity);
+  for (hipEvent_t e : g_timing.ev) (void)hipEventDestroy(e);
+  g_timing.ev.clear();
+  g_timing.cap = 0;
+  g_timing.used = 0;
+  if (capacity == 0) return SHAMPOO_OK;
+  g_timing.ev.resize(2 * (size_t)capacity);
+  for (auto& e : g_timing.ev) HIP_TRY(hipEventCreate(&e));
+  g_timing.cap = capacity;
+  return SHAMPOO_OK;
+}
+
+shampoo_status shampoo_timing_read(float* ms, int32_t capacity, int32_t* count) {
+  if (!count || (capacity > 0 && !ms) || capacity < 0) return fail(SHAMPOO_E_INVALID, "bad arguments");
+  const int n = g_timing.used < capacity ? g_timing.used : capacity;
+  for (int i = 0; i < n; ++i) {
+    HIP_TRY(hipEventSynchronize(g_timing.ev[2 * i + 1]));
+    HIP_TRY(hipEventElapsedTime(ms + i, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]));
+  }
+  *count = n;
+  g_timing.used = 0;
+  return SHAMPOO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+"""Optimizer facade over ``shampoo_step``: plans the blocks, owns the state
+tensors and calls the C ABI once per block-size stack.
+
+[3DS] "How to use" / "Hyperparameters": the optimizer is built from a list of
+parameters with ``lr``, ``momentum`` and a hyper-parameter set (block size,
+grafting type, preconditioning frequency); [DASH] "4. Blocking Strategy":
+blocks of every parameter that share a block size are stacked together (one
+stack per size over all parameters, the GPU-wide stacking the summary finds
+faster than per-layer stacking).
+"""
+
+import ctypes
+import math
+
+import numpy as np
+
+from . import (RootOpts, StepArgsC, GRAFTS, F32, BF16, shampoo_plan_blocks, shampoo_step,
+               shampoo_step_workspace, table_to_device, _ptr)
+
+
+def reshape_2d(shape):
+    """2-D view of a parameter shape: keep dim 0, merge the rest."""
+    shape = tuple(int(s) for s in shape)
+    if len(shape) == 0:
+        return (1, 1)
+    if len(shape) == 1:
+        return (1, shape[0])
+    return (shape[0], int(math.prod(shape[1:])))
+
+
+def _round64(x):
+    return (int(x) + 63) // 64 * 64
+
+
+class ShampooStack:
+    """The parameters whose blocks share one stack side B, with their state."""
+
+    def __init__(self, weights, block_sizes, hp, device):
+        import torch
+        self.torch = torch
+        self.hp = hp
+        self.weights = weights                      # 2-D float32 views
+        shapes = [tuple(w.shape) for w in weights]
+        self.table = shampoo_plan_blocks(shapes, block_sizes)
+        self.nblk = self.table.shape[0]
+        self.B = _round64(max(int(self.table[:, 7].max()), 1)) if self.nblk else 64
+        self.table_dev = table_to_device(self.table, device)
+        first = {}
+        for b in range(self.nblk):
+            first.setdefault(int(self.table[b, 0]), b)
+        self.first_block = [first.get(i, 0) for i in range(len(weights))]
+        f32 = torch.float32
+        self.LR = torch.zeros((2 * self.nblk, self.B, self.B), dtype=f32, device=device)
+        self.roots = torch.zeros_like(self.LR)
+        self.flags = torch.zeros(2 * self.nblk, dtype=torch.int32, device=device)
+        g = hp["graft"]
+        self.m = [torch.zeros_like(w) for w in weights] if g in ("momentum", "adam") else None
+        self.v = [torch.zeros_like(w) for w in weights] if g == "adam" else None
+        self.grad_dtype = hp["grad_dtype"]
+        self.params_dev = None
+        self._grad_ptrs = None
+        self.args = StepArgsC()
+        a = self.args
+        a.nparams = len(weights)
+        a.B = self.B
+        a.nblk = self.nblk
+        a.table_dev = self.table_dev.data_ptr()
+        a.g_dt = BF16 if self.grad_dtype == torch.bfloat16 else F32
+        a.p = hp["p"]
+        a.LR = self.LR.data_ptr()
+        a.roots = self.roots.data_ptr()
+        a.beta2 = hp["beta2"]
+        a.root = hp["root"].c()
+        a.graft = GRAFTS[g]
+        a.graft_blockwise = 1 if hp["graft_blockwise"] else 0
+        a.lr = hp["lr"]
+        a.momentum = hp["momentum"]
+        a.beta1 = hp["beta1"]
+        a.graft_beta2 = hp["graft_beta2"]
+        a.graft_eps = hp["graft_eps"]
+        a.flags_dev = self.flags.data_ptr()
+        a.dstack = None
+        nb = shampoo_step_workspace(a)
+        self.ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=device)
+        a.ws = self.ws.data_ptr()
+        a.ws_bytes = self.ws.numel()
+
+    def _descriptors(self, grads):
+        torch = self.torch
+        ptrs = tuple(g.data_ptr() for g in grads)
+        if ptrs == self._grad_ptrs:
+            return
+        rows = []
+        for i, (w, g) in enumerate(zip(self.weights, grads)):
+            rows.append([w.data_ptr(), g.data_ptr(),
+                         self.m[i].data_ptr() if self.m is not None else 0,
+                         self.v[i].data_ptr() if self.v is not None else 0,
+                         w.shape[0], w.shape[1], w.stride(0), self.first_block[i]])
+        self.params_dev = torch.tensor(rows, dtype=torch.int64).reshape(-1, 8).to(self.LR.device)
+        self.args.params_dev = self.params_dev.data_ptr()
+        self._grad_ptrs = ptrs
+
+    def step(self, grads, t, recompute, dstack=None, stream=None):
+        for g, w in zip(grads, self.weights):
+            if g.dtype != self.grad_dtype or tuple(g.shape) != tuple(w.shape) or not g.is_contiguous():
+                raise ValueError("gradient must be a contiguous %s tensor of shape %s" % (self.grad_dtype, tuple(w.shape)))
+        self._descriptors(grads)
+        self.args.t = int(t)
+        self.args.recompute_roots = 1 if recompute else 0
+        self.args.dstack = None if dstack is None else dstack.data_ptr()
+        shampoo_step(self.args, stream)
+
+
+class Shampoo:
+    """Block-diagonal Shampoo over a list of float32 device parameters.
+
+    block_size: int, or a callable (rows, cols) -> block size (0 = whole
+    parameter as one block).  graft: "sgd" | "momentum" | "adam" | "none".
+    precondition_frequency: roots recomputed every that many steps (the
+    statistics are updated every step).
+    """
+
+    def __init__(self, params, block_size=1024, beta2=1.0, eps=1e-12, p=4, root=None, graft="sgd",
+                 lr=0.1, momentum=0.9, beta1=0.9, graft_beta2=0.999, graft_eps=1e-8,
+                 graft_blockwise=False, precondition_frequency=1, grad_dtype=None):
+        import torch
+        params = list(params)
+        if not params:
+            raise ValueError("no parameters")
+        for w in params:
+            if w.dtype != torch.float32 or not w.is_cuda or not w.is_contiguous():
+                raise ValueError("parameters must be contiguous float32 device tensors")
+        self.params = params
+        self.views = [w.view(reshape_2d(w.shape)) for w in params]
+        root = root if root is not None else RootOpts(method="cn", iters=20, eps=eps)
+        if root.eps != eps:
+            root = RootOpts(**{**root.__dict__, "eps": eps})
+        self.hp = dict(beta2=float(beta2), p=int(p), root=root, graft=graft, lr=float(lr),
+                       momentum=float(momentum), beta1=float(beta1), graft_beta2=float(graft_beta2),
+                       graft_eps=float(graft_eps), graft_blockwise=bool(graft_blockwise),
+                       grad_dtype=grad_dtype if grad_dtype is not None else torch.float32)
+        bs_of = block_size if callable(block_size) else (lambda m, n, b=int(block_size): b)
+        groups = {}
+        for i, v in enumerate(self.views):
+            m, n = v.shape
+            b = int(bs_of(m, n))
+            plan_b = max(m, n) if (b == 0 or b >= max(m, n)) else b
+            groups.setdefault(_round64(plan_b), []).append((i, plan_b))
+        self.stacks = []
+        self.members = []
+        for side in sorted(groups):
+            idx = [i for i, _ in groups[side]]
+            st = ShampooStack([self.views[i] for i in idx], [b for _, b in groups[side]], self.hp,
+                              params[0].device)
+            self.stacks.append(st)
+            self.members.append(idx)
+        self.frequency = int(precondition_frequency)
+        self.t = 0
+
+    def step(self, grads, stream=None):
+        """One step with gradients given per parameter (same order as params)."""
+        self.t += 1
+        recompute = (self.t - 1) % self.frequency == 0
+        views = [g.reshape(v.shape) for g, v in zip(grads, self.views)]
+        for st, idx in zip(self.stacks, self.members):
+            st.step([views[i] for i in idx], self.t, recompute, stream=stream)
+
+    def flags(self):
+        return [st.flags for st in self.stacks]

@@ -1,0 +1,144 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every
+function include/shampoo.h declares, the host planner matches the oracle's
+table bit for bit, and bad arguments are rejected before any launch."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def mir():
+    import matrix_inverse_roots_amd as m
+    return m
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "shampoo.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(shampoo_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(mir):
+    names = declared_functions()
+    assert len(names) >= 13
+    lib = ctypes.CDLL(mir.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(mir.EXPORTS) == names
+    assert "gfx950" in mir.version()
+
+
+def test_struct_sizes_match_header(mir):
+    assert ctypes.sizeof(mir.Block) == 32
+    assert ctypes.sizeof(mir.Matrix) == 32
+    assert ctypes.sizeof(mir.Param) == 64
+    assert ctypes.sizeof(mir.RootOptsC) == 64
+
+
+@pytest.mark.parametrize("case", ["dash", "decoder", "bottleneck50", "mixed"])
+def test_plan_blocks_bit_exact_vs_oracle(mir, case):
+    if case == "dash":
+        shapes, bs = [(32000, 2048)], [1024]
+    elif case == "decoder":
+        shapes = synthetic.decoder_shapes()
+        bs = [1024] * len(shapes)
+    elif case == "bottleneck50":
+        shapes = synthetic.bottleneck50_shapes()
+        bs = synthetic.bottleneck50_block_sizes(shapes)
+    else:
+        shapes = [(300, 130), (64, 64), (5, 700), (1, 9), (77, 0), (129, 129)]
+        bs = [128, 128, 256, 0, 64, 0]
+    t_lib = mir.shampoo_plan_blocks(shapes, bs)
+    t_orc = oracle.plan_blocks(shapes, bs)
+    assert t_lib.dtype == np.int32
+    assert np.array_equal(t_lib.astype(np.int64), t_orc)
+
+
+def test_plan_blocks_rejects_bad_input(mir):
+    with pytest.raises(mir.ShampooError) as e:
+        mir.shampoo_plan_blocks([(-1, 4)], [2])
+    assert e.value.status == mir.E_INVALID
+    # capacity too small
+    shapes = np.asarray([[10, 10]], dtype=np.int64)
+    bs = np.asarray([4], dtype=np.int32)
+    out = np.zeros((2, 8), dtype=np.int32)
+    n = ctypes.c_int64(2)
+    st = mir.lib.shampoo_plan_blocks(shapes.ctypes.data, bs.ctypes.data, 1, out.ctypes.data, ctypes.byref(n))
+    assert st == mir.E_INVALID and n.value == 9
+
+
+def test_workspace_queries_and_support_matrix(mir):
+    o = mir.RootOpts(method="ndb", iters=28, iters2=17, scaling="power", pi_vectors=16)
+    b = mir.shampoo_inverse_root_workspace(1024, 512, 4, o)
+    assert b >= 1024 * 512 * 512 * 4 * 3
+    for opts, p, status in [
+        (mir.RootOpts(method="ndb", iters=5, iters2=5), 3, mir.E_UNSUPPORTED),
+        (mir.RootOpts(method="cn", iters=5), 3, mir.E_UNSUPPORTED),
+        (mir.RootOpts(method="cn", iters=0), 4, mir.E_INVALID),
+        (mir.RootOpts(method="cn", iters=5, compute="bf16"), 4, mir.E_UNSUPPORTED),
+        (mir.RootOpts(method="ndb", iters=5, iters2=5, scaling="power", pi_vectors=32), 4, mir.E_UNSUPPORTED),
+        (mir.RootOpts(method="chebyshev", cheb_degree=8, cheb_points=5), 4, mir.E_INVALID),
+    ]:
+        B = 1024
+        with pytest.raises(mir.ShampooError) as e:
+            mir.shampoo_inverse_root_workspace(4, B, p, opts)
+        assert e.value.status == status, (opts, p)
+    with pytest.raises(mir.ShampooError) as e:
+        mir.shampoo_inverse_root_workspace(4, 100, 4, mir.RootOpts())
+    assert e.value.status == mir.E_UNSUPPORTED
+
+
+def test_invalid_calls_fail_before_launch(mir):
+    oc = mir.RootOpts(method="cn", iters=5).c()
+    # null input
+    st = mir.lib.shampoo_inverse_root(None, None, mir.F32, 4, 128, 4, ctypes.byref(oc), None, None, None, None, 0, None)
+    assert st == mir.E_INVALID
+    # workspace too small (fake non-null device pointers: rejected before use)
+    fake = ctypes.c_void_p(0x1000)
+    st = mir.lib.shampoo_inverse_root(fake, fake, mir.F32, 4, 128, 4, ctypes.byref(oc), None, None, None, fake, 16, None)
+    assert st == mir.E_WORKSPACE
+    assert b"workspace" in mir.lib.shampoo_last_error()
+    # bad io dtype
+    st = mir.lib.shampoo_inverse_root(fake, fake, mir.BF16, 4, 128, 4, ctypes.byref(oc), None, None, None, fake, 1 << 40, None)
+    assert st == mir.E_UNSUPPORTED
+    # statistics: beta2 out of range, bad dtype
+    st = mir.lib.shampoo_update_stats(fake, fake, mir.F32, 2, 128, fake, ctypes.c_float(1.5), None)
+    assert st == mir.E_INVALID
+    st = mir.lib.shampoo_update_stats(fake, fake, mir.F16, 2, 128, fake, ctypes.c_float(0.9), None)
+    assert st == mir.E_UNSUPPORTED
+    # precondition: short workspace
+    st = mir.lib.shampoo_precondition(fake, fake, mir.F32, 2, 128, fake, fake, 10, None)
+    assert st == mir.E_WORKSPACE
+    # n == 0 is a no-op
+    st = mir.lib.shampoo_inverse_root(None, None, mir.F32, 0, 128, 4, ctypes.byref(oc), None, None, None, None, 0, None)
+    assert st == mir.OK
+
+
+def test_step_workspace_and_validation(mir):
+    a = mir.StepArgsC()
+    a.nparams, a.B, a.nblk = 1, 128, 2
+    a.g_dt, a.p = mir.F32, 4
+    a.root = mir.RootOpts(method="cn", iters=10).c()
+    b = mir.shampoo_step_workspace(a)
+    assert b >= 2 * 2 * 128 * 128 * 4
+    a.B = 96
+    with pytest.raises(mir.ShampooError):
+        mir.shampoo_step_workspace(a)
+
+
+def test_no_cpu_fallback_in_product():
+    """The product package has no path that computes on the host."""
+    pkg = os.path.join(ROOT, "matrix_inverse_roots_amd")
+    for f in os.listdir(pkg):
+        if f.endswith(".py"):
+            src = open(os.path.join(pkg, f)).read()
+            assert "torch.linalg" not in src and "np.linalg" not in src and "scipy" not in src, f

