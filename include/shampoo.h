@@ -159,9 +159,11 @@ typedef struct shampoo_step_args {
   const shampoo_block* table_dev;   /* device [nblk], as planned for B */
   shampoo_dtype g_dt;               /* SHAMPOO_F32 or SHAMPOO_BF16 */
   int32_t p;                        /* root order, 4 for Shampoo */
-  float* LR;                        /* device f32 [2 nblk, B, B]: L stack then R stack (state) */
-  float* roots;                     /* device f32 [2 nblk, B, B]: inverse roots (state) */
-  float beta2;                      /* statistics EMA; 1 = plain sum */
+  shampoo_dtype stats_dt;           /* SHAMPOO_F32 or SHAMPOO_F64: element type of LR and roots */
+  int32_t reserved0;
+  void* LR;                         /* device [2 nblk, B, B] stats_dt: L stack then R stack (state) */
+  void* roots;                      /* device [2 nblk, B, B] stats_dt: inverse roots (state) */
+  double beta2;                     /* statistics EMA; 1 = plain sum */
   int32_t recompute_roots;          /* 0: reuse `roots` from an earlier step */
   shampoo_root_opts root;
   int32_t graft;                    /* shampoo_graft */
@@ -218,11 +220,13 @@ shampoo_status shampoo_unpack_blocks(const float* stack, const shampoo_block* ta
  * and L_b += G_b G_b^T, R_b += G_b^T G_b when beta2 == 1.
  * gstack, gstack_t: device [nblk, B, B] block stack and its per-block
  * transpose (as written by shampoo_pack_blocks) in g_dt (F32 or BF16);
- * LR: device f32 [2 nblk, B, B], L_0..L_(nblk-1) then R_0..R_(nblk-1),
- * updated in place; kept exactly symmetric.  B must be a multiple of 64. */
+ * LR: device [2 nblk, B, B] in stats_dt (F32: float32 matrix cores; F64:
+ * float64 matrix cores, the gradient widened exactly), L_0..L_(nblk-1) then
+ * R_0..R_(nblk-1), updated in place; kept exactly symmetric.  B must be a
+ * multiple of 64. */
 shampoo_status shampoo_update_stats(const void* gstack, const void* gstack_t, shampoo_dtype g_dt,
-                                    int64_t nblk, int32_t B, float* LR, float beta2,
-                                    hipStream_t stream);
+                                    int64_t nblk, int32_t B, void* LR, shampoo_dtype stats_dt,
+                                    double beta2, hipStream_t stream);
 
 /* Workspace bytes for shampoo_inverse_root with these arguments. */
 shampoo_status shampoo_inverse_root_workspace(int64_t n, int32_t B, int32_t p,
@@ -248,18 +252,20 @@ shampoo_status shampoo_inverse_root(const void* in, void* out, shampoo_dtype io_
                                     int32_t* flags_dev, void* ws, size_t ws_bytes,
                                     hipStream_t stream);
 
-/* Workspace bytes for shampoo_precondition: nblk * B * B * 4. */
-shampoo_status shampoo_precondition_workspace(int64_t nblk, int32_t B, size_t* bytes);
+/* Workspace bytes for shampoo_precondition: nblk * B * B * sizeof(roots_dt). */
+shampoo_status shampoo_precondition_workspace(int64_t nblk, int32_t B, shampoo_dtype roots_dt,
+                                              size_t* bytes);
 
 /* Search direction per block.  [NOTES] "AdaGrad's regret argument goes
  * through with the Kronecker preconditioner": S^(-1) vec(G) with
  * S = L^(1/4) (x) R^(1/4), i.e. D_b = Lr_b G_b Rr_b.
- * roots: device f32 [2 nblk, B, B] (inverse roots of L then of R, symmetric);
- * gstack: device [nblk, B, B] in g_dt (F32 or BF16); dstack: device f32
- * [nblk, B, B].  B must be a multiple of 64. */
-shampoo_status shampoo_precondition(const float* roots, const void* gstack, shampoo_dtype g_dt,
-                                    int64_t nblk, int32_t B, float* dstack, void* ws,
-                                    size_t ws_bytes, hipStream_t stream);
+ * roots: device [2 nblk, B, B] in roots_dt (F32 or F64; inverse roots of L
+ * then of R, symmetric; the products run in that precision); gstack: device
+ * [nblk, B, B] in g_dt (F32 or BF16); dstack: device f32 [nblk, B, B].
+ * B must be a multiple of 64. */
+shampoo_status shampoo_precondition(const void* roots, shampoo_dtype roots_dt, const void* gstack,
+                                    shampoo_dtype g_dt, int64_t nblk, int32_t B, float* dstack,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes for shampoo_step with these arguments (ws fields ignored). */
 shampoo_status shampoo_step_workspace(const shampoo_step_args* args, size_t* bytes);

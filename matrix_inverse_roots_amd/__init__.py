@@ -72,8 +72,9 @@ class StepArgsC(ctypes.Structure):
     _fields_ = [("nparams", ctypes.c_int32), ("B", ctypes.c_int32), ("nblk", ctypes.c_int64),
                 ("params_dev", ctypes.c_void_p), ("table_dev", ctypes.c_void_p),
                 ("g_dt", ctypes.c_int32), ("p", ctypes.c_int32),
+                ("stats_dt", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("LR", ctypes.c_void_p), ("roots", ctypes.c_void_p),
-                ("beta2", ctypes.c_float), ("recompute_roots", ctypes.c_int32),
+                ("beta2", ctypes.c_double), ("recompute_roots", ctypes.c_int32),
                 ("root", RootOptsC),
                 ("graft", ctypes.c_int32), ("graft_blockwise", ctypes.c_int32),
                 ("lr", ctypes.c_float), ("momentum", ctypes.c_float),
@@ -108,12 +109,13 @@ def _load():
         "shampoo_plan_blocks": ([vp, vp, i32, vp, P(i64)], ctypes.c_int),
         "shampoo_pack_blocks": ([vp, i32, vp, i64, i32, ctypes.c_int, vp, vp, vp], ctypes.c_int),
         "shampoo_unpack_blocks": ([vp, vp, i64, i32, vp, i32, vp], ctypes.c_int),
-        "shampoo_update_stats": ([vp, vp, ctypes.c_int, i64, i32, vp, ctypes.c_float, vp], ctypes.c_int),
+        "shampoo_update_stats": ([vp, vp, ctypes.c_int, i64, i32, vp, ctypes.c_int, ctypes.c_double, vp],
+                                 ctypes.c_int),
         "shampoo_inverse_root_workspace": ([i64, i32, i32, P(RootOptsC), P(sz)], ctypes.c_int),
         "shampoo_inverse_root": ([vp, vp, ctypes.c_int, i64, i32, i32, P(RootOptsC), vp, vp, vp, vp, sz, vp],
                                  ctypes.c_int),
-        "shampoo_precondition_workspace": ([i64, i32, P(sz)], ctypes.c_int),
-        "shampoo_precondition": ([vp, vp, ctypes.c_int, i64, i32, vp, vp, sz, vp], ctypes.c_int),
+        "shampoo_precondition_workspace": ([i64, i32, ctypes.c_int, P(sz)], ctypes.c_int),
+        "shampoo_precondition": ([vp, ctypes.c_int, vp, ctypes.c_int, i64, i32, vp, vp, sz, vp], ctypes.c_int),
         "shampoo_step_workspace": ([P(StepArgsC), P(sz)], ctypes.c_int),
         "shampoo_step": ([P(StepArgsC), vp], ctypes.c_int),
         "shampoo_check_flags": ([vp, i64, vp], ctypes.c_int),
@@ -252,11 +254,13 @@ def shampoo_unpack_blocks(stack, table_dev, B, outs, stream=None):
 
 
 def shampoo_update_stats(gstack, gstack_t, LR, beta2, stream=None):
+    """L, R (the two halves of LR, float32 or float64) updated from a block
+    stack and its transpose."""
     for t, n in ((gstack, "gstack"), (gstack_t, "gstack_t"), (LR, "LR")):
         _dev(t, n)
     nblk, B = gstack.shape[0], gstack.shape[1]
     _check(lib.shampoo_update_stats(_ptr(gstack), _ptr(gstack_t), _dtype_code(gstack), nblk, B, _ptr(LR),
-                                    float(beta2), _stream(stream)))
+                                    _dtype_code(LR), float(beta2), _stream(stream)))
 
 
 def shampoo_inverse_root_workspace(n, B, p, opts):
@@ -285,14 +289,17 @@ def shampoo_inverse_root(inp, out, p, opts, valid=None, scale_out=None, flags=No
 
 
 def shampoo_precondition(roots, gstack, dstack, ws=None, stream=None):
+    """dstack = Lr G Rr per block; roots float32 or float64 [2 nblk, B, B]."""
     torch = _torch()
     for t, nm in ((roots, "roots"), (gstack, "gstack"), (dstack, "dstack")):
         _dev(t, nm)
     nblk, B = gstack.shape[0], gstack.shape[1]
     if ws is None:
-        ws = torch.empty(max(nblk * B * B * 4, 1), dtype=torch.uint8, device=gstack.device)
-    _check(lib.shampoo_precondition(_ptr(roots), _ptr(gstack), _dtype_code(gstack), nblk, B, _ptr(dstack),
-                                    _ptr(ws), ws.numel(), _stream(stream)))
+        b = ctypes.c_size_t(0)
+        _check(lib.shampoo_precondition_workspace(nblk, B, _dtype_code(roots), ctypes.byref(b)))
+        ws = torch.empty(max(b.value, 1), dtype=torch.uint8, device=gstack.device)
+    _check(lib.shampoo_precondition(_ptr(roots), _dtype_code(roots), _ptr(gstack), _dtype_code(gstack), nblk, B,
+                                    _ptr(dstack), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def shampoo_step_workspace(args):

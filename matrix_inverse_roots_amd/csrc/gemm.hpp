@@ -149,6 +149,32 @@ template <> struct Chunk<double, double, 2> {  // f64 -> f64
   __device__ __forceinline__ double get(int e) const { return w[e]; }
 };
 
+template <> struct Chunk<float, double, 2> {  // f32 -> f64 (exact)
+  u32x2 w;
+  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const u32x2*>(p); }
+  __device__ __forceinline__ double get(int e) const { return (double)__uint_as_float(w[e]); }
+  __device__ __forceinline__ void store(unsigned char* d) const {
+    doublex2 o;
+    o[0] = (double)__uint_as_float(w[0]);
+    o[1] = (double)__uint_as_float(w[1]);
+    *reinterpret_cast<doublex2*>(d) = o;
+  }
+};
+
+template <> struct Chunk<__bf16, double, 2> {  // bf16 -> f64 (exact)
+  uint32_t w;
+  __device__ __forceinline__ void load(const __bf16* p) { w = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ double get(int e) const {
+    return (double)__uint_as_float(e ? (w & 0xffff0000u) : (w << 16));
+  }
+  __device__ __forceinline__ void store(unsigned char* d) const {
+    doublex2 o;
+    o[0] = (double)__uint_as_float(w << 16);
+    o[1] = (double)__uint_as_float(w & 0xffff0000u);
+    *reinterpret_cast<doublex2*>(d) = o;
+  }
+};
+
 template <> struct Chunk<float, _Float16, 8> {  // f32 -> f16, round to nearest even
   floatx4 lo, hi;
   __device__ __forceinline__ void load(const float* p) {

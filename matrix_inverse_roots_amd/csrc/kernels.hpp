@@ -303,43 +303,52 @@ __global__ __launch_bounds__(256) void power_iter_kernel(const TS* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// finalize: out = X s^(-1/p) on the valid region, 0 elsewhere
+// finalize: out = X s^(-1/p) on the valid region, 0 elsewhere; with sym_out
+// the symmetric part (X + X^T)/2 is taken first.  One workgroup per 64 x 64
+// tile: the tile and its mirror are staged through LDS so that every global
+// access is a coalesced row segment; one flag update per workgroup.
 // ---------------------------------------------------------------------------
 template <typename TS, typename TO>
 __global__ __launch_bounds__(256) void finalize_kernel(const TS* __restrict__ X, TO* __restrict__ out, int B,
-                                                       int64_t nmat, const int32_t* __restrict__ valid,
+                                                       const int32_t* __restrict__ valid,
                                                        const double* __restrict__ s, double inv_p,
                                                        int sym_out, float* __restrict__ scale_out,
                                                        int32_t* __restrict__ flags) {
+  __shared__ TS mir_tile[64][65];
+  const int tps = B / 64;
+  const int64_t b = blockIdx.y;
+  const int tr = blockIdx.x / tps, tc = blockIdx.x - (blockIdx.x / tps) * tps;
   const int64_t BB = (int64_t)B * B;
-  const int64_t idx = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) * 4;
-  if (idx >= nmat * BB) return;
-  const int64_t b = idx / BB;
-  const int64_t e = idx - b * BB;
-  const int r = (int)(e / B);
-  const int c0 = (int)(e - (int64_t)r * B);
+  const TS* Xb = X + b * BB;
+  TO* ob = out + b * BB;
   const int v = valid ? min(max(valid[b], 0), B) : B;
   const double sb = s[b];
   const bool zero = !(sb > 0.0 && sb < 1.0e300);
   const double f = zero ? 0.0 : pow(sb, -inv_p);
-  bool bad = false;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c = c0 + q;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  if (sym_out) {
+    // mirror tile (tc, tr): element [cc][rr] = X[tc*64 + cc][tr*64 + rr]
+    for (int cc = ty; cc < 64; cc += 4) mir_tile[cc][tx] = Xb[(int64_t)(tc * 64 + cc) * B + tr * 64 + tx];
+    __syncthreads();
+  }
+  int bad = 0;
+  for (int rr = ty; rr < 64; rr += 4) {
+    const int r = tr * 64 + rr, c = tc * 64 + tx;
     double x = 0.0;
     if (r < v && c < v && !zero) {
-      x = (double)X[idx + q];
-      if (sym_out) x = 0.5 * (x + (double)X[b * BB + (int64_t)c * B + r]);
+      x = (double)Xb[(int64_t)r * B + c];
+      if (sym_out) x = 0.5 * (x + (double)mir_tile[tx][rr]);
       x *= f;
-      if (!isfinite(x)) bad = true;
+      if (!isfinite(x)) bad = 1;
     }
-    out[idx + q] = (TO)x;
+    ob[(int64_t)r * B + c] = (TO)x;
   }
-  if (flags) {
-    if (bad) atomicOr(flags + b, SHAMPOO_FLAG_NONFINITE);
-    if (zero && e == 0) atomicOr(flags + b, SHAMPOO_FLAG_ZERO_SCALE);
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    if (flags && zero) atomicOr(flags + b, SHAMPOO_FLAG_ZERO_SCALE);
+    if (scale_out) scale_out[b] = (float)sb;
   }
-  if (scale_out && e == 0) scale_out[b] = (float)sb;
+  if (threadIdx.x == 0 && bad && flags) atomicOr(flags + b, SHAMPOO_FLAG_NONFINITE);
 }
 
 // ---------------------------------------------------------------------------

@@ -515,9 +515,9 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
       HIP_TRY(timing_mark(1, st));
       timing_advance();
     } else {
-      const int64_t g = elementwise_grid(n * BB);
-      hipLaunchKernelGGL((finalize_kernel<TS, TI>), dim3((unsigned)g), dim3(256), 0, st, buf(op.a), (TI*)out, B, n,
-                         valid, sc, 1.0 / p, P.sym_out ? 1 : 0, scale_out, flags);
+      const int tps = B / 64;
+      hipLaunchKernelGGL((finalize_kernel<TS, TI>), dim3((unsigned)(tps * tps), (unsigned)n), dim3(256), 0, st,
+                         buf(op.a), (TI*)out, B, valid, sc, 1.0 / p, P.sym_out ? 1 : 0, scale_out, flags);
       LAUNCH_CHECK("finalize");
     }
   }
@@ -535,7 +535,7 @@ shampoo_status inverse_root_impl(const void* in, void* out, shampoo_dtype io_dt,
   if (!in || !out) return fail(SHAMPOO_E_INVALID, "in/out is NULL");
   if (o->scaling == SHAMPOO_SCALE_POWER && !o->pi_start_dev)
     return fail(SHAMPOO_E_INVALID, "power scaling needs pi_start_dev");
-  if (gemm_wgs(B, n, true) >= (int64_t)1 << 31 || n >= ((int64_t)1 << 31))
+  if (gemm_wgs(B, n, false) >= (int64_t)1 << 31 || n > 65535)
     return fail(SHAMPOO_E_UNSUPPORTED, "batch too large for one launch");
   const Plan P = build_plan(p, o);
   const size_t need = root_ws_bytes(n, B, P, o->compute);
@@ -584,24 +584,33 @@ shampoo_status pack_impl(const shampoo_matrix* mats, int32_t nparams, const sham
   return SHAMPOO_OK;
 }
 
-shampoo_status stats_impl(const void* g, const void* gt, shampoo_dtype gdt, int64_t nblk, int32_t B, float* LR,
-                          float beta2, hipStream_t st) {
+shampoo_status stats_impl(const void* g, const void* gt, shampoo_dtype gdt, int64_t nblk, int32_t B, void* LR,
+                          shampoo_dtype sdt, double beta2, hipStream_t st) {
   if (nblk < 0) return fail(SHAMPOO_E_INVALID, "nblk < 0");
   if (B < 64 || B % 64 != 0) return fail(SHAMPOO_E_UNSUPPORTED, "B = %d: must be a positive multiple of 64", B);
-  if (!(beta2 >= 0.0f && beta2 <= 1.0f)) return fail(SHAMPOO_E_INVALID, "beta2 = %g not in [0, 1]", beta2);
+  if (!(beta2 >= 0.0 && beta2 <= 1.0)) return fail(SHAMPOO_E_INVALID, "beta2 = %g not in [0, 1]", beta2);
   if (gdt != SHAMPOO_F32 && gdt != SHAMPOO_BF16) return fail(SHAMPOO_E_UNSUPPORTED, "gradient dtype %d (F32, BF16)", (int)gdt);
+  if (sdt != SHAMPOO_F32 && sdt != SHAMPOO_F64) return fail(SHAMPOO_E_UNSUPPORTED, "statistics dtype %d (F32, F64)", (int)sdt);
   if (nblk == 0) return SHAMPOO_OK;
   if (!g || !gt || !LR) return fail(SHAMPOO_E_INVALID, "null pointer argument");
   if (gemm_wgs(B, nblk, true) >= (int64_t)1 << 31) return fail(SHAMPOO_E_UNSUPPORTED, "batch too large");
-  const double a = beta2 == 1.0f ? 1.0 : 1.0 - (double)beta2;
+  const double a = beta2 == 1.0 ? 1.0 : 1.0 - beta2;
   const double b = beta2;
-  const size_t es = gdt == SHAMPOO_F32 ? 4 : 2;
-  (void)es;
+  const size_t half = (size_t)nblk * B * B * (sdt == SHAMPOO_F64 ? 8 : 4);
+  // L = beta2 L + (1 - beta2) G G^T and R from G^T, both as symmetric NT products in place
   GemmCall cl;
   cl.A = g; cl.B = g; cl.D = LR; cl.C = LR; cl.C2 = nullptr; cl.alpha = a; cl.beta = b; cl.sym = true;
   GemmCall cr = cl;
-  cr.A = gt; cr.B = gt; cr.D = LR + nblk * (int64_t)B * B; cr.C = (void*)cr.D;
-  if (gdt == SHAMPOO_F32) {
+  cr.A = gt; cr.B = gt; cr.D = (unsigned char*)LR + half; cr.C = (unsigned char*)LR + half;
+  if (sdt == SHAMPOO_F64) {
+    if (gdt == SHAMPOO_F32) {
+      HIP_TRY((gemm<Mma::F64, float, float, double>(cl, B, nblk, st)));
+      HIP_TRY((gemm<Mma::F64, float, float, double>(cr, B, nblk, st)));
+    } else {
+      HIP_TRY((gemm<Mma::F64, __bf16, __bf16, double>(cl, B, nblk, st)));
+      HIP_TRY((gemm<Mma::F64, __bf16, __bf16, double>(cr, B, nblk, st)));
+    }
+  } else if (gdt == SHAMPOO_F32) {
     HIP_TRY((gemm<Mma::F32, float, float, float>(cl, B, nblk, st)));
     HIP_TRY((gemm<Mma::F32, float, float, float>(cr, B, nblk, st)));
   } else {
@@ -611,26 +620,34 @@ shampoo_status stats_impl(const void* g, const void* gt, shampoo_dtype gdt, int6
   return SHAMPOO_OK;
 }
 
-shampoo_status precond_impl(const float* roots, const void* g, shampoo_dtype gdt, int64_t nblk, int32_t B,
-                            float* dstack, void* ws, size_t ws_bytes, hipStream_t st) {
+shampoo_status precond_impl(const void* roots, shampoo_dtype rdt, const void* g, shampoo_dtype gdt, int64_t nblk,
+                            int32_t B, float* dstack, void* ws, size_t ws_bytes, hipStream_t st) {
   if (nblk < 0) return fail(SHAMPOO_E_INVALID, "nblk < 0");
   if (B < 64 || B % 64 != 0) return fail(SHAMPOO_E_UNSUPPORTED, "B = %d: must be a positive multiple of 64", B);
   if (gdt != SHAMPOO_F32 && gdt != SHAMPOO_BF16) return fail(SHAMPOO_E_UNSUPPORTED, "gradient dtype %d (F32, BF16)", (int)gdt);
+  if (rdt != SHAMPOO_F32 && rdt != SHAMPOO_F64) return fail(SHAMPOO_E_UNSUPPORTED, "roots dtype %d (F32, F64)", (int)rdt);
   if (nblk == 0) return SHAMPOO_OK;
   if (!roots || !g || !dstack) return fail(SHAMPOO_E_INVALID, "null pointer argument");
-  const size_t need = (size_t)nblk * B * B * 4;
+  const size_t es = rdt == SHAMPOO_F64 ? 8 : 4;
+  const size_t need = (size_t)nblk * B * B * es;
   if (!ws || ws_bytes < need) return fail(SHAMPOO_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
   if (gemm_wgs(B, nblk, false) >= (int64_t)1 << 31) return fail(SHAMPOO_E_UNSUPPORTED, "batch too large");
-  const float* Lr = roots;
-  const float* Rr = roots + nblk * (int64_t)B * B;
+  const void* Lr = roots;
+  const void* Rr = (const unsigned char*)roots + (size_t)nblk * B * B * es;
   // E = G Rr, stored transposed; D = Lr E = Lr (E^T)^T.
   GemmCall c1;
   c1.A = g; c1.B = Rr; c1.D = nullptr; c1.C = ws; c1.C2 = nullptr; c1.sym = false; c1.transC = true;
-  if (gdt == SHAMPOO_F32) HIP_TRY((gemm<Mma::F32, float, float, float>(c1, B, nblk, st)));
-  else HIP_TRY((gemm<Mma::F32, __bf16, float, float>(c1, B, nblk, st)));
   GemmCall c2;
   c2.A = Lr; c2.B = ws; c2.D = nullptr; c2.C = dstack; c2.C2 = nullptr; c2.sym = false;
-  HIP_TRY((gemm<Mma::F32, float, float, float>(c2, B, nblk, st)));
+  if (rdt == SHAMPOO_F64) {
+    if (gdt == SHAMPOO_F32) HIP_TRY((gemm<Mma::F64, float, double, double>(c1, B, nblk, st)));
+    else HIP_TRY((gemm<Mma::F64, __bf16, double, double>(c1, B, nblk, st)));
+    HIP_TRY((gemm<Mma::F64, double, double, float>(c2, B, nblk, st)));
+  } else {
+    if (gdt == SHAMPOO_F32) HIP_TRY((gemm<Mma::F32, float, float, float>(c1, B, nblk, st)));
+    else HIP_TRY((gemm<Mma::F32, __bf16, float, float>(c1, B, nblk, st)));
+    HIP_TRY((gemm<Mma::F32, float, float, float>(c2, B, nblk, st)));
+  }
   return SHAMPOO_OK;
 }
 
@@ -648,7 +665,9 @@ shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
   if (a->nblk < 0 || a->nparams < 0) return fail(SHAMPOO_E_INVALID, "negative sizes");
   if (a->B < 64 || a->B % 64 != 0) return fail(SHAMPOO_E_UNSUPPORTED, "B = %d: must be a positive multiple of 64", a->B);
   if (a->g_dt != SHAMPOO_F32 && a->g_dt != SHAMPOO_BF16) return fail(SHAMPOO_E_UNSUPPORTED, "gradient dtype %d", (int)a->g_dt);
-  if (a->nblk > 65535) return fail(SHAMPOO_E_UNSUPPORTED, "nblk = %lld > 65535", (long long)a->nblk);
+  if (a->nblk > 32767) return fail(SHAMPOO_E_UNSUPPORTED, "nblk = %lld > 32767", (long long)a->nblk);
+  if (a->stats_dt != SHAMPOO_F32 && a->stats_dt != SHAMPOO_F64)
+    return fail(SHAMPOO_E_UNSUPPORTED, "statistics dtype %d (F32, F64)", (int)a->stats_dt);
   shampoo_status r = check_root_args(2 * a->nblk, a->B, a->p, &a->root);
   if (r != SHAMPOO_OK) return r;
   const Plan P = build_plan(a->p, &a->root);
@@ -657,8 +676,9 @@ shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
   L->nchunk = (a->B + GRAFT_ROWS - 1) / GRAFT_ROWS;
   L->root_bytes = root_ws_bytes(2 * a->nblk, a->B, P, a->root.compute);
   size_t root = L->root_bytes;
-  const size_t ed = align_up((size_t)a->nblk * BB * 4);
-  if (root < 2 * ed) root = 2 * ed;  // E^T and D reuse the root workspace
+  // E^T (in the roots' precision) and D (f32) reuse the root workspace
+  const size_t ed = align_up((size_t)a->nblk * BB * dtype_size(a->stats_dt)) + align_up((size_t)a->nblk * BB * 4);
+  if (root < ed) root = ed;
   size_t off = 0;
   L->g = off; off += align_up((size_t)a->nblk * BB * es);
   L->gt = off; off += align_up((size_t)a->nblk * BB * es);
@@ -705,18 +725,19 @@ shampoo_status step_impl(const shampoo_step_args* a, hipStream_t st) {
     LAUNCH_CHECK("valid");
   }
   // 2. statistics
-  r = stats_impl(g, gt, a->g_dt, nblk, B, a->LR, a->beta2, st);
+  r = stats_impl(g, gt, a->g_dt, nblk, B, a->LR, a->stats_dt, a->beta2, st);
   if (r != SHAMPOO_OK) return r;
   // 3. inverse roots of the 2 nblk factors
   if (a->recompute_roots) {
-    r = inverse_root_impl(a->LR, a->roots, SHAMPOO_F32, 2 * nblk, B, a->p, &a->root, valid, nullptr, a->flags_dev,
+    r = inverse_root_impl(a->LR, a->roots, a->stats_dt, 2 * nblk, B, a->p, &a->root, valid, nullptr, a->flags_dev,
                           root, L.root_bytes, st);
     if (r != SHAMPOO_OK) return r;
   }
   // 4. D = Lr G Rr
-  float* Et = (float*)root;
-  float* D = a->dstack ? a->dstack : (float*)(root + align_up((size_t)nblk * BB * 4));
-  r = precond_impl(a->roots, g, a->g_dt, nblk, B, D, Et, (size_t)nblk * BB * 4, st);
+  const size_t ebytes = align_up((size_t)nblk * BB * dtype_size(a->stats_dt));
+  void* Et = root;
+  float* D = a->dstack ? a->dstack : (float*)(root + ebytes);
+  r = precond_impl(a->roots, a->stats_dt, g, a->g_dt, nblk, B, D, Et, ebytes, st);
   if (r != SHAMPOO_OK) return r;
   // 5. grafting and update
   GraftArgs ga;
@@ -827,8 +848,8 @@ shampoo_status shampoo_unpack_blocks(const float* stack, const shampoo_block* ta
 }
 
 shampoo_status shampoo_update_stats(const void* gstack, const void* gstack_t, shampoo_dtype g_dt, int64_t nblk,
-                                    int32_t B, float* LR, float beta2, hipStream_t stream) {
-  return stats_impl(gstack, gstack_t, g_dt, nblk, B, LR, beta2, stream);
+                                    int32_t B, void* LR, shampoo_dtype stats_dt, double beta2, hipStream_t stream) {
+  return stats_impl(gstack, gstack_t, g_dt, nblk, B, LR, stats_dt, beta2, stream);
 }
 
 shampoo_status shampoo_inverse_root_workspace(int64_t n, int32_t B, int32_t p, const shampoo_root_opts* opts,
@@ -846,15 +867,17 @@ shampoo_status shampoo_inverse_root(const void* in, void* out, shampoo_dtype io_
   return inverse_root_impl(in, out, io_dt, n, B, p, opts, valid_dev, scale_out_dev, flags_dev, ws, ws_bytes, stream);
 }
 
-shampoo_status shampoo_precondition_workspace(int64_t nblk, int32_t B, size_t* bytes) {
+shampoo_status shampoo_precondition_workspace(int64_t nblk, int32_t B, shampoo_dtype roots_dt, size_t* bytes) {
   if (!bytes || nblk < 0 || B < 1) return fail(SHAMPOO_E_INVALID, "bad arguments");
-  *bytes = (size_t)nblk * B * B * 4;
+  if (roots_dt != SHAMPOO_F32 && roots_dt != SHAMPOO_F64) return fail(SHAMPOO_E_UNSUPPORTED, "roots dtype %d", (int)roots_dt);
+  *bytes = (size_t)nblk * B * B * dtype_size(roots_dt);
   return SHAMPOO_OK;
 }
 
-shampoo_status shampoo_precondition(const float* roots, const void* gstack, shampoo_dtype g_dt, int64_t nblk,
-                                    int32_t B, float* dstack, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return precond_impl(roots, gstack, g_dt, nblk, B, dstack, ws, ws_bytes, stream);
+shampoo_status shampoo_precondition(const void* roots, shampoo_dtype roots_dt, const void* gstack,
+                                    shampoo_dtype g_dt, int64_t nblk, int32_t B, float* dstack, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  return precond_impl(roots, roots_dt, gstack, g_dt, nblk, B, dstack, ws, ws_bytes, stream);
 }
 
 shampoo_status shampoo_step_workspace(const shampoo_step_args* args, size_t* bytes) {

@@ -14,7 +14,7 @@ import math
 
 import numpy as np
 
-from . import (RootOpts, StepArgsC, GRAFTS, F32, BF16, shampoo_plan_blocks, shampoo_step,
+from . import (RootOpts, StepArgsC, GRAFTS, F32, F64, BF16, shampoo_plan_blocks, shampoo_step,
                shampoo_step_workspace, table_to_device, _ptr)
 
 
@@ -49,8 +49,8 @@ class ShampooStack:
         for b in range(self.nblk):
             first.setdefault(int(self.table[b, 0]), b)
         self.first_block = [first.get(i, 0) for i in range(len(weights))]
-        f32 = torch.float32
-        self.LR = torch.zeros((2 * self.nblk, self.B, self.B), dtype=f32, device=device)
+        sdt = hp["stats_dtype"]
+        self.LR = torch.zeros((2 * self.nblk, self.B, self.B), dtype=sdt, device=device)
         self.roots = torch.zeros_like(self.LR)
         self.flags = torch.zeros(2 * self.nblk, dtype=torch.int32, device=device)
         g = hp["graft"]
@@ -67,10 +67,18 @@ class ShampooStack:
         a.table_dev = self.table_dev.data_ptr()
         a.g_dt = BF16 if self.grad_dtype == torch.bfloat16 else F32
         a.p = hp["p"]
+        a.stats_dt = F64 if sdt == torch.float64 else F32
         a.LR = self.LR.data_ptr()
         a.roots = self.roots.data_ptr()
         a.beta2 = hp["beta2"]
-        a.root = hp["root"].c()
+        ro = hp["root"]
+        self.pi_start = None
+        if ro.scaling == "power":
+            gen = torch.Generator(device=device)
+            gen.manual_seed(hp["pi_seed"] + self.B)
+            self.pi_start = torch.randn((ro.pi_vectors, self.B), generator=gen, device=device, dtype=torch.float32)
+            ro = RootOpts(**{**ro.__dict__, "pi_start": self.pi_start})
+        a.root = ro.c()
         a.graft = GRAFTS[g]
         a.graft_blockwise = 1 if hp["graft_blockwise"] else 0
         a.lr = hp["lr"]
@@ -117,12 +125,16 @@ class Shampoo:
     block_size: int, or a callable (rows, cols) -> block size (0 = whole
     parameter as one block).  graft: "sgd" | "momentum" | "adam" | "none".
     precondition_frequency: roots recomputed every that many steps (the
-    statistics are updated every step).
+    statistics are updated every step).  stats_dtype: torch.float32 (the
+    pages' float32 statistics) or torch.float64 (statistics, roots and
+    preconditioning products in float64).  Power-iteration scaling draws its
+    start vectors once per stack from ``pi_seed``.
     """
 
     def __init__(self, params, block_size=1024, beta2=1.0, eps=1e-12, p=4, root=None, graft="sgd",
                  lr=0.1, momentum=0.9, beta1=0.9, graft_beta2=0.999, graft_eps=1e-8,
-                 graft_blockwise=False, precondition_frequency=1, grad_dtype=None):
+                 graft_blockwise=False, precondition_frequency=1, grad_dtype=None, stats_dtype=None,
+                 pi_seed=0):
         import torch
         params = list(params)
         if not params:
@@ -138,7 +150,9 @@ class Shampoo:
         self.hp = dict(beta2=float(beta2), p=int(p), root=root, graft=graft, lr=float(lr),
                        momentum=float(momentum), beta1=float(beta1), graft_beta2=float(graft_beta2),
                        graft_eps=float(graft_eps), graft_blockwise=bool(graft_blockwise),
-                       grad_dtype=grad_dtype if grad_dtype is not None else torch.float32)
+                       grad_dtype=grad_dtype if grad_dtype is not None else torch.float32,
+                       stats_dtype=stats_dtype if stats_dtype is not None else torch.float32,
+                       pi_seed=int(pi_seed))
         bs_of = block_size if callable(block_size) else (lambda m, n, b=int(block_size): b)
         groups = {}
         for i, v in enumerate(self.views):

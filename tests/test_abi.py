@@ -37,11 +37,30 @@ def test_every_declared_symbol_is_exported(mir):
     assert "gfx950" in mir.version()
 
 
-def test_struct_sizes_match_header(mir):
+def test_struct_sizes_match_header(mir, tmp_path):
+    """Compile a C program against include/shampoo.h and compare every
+    struct's size and field offsets with the ctypes mirrors."""
+    import subprocess
+    structs = {"shampoo_block": mir.Block, "shampoo_matrix": mir.Matrix, "shampoo_param": mir.Param,
+               "shampoo_root_opts": mir.RootOptsC, "shampoo_step_args": mir.StepArgsC}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "shampoo.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append('printf("%s %%zu\\n", sizeof(%s));' % (cname, cname))
+        for f, _ in py._fields_:
+            lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (cname, f, cname, f))
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                    str(src), "-o", str(exe)], check=True, capture_output=True)
+    out = dict(l.rsplit(" ", 1) for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                         check=True).stdout.splitlines())
+    for cname, py in structs.items():
+        assert int(out[cname]) == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert int(out[cname + "." + f]) == getattr(py, f).offset, (cname, f)
     assert ctypes.sizeof(mir.Block) == 32
-    assert ctypes.sizeof(mir.Matrix) == 32
-    assert ctypes.sizeof(mir.Param) == 64
-    assert ctypes.sizeof(mir.RootOptsC) == 64
 
 
 @pytest.mark.parametrize("case", ["dash", "decoder", "bottleneck50", "mixed"])
@@ -111,12 +130,16 @@ def test_invalid_calls_fail_before_launch(mir):
     st = mir.lib.shampoo_inverse_root(fake, fake, mir.BF16, 4, 128, 4, ctypes.byref(oc), None, None, None, fake, 1 << 40, None)
     assert st == mir.E_UNSUPPORTED
     # statistics: beta2 out of range, bad dtype
-    st = mir.lib.shampoo_update_stats(fake, fake, mir.F32, 2, 128, fake, ctypes.c_float(1.5), None)
+    st = mir.lib.shampoo_update_stats(fake, fake, mir.F32, 2, 128, fake, mir.F32, 1.5, None)
     assert st == mir.E_INVALID
-    st = mir.lib.shampoo_update_stats(fake, fake, mir.F16, 2, 128, fake, ctypes.c_float(0.9), None)
+    st = mir.lib.shampoo_update_stats(fake, fake, mir.F16, 2, 128, fake, mir.F32, 0.9, None)
     assert st == mir.E_UNSUPPORTED
-    # precondition: short workspace
-    st = mir.lib.shampoo_precondition(fake, fake, mir.F32, 2, 128, fake, fake, 10, None)
+    st = mir.lib.shampoo_update_stats(fake, fake, mir.F32, 2, 128, fake, mir.F16, 0.9, None)
+    assert st == mir.E_UNSUPPORTED
+    # precondition: short workspace (f32 and f64 roots)
+    st = mir.lib.shampoo_precondition(fake, mir.F32, fake, mir.F32, 2, 128, fake, fake, 10, None)
+    assert st == mir.E_WORKSPACE
+    st = mir.lib.shampoo_precondition(fake, mir.F64, fake, mir.F32, 2, 128, fake, fake, 2 * 128 * 128 * 4, None)
     assert st == mir.E_WORKSPACE
     # n == 0 is a no-op
     st = mir.lib.shampoo_inverse_root(None, None, mir.F32, 0, 128, 4, ctypes.byref(oc), None, None, None, None, 0, None)

@@ -132,16 +132,56 @@ def test_precondition_vs_oracle(mir, dt):
         assert rel_fro(Dh[i], ref) < 1e-5
 
 
+@pytest.mark.parametrize("gdt", ["f32", "bf16"])
+def test_float64_statistics_and_direction(mir, gdt):
+    """float64 statistics (gradients widened exactly) and float64 roots in the
+    preconditioning products: sums of exact float64 products of length K
+    accumulate at most K u64 relative error."""
+    import torch
+    B, nblk, b2 = 256, 3, 0.999
+    gen = np.random.default_rng(5)
+    LR = torch.zeros((2 * nblk, B, B), dtype=torch.float64, device="cuda")
+    Lo = [np.zeros((B, B)) for _ in range(nblk)]
+    Ro = [np.zeros((B, B)) for _ in range(nblk)]
+    for _ in range(2):
+        st = (gen.standard_normal((nblk, B, B)) * 0.02).astype(np.float32)
+        stt = np.ascontiguousarray(np.swapaxes(st, 1, 2))
+        if gdt == "bf16":
+            bits, bitst = synthetic.f32_to_bf16_bits(st), synthetic.f32_to_bf16_bits(stt)
+            mir.shampoo_update_stats(bf16_tensor(bits), bf16_tensor(bitst), LR, b2)
+            st = synthetic.bf16_bits_to_f32(bits)
+        else:
+            mir.shampoo_update_stats(to_dev(st), to_dev(stt), LR, b2)
+        for i in range(nblk):
+            Lo[i], Ro[i] = oracle.update_stats(Lo[i], Ro[i], st[i], b2)
+    torch.cuda.synchronize()
+    got = LR.cpu().numpy()
+    for i in range(nblk):
+        assert rel_fro(got[i], Lo[i]) < 1e-13 and rel_fro(got[nblk + i], Ro[i]) < 1e-13
+    roots = np.concatenate([synthetic.spd_stack(32, nblk, B, 0.1, 1.0), synthetic.spd_stack(33, nblk, B, 0.1, 1.0)])
+    D = torch.empty((nblk, B, B), dtype=torch.float32, device="cuda")
+    gdev = to_dev(st) if gdt == "f32" else bf16_tensor(synthetic.f32_to_bf16_bits(st))
+    mir.shampoo_precondition(to_dev(roots), gdev, D)
+    torch.cuda.synchronize()
+    Dh = D.cpu().numpy()
+    for i in range(nblk):
+        ref = oracle.precondition(roots[i], st[i].astype(np.float64), roots[nblk + i])
+        # the float64 products end in one rounding to float32
+        assert rel_fro(Dh[i], ref) < 2 ** -23
+
+
 def run_steps(mir, shapes, block_sizes, grads, steps, hp, root_kw, oracle_root="eigh", grad_bf16=False,
-              cheb_degree=16, check_every=True, floor=False):
+              cheb_degree=16, check_every=True, floor=False, stats64=False):
     """Run the GPU optimizer and the oracle side by side; return per-step
     (error, tolerance).  The tolerance is 1e-4, or with ``floor`` the larger of
     1e-4 and 4x the float32 rounding floor of the directions so far
-    (helpers.f32_direction_floor over every block's factors)."""
+    (helpers.f32_direction_floor over every block's factors).  ``stats64``
+    keeps statistics, roots and preconditioning products in float64."""
     import torch
     W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
     opt = mir.Shampoo(W, block_size=(lambda m, n: block_sizes[(m, n)]) if isinstance(block_sizes, dict) else block_sizes,
-                      root=mir.RootOpts(**root_kw), grad_dtype=torch.bfloat16 if grad_bf16 else torch.float32, **hp)
+                      root=mir.RootOpts(**root_kw), grad_dtype=torch.bfloat16 if grad_bf16 else torch.float32,
+                      stats_dtype=torch.float64 if stats64 else torch.float32, **hp)
     bs_list = [block_sizes[s] for s in shapes] if isinstance(block_sizes, dict) else [block_sizes] * len(shapes)
     orc = oracle.ShampooOracle(shapes, bs_list, beta2=hp["beta2"], eps=hp["eps"], root=oracle_root,
                                cheb_degree=cheb_degree, graft=hp["graft"], lr=hp["lr"],
@@ -177,12 +217,13 @@ def test_single_matrix_ten_steps(mir, compute):
     """One 256 x 128 float32 parameter, block 128 (2 blocks), N(0,1) gradients
     from seed 0, 10 steps, beta2 = 1, eps = 1e-12, SGD grafting lr 0.1;
     coupled Newton 30 iterations.  The step-1 factors of a square Gaussian
-    block have condition numbers up to 1e6: float32 is held to its floor,
-    float64 to 1e-4."""
+    block have condition numbers up to 1e6: float32 (statistics and chain) is
+    held to its floor, the float64 path (statistics, chain and products) to
+    1e-4."""
     grads = synthetic.gaussian_grads(0, [(256, 128)], 10, 1.0)
     errs = run_steps(mir, [(256, 128)], 128, grads, 10,
                      dict(beta2=1.0, eps=1e-12, graft="sgd", lr=0.1), dict(method="cn", iters=30, compute=compute),
-                     floor=(compute == "f32"))
+                     floor=(compute == "f32"), stats64=(compute == "f64"))
     assert all(e < t for e, t in errs)
 
 
@@ -198,13 +239,14 @@ def test_ragged_blocks_momentum_and_ndb(mir):
 def test_decoder_layer_adam_bf16(mir):
     """One decoder layer of the d_model 1024 / MLP 4096 set (QKV, out, MLP up,
     MLP down), bfloat16 gradients N(0, 0.02^2), beta2 = 0.999, eps = 1e-12,
-    Adam grafting lr 1e-3, block 1024, 3 steps; coupled Newton in float64
-    (the float32 chain's floor on the step-1 factors, whose condition number
-    is about 4 B^2, is reported by the float32 variant below)."""
+    Adam grafting lr 1e-3, block 1024, 3 steps; coupled Newton 26 iterations
+    with statistics, chain and products in float64 (the float32 path's floor
+    on the step-1 factors, whose condition number is about 4 B^2, is checked
+    by the float32 variant below)."""
     shapes = synthetic.decoder_shapes(layers=1)
     grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
     errs = run_steps(mir, shapes, 1024, grads, 3, dict(beta2=0.999, eps=1e-12, graft="adam", lr=1e-3),
-                     dict(method="cn", iters=26, compute="f64"), grad_bf16=True, check_every=True)
+                     dict(method="cn", iters=26, compute="f64"), grad_bf16=True, check_every=True, stats64=True)
     assert all(e < 1e-4 for e, _ in errs)
 
 
@@ -250,7 +292,7 @@ def test_step_deterministic_and_infrequent_roots(mir):
     # frequency 2: steps 1 and 3 recompute roots; steps 2 and 4 reuse them
     W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
     opt = mir.Shampoo(W, block_size=128, beta2=0.9, eps=1e-6, root=mir.RootOpts(method="cn", iters=30, compute="f64"),
-                      graft="none", lr=1.0, precondition_frequency=2)
+                      graft="none", lr=1.0, precondition_frequency=2, stats_dtype=torch.float64)
     Wo = [np.zeros(s) for s in shapes]
     t_ = oracle.plan_blocks(shapes, [128, 128])
     L = [np.zeros((int(t_[b, 5]),) * 2) for b in range(t_.shape[0])]
