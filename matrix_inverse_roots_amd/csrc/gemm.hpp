@@ -262,8 +262,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   constexpr int KNQ = (KNB + 255) / 256;          // ... per thread
   static_assert(BK * sizeof(L) == 128, "LDS row must hold 128 bytes of k");
 
-  __shared__ __attribute__((aligned(16))) unsigned char sA[T * ROWB];
-  __shared__ __attribute__((aligned(16))) unsigned char sB[T * ROWB];
+  // Two stages of A and B tiles (double buffering: one barrier per k-stage);
+  // the epilogue reuses the same bytes to stage the C tile.
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * T * ROWB];
+  auto sA = [&](int buf) { return smem + buf * T * ROWB; };
+  auto sB = [&](int buf) { return smem + (2 + buf) * T * ROWB; };
 
   const int64_t w = xcd_remap((int64_t)blockIdx.x, g.total);
   const int64_t mat = w / g.tiles;
@@ -317,12 +320,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       }
     }
   };
-  auto sstore = [&]() {
+  auto sstore = [&](int buf) {
+    unsigned char* a = sA(buf);
+    unsigned char* bb = sB(buf);
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
       const int c = tid + 256 * q, row = c >> 3, cc = c & 7;
-      ra[q].store(sA + row * ROWB + cc * 16);
-      if constexpr (!BKN) rb[q].store(sB + row * ROWB + cc * 16);
+      ra[q].store(a + row * ROWB + cc * 16);
+      if constexpr (!BKN) rb[q].store(bb + row * ROWB + cc * 16);
     }
     if constexpr (BKN) {
 #pragma unroll
@@ -330,28 +335,34 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         const int blk = tid + 256 * q;
         if (KNB % 256 == 0 || blk < KNB) {
           const int jb = blk % (T / VE), kq = blk / (T / VE);
-          kb[q].store_t(sB + (jb * VE) * ROWB + kq * VE * (int)sizeof(L), ROWB);
+          kb[q].store_t(bb + (jb * VE) * ROWB + kq * VE * (int)sizeof(L), ROWB);
         }
       }
     }
   };
 
+  // Stage s computes from buffer s % 2 while the loads of stage s + 1 are in
+  // flight; their registers go to the other buffer after the compute, and one
+  // barrier per stage publishes them.
   gload(0);
-  for (int k0 = 0; k0 < n; k0 += BK) {
-    __syncthreads();
-    sstore();
-    __syncthreads();
-    if (k0 + BK < n) gload(k0 + BK);
+  sstore(0);
+  __syncthreads();
+  const int nstage = n / BK;
+  for (int s = 0; s < nstage; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nstage) gload((s + 1) * BK);
+    const unsigned char* a_s = sA(cur);
+    const unsigned char* b_s = sB(cur);
 #pragma unroll
     for (int r = 0; r < NREAD; ++r) {
       frag_t a[NB], b[NB];
       const int off = (r * 4 * VE + grp * VE) * (int)sizeof(L);
 #pragma unroll
       for (int i = 0; i < NB; ++i)
-        a[i] = *reinterpret_cast<const frag_t*>(sA + (wm * WT + i * 16 + i16) * ROWB + off);
+        a[i] = *reinterpret_cast<const frag_t*>(a_s + (wm * WT + i * 16 + i16) * ROWB + off);
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        b[j] = *reinterpret_cast<const frag_t*>(sB + (wn * WT + j * 16 + i16) * ROWB + off);
+        b[j] = *reinterpret_cast<const frag_t*>(b_s + (wn * WT + j * 16 + i16) * ROWB + off);
 #pragma unroll
       for (int u = 0; u < VE / KV; ++u)
 #pragma unroll
@@ -359,6 +370,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
           for (int j = 0; j < NB; ++j) acc[i][j] = Tr::mma(a[i], b[j], u, acc[i][j]);
     }
+    if (s + 1 < nstage) sstore(cur ^ 1);
+    __syncthreads();
   }
 
   // Epilogue.
@@ -367,6 +380,82 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const TC* D = g.D ? reinterpret_cast<const TC*>(g.D) + mat * g.stride : nullptr;
   const bool diag = g.sym && ti == tj;
   const bool mirror = g.sym != 0;
+
+  if constexpr (sizeof(acc_t) == 4) {
+    // Stage the tile in LDS ([T][T+1] floats, conflict-free by rows and by
+    // columns), then write whole rows with 16-byte stores.  The mirrored tile
+    // (symmetric mode) and the transposed output read the staged tile by
+    // columns; a diagonal tile takes its lower triangle from its upper one.
+    constexpr int LP = T + 1;
+    float* sC = reinterpret_cast<float*>(smem);
+    static_assert(T * LP * 4 <= 4 * T * ROWB, "C tile must fit the operand buffers");
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          sC[(wm * WT + i * 16 + Tr::row(grp, v)) * LP + wn * WT + j * 16 + i16] = acc[i][j][v];
+    __syncthreads();
+    auto emit = [&](int oti, int otj, bool transposed, bool upper) {
+      for (int e = tid; e < T * T / 4; e += 256) {
+        const int r = e / (T / 4), c4 = (e - r * (T / 4)) * 4;
+        const int R = oti * T + r;
+        const int64_t base = (int64_t)R * n + otj * T + c4;
+        float x[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          int sr = transposed ? c4 + q : r, sc = transposed ? r : c4 + q;
+          if (upper && sr > sc) { const int tmp = sr; sr = sc; sc = tmp; }
+          x[q] = sC[sr * LP + sc];
+        }
+        double y[4];
+        double dv[4] = {0.0, 0.0, 0.0, 0.0};
+        if (D) {
+          if constexpr (sizeof(TC) == 4) {
+            const floatx4 d4 = *reinterpret_cast<const floatx4*>(D + base);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dv[q] = (double)d4[q];
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dv[q] = (double)D[base + q];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          y[q] = g.alpha * (double)x[q] + g.beta * dv[q];
+          if (R == otj * T + c4 + q) y[q] += g.gamma;
+        }
+        if constexpr (sizeof(TC) == 4) {
+          *reinterpret_cast<floatx4*>(C + base) = floatx4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]};
+          if (C2) {
+            float z[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) z[q] = (float)(g.alpha2 * y[q] + (R == otj * T + c4 + q ? g.gamma2 : 0.0));
+            *reinterpret_cast<floatx4*>(C2 + base) = floatx4{z[0], z[1], z[2], z[3]};
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) put<TC>(C + base + q, y[q]);
+          if (C2) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              put<TC>(C2 + base + q, g.alpha2 * y[q] + (R == otj * T + c4 + q ? g.gamma2 : 0.0));
+          }
+        }
+      }
+    };
+    if (g.transC) {
+      emit(tj, ti, true, false);
+    } else if (diag) {
+      emit(ti, tj, false, true);
+    } else {
+      emit(ti, tj, false, false);
+      if (mirror) emit(tj, ti, true, false);
+    }
+    return;
+  }
+
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
