@@ -246,7 +246,7 @@ template <> __device__ __forceinline__ void put<float>(float* p, double v) { *p 
 template <> __device__ __forceinline__ void put<double>(double* p, double v) { *p = v; }
 
 template <Mma MM, int T, bool BKN, typename TA, typename TB, typename TC>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   using Tr = MmaTraits<MM>;
   using L = typename Tr::lds_t;
   using acc_t = typename Tr::acc_t;
