@@ -121,13 +121,13 @@ def traffic_from_profiles(kernel_tag):
 def full_step_ms(mir, steps, warmup):
     """Full step on the 12-layer decoder set (151 M parameters, block 1024,
     bfloat16 gradients N(0, 0.02^2), beta2 0.999, eps 1e-12, Adam grafting,
-    coupled Newton 26 iterations in float32, roots every step)."""
+    coupled Newton 34 iterations in float32, roots every step)."""
     import numpy as np
     import torch
     import synthetic
     shapes = synthetic.decoder_shapes()
     W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
-    opt = mir.Shampoo(W, block_size=1024, beta2=0.999, eps=1e-12, root=mir.RootOpts(method="cn", iters=26),
+    opt = mir.Shampoo(W, block_size=1024, beta2=0.999, eps=1e-12, root=mir.RootOpts(method="cn", iters=34),
                       graft="adam", lr=1e-3, grad_dtype=torch.bfloat16)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(4)
@@ -236,7 +236,7 @@ def main():
         result["variants"] = var
     if not args.no_full_step:
         ms, nf = full_step_ms(mir, max(3, args.steps), 1)
-        result["full_step"] = {"workload": "decoder_12x(1024x3072,1024x1024,1024x4096,4096x1024)_bf16_adam_cn26_f32",
+        result["full_step"] = {"workload": "decoder_12x(1024x3072,1024x1024,1024x4096,4096x1024)_bf16_adam_cn34_f32",
                                "ms": round(ms, 2), "flagged_factors": nf}
         log(f"full step: {ms:.1f} ms")
     if not args.no_cpu_baseline:

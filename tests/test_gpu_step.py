@@ -239,14 +239,14 @@ def test_ragged_blocks_momentum_and_ndb(mir):
 def test_decoder_layer_adam_bf16(mir):
     """One decoder layer of the d_model 1024 / MLP 4096 set (QKV, out, MLP up,
     MLP down), bfloat16 gradients N(0, 0.02^2), beta2 = 0.999, eps = 1e-12,
-    Adam grafting lr 1e-3, block 1024, 3 steps; coupled Newton 26 iterations
+    Adam grafting lr 1e-3, block 1024, 3 steps; coupled Newton 34 iterations
     with statistics, chain and products in float64 (the float32 path's floor
     on the step-1 factors, whose condition number is about 4 B^2, is checked
     by the float32 variant below)."""
     shapes = synthetic.decoder_shapes(layers=1)
     grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
     errs = run_steps(mir, shapes, 1024, grads, 3, dict(beta2=0.999, eps=1e-12, graft="adam", lr=1e-3),
-                     dict(method="cn", iters=26, compute="f64"), grad_bf16=True, check_every=True, stats64=True)
+                     dict(method="cn", iters=34, compute="f64"), grad_bf16=True, check_every=True, stats64=True)
     assert all(e < 1e-4 for e, _ in errs)
 
 
@@ -254,7 +254,7 @@ def test_decoder_layer_adam_bf16_f32_chain(mir):
     shapes = synthetic.decoder_shapes(layers=1)
     grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
     errs = run_steps(mir, shapes, 1024, grads, 3, dict(beta2=0.999, eps=1e-12, graft="adam", lr=1e-3),
-                     dict(method="cn", iters=26), grad_bf16=True, check_every=True, floor=True)
+                     dict(method="cn", iters=34), grad_bf16=True, check_every=True, floor=True)
     log(f"decoder layer f32 chain (error, tolerance) per step: {errs}")
     assert all(e < t for e, t in errs)
 
