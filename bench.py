@@ -202,7 +202,7 @@ def main():
     achieved = flops_alg / mean_gemm / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP32_MFMA, 4), "traffic": traffic_from_profiles("gemm_f32_b512"),
-            "kernel": "gemm_kernel<F32, 128, NN, float, float, float>", "launches_timed": len(gemm_ms),
+            "kernel": "gemm_f32_nn256_kernel", "launches_timed": len(gemm_ms),
             "mean_launch_ms": round(mean_gemm * 1e3, 4), "flop_per_launch": flops_alg,
             "algorithmic_bytes_per_launch": 3 * N_BLOCKS * B * B * 4}
     gemm_share = float(np.sum(gemm_ms)) * 1e-3 / (dt * args.steps) if gemm_ms else None

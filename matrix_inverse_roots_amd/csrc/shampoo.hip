@@ -5,6 +5,7 @@
 // device memory; every launch goes to the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -73,6 +74,43 @@ struct GemmCall {
   bool nn = false;  // B read k-major: C = A B (no symmetry assumed)
 };
 
+#define HIP_TRY_ERR(expr)         \
+  do {                            \
+    hipError_t e_ = (expr);       \
+    if (e_ != hipSuccess) return e_; \
+  } while (0)
+
+constexpr int MAX_DEVICES = 64;
+
+// Compute units of the current device, queried once per device.
+hipError_t cu_count(int* cus) {
+  static int cache[MAX_DEVICES] = {0};
+  int dev = 0;
+  HIP_TRY_ERR(hipGetDevice(&dev));
+  if (dev >= 0 && dev < MAX_DEVICES && cache[dev] > 0) {
+    *cus = cache[dev];
+    return hipSuccess;
+  }
+  int v = 0;
+  HIP_TRY_ERR(hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev));
+  if (dev >= 0 && dev < MAX_DEVICES) cache[dev] = v;
+  *cus = v;
+  return hipSuccess;
+}
+
+// The large-tile product needs 128 KB of dynamic LDS, above the default
+// limit; raise the kernel's limit once per device.
+hipError_t nn256_prepare() {
+  static bool done[MAX_DEVICES] = {false};
+  int dev = 0;
+  HIP_TRY_ERR(hipGetDevice(&dev));
+  if (dev >= 0 && dev < MAX_DEVICES && done[dev]) return hipSuccess;
+  HIP_TRY_ERR(hipFuncSetAttribute((const void*)gemm_f32_nn256_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  NN256_LDS));
+  if (dev >= 0 && dev < MAX_DEVICES) done[dev] = true;
+  return hipSuccess;
+}
+
 template <Mma MM, typename TA, typename TB, typename TC>
 hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
   const int T = (n % 128 == 0) ? 128 : 64;
@@ -96,6 +134,22 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
   g.gamma2 = c.gamma2;
   if (g.total == 0) return hipSuccess;
   dim3 grid((unsigned)g.total);
+  if constexpr (MM == Mma::F32 && std::is_same<TA, float>::value && std::is_same<TB, float>::value &&
+                std::is_same<TC, float>::value) {
+    if (c.nn && n % NN256_T == 0 && c.D == nullptr && !c.transC) {
+      int cus = 0;
+      HIP_TRY_ERR(cu_count(&cus));
+      GemmArgs h = g;
+      h.nt = n / NN256_T;
+      h.tiles = h.nt * h.nt;
+      h.total = batch * h.tiles;
+      // persistent grid: at most one workgroup per CU, a multiple of the 8 XCDs
+      const int64_t wgs = std::min<int64_t>(((h.total + 7) / 8) * 8, std::max(8, (cus / 8) * 8));
+      HIP_TRY_ERR(nn256_prepare());
+      hipLaunchKernelGGL(gemm_f32_nn256_kernel, dim3((unsigned)wgs), dim3(512), NN256_LDS, st, h);
+      return hipGetLastError();
+    }
+  }
   if constexpr (std::is_same<TB, float>::value || std::is_same<TB, double>::value) {
     if (c.nn) {
       if (T == 128)

@@ -71,6 +71,37 @@ def test_well_conditioned_f32(mir, B, method, scaling):
     assert worst < 1e-4
 
 
+@pytest.mark.parametrize("B,n", [(256, 13), (768, 3), (512, 70)])
+def test_newton_db_large_tile_products(mir, B, n):
+    """Sides that are multiples of 256 run the float32 Newton-DB products on
+    256 x 256 tiles with a persistent grid: 13 and 27 tiles leave most
+    workgroups idle or with one tile, 280 tiles make some walk two."""
+    A = synthetic.spd_stack(B + 7, n, B, WELL["lo"], WELL["hi"]).astype(np.float32)
+    X, s, fl = run_root(mir, A, 4, method="ndb", scaling="frobenius", iters=20, iters2=14)
+    idx = range(n) if n <= 13 else [0, 1, 2, n // 2, n - 2, n - 1]
+    worst = max(rel_fro(X[i], oracle.inverse_root_eigh(A[i].astype(np.float64), 4)) for i in idx)
+    log(f"f32 ndb B={B} n={n} (large tiles): worst rel err {worst:.2e}")
+    assert not fl.any()
+    assert worst < 1e-4
+
+
+def test_large_and_small_tile_products_bit_identical(mir):
+    """The 256-tile float32 product walks k in the same order as the 128-tile
+    one, and identity padding adds exact zeros: a 384 x 384 stack (128-tile
+    kernel) and the same stack padded to 512 with valid = 384 (256-tile
+    kernel) give bit-identical roots under Frobenius scaling."""
+    n, v = 6, 384
+    A = synthetic.spd_stack(384, n, v, 1e-3, 1.0).astype(np.float32)
+    X1, s1, f1 = run_root(mir, A, 4, method="ndb", scaling="frobenius", iters=22, iters2=15)
+    Ap = np.zeros((n, 512, 512), dtype=np.float32)
+    Ap[:, :v, :v] = A
+    X2, s2, f2 = run_root(mir, Ap, 4, valid=[v] * n, method="ndb", scaling="frobenius", iters=22, iters2=15)
+    assert not f1.any() and not f2.any()
+    np.testing.assert_array_equal(s1, s2)
+    np.testing.assert_array_equal(X1, X2[:, :v, :v])
+    assert not X2[:, v:, :].any() and not X2[:, :, v:].any()
+
+
 @pytest.mark.parametrize("p,method", [(2, "cn"), (8, "cn"), (1, "cn"), (2, "ndb")])
 def test_other_orders(mir, p, method):
     A = synthetic.spd_stack(7, 4, 128, 1e-2, 1.0).astype(np.float32)
