@@ -671,4 +671,226 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_nn256_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// float32 NT product on 128 x 128 tiles (n a multiple of 128), all modes of
+// gemm_kernel: D operand, second output, symmetric (upper tiles, mirrored)
+// and transposed output.
+//
+// Same scheme as the large-tile NN product: persistent grid (two workgroups
+// of 4 waves per CU, 64 KB of LDS each), direct-to-LDS stage loads one stage
+// ahead, fence-free barriers, float4 stores straight from the accumulators.
+// Both operands are row-major with k contiguous and use the swizzled A
+// layout.  For B the LDS row order is permuted: output column
+// wn*64 + 4 c + jb (lane c, column block jb) comes from B-tile row
+// wn*64 + 4 c + jb, stored at LDS row wn*64 + 16 jb + c, so a fragment read
+// covers 16 consecutive LDS rows, as for A.  A lane then owns 4 consecutive
+// columns of 4 consecutive rows of each 16 x 16 block, which gives float4
+// runs both for the direct output (along the columns) and for the mirrored
+// or transposed output (along the rows).  D is read during the tile's last
+// k-stage, so its latency hides behind the MFMAs; it may alias C (each
+// element is read before any write to it: the stores of a tile follow its
+// loads, and mirrored writes only reach lower tiles, whose D is never read).
+// ---------------------------------------------------------------------------
+constexpr int NT128_T = 128;
+constexpr int NT128_BK = 32;
+constexpr int NT128_TILE_BYTES = NT128_T * 128;  // 16 KB per operand and stage
+
+// LDS row -> B-tile row (the inverse of j -> (j & 64) | 16 (j & 3) | ((j >> 2) & 15))
+__device__ __forceinline__ int nt128_brow(int rho) { return (rho & 64) | (4 * (rho & 15)) | ((rho >> 4) & 3); }
+
+__global__ __launch_bounds__(256, 2) void gemm_f32_nt128_kernel(GemmArgs g) {
+  constexpr int T = NT128_T, BK = NT128_BK, TB = NT128_TILE_BYTES, SB = 2 * TB;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * SB];
+  const int per = gridDim.x >> 3;
+  const int x = blockIdx.x & 7, l = blockIdx.x >> 3;
+  const int64_t q = g.total >> 3, r = g.total & 7;
+  const int64_t mine = q + (x < r ? 1 : 0);
+  if (mine <= l) return;
+  const int64_t first = x * q + (x < r ? x : r) + l;
+  const int ntile = (int)((mine - l + per - 1) / per);
+  const int n = g.n, nst = n / BK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int i16 = lane & 15, grp = lane >> 4;
+  const float* Ag = reinterpret_cast<const float*>(g.A);
+  const float* Bg = reinterpret_cast<const float*>(g.B);
+
+  // Each wave issues 4 A and 4 B loads of 8 LDS rows x 128 B per stage.
+  int aoff[4], boff[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int row = 8 * (4 * wave + qq) + (lane >> 3), pos = lane & 7;
+    aoff[qq] = row * n + 4 * (pos ^ nn256_swz(row));
+    boff[qq] = nt128_brow(row) * n + 4 * (pos ^ nn256_swz(row));
+  }
+  auto coords = [&](int it, int64_t& moff, int& ti, int& tj) {
+    const int64_t w = first + (int64_t)it * per;
+    const int64_t mat = w / g.tiles;
+    int t = (int)(w - mat * g.tiles);
+    if (g.sym) {
+      ti = 0;
+      int rowlen = g.nt;
+      while (t >= rowlen) {
+        t -= rowlen;
+        ++ti;
+        --rowlen;
+      }
+      tj = ti + t;
+    } else {
+      ti = t / g.nt;
+      tj = t - ti * g.nt;
+    }
+    moff = mat * g.stride;
+  };
+  int lt = 0, lk = 0;
+  const float *LA, *LB;
+  int64_t cmo;  // compute cursor: current tile's matrix offset and tile indices
+  int cti, ctj;
+  coords(0, cmo, cti, ctj);
+  LA = Ag + cmo + (int64_t)cti * T * n;
+  LB = Bg + cmo + (int64_t)ctj * T * n;
+  auto issue = [&](int buf) {
+    unsigned char* sa = smem + buf * SB;
+    unsigned char* sb = sa + TB;
+    const float* pa = LA + lk * BK;
+    const float* pb = LB + lk * BK;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      __builtin_amdgcn_global_load_lds((const void*)(pa + aoff[qq]), (void*)(sa + (4 * wave + qq) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(pb + boff[qq]), (void*)(sb + (4 * wave + qq) * 1024), 16, 0, 0);
+    }
+  };
+  auto advance = [&]() {
+    if (++lk == nst) {
+      lk = 0;
+      if (++lt < ntile) {
+        int64_t mo;
+        int ti, tj;
+        coords(lt, mo, ti, tj);
+        LA = Ag + mo + (int64_t)ti * T * n;
+        LB = Bg + mo + (int64_t)tj * T * n;
+      }
+    }
+  };
+
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const float* Dg = reinterpret_cast<const float*>(g.D);
+  floatx4 dv[4][4];  // D of the current tile, rows (i, v), 4 columns
+  const bool plain = g.alpha == 1.0 && g.gamma == 0.0 && Dg == nullptr && g.C2 == nullptr;
+  const int total_steps = ntile * nst;
+
+  issue(0);
+  advance();
+  wait_vmcnt0();
+  barrier_no_fence();
+  int ck = 0, ct = 0;
+  for (int step = 0; step < total_steps; ++step) {
+    const bool more = step + 1 < total_steps;
+    if (more) issue((step + 1) & 1);
+    if (Dg && ck == nst - 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          dv[i][v] = *reinterpret_cast<const floatx4*>(
+              Dg + cmo + (int64_t)(cti * T + wm * 64 + i * 16 + 4 * grp + v) * n + ctj * T + wn * 64 + 4 * i16);
+    }
+    const unsigned char* sa = smem + (step & 1) * SB;
+    const unsigned char* sb = sa + TB;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int kc = rr * 4 + grp;
+      floatx4 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = wm * 64 + i * 16 + i16;
+        a[i] = *reinterpret_cast<const floatx4*>(sa + m * 128 + 16 * (kc ^ nn256_swz(m)));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rho = wn * 64 + 16 * j + i16;
+        b[j] = *reinterpret_cast<const floatx4*>(sb + rho * 128 + 16 * (kc ^ nn256_swz(rho)));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][u], b[j][u], acc[i][j], 0, 0, 0);
+    }
+    if (more) advance();
+    wait_vmcnt0();
+    barrier_no_fence();
+    if (++ck < nst) continue;
+    ck = 0;
+    float* C = reinterpret_cast<float*>(g.C) + cmo;
+    float* C2 = g.C2 ? reinterpret_cast<float*>(g.C2) + cmo : nullptr;
+    const int R0 = cti * T + wm * 64, C0 = ctj * T + wn * 64;
+    const bool diag = g.sym && cti == ctj;
+    const bool mirror = (g.sym && !diag) || g.transC;
+    const bool direct = !g.transC;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float y[4][4], z[4][4];  // [v][j]
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int R = R0 + i * 16 + 4 * grp + v, Cc = C0 + 4 * i16 + j;
+          if (plain) {
+            y[v][j] = acc[i][j][v];
+            continue;
+          }
+          double t = g.alpha * (double)acc[i][j][v];
+          if (Dg) t += g.beta * (double)dv[i][v][j];
+          if (R == Cc) t += g.gamma;
+          y[v][j] = (float)t;
+          if (C2) z[v][j] = (float)(g.alpha2 * t + (R == Cc ? g.gamma2 : 0.0));
+        }
+      if (diag) {
+        // diagonal tile: the upper element (R <= Cc) is written in place and mirrored
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int R = R0 + i * 16 + 4 * grp + v, Cc = C0 + 4 * i16 + j;
+            if (R > Cc) continue;
+            C[(int64_t)R * n + Cc] = y[v][j];
+            C[(int64_t)Cc * n + R] = y[v][j];
+            if (C2) {
+              C2[(int64_t)R * n + Cc] = z[v][j];
+              C2[(int64_t)Cc * n + R] = z[v][j];
+            }
+          }
+        continue;
+      }
+      if (direct) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t at = (int64_t)(R0 + i * 16 + 4 * grp + v) * n + C0 + 4 * i16;
+          *reinterpret_cast<floatx4*>(C + at) = floatx4{y[v][0], y[v][1], y[v][2], y[v][3]};
+          if (C2) *reinterpret_cast<floatx4*>(C2 + at) = floatx4{z[v][0], z[v][1], z[v][2], z[v][3]};
+        }
+      }
+      if (mirror) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t at = (int64_t)(C0 + 4 * i16 + j) * n + R0 + i * 16 + 4 * grp;
+          *reinterpret_cast<floatx4*>(C + at) = floatx4{y[0][j], y[1][j], y[2][j], y[3][j]};
+          if (C2) *reinterpret_cast<floatx4*>(C2 + at) = floatx4{z[0][j], z[1][j], z[2][j], z[3][j]};
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (++ct < ntile) coords(ct, cmo, cti, ctj);
+  }
+}
+
 }  // namespace shampoo

@@ -149,6 +149,14 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
       hipLaunchKernelGGL(gemm_f32_nn256_kernel, dim3((unsigned)wgs), dim3(512), NN256_LDS, st, h);
       return hipGetLastError();
     }
+    if (!c.nn && T == NT128_T) {
+      int cus = 0;
+      HIP_TRY_ERR(cu_count(&cus));
+      // persistent grid: two workgroups per CU, a multiple of the 8 XCDs
+      const int64_t wgs = std::min<int64_t>(((g.total + 7) / 8) * 8, std::max(8, (cus / 8) * 8) * 2);
+      hipLaunchKernelGGL(gemm_f32_nt128_kernel, dim3((unsigned)wgs), dim3(256), 0, st, g);
+      return hipGetLastError();
+    }
   }
   if constexpr (std::is_same<TB, float>::value || std::is_same<TB, double>::value) {
     if (c.nn) {

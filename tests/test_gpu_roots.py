@@ -102,6 +102,24 @@ def test_large_and_small_tile_products_bit_identical(mir):
     assert not X2[:, v:, :].any() and not X2[:, :, v:].any()
 
 
+@pytest.mark.parametrize("method", ["cn", "chebyshev"])
+def test_nt_product_kernels_bit_identical(mir, method):
+    """Symmetric NT products: a 192 x 192 stack runs on the 64-tile kernel,
+    the same stack padded to 256 (valid = 192) on the persistent 128-tile
+    kernel; both walk k in the same order and the padding adds exact zeros,
+    so the roots agree bit for bit (Chebyshev exercises the D operand)."""
+    n, v = 5, 192
+    A = synthetic.spd_stack(192, n, v, 1e-2, 1.0).astype(np.float32)
+    kw = dict(method=method, scaling="frobenius", iters=20, cheb_degree=12, eps=1e-3)
+    X1, s1, f1 = run_root(mir, A, 4, **kw)
+    Ap = np.zeros((n, 256, 256), dtype=np.float32)
+    Ap[:, :v, :v] = A
+    X2, s2, f2 = run_root(mir, Ap, 4, valid=[v] * n, **kw)
+    assert not f1.any() and not f2.any()
+    np.testing.assert_array_equal(X1, X2[:, :v, :v])
+    assert not X2[:, v:, :].any() and not X2[:, :, v:].any()
+
+
 @pytest.mark.parametrize("p,method", [(2, "cn"), (8, "cn"), (1, "cn"), (2, "ndb")])
 def test_other_orders(mir, p, method):
     A = synthetic.spd_stack(7, 4, 128, 1e-2, 1.0).astype(np.float32)
