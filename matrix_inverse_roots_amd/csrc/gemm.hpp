@@ -672,34 +672,97 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_nn256_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// float32 NT product on 128 x 128 tiles (n a multiple of 128), all modes of
-// gemm_kernel: D operand, second output, symmetric (upper tiles, mirrored)
-// and transposed output.
+// Persistent 128 x 128-tile product for float32 and float64 operands of one
+// type (n a multiple of 128), NT (B row-major, k contiguous) or NN (B
+// k-major), with every mode of gemm_kernel: D operand, second output,
+// symmetric (upper tiles, mirrored) and transposed output (NT).
 //
 // Same scheme as the large-tile NN product: persistent grid (two workgroups
 // of 4 waves per CU, 64 KB of LDS each), direct-to-LDS stage loads one stage
-// ahead, fence-free barriers, float4 stores straight from the accumulators.
-// Both operands are row-major with k contiguous and use the swizzled A
-// layout.  For B the LDS row order is permuted: output column
-// wn*64 + 4 c + jb (lane c, column block jb) comes from B-tile row
-// wn*64 + 4 c + jb, stored at LDS row wn*64 + 16 jb + c, so a fragment read
-// covers 16 consecutive LDS rows, as for A.  A lane then owns 4 consecutive
-// columns of 4 consecutive rows of each 16 x 16 block, which gives float4
-// runs both for the direct output (along the columns) and for the mirrored
-// or transposed output (along the rows).  D is read during the tile's last
-// k-stage, so its latency hides behind the MFMAs; it may alias C (each
-// element is read before any write to it: the stores of a tile follow its
-// loads, and mirrored writes only reach lower tiles, whose D is never read).
+// ahead, fence-free barriers, vector stores straight from the accumulators.
+// A stage holds 128 B of k per operand row (32 floats or 16 doubles):
+//   A tile  [128 rows][128 B], swizzled as in the NN product.
+//   B (NT)  [128 rows][128 B], swizzled, with the LDS row order permuted:
+//           output column wn*64 + 4 c + jb (lane c, column block jb) comes
+//           from B-tile row wn*64 + 4 c + jb, stored at LDS row
+//           wn*64 + 16 jb + c, so a fragment read covers 16 consecutive LDS
+//           rows, as for A.
+//   B (NN)  [k rows][128 columns], B's own layout; a 16-byte read gives VE
+//           consecutive columns of one k-row, so column block jb of lane c
+//           is column wn*64 + (jb / VE) 16 VE + VE c + jb % VE.
+// The float64 matrix core returns row grp + 4 v of a 16 x 16 block in value
+// v of lane group grp; A-lane row r reads tile row 4 (r % 4) + r / 4, which
+// turns that into row 4 grp + v, as for float32.  A lane thus owns 4
+// consecutive rows and runs of consecutive columns of each block: vector
+// runs for the direct output (along columns) and for the mirrored or
+// transposed output (along rows).  k is walked in the same order as in
+// gemm_kernel, so the results are bit-identical to it.
+//
+// D may alias C: each element is read before any write to it (a tile's
+// stores follow its loads, mirrored writes reach only lower tiles, whose D
+// is never read).  float32 reads D during the tile's last k-stage, so its
+// latency hides behind the MFMAs; float64 (twice the registers) reads it
+// in the epilogue.
 // ---------------------------------------------------------------------------
-constexpr int NT128_T = 128;
-constexpr int NT128_BK = 32;
-constexpr int NT128_TILE_BYTES = NT128_T * 128;  // 16 KB per operand and stage
+constexpr int P128_T = 128;
+constexpr int P128_TILE_BYTES = P128_T * 128;  // 16 KB per operand and stage
 
-// LDS row -> B-tile row (the inverse of j -> (j & 64) | 16 (j & 3) | ((j >> 2) & 15))
-__device__ __forceinline__ int nt128_brow(int rho) { return (rho & 64) | (4 * (rho & 15)) | ((rho >> 4) & 3); }
+template <typename E> struct P128;
+template <> struct P128<float> {
+  using acc_t = floatx4;
+  using frag_t = floatx4;
+  static constexpr int VE = 4;
+  static __device__ __forceinline__ acc_t mma(float a, float b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int arow(int r) { return r; }
+};
+template <> struct P128<double> {
+  using acc_t = doublex4;
+  using frag_t = doublex2;
+  static constexpr int VE = 2;
+  static __device__ __forceinline__ acc_t mma(double a, double b, acc_t c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int arow(int r) { return 4 * (r & 3) + (r >> 2); }
+};
 
-__global__ __launch_bounds__(256, 2) void gemm_f32_nt128_kernel(GemmArgs g) {
-  constexpr int T = NT128_T, BK = NT128_BK, TB = NT128_TILE_BYTES, SB = 2 * TB;
+// LDS row -> B-tile row of an NT operand (the inverse of
+// j -> (j & 64) | 16 (j & 3) | ((j >> 2) & 15))
+__device__ __forceinline__ int p128_brow(int rho) { return (rho & 64) | (4 * (rho & 15)) | ((rho >> 4) & 3); }
+
+// RUN consecutive elements with 16-byte accesses
+template <typename E, int RUN> __device__ __forceinline__ void store_run(E* p, const E* v) {
+#pragma unroll
+  for (int s = 0; s < RUN * (int)sizeof(E) / 16; ++s) {
+    if constexpr (sizeof(E) == 4)
+      *reinterpret_cast<floatx4*>(p + 4 * s) = floatx4{v[4 * s], v[4 * s + 1], v[4 * s + 2], v[4 * s + 3]};
+    else
+      *reinterpret_cast<doublex2*>(p + 2 * s) = doublex2{v[2 * s], v[2 * s + 1]};
+  }
+}
+template <typename E, int RUN> __device__ __forceinline__ void load_run(const E* p, E* v) {
+#pragma unroll
+  for (int s = 0; s < RUN * (int)sizeof(E) / 16; ++s) {
+    if constexpr (sizeof(E) == 4) {
+      const floatx4 t = *reinterpret_cast<const floatx4*>(p + 4 * s);
+      v[4 * s] = t[0]; v[4 * s + 1] = t[1]; v[4 * s + 2] = t[2]; v[4 * s + 3] = t[3];
+    } else {
+      const doublex2 t = *reinterpret_cast<const doublex2*>(p + 2 * s);
+      v[2 * s] = t[0]; v[2 * s + 1] = t[1];
+    }
+  }
+}
+
+template <typename E, bool NN>
+__global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
+  using P = P128<E>;
+  using acc_t = typename P::acc_t;
+  using frag_t = typename P::frag_t;
+  constexpr int T = P128_T, VE = P::VE, BK = 128 / (int)sizeof(E), TB = P128_TILE_BYTES, SB = 2 * TB;
+  constexpr int RB = T * (int)sizeof(E);  // bytes per k-row of an NN B tile
+  constexpr int RUN = NN ? VE : 4;        // consecutive output columns per lane and run
+  constexpr bool PREFETCH_D = sizeof(E) == 4;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * SB];
   const int per = gridDim.x >> 3;
   const int x = blockIdx.x & 7, l = blockIdx.x >> 3;
@@ -712,16 +775,22 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_nt128_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int i16 = lane & 15, grp = lane >> 4;
-  const float* Ag = reinterpret_cast<const float*>(g.A);
-  const float* Bg = reinterpret_cast<const float*>(g.B);
+  const E* Ag = reinterpret_cast<const E*>(g.A);
+  const E* Bg = reinterpret_cast<const E*>(g.B);
+  auto colmap = [&](int jb) { return NN ? (jb / VE) * 16 * VE + VE * i16 + jb % VE : 4 * i16 + jb; };
 
-  // Each wave issues 4 A and 4 B loads of 8 LDS rows x 128 B per stage.
+  // Each wave issues 4 A and 4 B loads of 1 KB per stage; lane offsets in elements.
   int aoff[4], boff[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
     const int row = 8 * (4 * wave + qq) + (lane >> 3), pos = lane & 7;
-    aoff[qq] = row * n + 4 * (pos ^ nn256_swz(row));
-    boff[qq] = nt128_brow(row) * n + 4 * (pos ^ nn256_swz(row));
+    aoff[qq] = row * n + VE * (pos ^ nn256_swz(row));
+    if constexpr (NN) {
+      const int byte = (4 * wave + qq) * 1024 + 16 * lane;
+      boff[qq] = (byte / RB) * n + (byte % RB) / (int)sizeof(E);
+    } else {
+      boff[qq] = p128_brow(row) * n + VE * (pos ^ nn256_swz(row));
+    }
   }
   auto coords = [&](int it, int64_t& moff, int& ti, int& tj) {
     const int64_t w = first + (int64_t)it * per;
@@ -742,18 +811,18 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_nt128_kernel(GemmArgs g) {
     }
     moff = mat * g.stride;
   };
+  auto bbase = [&](int64_t mo, int tj) { return Bg + mo + (NN ? (int64_t)tj * T : (int64_t)tj * T * n); };
   int lt = 0, lk = 0;
-  const float *LA, *LB;
-  int64_t cmo;  // compute cursor: current tile's matrix offset and tile indices
+  int64_t cmo;  // compute cursor: the current tile's matrix offset and tile indices
   int cti, ctj;
   coords(0, cmo, cti, ctj);
-  LA = Ag + cmo + (int64_t)cti * T * n;
-  LB = Bg + cmo + (int64_t)ctj * T * n;
+  const E* LA = Ag + cmo + (int64_t)cti * T * n;
+  const E* LB = bbase(cmo, ctj);
   auto issue = [&](int buf) {
     unsigned char* sa = smem + buf * SB;
     unsigned char* sb = sa + TB;
-    const float* pa = LA + lk * BK;
-    const float* pb = LB + lk * BK;
+    const E* pa = LA + lk * BK;
+    const E* pb = NN ? LB + (int64_t)lk * BK * n : LB + lk * BK;
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       __builtin_amdgcn_global_load_lds((const void*)(pa + aoff[qq]), (void*)(sa + (4 * wave + qq) * 1024), 16, 0, 0);
@@ -768,20 +837,29 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_nt128_kernel(GemmArgs g) {
         int ti, tj;
         coords(lt, mo, ti, tj);
         LA = Ag + mo + (int64_t)ti * T * n;
-        LB = Bg + mo + (int64_t)tj * T * n;
+        LB = bbase(mo, tj);
       }
     }
   };
 
-  floatx4 acc[4][4];
+  acc_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const float* Dg = reinterpret_cast<const float*>(g.D);
-  floatx4 dv[4][4];  // D of the current tile, rows (i, v), 4 columns
+    for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+  const E* Dg = reinterpret_cast<const E*>(g.D);
+  E dpre[PREFETCH_D ? 4 : 1][4][4];  // D of the current tile [i][v][jb] (float32)
   const bool plain = g.alpha == 1.0 && g.gamma == 0.0 && Dg == nullptr && g.C2 == nullptr;
   const int total_steps = ntile * nst;
+  auto dload = [&](int i, E (*d)[4]) {  // D at the lane's outputs of row block i
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int h = 0; h < 4 / RUN; ++h)
+        load_run<E, RUN>(Dg + cmo + (int64_t)(cti * T + wm * 64 + i * 16 + 4 * grp + v) * n + ctj * T + wn * 64 +
+                             colmap(h * RUN),
+                         &d[v][h * RUN]);
+  };
 
   issue(0);
   advance();
@@ -791,104 +869,145 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_nt128_kernel(GemmArgs g) {
   for (int step = 0; step < total_steps; ++step) {
     const bool more = step + 1 < total_steps;
     if (more) issue((step + 1) & 1);
-    if (Dg && ck == nst - 1) {
+    if constexpr (PREFETCH_D) {
+      if (Dg && ck == nst - 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          dv[i][v] = *reinterpret_cast<const floatx4*>(
-              Dg + cmo + (int64_t)(cti * T + wm * 64 + i * 16 + 4 * grp + v) * n + ctj * T + wn * 64 + 4 * i16);
+        for (int i = 0; i < 4; ++i) dload(i, dpre[i]);
+      }
     }
     const unsigned char* sa = smem + (step & 1) * SB;
     const unsigned char* sb = sa + TB;
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int kc = rr * 4 + grp;
-      floatx4 a[4], b[4];
+      frag_t a[4], b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = wm * 64 + i * 16 + i16;
-        a[i] = *reinterpret_cast<const floatx4*>(sa + m * 128 + 16 * (kc ^ nn256_swz(m)));
+        const int m = wm * 64 + i * 16 + P::arow(i16);
+        a[i] = *reinterpret_cast<const frag_t*>(sa + m * 128 + 16 * (kc ^ nn256_swz(m)));
       }
+      if constexpr (NN) {
+        // b[u * (4 / VE) + h]: k-row kc VE + u, columns wn*64 + h 16 VE + VE i16 ..
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rho = wn * 64 + 16 * j + i16;
-        b[j] = *reinterpret_cast<const floatx4*>(sb + rho * 128 + 16 * (kc ^ nn256_swz(rho)));
+        for (int u = 0; u < VE; ++u)
+#pragma unroll
+          for (int h = 0; h < 4 / VE; ++h)
+            b[u * (4 / VE) + h] =
+                *reinterpret_cast<const frag_t*>(sb + (kc * VE + u) * RB + wn * 64 * (int)sizeof(E) + h * 256 + 16 * i16);
+#pragma unroll
+        for (int u = 0; u < VE; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[i][j] = P::mma(a[i][u], b[u * (4 / VE) + j / VE][j % VE], acc[i][j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rho = wn * 64 + 16 * j + i16;
+          b[j] = *reinterpret_cast<const frag_t*>(sb + rho * 128 + 16 * (kc ^ nn256_swz(rho)));
+        }
+#pragma unroll
+        for (int u = 0; u < VE; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = P::mma(a[i][u], b[j][u], acc[i][j]);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][u], b[j][u], acc[i][j], 0, 0, 0);
     }
     if (more) advance();
     wait_vmcnt0();
     barrier_no_fence();
     if (++ck < nst) continue;
     ck = 0;
-    float* C = reinterpret_cast<float*>(g.C) + cmo;
-    float* C2 = g.C2 ? reinterpret_cast<float*>(g.C2) + cmo : nullptr;
+    E* C = reinterpret_cast<E*>(g.C) + cmo;
+    E* C2 = g.C2 ? reinterpret_cast<E*>(g.C2) + cmo : nullptr;
     const int R0 = cti * T + wm * 64, C0 = ctj * T + wn * 64;
     const bool diag = g.sym && cti == ctj;
     const bool mirror = (g.sym && !diag) || g.transC;
     const bool direct = !g.transC;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float y[4][4], z[4][4];  // [v][j]
+      E d[4][4];  // [v][jb]
+      if constexpr (PREFETCH_D) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int R = R0 + i * 16 + 4 * grp + v, Cc = C0 + 4 * i16 + j;
-          if (plain) {
-            y[v][j] = acc[i][j][v];
-            continue;
-          }
-          double t = g.alpha * (double)acc[i][j][v];
-          if (Dg) t += g.beta * (double)dv[i][v][j];
-          if (R == Cc) t += g.gamma;
-          y[v][j] = (float)t;
-          if (C2) z[v][j] = (float)(g.alpha2 * t + (R == Cc ? g.gamma2 : 0.0));
-        }
+          for (int j = 0; j < 4; ++j) d[v][j] = dpre[i][v][j];
+      } else {
+        if (Dg) dload(i, d);
+      }
+      // output (v, jb) of row block i: C value, and the second output from it
+      auto val = [&](int v, int j, double& t) {
+        const int R = R0 + i * 16 + 4 * grp + v, Cc = C0 + colmap(j);
+        t = g.alpha * (double)acc[i][j][v];
+        if (Dg) t += g.beta * (double)d[v][j];
+        if (R == Cc) t += g.gamma;
+        return plain ? acc[i][j][v] : (E)t;
+      };
+      auto val2 = [&](int v, int j, double t) {
+        const int R = R0 + i * 16 + 4 * grp + v, Cc = C0 + colmap(j);
+        return (E)(g.alpha2 * t + (R == Cc ? g.gamma2 : 0.0));
+      };
       if (diag) {
         // diagonal tile: the upper element (R <= Cc) is written in place and mirrored
 #pragma unroll
         for (int v = 0; v < 4; ++v)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int R = R0 + i * 16 + 4 * grp + v, Cc = C0 + 4 * i16 + j;
+            const int R = R0 + i * 16 + 4 * grp + v, Cc = C0 + colmap(j);
             if (R > Cc) continue;
-            C[(int64_t)R * n + Cc] = y[v][j];
-            C[(int64_t)Cc * n + R] = y[v][j];
+            double t;
+            const E y = val(v, j, t);
+            C[(int64_t)R * n + Cc] = y;
+            C[(int64_t)Cc * n + R] = y;
             if (C2) {
-              C2[(int64_t)R * n + Cc] = z[v][j];
-              C2[(int64_t)Cc * n + R] = z[v][j];
+              const E z = val2(v, j, t);
+              C2[(int64_t)R * n + Cc] = z;
+              C2[(int64_t)Cc * n + R] = z;
             }
           }
         continue;
       }
       if (direct) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int64_t at = (int64_t)(R0 + i * 16 + 4 * grp + v) * n + C0 + 4 * i16;
-          *reinterpret_cast<floatx4*>(C + at) = floatx4{y[v][0], y[v][1], y[v][2], y[v][3]};
-          if (C2) *reinterpret_cast<floatx4*>(C2 + at) = floatx4{z[v][0], z[v][1], z[v][2], z[v][3]};
-        }
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int h = 0; h < 4 / RUN; ++h) {
+            const int64_t at = (int64_t)(R0 + i * 16 + 4 * grp + v) * n + C0 + colmap(h * RUN);
+            E y[RUN], z[RUN];
+            double t[RUN];
+#pragma unroll
+            for (int e = 0; e < RUN; ++e) y[e] = val(v, h * RUN + e, t[e]);
+            store_run<E, RUN>(C + at, y);
+            if (C2) {
+#pragma unroll
+              for (int e = 0; e < RUN; ++e) z[e] = val2(v, h * RUN + e, t[e]);
+              store_run<E, RUN>(C2 + at, z);
+            }
+          }
       }
       if (mirror) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int64_t at = (int64_t)(C0 + 4 * i16 + j) * n + R0 + i * 16 + 4 * grp;
-          *reinterpret_cast<floatx4*>(C + at) = floatx4{y[0][j], y[1][j], y[2][j], y[3][j]};
-          if (C2) *reinterpret_cast<floatx4*>(C2 + at) = floatx4{z[0][j], z[1][j], z[2][j], z[3][j]};
+          const int64_t at = (int64_t)(C0 + colmap(j)) * n + R0 + i * 16 + 4 * grp;
+          E y[4], z[4];
+          double t[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) y[v] = val(v, j, t[v]);
+          store_run<E, 4>(C + at, y);
+          if (C2) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) z[v] = val2(v, j, t[v]);
+            store_run<E, 4>(C2 + at, z);
+          }
         }
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
     if (++ct < ntile) coords(ct, cmo, cti, ctj);
   }
 }

@@ -149,12 +149,30 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
       hipLaunchKernelGGL(gemm_f32_nn256_kernel, dim3((unsigned)wgs), dim3(512), NN256_LDS, st, h);
       return hipGetLastError();
     }
-    if (!c.nn && T == NT128_T) {
+  }
+  // One operand type throughout, float32 or float64, n a multiple of 128:
+  // persistent 128-tile kernel (NT in every mode; NN without sym/transC).
+  constexpr bool same32 = MM == Mma::F32 && std::is_same<TA, float>::value && std::is_same<TB, float>::value &&
+                          std::is_same<TC, float>::value;
+  constexpr bool same64 = MM == Mma::F64 && std::is_same<TA, double>::value && std::is_same<TB, double>::value &&
+                          std::is_same<TC, double>::value;
+  if constexpr (same32 || same64) {
+    if (T == P128_T && (!c.nn || (!c.sym && !c.transC))) {
+      using E = typename std::conditional<same32, float, double>::type;
       int cus = 0;
       HIP_TRY_ERR(cu_count(&cus));
+      GemmArgs h = g;
+      if (c.nn) {
+        h.sym = 0;
+        h.tiles = h.nt * h.nt;
+        h.total = batch * h.tiles;
+      }
       // persistent grid: two workgroups per CU, a multiple of the 8 XCDs
-      const int64_t wgs = std::min<int64_t>(((g.total + 7) / 8) * 8, std::max(8, (cus / 8) * 8) * 2);
-      hipLaunchKernelGGL(gemm_f32_nt128_kernel, dim3((unsigned)wgs), dim3(256), 0, st, g);
+      const int64_t wgs = std::min<int64_t>(((h.total + 7) / 8) * 8, std::max(8, (cus / 8) * 8) * 2);
+      if (c.nn)
+        hipLaunchKernelGGL((gemm_p128_kernel<E, true>), dim3((unsigned)wgs), dim3(256), 0, st, h);
+      else
+        hipLaunchKernelGGL((gemm_p128_kernel<E, false>), dim3((unsigned)wgs), dim3(256), 0, st, h);
       return hipGetLastError();
     }
   }

@@ -86,10 +86,11 @@ def test_newton_db_large_tile_products(mir, B, n):
 
 
 def test_large_and_small_tile_products_bit_identical(mir):
-    """The 256-tile float32 product walks k in the same order as the 128-tile
-    one, and identity padding adds exact zeros: a 384 x 384 stack (128-tile
-    kernel) and the same stack padded to 512 with valid = 384 (256-tile
-    kernel) give bit-identical roots under Frobenius scaling."""
+    """The 256-tile float32 NN product walks k in the same order as the
+    persistent 128-tile one, and identity padding adds exact zeros: a
+    384 x 384 stack (128-tile kernel) and the same stack padded to 512 with
+    valid = 384 (256-tile kernel) give bit-identical roots under Frobenius
+    scaling."""
     n, v = 6, 384
     A = synthetic.spd_stack(384, n, v, 1e-3, 1.0).astype(np.float32)
     X1, s1, f1 = run_root(mir, A, 4, method="ndb", scaling="frobenius", iters=22, iters2=15)
@@ -102,15 +103,17 @@ def test_large_and_small_tile_products_bit_identical(mir):
     assert not X2[:, v:, :].any() and not X2[:, :, v:].any()
 
 
-@pytest.mark.parametrize("method", ["cn", "chebyshev"])
-def test_nt_product_kernels_bit_identical(mir, method):
-    """Symmetric NT products: a 192 x 192 stack runs on the 64-tile kernel,
-    the same stack padded to 256 (valid = 192) on the persistent 128-tile
-    kernel; both walk k in the same order and the padding adds exact zeros,
-    so the roots agree bit for bit (Chebyshev exercises the D operand)."""
+@pytest.mark.parametrize("compute", ["f32", "f64"])
+@pytest.mark.parametrize("method", ["cn", "ndb", "chebyshev"])
+def test_product_kernels_bit_identical(mir, method, compute):
+    """A 192 x 192 stack runs on the 64-tile product kernel, the same stack
+    padded to 256 (valid = 192) on the persistent kernels (128-tile NT and
+    float64 NN, 256-tile float32 NN); all walk k in the same order and the
+    padding adds exact zeros, so the roots agree bit for bit.  Chebyshev
+    exercises the D operand, Newton-DB p = 4 the second output."""
     n, v = 5, 192
     A = synthetic.spd_stack(192, n, v, 1e-2, 1.0).astype(np.float32)
-    kw = dict(method=method, scaling="frobenius", iters=20, cheb_degree=12, eps=1e-3)
+    kw = dict(method=method, scaling="frobenius", iters=20, iters2=14, cheb_degree=12, eps=1e-3, compute=compute)
     X1, s1, f1 = run_root(mir, A, 4, **kw)
     Ap = np.zeros((n, 256, 256), dtype=np.float32)
     Ap[:, :v, :v] = A
