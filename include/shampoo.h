@@ -296,6 +296,19 @@ shampoo_status shampoo_check_flags(const int32_t* flags_dev, int64_t n, hipStrea
 shampoo_status shampoo_timing_enable(int32_t capacity);
 shampoo_status shampoo_timing_read(float* ms, int32_t capacity, int32_t* count);
 
+/* Matrix-core throughput microbenchmark (for the roofline denominators).
+ * Launches, on `stream`, a kernel whose waves (8 per SIMD on every CU) each
+ * issue a long chain of independent 16x16 MFMAs from registers (no memory
+ * traffic), times it with a HIP event pair and waits for it.
+ *   dt    F32 (v_mfma_f32_16x16x4_f32), F64 (v_mfma_f64_16x16x4_f64),
+ *         F16 (v_mfma_f32_16x16x32_f16) or BF16 (v_mfma_f32_16x16x32_bf16);
+ *   sink_dev  device buffer of at least 64 bytes (written only under a
+ *         condition that never holds; it keeps the results live);
+ *   tflops    out: dense TFLOP/s achieved.
+ * Errors: E_UNSUPPORTED for another dtype, E_INVALID for null pointers,
+ * E_HIP for launch/event failures. */
+shampoo_status shampoo_mfma_peak(shampoo_dtype dt, void* sink_dev, hipStream_t stream, double* tflops);
+
 #ifdef __cplusplus
 }
 #endif

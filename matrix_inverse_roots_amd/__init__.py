@@ -88,7 +88,7 @@ EXPORTS = [
     "shampoo_unpack_blocks", "shampoo_update_stats", "shampoo_inverse_root_workspace",
     "shampoo_inverse_root", "shampoo_precondition_workspace", "shampoo_precondition",
     "shampoo_step_workspace", "shampoo_step", "shampoo_check_flags", "shampoo_timing_enable",
-    "shampoo_timing_read",
+    "shampoo_timing_read", "shampoo_mfma_peak",
 ]
 
 
@@ -121,6 +121,7 @@ def _load():
         "shampoo_check_flags": ([vp, i64, vp], ctypes.c_int),
         "shampoo_timing_enable": ([i32], ctypes.c_int),
         "shampoo_timing_read": ([vp, i32, P(i32)], ctypes.c_int),
+        "shampoo_mfma_peak": ([ctypes.c_int, vp, vp, P(ctypes.c_double)], ctypes.c_int),
     }
     for name in EXPORTS:
         f = getattr(lib, name)
@@ -332,6 +333,16 @@ def shampoo_timing_read(capacity):
     n = ctypes.c_int32(0)
     _check(lib.shampoo_timing_read(buf, int(capacity), ctypes.byref(n)))
     return [buf[i] for i in range(n.value)]
+
+
+def shampoo_mfma_peak(dtype, stream=None):
+    """Measured dense matrix-core TFLOP/s for dtype "f32", "f64", "f16" or "bf16"."""
+    import torch
+    sink = torch.zeros(16, dtype=torch.float32, device="cuda")
+    out = ctypes.c_double(0.0)
+    _check(lib.shampoo_mfma_peak(DTYPES[dtype], ctypes.c_void_p(sink.data_ptr()), _stream(stream),
+                                 ctypes.byref(out)))
+    return out.value
 
 
 from .optimizer import Shampoo, ShampooStack  # noqa: E402  (needs the binding above)

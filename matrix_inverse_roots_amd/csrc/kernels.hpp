@@ -3,7 +3,7 @@
 // pack/unpack   parameter layout <-> zero-padded [nblk, B, B] block stacks
 //               ([DASH] "4. Blocking Strategy"), with an LDS tile transpose
 //               for the transposed stack the right-factor products read.
-// frob_norm     s = ||A + eps I||_F over each matrix's valid region
+// frob_*        s = ||A + eps I||_F over each matrix's valid region
 //               ([DASH] "3. Inverse Root Methods", Matrix scaling).
 // prep          A_s = (A + eps I)/s with the padding set to the identity (or
 //               to zero for the power iteration), and up to three affine
@@ -116,69 +116,149 @@ __global__ void valid_from_table_kernel(const shampoo_block* __restrict__ table,
 }
 
 // ---------------------------------------------------------------------------
-// Frobenius norm of A + eps I over the valid region; one workgroup per matrix
+// Four consecutive elements (16-byte aligned) as doubles, and back.
+// ---------------------------------------------------------------------------
+template <typename T> struct Quad;
+template <> struct Quad<float> {
+  static __device__ __forceinline__ void load(const float* p, double* o) {
+    const floatx4 t = *reinterpret_cast<const floatx4*>(p);
+    o[0] = t[0]; o[1] = t[1]; o[2] = t[2]; o[3] = t[3];
+  }
+  static __device__ __forceinline__ void store(float* p, const double* v) {
+    *reinterpret_cast<floatx4*>(p) = floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  }
+};
+template <> struct Quad<double> {
+  static __device__ __forceinline__ void load(const double* p, double* o) {
+    const doublex2 t0 = *reinterpret_cast<const doublex2*>(p), t1 = *reinterpret_cast<const doublex2*>(p + 2);
+    o[0] = t0[0]; o[1] = t0[1]; o[2] = t1[0]; o[3] = t1[1];
+  }
+  static __device__ __forceinline__ void store(double* p, const double* v) {
+    *reinterpret_cast<doublex2*>(p) = doublex2{v[0], v[1]};
+    *reinterpret_cast<doublex2*>(p + 2) = doublex2{v[2], v[3]};
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Frobenius norm of A + eps I over the valid region, in two passes.
+// frob_partial: grid (P, n).  The valid region is read as rows of ceil(v/4)
+// four-element chunks; part p of matrix b sums the chunks
+// [p total / P, (p + 1) total / P) of that sequence, chunk k going to thread
+// k % 256, 8 chunks in flight per thread.  frob_finish adds the P partial
+// sums of each matrix in order.  The summation order thus depends on the
+// valid side v and on P (a function of the batch size) alone: a padded and
+// an unpadded stack give the same bits.
 // ---------------------------------------------------------------------------
 template <typename TI>
-__global__ __launch_bounds__(256) void frob_norm_kernel(const TI* __restrict__ in, int B,
-                                                        const int32_t* __restrict__ valid, double eps,
-                                                        double* __restrict__ s_out) {
+__global__ __launch_bounds__(256) void frob_partial_kernel(const TI* __restrict__ in, int B,
+                                                           const int32_t* __restrict__ valid, double eps,
+                                                           int P, double* __restrict__ part) {
+  constexpr int U = 8;
   __shared__ double red[4];
-  const int64_t b = blockIdx.x;
+  const int p = blockIdx.x;
+  const int64_t b = blockIdx.y;
   const int v = valid ? min(max(valid[b], 0), B) : B;
   const TI* A = in + b * (int64_t)B * B;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cv = (v + 3) / 4;
+  const int64_t total = (int64_t)v * cv;
+  const int k0 = (int)(total * p / P), k1 = (int)(total * (p + 1) / P);
   double acc = 0.0;
-  for (int r = wave; r < v; r += 4) {
-    const TI* row = A + (int64_t)r * B;
-    for (int c = lane; c < v; c += 64) {
-      double x = (double)row[c];
-      if (c == r) x += eps;
-      acc += x * x;
+  for (int base = k0; base < k1; base += 256 * U) {
+    double x[U][4];
+    int rr[U], cc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = base + u * 256 + (int)threadIdx.x;
+      rr[u] = k / cv;
+      cc[u] = 4 * (k - rr[u] * cv);
+      if (k < k1) Quad<TI>::load(A + (int64_t)rr[u] * B + cc[u], x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (base + u * 256 + (int)threadIdx.x >= k1) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (cc[u] + e >= v) continue;
+        double y = x[u][e];
+        if (rr[u] == cc[u] + e) y += eps;
+        acc += y * y;
+      }
     }
   }
   acc = block_sum256(acc, red);
-  if (threadIdx.x == 0) s_out[b] = sqrt(acc);
+  if (threadIdx.x == 0) part[b * P + p] = acc;
+}
+
+__global__ __launch_bounds__(256) void frob_finish_kernel(const double* __restrict__ part, int P, int64_t n,
+                                                          double* __restrict__ s_out) {
+  const int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (b >= n) return;
+  double acc = 0.0;
+  for (int p = 0; p < P; ++p) acc += part[b * P + p];
+  s_out[b] = sqrt(acc);
 }
 
 // ---------------------------------------------------------------------------
 // prep: a = (A + eps I)/s on the valid region, delta_ij * pad_diag elsewhere;
-// out_q = alpha_q a + gamma_q I for up to three outputs.
+// out_q = alpha_q a + gamma_q I for up to three outputs.  Grid (chunks, n):
+// each thread maps PREP_U four-element chunks of one matrix.
 // ---------------------------------------------------------------------------
 struct PrepOut {
   void* p;
   double alpha, gamma;
 };
+constexpr int PREP_U = 4;
 
 template <typename TI, typename TS>
 __global__ __launch_bounds__(256) void prep_kernel(const TI* __restrict__ in, int B, int64_t nmat,
                                                    const int32_t* __restrict__ valid, double eps,
                                                    const double* __restrict__ s, double pad_diag,
                                                    PrepOut o0, PrepOut o1, PrepOut o2) {
+  const int64_t b = blockIdx.y;
   const int64_t BB = (int64_t)B * B;
-  const int64_t idx = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) * 4;
-  if (idx >= nmat * BB) return;
-  const int64_t b = idx / BB;
-  const int64_t e = idx - b * BB;
-  const int r = (int)(e / B);
-  const int c0 = (int)(e - (int64_t)r * B);
+  const int cpr = B / 4;  // chunks per row
   const int v = valid ? min(max(valid[b], 0), B) : B;
   const double sb = s[b];
   const double inv = (sb > 0.0 && sb < 1.0e300) ? 1.0 / sb : 0.0;
+  const TI* A = in + b * BB;
+  TS* out[3] = {o0.p ? reinterpret_cast<TS*>(o0.p) + b * BB : nullptr,
+                o1.p ? reinterpret_cast<TS*>(o1.p) + b * BB : nullptr,
+                o2.p ? reinterpret_cast<TS*>(o2.p) + b * BB : nullptr};
+  const double al[3] = {o0.alpha, o1.alpha, o2.alpha}, ga[3] = {o0.gamma, o1.gamma, o2.gamma};
+  const int total = B * cpr;
+  double x[PREP_U][4];
+  int rr[PREP_U], cc[PREP_U];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c = c0 + q;
-    double a;
-    if (r < v && c < v) {
-      a = (double)in[idx + q];
-      if (r == c) a += eps;
-      a *= inv;
-    } else {
-      a = (r == c) ? pad_diag : 0.0;
+  for (int u = 0; u < PREP_U; ++u) {
+    const int k = ((int)blockIdx.x * PREP_U + u) * 256 + (int)threadIdx.x;
+    rr[u] = k / cpr;
+    cc[u] = 4 * (k - rr[u] * cpr);
+    if (k < total && rr[u] < v && cc[u] < v) Quad<TI>::load(A + (int64_t)rr[u] * B + cc[u], x[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < PREP_U; ++u) {
+    const int k = ((int)blockIdx.x * PREP_U + u) * 256 + (int)threadIdx.x;
+    if (k >= total) continue;
+    double a[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = rr[u], c = cc[u] + e;
+      if (r < v && c < v) {
+        a[e] = x[u][e];
+        if (r == c) a[e] += eps;
+        a[e] *= inv;
+      } else {
+        a[e] = (r == c) ? pad_diag : 0.0;
+      }
     }
-    const double d = (r == c) ? 1.0 : 0.0;
-    if (o0.p) reinterpret_cast<TS*>(o0.p)[idx + q] = (TS)(o0.alpha * a + o0.gamma * d);
-    if (o1.p) reinterpret_cast<TS*>(o1.p)[idx + q] = (TS)(o1.alpha * a + o1.gamma * d);
-    if (o2.p) reinterpret_cast<TS*>(o2.p)[idx + q] = (TS)(o2.alpha * a + o2.gamma * d);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      if (!out[q]) continue;
+      double y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = al[q] * a[e] + ga[q] * (rr[u] == cc[u] + e ? 1.0 : 0.0);
+      Quad<TS>::store(out[q] + (int64_t)rr[u] * B + cc[u], y);
+    }
   }
 }
 
@@ -325,23 +405,39 @@ __global__ __launch_bounds__(256) void finalize_kernel(const TS* __restrict__ X,
   const double sb = s[b];
   const bool zero = !(sb > 0.0 && sb < 1.0e300);
   const double f = zero ? 0.0 : pow(sb, -inv_p);
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  // thread: 4 consecutive columns (c4) of rows rg, rg + 16, rg + 32, rg + 48
+  const int c4 = 4 * (threadIdx.x & 15), rg = threadIdx.x >> 4;
   if (sym_out) {
-    // mirror tile (tc, tr): element [cc][rr] = X[tc*64 + cc][tr*64 + rr]
-    for (int cc = ty; cc < 64; cc += 4) mir_tile[cc][tx] = Xb[(int64_t)(tc * 64 + cc) * B + tr * 64 + tx];
+    // mirror tile (tc, tr): mir_tile[cc][rr] = X[tc*64 + cc][tr*64 + rr]
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int cc = rg + 16 * k;
+      double t[4];
+      Quad<TS>::load(Xb + (int64_t)(tc * 64 + cc) * B + tr * 64 + c4, t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mir_tile[cc][c4 + e] = (TS)t[e];
+    }
     __syncthreads();
   }
   int bad = 0;
-  for (int rr = ty; rr < 64; rr += 4) {
-    const int r = tr * 64 + rr, c = tc * 64 + tx;
-    double x = 0.0;
-    if (r < v && c < v && !zero) {
-      x = (double)Xb[(int64_t)r * B + c];
-      if (sym_out) x = 0.5 * (x + (double)mir_tile[tx][rr]);
-      x *= f;
-      if (!isfinite(x)) bad = 1;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int rr = rg + 16 * k, r = tr * 64 + rr, c0 = tc * 64 + c4;
+    double x[4] = {0.0, 0.0, 0.0, 0.0};
+    if (r < v && c0 < v && !zero) {
+      double t[4];
+      Quad<TS>::load(Xb + (int64_t)r * B + c0, t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (c0 + e >= v) continue;
+        double y = t[e];
+        if (sym_out) y = 0.5 * (y + (double)mir_tile[c4 + e][rr]);
+        y *= f;
+        if (!isfinite(y)) bad = 1;
+        x[e] = y;
+      }
     }
-    ob[(int64_t)r * B + c] = (TO)x;
+    Quad<TO>::store(ob + (int64_t)r * B + c0, x);
   }
   bad = __syncthreads_or(bad);
   if (threadIdx.x == 0 && blockIdx.x == 0) {
@@ -465,6 +561,82 @@ __global__ __launch_bounds__(256) void graft_update_kernel(GraftArgs a) {
         P.w[prow + c] -= a.lr * dg;
       }
     }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Matrix-core throughput: each wave runs `iters` rounds of CHAINS independent
+// MFMAs on register operands (64 accumulator registers per lane, so the
+// compiler keeps them in place across the loop).  `never` is 0 at run time; the store it guards
+// keeps the accumulators live.
+// ---------------------------------------------------------------------------
+template <Mma M> struct PeakOp;
+template <> struct PeakOp<Mma::F32> {
+  using acc_t = floatx4;
+  using op_t = float;
+  static constexpr int CHAINS = 16;
+  static constexpr double flops = 2.0 * 16 * 16 * 4;
+  static __device__ __forceinline__ op_t make(float x) { return x; }
+  static __device__ __forceinline__ acc_t mma(op_t a, op_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct PeakOp<Mma::F64> {
+  using acc_t = doublex4;
+  using op_t = double;
+  static constexpr int CHAINS = 8;
+  static constexpr double flops = 2.0 * 16 * 16 * 4;
+  static __device__ __forceinline__ op_t make(float x) { return (double)x; }
+  static __device__ __forceinline__ acc_t mma(op_t a, op_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct PeakOp<Mma::F16> {
+  using acc_t = floatx4;
+  using op_t = halfx8;
+  static constexpr int CHAINS = 16;
+  static constexpr double flops = 2.0 * 16 * 16 * 32;
+  static __device__ __forceinline__ op_t make(float x) {
+    const _Float16 h = (_Float16)x;
+    return op_t{h, h, h, h, h, h, h, h};
+  }
+  static __device__ __forceinline__ acc_t mma(op_t a, op_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct PeakOp<Mma::BF16> {
+  using acc_t = floatx4;
+  using op_t = bf16x8;
+  static constexpr int CHAINS = 16;
+  static constexpr double flops = 2.0 * 16 * 16 * 32;
+  static __device__ __forceinline__ op_t make(float x) {
+    const __bf16 h = (__bf16)x;
+    return op_t{h, h, h, h, h, h, h, h};
+  }
+  static __device__ __forceinline__ acc_t mma(op_t a, op_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <Mma M>
+__global__ __launch_bounds__(256, 4) void mfma_peak_kernel(int iters, int never, float* __restrict__ sink) {
+  using Op = PeakOp<M>;
+  constexpr int NC = Op::CHAINS;
+  typename Op::acc_t acc[NC];
+  const float t = 1.0f + 1e-3f * (float)(threadIdx.x & 63);
+  const typename Op::op_t a = Op::make(t), b = Op::make(2.0f - t);
+#pragma unroll
+  for (int j = 0; j < NC; ++j) acc[j] = typename Op::acc_t{0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) acc[j] = Op::mma(a, b, acc[j]);
+  }
+  if (never) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) s += (float)(acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3]);
+    sink[threadIdx.x & 15] = s;
   }
 }
 

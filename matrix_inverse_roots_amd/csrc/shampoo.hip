@@ -514,8 +514,6 @@ size_t root_ws_bytes(int64_t n, int32_t B, const Plan& P, int compute) {
   return 2 * align_up((size_t)n * 8) + (size_t)nbuf * align_up((size_t)n * B * B * es);
 }
 
-int64_t elementwise_grid(int64_t nelem) { return (nelem / 4 + 255) / 256; }
-
 // Benchmark timing of the batched products (shampoo_timing_enable).
 struct Timing {
   std::vector<hipEvent_t> ev;  // 2 per launch
@@ -536,8 +534,9 @@ template <typename TI, typename TS>
 hipError_t launch_prep(const void* in, int B, int64_t n, const int32_t* valid, double eps, const double* s,
                        double pad_diag, const PrepOut& o0, const PrepOut& o1, const PrepOut& o2,
                        hipStream_t st) {
-  const int64_t g = elementwise_grid(n * (int64_t)B * B);
-  hipLaunchKernelGGL((prep_kernel<TI, TS>), dim3((unsigned)g), dim3(256), 0, st, (const TI*)in, B, n, valid,
+  const int64_t chunks = (int64_t)B * B / 4;
+  const unsigned gx = (unsigned)((chunks + 256 * PREP_U - 1) / (256 * PREP_U));
+  hipLaunchKernelGGL((prep_kernel<TI, TS>), dim3(gx, (unsigned)n), dim3(256), 0, st, (const TI*)in, B, n, valid,
                      eps, s, pad_diag, o0, o1, o2);
   return hipGetLastError();
 }
@@ -554,9 +553,15 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
   const size_t bufstride = align_up((size_t)n * BB * sizeof(TS));
   auto buf = [&](int i) -> TS* { return (TS*)(bufbase + (size_t)i * bufstride); };
 
-  hipLaunchKernelGGL((frob_norm_kernel<TI>), dim3((unsigned)n), dim3(256), 0, st, (const TI*)in, B, valid,
-                     o->eps, sf);
-  LAUNCH_CHECK("frob_norm");
+  // Frobenius norms: P workgroups per matrix (about 2048 in all), partial
+  // sums in the first iterate buffer, which prep overwrites afterwards.
+  const int parts = (int)std::max<int64_t>(1, std::min<int64_t>(32, (2048 + n - 1) / n));
+  hipLaunchKernelGGL((frob_partial_kernel<TI>), dim3((unsigned)parts, (unsigned)n), dim3(256), 0, st, (const TI*)in,
+                     B, valid, o->eps, parts, (double*)buf(0));
+  LAUNCH_CHECK("frob_partial");
+  hipLaunchKernelGGL(frob_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const double*)buf(0),
+                     parts, n, sf);
+  LAUNCH_CHECK("frob_finish");
   const double* sc = sf;
   if (o->scaling == SHAMPOO_SCALE_POWER) {
     if (!o->pi_start_dev) return fail(SHAMPOO_E_INVALID, "power scaling needs pi_start_dev");
@@ -1010,6 +1015,56 @@ shampoo_status shampoo_timing_read(float* ms, int32_t capacity, int32_t* count) 
   }
   *count = n;
   g_timing.used = 0;
+  return SHAMPOO_OK;
+}
+
+shampoo_status shampoo_mfma_peak(shampoo_dtype dt, void* sink_dev, hipStream_t stream, double* tflops) {
+  if (!sink_dev || !tflops) return fail(SHAMPOO_E_INVALID, "null pointer argument");
+  int cus = 0;
+  HIP_TRY(cu_count(&cus));
+  const unsigned grid = (unsigned)(cus * 8);  // 8 workgroups of 4 waves per CU
+  const int iters = 4096;
+  double flops_per_round = 0;  // per wave and loop round
+  auto launch = [&](int it) -> hipError_t {
+    switch (dt) {
+      case SHAMPOO_F32:
+        hipLaunchKernelGGL(mfma_peak_kernel<Mma::F32>, dim3(grid), dim3(256), 0, stream, it, 0, (float*)sink_dev);
+        flops_per_round = PeakOp<Mma::F32>::flops * PeakOp<Mma::F32>::CHAINS;
+        break;
+      case SHAMPOO_F64:
+        hipLaunchKernelGGL(mfma_peak_kernel<Mma::F64>, dim3(grid), dim3(256), 0, stream, it, 0, (float*)sink_dev);
+        flops_per_round = PeakOp<Mma::F64>::flops * PeakOp<Mma::F64>::CHAINS;
+        break;
+      case SHAMPOO_F16:
+        hipLaunchKernelGGL(mfma_peak_kernel<Mma::F16>, dim3(grid), dim3(256), 0, stream, it, 0, (float*)sink_dev);
+        flops_per_round = PeakOp<Mma::F16>::flops * PeakOp<Mma::F16>::CHAINS;
+        break;
+      case SHAMPOO_BF16:
+        hipLaunchKernelGGL(mfma_peak_kernel<Mma::BF16>, dim3(grid), dim3(256), 0, stream, it, 0, (float*)sink_dev);
+        flops_per_round = PeakOp<Mma::BF16>::flops * PeakOp<Mma::BF16>::CHAINS;
+        break;
+      default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  };
+  if (dt != SHAMPOO_F32 && dt != SHAMPOO_F64 && dt != SHAMPOO_F16 && dt != SHAMPOO_BF16)
+    return fail(SHAMPOO_E_UNSUPPORTED, "dtype %d (F32, F64, F16, BF16)", (int)dt);
+  HIP_TRY(launch(iters / 8));  // warm-up
+  hipEvent_t e0, e1;
+  HIP_TRY(hipEventCreate(&e0));
+  HIP_TRY(hipEventCreate(&e1));
+  hipError_t err = hipEventRecord(e0, stream);
+  if (err == hipSuccess) err = launch(iters);
+  if (err == hipSuccess) err = hipEventRecord(e1, stream);
+  if (err == hipSuccess) err = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  HIP_TRY(err);
+  const double waves = (double)grid * 4;
+  *tflops = waves * iters * flops_per_round / (ms * 1e-3) / 1e12;
   return SHAMPOO_OK;
 }
 
