@@ -87,6 +87,24 @@ typedef enum shampoo_graft {
 #define SHAMPOO_FLAG_ZERO_SCALE 2 /* scale s was 0 or not finite: output set to 0 */
 #define SHAMPOO_FLAG_PI_FALLBACK 4 /* power iteration gave no positive finite
                                       quotient: Frobenius scale used instead */
+#define SHAMPOO_FLAG_RECOMPUTED_F64 8 /* shampoo_step fallback: the root was
+                                         recomputed with the float64 chain */
+#define SHAMPOO_FLAG_KEPT_PREVIOUS 16 /* shampoo_step fallback: the factor's
+                                         previous root was kept */
+
+/* What shampoo_step does with a factor whose new root is not finite (or
+ * whose scale is zero).  [DIST] abstract: the distributed implementation
+ * retries a failed lower-precision root computation at higher precision. */
+typedef enum shampoo_fallback {
+  SHAMPOO_FALLBACK_NONE = 0,     /* write the root as computed and flag it */
+  SHAMPOO_FALLBACK_KEEP = 1,     /* keep the factor's previous root */
+  SHAMPOO_FALLBACK_F64 = 2       /* recompute the non-finite factors with the
+                                    float64 chain (same method and counts),
+                                    keeping the previous root where that also
+                                    fails (and for zero scales); synchronises
+                                    the stream to count them; as KEEP when
+                                    root.compute is already F64 */
+} shampoo_fallback;
 
 /* One row of a block table (32 bytes, plain old data).  [DASH] "4. Blocking
  * Strategy"; [3DS] "Hyperparameters" (block_size, 0 = never split).
@@ -160,7 +178,7 @@ typedef struct shampoo_step_args {
   shampoo_dtype g_dt;               /* SHAMPOO_F32 or SHAMPOO_BF16 */
   int32_t p;                        /* root order, 4 for Shampoo */
   shampoo_dtype stats_dt;           /* SHAMPOO_F32 or SHAMPOO_F64: element type of LR and roots */
-  int32_t reserved0;
+  int32_t fallback;                 /* shampoo_fallback, for factors whose new root is not finite */
   void* LR;                         /* device [2 nblk, B, B] stats_dt: L stack then R stack (state) */
   void* roots;                      /* device [2 nblk, B, B] stats_dt: inverse roots (state) */
   double beta2;                     /* statistics EMA; 1 = plain sum */
@@ -278,7 +296,13 @@ shampoo_status shampoo_step_workspace(const shampoo_step_args* args, size_t* byt
  * ||D||_F) D (0 when D = 0) with Delta = G (SGD, MOMENTUM) or the
  * bias-corrected Adam direction; SGD/ADAM: W -= lr D_g; MOMENTUM:
  * M = momentum M + D_g, W -= lr M; NONE: W -= lr D.  Norms are reduced in a
- * fixed order, so two identical calls give identical bits. */
+ * fixed order, so two identical calls give identical bits.
+ * Roots that come out non-finite or with a zero scale are handled by
+ * args->fallback (shampoo_fallback); the flags of the step's factors are
+ * OR-ed into flags_dev (NONFINITE and ZERO_SCALE describe the first attempt,
+ * RECOMPUTED_F64 and KEPT_PREVIOUS what the fallback did).  FALLBACK_F64
+ * waits for the stream once (to count the flagged factors) and needs the
+ * larger workspace that shampoo_step_workspace reports for it. */
 shampoo_status shampoo_step(const shampoo_step_args* args, hipStream_t stream);
 
 /* Synchronises `stream`, then returns E_NONFINITE if any of the n flags is

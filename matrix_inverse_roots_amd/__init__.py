@@ -27,7 +27,8 @@ F32, F16, BF16, F64 = 0, 1, 2, 3
 CN, NDB, CHEBYSHEV = 0, 1, 2
 SCALE_FROBENIUS, SCALE_POWER = 0, 1
 GRAFT_SGD, GRAFT_MOMENTUM, GRAFT_ADAM, GRAFT_NONE = 0, 1, 2, 3
-FLAG_NONFINITE, FLAG_ZERO_SCALE, FLAG_PI_FALLBACK = 1, 2, 4
+FLAG_NONFINITE, FLAG_ZERO_SCALE, FLAG_PI_FALLBACK, FLAG_RECOMPUTED_F64, FLAG_KEPT_PREVIOUS = 1, 2, 4, 8, 16
+FALLBACKS = {"none": 0, "keep": 1, "f64": 2}
 
 METHODS = {"cn": CN, "ndb": NDB, "chebyshev": CHEBYSHEV}
 SCALINGS = {"frobenius": SCALE_FROBENIUS, "power": SCALE_POWER}
@@ -72,7 +73,7 @@ class StepArgsC(ctypes.Structure):
     _fields_ = [("nparams", ctypes.c_int32), ("B", ctypes.c_int32), ("nblk", ctypes.c_int64),
                 ("params_dev", ctypes.c_void_p), ("table_dev", ctypes.c_void_p),
                 ("g_dt", ctypes.c_int32), ("p", ctypes.c_int32),
-                ("stats_dt", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("stats_dt", ctypes.c_int32), ("fallback", ctypes.c_int32),
                 ("LR", ctypes.c_void_p), ("roots", ctypes.c_void_p),
                 ("beta2", ctypes.c_double), ("recompute_roots", ctypes.c_int32),
                 ("root", RootOptsC),

@@ -388,15 +388,21 @@ __global__ __launch_bounds__(256) void power_iter_kernel(const TS* __restrict__ 
 // tile: the tile and its mirror are staged through LDS so that every global
 // access is a coalesced row segment; one flag update per workgroup.
 // ---------------------------------------------------------------------------
+// mode FIN_WRITE: write and flag; FIN_CHECK: flag only (out unused);
+// FIN_COMMIT: write only matrices whose flags show neither NONFINITE nor
+// ZERO_SCALE (set by a FIN_CHECK pass), flags untouched.
+enum { FIN_WRITE = 0, FIN_CHECK = 1, FIN_COMMIT = 2 };
+
 template <typename TS, typename TO>
 __global__ __launch_bounds__(256) void finalize_kernel(const TS* __restrict__ X, TO* __restrict__ out, int B,
                                                        const int32_t* __restrict__ valid,
                                                        const double* __restrict__ s, double inv_p,
                                                        int sym_out, float* __restrict__ scale_out,
-                                                       int32_t* __restrict__ flags) {
+                                                       int32_t* __restrict__ flags, int mode) {
   __shared__ TS mir_tile[64][65];
   const int tps = B / 64;
   const int64_t b = blockIdx.y;
+  if (mode == FIN_COMMIT && (flags[b] & (SHAMPOO_FLAG_NONFINITE | SHAMPOO_FLAG_ZERO_SCALE))) return;  // uniform
   const int tr = blockIdx.x / tps, tc = blockIdx.x - (blockIdx.x / tps) * tps;
   const int64_t BB = (int64_t)B * B;
   const TS* Xb = X + b * BB;
@@ -437,14 +443,69 @@ __global__ __launch_bounds__(256) void finalize_kernel(const TS* __restrict__ X,
         x[e] = y;
       }
     }
-    Quad<TO>::store(ob + (int64_t)r * B + c0, x);
+    if (mode != FIN_CHECK) Quad<TO>::store(ob + (int64_t)r * B + c0, x);
   }
+  if (mode == FIN_COMMIT) return;
   bad = __syncthreads_or(bad);
   if (threadIdx.x == 0 && blockIdx.x == 0) {
     if (flags && zero) atomicOr(flags + b, SHAMPOO_FLAG_ZERO_SCALE);
     if (scale_out) scale_out[b] = (float)sb;
   }
   if (threadIdx.x == 0 && bad && flags) atomicOr(flags + b, SHAMPOO_FLAG_NONFINITE);
+}
+
+// ---------------------------------------------------------------------------
+// step fallback helpers
+// ---------------------------------------------------------------------------
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void gather_i32_kernel(const int32_t* __restrict__ src, const int32_t* __restrict__ idx, int m,
+                                  int32_t* __restrict__ dst) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < m) dst[i] = src[idx[i]];
+}
+
+// dst[i] = src[idx[i]] for matrices of `bytes` bytes (a multiple of 16);
+// grid (chunks, m)
+__global__ __launch_bounds__(256) void gather_matrices_kernel(const unsigned char* __restrict__ src,
+                                                              unsigned char* __restrict__ dst,
+                                                              const int32_t* __restrict__ idx, int64_t bytes) {
+  const int64_t i = blockIdx.y;
+  const uint4* s = reinterpret_cast<const uint4*>(src + (int64_t)idx[i] * bytes);
+  uint4* d = reinterpret_cast<uint4*>(dst + i * bytes);
+  for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < bytes / 16; k += (int64_t)gridDim.x * blockDim.x)
+    d[k] = s[k];
+}
+
+// dst[idx[i]] = src[i] where flags_src[i] shows neither NONFINITE nor
+// ZERO_SCALE, and then fl_dst[idx[i]] |= RECOMPUTED_F64
+__global__ __launch_bounds__(256) void scatter_matrices_kernel(const unsigned char* __restrict__ src,
+                                                               unsigned char* __restrict__ dst,
+                                                               const int32_t* __restrict__ idx,
+                                                               const int32_t* __restrict__ flags_src, int64_t bytes,
+                                                               int32_t* __restrict__ fl_dst) {
+  const int64_t i = blockIdx.y;
+  if (flags_src[i] & (SHAMPOO_FLAG_NONFINITE | SHAMPOO_FLAG_ZERO_SCALE)) return;  // uniform
+  const uint4* s = reinterpret_cast<const uint4*>(src + i * bytes);
+  uint4* d = reinterpret_cast<uint4*>(dst + (int64_t)idx[i] * bytes);
+  for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < bytes / 16; k += (int64_t)gridDim.x * blockDim.x)
+    d[k] = s[k];
+  if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(fl_dst + idx[i], SHAMPOO_FLAG_RECOMPUTED_F64);
+}
+
+// Step flags after the fallback: a factor flagged NONFINITE or ZERO_SCALE
+// that was not recomputed kept its previous root; the result is OR-ed into
+// the caller's flags.
+__global__ void merge_fallback_flags_kernel(const int32_t* __restrict__ fl, int64_t n, int32_t* __restrict__ out) {
+  const int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (b >= n) return;
+  int32_t f = fl[b];
+  if ((f & (SHAMPOO_FLAG_NONFINITE | SHAMPOO_FLAG_ZERO_SCALE)) && !(f & SHAMPOO_FLAG_RECOMPUTED_F64))
+    f |= SHAMPOO_FLAG_KEPT_PREVIOUS;
+  out[b] |= f;
 }
 
 // ---------------------------------------------------------------------------

@@ -541,10 +541,13 @@ hipError_t launch_prep(const void* in, int B, int64_t n, const int32_t* valid, d
   return hipGetLastError();
 }
 
+// keep_flagged: the final pass first only flags (NONFINITE, ZERO_SCALE) and
+// then writes just the matrices left unflagged, so a flagged matrix keeps the
+// previous content of `out` (flags must then be non-null and start at 0).
 template <typename TI, typename TS, Mma MM>
 shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t p, const shampoo_root_opts* o,
                         const Plan& P, const int32_t* valid, float* scale_out, int32_t* flags, void* ws,
-                        hipStream_t st) {
+                        bool keep_flagged, hipStream_t st) {
   const int64_t BB = (int64_t)B * B;
   unsigned char* w = (unsigned char*)ws;
   double* sf = (double*)w;
@@ -601,8 +604,18 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
       timing_advance();
     } else {
       const int tps = B / 64;
-      hipLaunchKernelGGL((finalize_kernel<TS, TI>), dim3((unsigned)(tps * tps), (unsigned)n), dim3(256), 0, st,
-                         buf(op.a), (TI*)out, B, valid, sc, 1.0 / p, P.sym_out ? 1 : 0, scale_out, flags);
+      const dim3 fgrid((unsigned)(tps * tps), (unsigned)n);
+      const int sym = P.sym_out ? 1 : 0;
+      if (keep_flagged) {
+        hipLaunchKernelGGL((finalize_kernel<TS, TI>), fgrid, dim3(256), 0, st, buf(op.a), (TI*)out, B, valid, sc,
+                           1.0 / p, sym, scale_out, flags, (int)FIN_CHECK);
+        LAUNCH_CHECK("finalize");
+        hipLaunchKernelGGL((finalize_kernel<TS, TI>), fgrid, dim3(256), 0, st, buf(op.a), (TI*)out, B, valid, sc,
+                           1.0 / p, sym, scale_out, flags, (int)FIN_COMMIT);
+      } else {
+        hipLaunchKernelGGL((finalize_kernel<TS, TI>), fgrid, dim3(256), 0, st, buf(op.a), (TI*)out, B, valid, sc,
+                           1.0 / p, sym, scale_out, flags, (int)FIN_WRITE);
+      }
       LAUNCH_CHECK("finalize");
     }
   }
@@ -611,7 +624,8 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
 
 shampoo_status inverse_root_impl(const void* in, void* out, shampoo_dtype io_dt, int64_t n, int32_t B, int32_t p,
                                  const shampoo_root_opts* o, const int32_t* valid, float* scale_out,
-                                 int32_t* flags, void* ws, size_t ws_bytes, hipStream_t st) {
+                                 int32_t* flags, void* ws, size_t ws_bytes, hipStream_t st,
+                                 bool keep_flagged = false) {
   shampoo_status r = check_root_args(n, B, p, o);
   if (r != SHAMPOO_OK) return r;
   if (io_dt != SHAMPOO_F32 && io_dt != SHAMPOO_F64)
@@ -629,14 +643,14 @@ shampoo_status inverse_root_impl(const void* in, void* out, shampoo_dtype io_dt,
   const bool in64 = io_dt == SHAMPOO_F64;
   switch (o->compute) {
     case SHAMPOO_F32:
-      return in64 ? run_root<double, float, Mma::F32>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, st)
-                  : run_root<float, float, Mma::F32>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, st);
+      return in64 ? run_root<double, float, Mma::F32>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, keep_flagged, st)
+                  : run_root<float, float, Mma::F32>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, keep_flagged, st);
     case SHAMPOO_F16:
-      return in64 ? run_root<double, float, Mma::F16>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, st)
-                  : run_root<float, float, Mma::F16>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, st);
+      return in64 ? run_root<double, float, Mma::F16>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, keep_flagged, st)
+                  : run_root<float, float, Mma::F16>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, keep_flagged, st);
     default:
-      return in64 ? run_root<double, double, Mma::F64>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, st)
-                  : run_root<float, double, Mma::F64>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, st);
+      return in64 ? run_root<double, double, Mma::F64>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, keep_flagged, st)
+                  : run_root<float, double, Mma::F64>(in, out, n, B, p, o, P, valid, scale_out, flags, ws, keep_flagged, st);
   }
 }
 
@@ -743,6 +757,12 @@ struct StepLayout {
   size_t g, gt, valid, root, partials, scales, total;
   size_t root_bytes;
   int nchunk;
+  // fallback: this step's factor flags; for FALLBACK_F64 the compacted
+  // factors (indices, valid sizes, flags, inputs, roots) and their float64
+  // chain workspace
+  size_t fl, fidx, fvalid, fflags, fin, fout, froot;
+  size_t froot_bytes;
+  bool redo64;
 };
 
 shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
@@ -753,6 +773,8 @@ shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
   if (a->nblk > 32767) return fail(SHAMPOO_E_UNSUPPORTED, "nblk = %lld > 32767", (long long)a->nblk);
   if (a->stats_dt != SHAMPOO_F32 && a->stats_dt != SHAMPOO_F64)
     return fail(SHAMPOO_E_UNSUPPORTED, "statistics dtype %d (F32, F64)", (int)a->stats_dt);
+  if (a->fallback < SHAMPOO_FALLBACK_NONE || a->fallback > SHAMPOO_FALLBACK_F64)
+    return fail(SHAMPOO_E_INVALID, "unknown fallback %d", a->fallback);
   shampoo_status r = check_root_args(2 * a->nblk, a->B, a->p, &a->root);
   if (r != SHAMPOO_OK) return r;
   const Plan P = build_plan(a->p, &a->root);
@@ -771,7 +793,82 @@ shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
   L->root = off; off += root;
   L->partials = off; off += align_up((size_t)a->nblk * L->nchunk * 2 * 8);
   L->scales = off; off += align_up((size_t)a->nblk * 4);
+  const int64_t nf = 2 * a->nblk;
+  L->fl = L->fidx = L->fvalid = L->fflags = L->fin = L->fout = L->froot = 0;
+  L->froot_bytes = 0;
+  L->redo64 = a->fallback == SHAMPOO_FALLBACK_F64 && a->root.compute != SHAMPOO_F64;
+  if (a->fallback != SHAMPOO_FALLBACK_NONE) {
+    L->fl = off; off += align_up((size_t)nf * 4);
+  }
+  if (L->redo64) {
+    const size_t mb = (size_t)BB * dtype_size(a->stats_dt);
+    L->froot_bytes = root_ws_bytes(nf, a->B, P, SHAMPOO_F64);
+    L->fidx = off; off += align_up((size_t)nf * 4);
+    L->fvalid = off; off += align_up((size_t)nf * 4);
+    L->fflags = off; off += align_up((size_t)nf * 4);
+    L->fin = off; off += align_up((size_t)nf * mb);
+    L->fout = off; off += align_up((size_t)nf * mb);
+    L->froot = off; off += L->froot_bytes;
+  }
   L->total = off;
+  return SHAMPOO_OK;
+}
+
+// Inverse roots of the step's 2 nblk factors with the fallback of
+// a->fallback for those whose new root is not finite (see shampoo_fallback).
+shampoo_status step_roots(const shampoo_step_args* a, const StepLayout& L, unsigned char* w, const int32_t* valid,
+                          hipStream_t st) {
+  const int64_t nf = 2 * a->nblk;
+  const int B = a->B;
+  unsigned char* root = w + L.root;
+  if (a->fallback == SHAMPOO_FALLBACK_NONE)
+    return inverse_root_impl(a->LR, a->roots, a->stats_dt, nf, B, a->p, &a->root, valid, nullptr, a->flags_dev, root,
+                             L.root_bytes, st);
+  int32_t* fl = (int32_t*)(w + L.fl);
+  const unsigned g1 = (unsigned)((nf + 255) / 256);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(g1), dim3(256), 0, st, fl, nf, 0);
+  LAUNCH_CHECK("fill");
+  shampoo_status r = inverse_root_impl(a->LR, a->roots, a->stats_dt, nf, B, a->p, &a->root, valid, nullptr, fl, root,
+                                       L.root_bytes, st, true);
+  if (r != SHAMPOO_OK) return r;
+  if (L.redo64) {
+    // count the flagged factors on the host, then recompute them in float64
+    std::vector<int32_t> hf((size_t)nf), idx;
+    HIP_TRY(hipMemcpyAsync(hf.data(), fl, (size_t)nf * 4, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    for (int64_t b = 0; b < nf; ++b)
+      if (hf[(size_t)b] & SHAMPOO_FLAG_NONFINITE) idx.push_back((int32_t)b);
+    const int m = (int)idx.size();
+    if (m > 0) {
+      int32_t* fidx = (int32_t*)(w + L.fidx);
+      int32_t* fvalid = (int32_t*)(w + L.fvalid);
+      int32_t* fflags = (int32_t*)(w + L.fflags);
+      const int64_t mbytes = (int64_t)B * B * (int64_t)dtype_size(a->stats_dt);
+      HIP_TRY(hipMemcpyAsync(fidx, idx.data(), (size_t)m * 4, hipMemcpyHostToDevice, st));
+      const unsigned chunks = (unsigned)std::min<int64_t>(64, (mbytes / 16 + 255) / 256);
+      hipLaunchKernelGGL(gather_matrices_kernel, dim3(chunks, (unsigned)m), dim3(256), 0, st,
+                         (const unsigned char*)a->LR, w + L.fin, fidx, mbytes);
+      LAUNCH_CHECK("gather");
+      hipLaunchKernelGGL(gather_i32_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, valid, fidx, m, fvalid);
+      LAUNCH_CHECK("gather_valid");
+      hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, fflags, (int64_t)m, 0);
+      LAUNCH_CHECK("fill");
+      shampoo_root_opts o64 = a->root;
+      o64.compute = SHAMPOO_F64;
+      r = inverse_root_impl(w + L.fin, w + L.fout, a->stats_dt, m, B, a->p, &o64, fvalid, nullptr, fflags,
+                            w + L.froot, L.froot_bytes, st, true);
+      if (r != SHAMPOO_OK) return r;
+      hipLaunchKernelGGL(scatter_matrices_kernel, dim3(chunks, (unsigned)m), dim3(256), 0, st,
+                         (const unsigned char*)(w + L.fout), (unsigned char*)a->roots, fidx, fflags, mbytes, fl);
+      LAUNCH_CHECK("scatter");
+      // the pageable index vector must outlive its copy
+      HIP_TRY(hipStreamSynchronize(st));
+    }
+  }
+  if (a->flags_dev) {
+    hipLaunchKernelGGL(merge_fallback_flags_kernel, dim3(g1), dim3(256), 0, st, fl, nf, a->flags_dev);
+    LAUNCH_CHECK("merge_flags");
+  }
   return SHAMPOO_OK;
 }
 
@@ -814,8 +911,7 @@ shampoo_status step_impl(const shampoo_step_args* a, hipStream_t st) {
   if (r != SHAMPOO_OK) return r;
   // 3. inverse roots of the 2 nblk factors
   if (a->recompute_roots) {
-    r = inverse_root_impl(a->LR, a->roots, a->stats_dt, 2 * nblk, B, a->p, &a->root, valid, nullptr, a->flags_dev,
-                          root, L.root_bytes, st);
+    r = step_roots(a, L, w, valid, st);
     if (r != SHAMPOO_OK) return r;
   }
   // 4. D = Lr G Rr

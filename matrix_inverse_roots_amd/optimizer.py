@@ -14,7 +14,7 @@ import math
 
 import numpy as np
 
-from . import (RootOpts, StepArgsC, GRAFTS, F32, F64, BF16, shampoo_plan_blocks, shampoo_step,
+from . import (RootOpts, StepArgsC, GRAFTS, FALLBACKS, F32, F64, BF16, shampoo_plan_blocks, shampoo_step,
                shampoo_step_workspace, table_to_device, _ptr)
 
 
@@ -68,6 +68,7 @@ class ShampooStack:
         a.g_dt = BF16 if self.grad_dtype == torch.bfloat16 else F32
         a.p = hp["p"]
         a.stats_dt = F64 if sdt == torch.float64 else F32
+        a.fallback = FALLBACKS[hp["fallback"]]
         a.LR = self.LR.data_ptr()
         a.roots = self.roots.data_ptr()
         a.beta2 = hp["beta2"]
@@ -127,14 +128,17 @@ class Shampoo:
     precondition_frequency: roots recomputed every that many steps (the
     statistics are updated every step).  stats_dtype: torch.float32 (the
     pages' float32 statistics) or torch.float64 (statistics, roots and
-    preconditioning products in float64).  Power-iteration scaling draws its
-    start vectors once per stack from ``pi_seed``.
+    preconditioning products in float64).  fallback: "none" | "keep" |
+    "f64", what a step does with a factor whose new root is not finite (flag
+    it; keep its previous root; recompute it with the float64 chain).
+    Power-iteration scaling draws its start vectors once per stack from
+    ``pi_seed``.
     """
 
     def __init__(self, params, block_size=1024, beta2=1.0, eps=1e-12, p=4, root=None, graft="sgd",
                  lr=0.1, momentum=0.9, beta1=0.9, graft_beta2=0.999, graft_eps=1e-8,
                  graft_blockwise=False, precondition_frequency=1, grad_dtype=None, stats_dtype=None,
-                 pi_seed=0):
+                 pi_seed=0, fallback="none"):
         import torch
         params = list(params)
         if not params:
@@ -152,7 +156,9 @@ class Shampoo:
                        graft_eps=float(graft_eps), graft_blockwise=bool(graft_blockwise),
                        grad_dtype=grad_dtype if grad_dtype is not None else torch.float32,
                        stats_dtype=stats_dtype if stats_dtype is not None else torch.float32,
-                       pi_seed=int(pi_seed))
+                       pi_seed=int(pi_seed), fallback=str(fallback))
+        if fallback not in FALLBACKS:
+            raise ValueError("fallback must be one of %s" % sorted(FALLBACKS))
         bs_of = block_size if callable(block_size) else (lambda m, n, b=int(block_size): b)
         groups = {}
         for i, v in enumerate(self.views):

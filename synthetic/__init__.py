@@ -139,3 +139,20 @@ def gaussian_grads(seed, shapes, steps, std, dtype=np.float32):
             gs.append(f32_to_bf16_bits(g) if dtype == "bf16" else g)
         out.append(gs)
     return out
+
+
+def gram_spectrum_grads(seed, n, b, lam_lo, lam_hi):
+    """n gradients G = Q diag(sqrt(lambda)) P^T (float32, b x b) with Q, P
+    Haar and lambda log-uniform in [lam_lo, lam_hi]: G G^T and G^T G then
+    have the eigenvalues lambda (up to float32 rounding of G).
+
+    Draw order: all Gaussian matrices for Q, then for P, then the eigenvalue
+    uniforms.
+    """
+    gen = rng(seed)
+    Q = haar_orthogonal(gen, n, b)
+    P = haar_orthogonal(gen, n, b)
+    u = gen.uniform(size=(n, b))
+    lam = 10.0 ** (np.log10(lam_lo) + u * (np.log10(lam_hi) - np.log10(lam_lo)))
+    G = (Q * np.sqrt(lam)[:, None, :]) @ np.swapaxes(P, 1, 2)
+    return G.astype(np.float32)
