@@ -146,6 +146,35 @@ def full_step_ms(mir, steps, warmup):
     return float(np.median(times)), nflag
 
 
+def bottleneck_step_ms(mir, steps, warmup, group):
+    """Full step on the bottleneck-50 set (53 matrices, 25.5 M parameters,
+    block 1024 if max(m, n) >= 2048 else 256, float32 gradients N(0, 1e-2),
+    beta2 0.999, eps 1e-12, Chebyshev degree 16, momentum grafting), with the
+    roots grouped by factor side or computed at the block size."""
+    import numpy as np
+    import torch
+    import synthetic
+    shapes = synthetic.bottleneck50_shapes()
+    W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    opt = mir.Shampoo(W, block_size=lambda m, n: 1024 if max(m, n) >= 2048 else 256, beta2=0.999, eps=1e-12,
+                      root=mir.RootOpts(method="chebyshev", cheb_degree=16), graft="momentum", lr=0.1,
+                      momentum=0.9, group_factors=group)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    grads = [[torch.randn(s, generator=gen, device="cuda") * 0.1 for s in shapes] for _ in range(2)]
+    for i in range(warmup):
+        opt.step(grads[i % 2])
+    torch.cuda.synchronize()
+    times = []
+    for i in range(steps):
+        t0 = time.perf_counter()
+        opt.step(grads[i % 2])
+        torch.cuda.synchronize()
+        times.append((time.perf_counter() - t0) * 1e3)
+    nflag = sum(int((f != 0).sum().item()) for f in opt.flags())
+    return float(np.median(times)), nflag
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,8 +183,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-full-step", action="store_true")
-    ap.add_argument("--only", choices=["roots", "copy", "step"], default=None,
-                    help="profiling runs: only the float32 solve, only a 1 GiB copy, or only the full step")
+    ap.add_argument("--only", choices=["roots", "copy", "step", "step5"], default=None,
+                    help="profiling runs: only the float32 solve, only a 1 GiB copy, only the decoder-set step or only the bottleneck-50 step")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -180,6 +209,10 @@ def main():
     if args.only == "step":
         ms, nf = full_step_ms(mir, args.steps, args.warmup)
         log(f"full step {ms:.2f} ms, flags {nf}")
+        return
+    if args.only == "step5":
+        ms, nf = bottleneck_step_ms(mir, args.steps, args.warmup, True)
+        log(f"bottleneck-50 step {ms:.2f} ms, flags {nf}")
         return
 
     A64 = make_stack(np.float64)
@@ -245,6 +278,13 @@ def main():
         result["full_step"] = {"workload": "decoder_12x(1024x3072,1024x1024,1024x4096,4096x1024)_bf16_adam_cn34_f32",
                                "ms": round(ms, 2), "flagged_factors": nf}
         log(f"full step: {ms:.1f} ms")
+        msg, nfg = bottleneck_step_ms(mir, max(5, args.steps), 2, True)
+        msu, nfu = bottleneck_step_ms(mir, max(5, args.steps), 2, False)
+        result["full_step_bottleneck50"] = {
+            "workload": "bottleneck50_53_matrices_b256_1024_chebyshev16_f32_momentum",
+            "ms_grouped_by_factor_side": round(msg, 2), "ms_padded_to_block": round(msu, 2),
+            "flagged_factors": nfg + nfu}
+        log(f"bottleneck-50 step: {msg:.1f} ms grouped, {msu:.1f} ms padded")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp[:256].cpu().numpy())
         log(f"cpu baseline: {result['cpu_baseline']}")

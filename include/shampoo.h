@@ -194,6 +194,12 @@ typedef struct shampoo_step_args {
   float* dstack;                    /* device f32 [nblk, B, B] or NULL: receives D (ungrafted) */
   void* ws;
   size_t ws_bytes;
+  const shampoo_block* table_host;  /* host copy of table_dev, or NULL.  When given, each factor's
+                                       root is computed in a stack of side roundup64(valid size)
+                                       (L: rows, R: cols) rather than B, grouped by that side, and
+                                       written back zero-padded to B: the padded work of narrow
+                                       blocks disappears ([DASH] "4. Blocking Strategy" groups
+                                       blocks by shape).  The workspace then depends on it. */
 } shampoo_step_args;
 
 /* Version string of the library. */

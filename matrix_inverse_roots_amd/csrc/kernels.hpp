@@ -496,6 +496,50 @@ __global__ __launch_bounds__(256) void scatter_matrices_kernel(const unsigned ch
   if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(fl_dst + idx[i], SHAMPOO_FLAG_RECOMPUTED_F64);
 }
 
+// Factor-side groups.  gather_sub: dst[i] (s x s) = leading s x s block of
+// the B x B matrix src[idx[i]]; scatter_sub: the B x B matrix dst[idx[i]] =
+// src[i] (s x s) zero-padded to B, skipped where keep is set and flags[i]
+// shows NONFINITE or ZERO_SCALE.  E: raw element type (bit copies); s and B
+// multiples of 64; grid (chunks, m).
+template <typename E>
+__global__ __launch_bounds__(256) void gather_sub_kernel(const E* __restrict__ src, E* __restrict__ dst,
+                                                         const int32_t* __restrict__ idx, int B, int s) {
+  constexpr int V = 16 / sizeof(E);
+  const int64_t i = blockIdx.y;
+  const E* a = src + (int64_t)idx[i] * B * B;
+  E* d = dst + i * (int64_t)s * s;
+  const int cpr = s / V;
+  for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < s * cpr; k += gridDim.x * blockDim.x) {
+    const int r = k / cpr, c = (k - r * cpr) * V;
+    *reinterpret_cast<uint4*>(d + (int64_t)r * s + c) = *reinterpret_cast<const uint4*>(a + (int64_t)r * B + c);
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void scatter_sub_kernel(const E* __restrict__ src, E* __restrict__ dst,
+                                                          const int32_t* __restrict__ idx, int B, int s,
+                                                          const int32_t* __restrict__ flags, int keep) {
+  constexpr int V = 16 / sizeof(E);
+  const int64_t i = blockIdx.y;
+  if (keep && (flags[i] & (SHAMPOO_FLAG_NONFINITE | SHAMPOO_FLAG_ZERO_SCALE))) return;  // uniform
+  const E* a = src + i * (int64_t)s * s;
+  E* d = dst + (int64_t)idx[i] * B * B;
+  const int cpr = B / V;
+  for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < B * cpr; k += gridDim.x * blockDim.x) {
+    const int r = k / cpr, c = (k - r * cpr) * V;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < s && c < s) v = *reinterpret_cast<const uint4*>(a + (int64_t)r * s + c);
+    *reinterpret_cast<uint4*>(d + (int64_t)r * B + c) = v;
+  }
+}
+
+// dst[idx[i]] |= src[i] (distinct indices)
+__global__ void or_flags_kernel(const int32_t* __restrict__ src, const int32_t* __restrict__ idx, int m,
+                                int32_t* __restrict__ dst) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < m) dst[idx[i]] |= src[i];
+}
+
 // Step flags after the fallback: a factor flagged NONFINITE or ZERO_SCALE
 // that was not recomputed kept its previous root; the result is OR-ed into
 // the caller's flags.

@@ -763,6 +763,13 @@ struct StepLayout {
   size_t fl, fidx, fvalid, fflags, fin, fout, froot;
   size_t froot_bytes;
   bool redo64;
+  // factor-side groups (table_host given and some factor narrower than B):
+  // group g roots gcount[g] factors, listed in gorder from gstart[g], in a
+  // stack of side gside[g]; their chains use the root region
+  std::vector<int> gside;
+  std::vector<int64_t> gstart, gcount;
+  std::vector<int32_t> gorder;
+  size_t gidx, gvalid, gflags, gin, gout;
 };
 
 shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
@@ -810,8 +817,95 @@ shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
     L->fout = off; off += align_up((size_t)nf * mb);
     L->froot = off; off += L->froot_bytes;
   }
+  L->gidx = L->gvalid = L->gflags = L->gin = L->gout = 0;
+  L->gside.clear();
+  L->gstart.clear();
+  L->gcount.clear();
+  L->gorder.clear();
+  if (a->table_host) {
+    // factor f < nblk is L of block f (valid rows), f >= nblk is R (valid cols)
+    std::vector<int> side((size_t)nf);
+    bool narrow = false;
+    for (int64_t b = 0; b < a->nblk; ++b) {
+      const shampoo_block& t = a->table_host[b];
+      const int vr = std::min(std::max(t.rows, 1), a->B), vc = std::min(std::max(t.cols, 1), a->B);
+      side[(size_t)b] = (vr + 63) / 64 * 64;
+      side[(size_t)(a->nblk + b)] = (vc + 63) / 64 * 64;
+      narrow = narrow || side[(size_t)b] < a->B || side[(size_t)(a->nblk + b)] < a->B;
+    }
+    if (narrow) {
+      size_t need_io = 0, need_root = 0;
+      for (int sd = 64; sd <= a->B; sd += 64) {
+        const int64_t start = (int64_t)L->gorder.size();
+        for (int64_t f = 0; f < nf; ++f)
+          if (side[(size_t)f] == sd) L->gorder.push_back((int32_t)f);
+        const int64_t cnt = (int64_t)L->gorder.size() - start;
+        if (cnt == 0) continue;
+        L->gside.push_back(sd);
+        L->gstart.push_back(start);
+        L->gcount.push_back(cnt);
+        need_io = std::max(need_io, align_up((size_t)cnt * sd * sd * dtype_size(a->stats_dt)));
+        need_root = std::max(need_root, root_ws_bytes(cnt, sd, P, a->root.compute));
+      }
+      if (need_root > L->root_bytes) return fail(SHAMPOO_E_INVALID, "internal: group workspace");
+      L->gidx = off; off += align_up((size_t)nf * 4);
+      L->gvalid = off; off += align_up((size_t)nf * 4);
+      L->gflags = off; off += align_up((size_t)nf * 4);
+      L->gin = off; off += need_io;
+      L->gout = off; off += need_io;
+    }
+  }
   L->total = off;
   return SHAMPOO_OK;
+}
+
+// Roots of the factors grouped by side (StepLayout).  Flags of each factor go
+// to fl[f] (OR-ed); with keep_flagged a flagged factor keeps its previous root.
+template <typename E>
+shampoo_status step_roots_grouped(const shampoo_step_args* a, const StepLayout& L, unsigned char* w,
+                                  const int32_t* valid, int32_t* fl, bool keep_flagged, hipStream_t st) {
+  const int B = a->B;
+  int32_t* gidx = (int32_t*)(w + L.gidx);
+  int32_t* gvalid = (int32_t*)(w + L.gvalid);
+  int32_t* gflags = (int32_t*)(w + L.gflags);
+  const int64_t nf = (int64_t)L.gorder.size();
+  HIP_TRY(hipMemcpyAsync(gidx, L.gorder.data(), (size_t)nf * 4, hipMemcpyHostToDevice, st));
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, st, gflags, nf, 0);
+  LAUNCH_CHECK("fill");
+  for (size_t g = 0; g < L.gside.size(); ++g) {
+    const int sd = L.gside[g];
+    const int m = (int)L.gcount[g];
+    int32_t* idx = gidx + L.gstart[g];
+    int32_t* gv = gvalid + L.gstart[g];
+    int32_t* gf = gflags + L.gstart[g];
+    hipLaunchKernelGGL(gather_i32_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, valid, idx, m, gv);
+    LAUNCH_CHECK("gather_valid");
+    const unsigned gchunks = (unsigned)std::min<int64_t>(64, ((int64_t)sd * sd / (16 / sizeof(E)) + 255) / 256);
+    hipLaunchKernelGGL((gather_sub_kernel<E>), dim3(gchunks, (unsigned)m), dim3(256), 0, st, (const E*)a->LR,
+                       (E*)(w + L.gin), idx, B, sd);
+    LAUNCH_CHECK("gather_sub");
+    shampoo_status r = inverse_root_impl(w + L.gin, w + L.gout, a->stats_dt, m, sd, a->p, &a->root, gv, nullptr, gf,
+                                         w + L.root, L.root_bytes, st, keep_flagged);
+    if (r != SHAMPOO_OK) return r;
+    const unsigned schunks = (unsigned)std::min<int64_t>(64, ((int64_t)B * B / (16 / sizeof(E)) + 255) / 256);
+    hipLaunchKernelGGL((scatter_sub_kernel<E>), dim3(schunks, (unsigned)m), dim3(256), 0, st, (const E*)(w + L.gout),
+                       (E*)a->roots, idx, B, sd, gf, keep_flagged ? 1 : 0);
+    LAUNCH_CHECK("scatter_sub");
+    if (fl) {
+      hipLaunchKernelGGL(or_flags_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, gf, idx, m, fl);
+      LAUNCH_CHECK("or_flags");
+    }
+  }
+  return SHAMPOO_OK;
+}
+
+shampoo_status roots_of_factors(const shampoo_step_args* a, const StepLayout& L, unsigned char* w,
+                                const int32_t* valid, int32_t* fl, bool keep_flagged, hipStream_t st) {
+  if (!L.gside.empty())
+    return a->stats_dt == SHAMPOO_F64 ? step_roots_grouped<uint64_t>(a, L, w, valid, fl, keep_flagged, st)
+                                      : step_roots_grouped<uint32_t>(a, L, w, valid, fl, keep_flagged, st);
+  return inverse_root_impl(a->LR, a->roots, a->stats_dt, 2 * a->nblk, a->B, a->p, &a->root, valid, nullptr, fl,
+                           w + L.root, L.root_bytes, st, keep_flagged);
 }
 
 // Inverse roots of the step's 2 nblk factors with the fallback of
@@ -821,15 +915,12 @@ shampoo_status step_roots(const shampoo_step_args* a, const StepLayout& L, unsig
   const int64_t nf = 2 * a->nblk;
   const int B = a->B;
   unsigned char* root = w + L.root;
-  if (a->fallback == SHAMPOO_FALLBACK_NONE)
-    return inverse_root_impl(a->LR, a->roots, a->stats_dt, nf, B, a->p, &a->root, valid, nullptr, a->flags_dev, root,
-                             L.root_bytes, st);
+  if (a->fallback == SHAMPOO_FALLBACK_NONE) return roots_of_factors(a, L, w, valid, a->flags_dev, false, st);
   int32_t* fl = (int32_t*)(w + L.fl);
   const unsigned g1 = (unsigned)((nf + 255) / 256);
   hipLaunchKernelGGL(fill_i32_kernel, dim3(g1), dim3(256), 0, st, fl, nf, 0);
   LAUNCH_CHECK("fill");
-  shampoo_status r = inverse_root_impl(a->LR, a->roots, a->stats_dt, nf, B, a->p, &a->root, valid, nullptr, fl, root,
-                                       L.root_bytes, st, true);
+  shampoo_status r = roots_of_factors(a, L, w, valid, fl, true, st);
   if (r != SHAMPOO_OK) return r;
   if (L.redo64) {
     // count the flagged factors on the host, then recompute them in float64

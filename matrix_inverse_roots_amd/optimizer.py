@@ -89,6 +89,9 @@ class ShampooStack:
         a.graft_eps = hp["graft_eps"]
         a.flags_dev = self.flags.data_ptr()
         a.dstack = None
+        # host copy of the table: roots grouped by each factor's own side
+        self.table_host = np.ascontiguousarray(self.table, dtype=np.int32)
+        a.table_host = self.table_host.ctypes.data if hp["group_factors"] and self.nblk else None
         nb = shampoo_step_workspace(a)
         self.ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=device)
         a.ws = self.ws.data_ptr()
@@ -131,6 +134,8 @@ class Shampoo:
     preconditioning products in float64).  fallback: "none" | "keep" |
     "f64", what a step does with a factor whose new root is not finite (flag
     it; keep its previous root; recompute it with the float64 chain).
+    group_factors: root each factor in a stack of its own side (rounded up
+    to 64) rather than the block size, grouped by side.
     Power-iteration scaling draws its start vectors once per stack from
     ``pi_seed``.
     """
@@ -138,7 +143,7 @@ class Shampoo:
     def __init__(self, params, block_size=1024, beta2=1.0, eps=1e-12, p=4, root=None, graft="sgd",
                  lr=0.1, momentum=0.9, beta1=0.9, graft_beta2=0.999, graft_eps=1e-8,
                  graft_blockwise=False, precondition_frequency=1, grad_dtype=None, stats_dtype=None,
-                 pi_seed=0, fallback="none"):
+                 pi_seed=0, fallback="none", group_factors=True):
         import torch
         params = list(params)
         if not params:
@@ -156,7 +161,7 @@ class Shampoo:
                        graft_eps=float(graft_eps), graft_blockwise=bool(graft_blockwise),
                        grad_dtype=grad_dtype if grad_dtype is not None else torch.float32,
                        stats_dtype=stats_dtype if stats_dtype is not None else torch.float32,
-                       pi_seed=int(pi_seed), fallback=str(fallback))
+                       pi_seed=int(pi_seed), fallback=str(fallback), group_factors=bool(group_factors))
         if fallback not in FALLBACKS:
             raise ValueError("fallback must be one of %s" % sorted(FALLBACKS))
         bs_of = block_size if callable(block_size) else (lambda m, n, b=int(block_size): b)
