@@ -241,6 +241,14 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t w, int64_t total) {
   return xcd * q + (xcd < r ? xcd : r) + local;
 }
 
+// The fused epilogue's affine maps in double, written as explicit FMAs so
+// that every product kernel rounds them identically:
+//   C  = alpha acc + beta D + gamma [diagonal],   C2 = alpha2 C + gamma2 [diagonal].
+__device__ __forceinline__ double epi_c(double alpha, double acc, double beta, double d, double diag) {
+  return __builtin_fma(alpha, acc, __builtin_fma(beta, d, diag));
+}
+__device__ __forceinline__ double epi_c2(double alpha2, double c, double diag2) { return __builtin_fma(alpha2, c, diag2); }
+
 template <typename TC> __device__ __forceinline__ void put(TC* p, double v);
 template <> __device__ __forceinline__ void put<float>(float* p, double v) { *p = (float)v; }
 template <> __device__ __forceinline__ void put<double>(double* p, double v) { *p = v; }
@@ -423,15 +431,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          y[q] = g.alpha * (double)x[q] + g.beta * dv[q];
-          if (R == otj * T + c4 + q) y[q] += g.gamma;
+          y[q] = epi_c(g.alpha, (double)x[q], D ? g.beta : 0.0, dv[q], R == otj * T + c4 + q ? g.gamma : 0.0);
         }
         if constexpr (sizeof(TC) == 4) {
           *reinterpret_cast<floatx4*>(C + base) = floatx4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]};
           if (C2) {
             float z[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) z[q] = (float)(g.alpha2 * y[q] + (R == otj * T + c4 + q ? g.gamma2 : 0.0));
+            for (int q = 0; q < 4; ++q) z[q] = (float)epi_c2(g.alpha2, y[q], R == otj * T + c4 + q ? g.gamma2 : 0.0);
             *reinterpret_cast<floatx4*>(C2 + base) = floatx4{z[0], z[1], z[2], z[3]};
           }
         } else {
@@ -440,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
           if (C2) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              put<TC>(C2 + base + q, g.alpha2 * y[q] + (R == otj * T + c4 + q ? g.gamma2 : 0.0));
+              put<TC>(C2 + base + q, epi_c2(g.alpha2, y[q], R == otj * T + c4 + q ? g.gamma2 : 0.0));
           }
         }
       }
@@ -466,9 +473,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
         const int col = wn * WT + j * 16 + i16;
         if (diag && row > col) continue;
         const int R = ti * T + row, Cc = tj * T + col;
-        double x = g.alpha * (double)acc[i][j][v];
-        if (D) x += g.beta * (double)D[(int64_t)R * n + Cc];
-        if (R == Cc) x += g.gamma;
+        const double x = epi_c(g.alpha, (double)acc[i][j][v], D ? g.beta : 0.0,
+                               D ? (double)D[(int64_t)R * n + Cc] : 0.0, R == Cc ? g.gamma : 0.0);
         if (g.transC) {
           put<TC>(C + (int64_t)Cc * n + R, x);
           continue;
@@ -476,7 +482,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
         put<TC>(C + (int64_t)R * n + Cc, x);
         double x2 = 0.0;
         if (C2) {
-          x2 = g.alpha2 * x + (R == Cc ? g.gamma2 : 0.0);
+          x2 = epi_c2(g.alpha2, x, R == Cc ? g.gamma2 : 0.0);
           put<TC>(C2 + (int64_t)R * n + Cc, x2);
         }
         if (mirror && R != Cc) {
@@ -655,12 +661,12 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_nn256_kernel(GemmArgs g) {
         }
         double y[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) y[j] = g.alpha * (double)acc[i][j][v] + (R == c0 + j ? g.gamma : 0.0);
+        for (int j = 0; j < 4; ++j) y[j] = epi_c(g.alpha, (double)acc[i][j][v], 0.0, 0.0, R == c0 + j ? g.gamma : 0.0);
         *reinterpret_cast<floatx4*>(C + at) = floatx4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]};
         if (C2) {
           float z[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) z[j] = (float)(g.alpha2 * y[j] + (R == c0 + j ? g.gamma2 : 0.0));
+          for (int j = 0; j < 4; ++j) z[j] = (float)epi_c2(g.alpha2, y[j], R == c0 + j ? g.gamma2 : 0.0);
           *reinterpret_cast<floatx4*>(C2 + at) = floatx4{z[0], z[1], z[2], z[3]};
         }
       }
@@ -707,24 +713,46 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_nn256_kernel(GemmArgs g) {
 constexpr int P128_T = 128;
 constexpr int P128_TILE_BYTES = P128_T * 128;  // 16 KB per operand and stage
 
-template <typename E> struct P128;
+// Operand type EI -> 16-byte fragment, accumulator, output type and the
+// k-steps (MFMAs) one fragment feeds.  float32/float64 fragments hold 4/2
+// consecutive k, one per 16x16x4 MFMA; a bfloat16 fragment holds the 8 k a
+// lane supplies to one 16x16x32 MFMA (NT only).
+template <typename EI> struct P128;
 template <> struct P128<float> {
   using acc_t = floatx4;
   using frag_t = floatx4;
-  static constexpr int VE = 4;
-  static __device__ __forceinline__ acc_t mma(float a, float b, acc_t c) {
+  using out_t = float;
+  static constexpr int VE = 4, KS = 4;
+  static __device__ __forceinline__ acc_t mma_s(float a, float b, acc_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ acc_t mma(const frag_t& a, const frag_t& b, int u, acc_t c) {
+    return mma_s(a[u], b[u], c);
   }
   static __device__ __forceinline__ int arow(int r) { return r; }
 };
 template <> struct P128<double> {
   using acc_t = doublex4;
   using frag_t = doublex2;
-  static constexpr int VE = 2;
-  static __device__ __forceinline__ acc_t mma(double a, double b, acc_t c) {
+  using out_t = double;
+  static constexpr int VE = 2, KS = 2;
+  static __device__ __forceinline__ acc_t mma_s(double a, double b, acc_t c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ acc_t mma(const frag_t& a, const frag_t& b, int u, acc_t c) {
+    return mma_s(a[u], b[u], c);
+  }
   static __device__ __forceinline__ int arow(int r) { return 4 * (r & 3) + (r >> 2); }
+};
+template <> struct P128<__bf16> {
+  using acc_t = floatx4;
+  using frag_t = bf16x8;
+  using out_t = float;
+  static constexpr int VE = 8, KS = 1;
+  static __device__ __forceinline__ acc_t mma(const frag_t& a, const frag_t& b, int, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int arow(int r) { return r; }
 };
 
 // LDS row -> B-tile row of an NT operand (the inverse of
@@ -757,12 +785,13 @@ template <typename E, int RUN> __device__ __forceinline__ void load_run(const E*
 template <typename E, bool NN>
 __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
   using P = P128<E>;
+  using EO = typename P::out_t;  // C, D, C2
   using acc_t = typename P::acc_t;
   using frag_t = typename P::frag_t;
   constexpr int T = P128_T, VE = P::VE, BK = 128 / (int)sizeof(E), TB = P128_TILE_BYTES, SB = 2 * TB;
   constexpr int RB = T * (int)sizeof(E);  // bytes per k-row of an NN B tile
   constexpr int RUN = NN ? VE : 4;        // consecutive output columns per lane and run
-  constexpr bool PREFETCH_D = sizeof(E) == 4;
+  constexpr bool PREFETCH_D = sizeof(EO) == 4;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * SB];
   const int per = gridDim.x >> 3;
   const int x = blockIdx.x & 7, l = blockIdx.x >> 3;
@@ -847,16 +876,16 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
-  const E* Dg = reinterpret_cast<const E*>(g.D);
-  E dpre[PREFETCH_D ? 4 : 1][4][4];  // D of the current tile [i][v][jb] (float32)
+  const EO* Dg = reinterpret_cast<const EO*>(g.D);
+  EO dpre[PREFETCH_D ? 4 : 1][4][4];  // D of the current tile [i][v][jb] (float32)
   const bool plain = g.alpha == 1.0 && g.gamma == 0.0 && Dg == nullptr && g.C2 == nullptr;
   const int total_steps = ntile * nst;
-  auto dload = [&](int i, E (*d)[4]) {  // D at the lane's outputs of row block i
+  auto dload = [&](int i, EO (*d)[4]) {  // D at the lane's outputs of row block i
 #pragma unroll
     for (int v = 0; v < 4; ++v)
 #pragma unroll
       for (int h = 0; h < 4 / RUN; ++h)
-        load_run<E, RUN>(Dg + cmo + (int64_t)(cti * T + wm * 64 + i * 16 + 4 * grp + v) * n + ctj * T + wn * 64 +
+        load_run<EO, RUN>(Dg + cmo + (int64_t)(cti * T + wm * 64 + i * 16 + 4 * grp + v) * n + ctj * T + wn * 64 +
                              colmap(h * RUN),
                          &d[v][h * RUN]);
   };
@@ -900,7 +929,7 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              acc[i][j] = P::mma(a[i][u], b[u * (4 / VE) + j / VE][j % VE], acc[i][j]);
+              acc[i][j] = P::mma_s(a[i][u], b[u * (4 / VE) + j / VE][j % VE], acc[i][j]);
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -908,11 +937,11 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
           b[j] = *reinterpret_cast<const frag_t*>(sb + rho * 128 + 16 * (kc ^ nn256_swz(rho)));
         }
 #pragma unroll
-        for (int u = 0; u < VE; ++u)
+        for (int u = 0; u < P::KS; ++u)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = P::mma(a[i][u], b[j][u], acc[i][j]);
+            for (int j = 0; j < 4; ++j) acc[i][j] = P::mma(a[i], b[j], u, acc[i][j]);
       }
     }
     if (more) advance();
@@ -920,15 +949,15 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
     barrier_no_fence();
     if (++ck < nst) continue;
     ck = 0;
-    E* C = reinterpret_cast<E*>(g.C) + cmo;
-    E* C2 = g.C2 ? reinterpret_cast<E*>(g.C2) + cmo : nullptr;
+    EO* C = reinterpret_cast<EO*>(g.C) + cmo;
+    EO* C2 = g.C2 ? reinterpret_cast<EO*>(g.C2) + cmo : nullptr;
     const int R0 = cti * T + wm * 64, C0 = ctj * T + wn * 64;
     const bool diag = g.sym && cti == ctj;
     const bool mirror = (g.sym && !diag) || g.transC;
     const bool direct = !g.transC;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      E d[4][4];  // [v][jb]
+      EO d[4][4];  // [v][jb]
       if constexpr (PREFETCH_D) {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
@@ -940,14 +969,13 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
       // output (v, jb) of row block i: C value, and the second output from it
       auto val = [&](int v, int j, double& t) {
         const int R = R0 + i * 16 + 4 * grp + v, Cc = C0 + colmap(j);
-        t = g.alpha * (double)acc[i][j][v];
-        if (Dg) t += g.beta * (double)d[v][j];
-        if (R == Cc) t += g.gamma;
-        return plain ? acc[i][j][v] : (E)t;
+        t = epi_c(g.alpha, (double)acc[i][j][v], Dg ? g.beta : 0.0, Dg ? (double)d[v][j] : 0.0,
+                  R == Cc ? g.gamma : 0.0);
+        return plain ? (EO)acc[i][j][v] : (EO)t;
       };
       auto val2 = [&](int v, int j, double t) {
         const int R = R0 + i * 16 + 4 * grp + v, Cc = C0 + colmap(j);
-        return (E)(g.alpha2 * t + (R == Cc ? g.gamma2 : 0.0));
+        return (EO)epi_c2(g.alpha2, t, R == Cc ? g.gamma2 : 0.0);
       };
       if (diag) {
         // diagonal tile: the upper element (R <= Cc) is written in place and mirrored
@@ -958,11 +986,11 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
             const int R = R0 + i * 16 + 4 * grp + v, Cc = C0 + colmap(j);
             if (R > Cc) continue;
             double t;
-            const E y = val(v, j, t);
+            const EO y = val(v, j, t);
             C[(int64_t)R * n + Cc] = y;
             C[(int64_t)Cc * n + R] = y;
             if (C2) {
-              const E z = val2(v, j, t);
+              const EO z = val2(v, j, t);
               C2[(int64_t)R * n + Cc] = z;
               C2[(int64_t)Cc * n + R] = z;
             }
@@ -975,15 +1003,15 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
 #pragma unroll
           for (int h = 0; h < 4 / RUN; ++h) {
             const int64_t at = (int64_t)(R0 + i * 16 + 4 * grp + v) * n + C0 + colmap(h * RUN);
-            E y[RUN], z[RUN];
+            EO y[RUN], z[RUN];
             double t[RUN];
 #pragma unroll
             for (int e = 0; e < RUN; ++e) y[e] = val(v, h * RUN + e, t[e]);
-            store_run<E, RUN>(C + at, y);
+            store_run<EO, RUN>(C + at, y);
             if (C2) {
 #pragma unroll
               for (int e = 0; e < RUN; ++e) z[e] = val2(v, h * RUN + e, t[e]);
-              store_run<E, RUN>(C2 + at, z);
+              store_run<EO, RUN>(C2 + at, z);
             }
           }
       }
@@ -991,15 +1019,15 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int64_t at = (int64_t)(C0 + colmap(j)) * n + R0 + i * 16 + 4 * grp;
-          E y[4], z[4];
+          EO y[4], z[4];
           double t[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) y[v] = val(v, j, t[v]);
-          store_run<E, 4>(C + at, y);
+          store_run<EO, 4>(C + at, y);
           if (C2) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) z[v] = val2(v, j, t[v]);
-            store_run<E, 4>(C2 + at, z);
+            store_run<EO, 4>(C2 + at, z);
           }
         }
       }

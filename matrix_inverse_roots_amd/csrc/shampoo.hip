@@ -176,6 +176,18 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
       return hipGetLastError();
     }
   }
+  // bfloat16 operands into float32 (statistics of bf16 gradients), NT
+  constexpr bool bf16_in = MM == Mma::BF16 && std::is_same<TA, __bf16>::value && std::is_same<TB, __bf16>::value &&
+                           std::is_same<TC, float>::value;
+  if constexpr (bf16_in) {
+    if (T == P128_T && !c.nn) {
+      int cus = 0;
+      HIP_TRY_ERR(cu_count(&cus));
+      const int64_t wgs = std::min<int64_t>(((g.total + 7) / 8) * 8, std::max(8, (cus / 8) * 8) * 2);
+      hipLaunchKernelGGL((gemm_p128_kernel<__bf16, false>), dim3((unsigned)wgs), dim3(256), 0, st, g);
+      return hipGetLastError();
+    }
+  }
   if constexpr (std::is_same<TB, float>::value || std::is_same<TB, double>::value) {
     if (c.nn) {
       if (T == 128)

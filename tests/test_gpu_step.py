@@ -110,6 +110,38 @@ def test_stats_ema_gaussian(mir):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_stats_kernels_bit_identical(mir, dt):
+    """Gaussian gradients, EMA statistics: a 192-side stack runs on the
+    64-tile kernel, the same blocks zero-padded to 256 on the persistent
+    128-tile kernel (bf16 operands into float32 for dt = bf16); the k order
+    is the same and the padding adds exact zeros, so the valid regions agree
+    bit for bit, and the padding stays zero."""
+    import torch
+    nblk, v, b2 = 3, 192, 0.999
+    gen = np.random.default_rng(7)
+    outs = []
+    for B in (v, 256):
+        LR = torch.zeros((2 * nblk, B, B), dtype=torch.float32, device="cuda")
+        g2 = np.random.default_rng(7)
+        for _ in range(2):
+            st = np.zeros((nblk, B, B), dtype=np.float32)
+            st[:, :v, :v] = (g2.standard_normal((nblk, v, v)) * 0.02).astype(np.float32)
+            stt = np.ascontiguousarray(np.swapaxes(st, 1, 2))
+            if dt == "bf16":
+                gs = bf16_tensor(synthetic.f32_to_bf16_bits(st))
+                gts = bf16_tensor(synthetic.f32_to_bf16_bits(stt))
+            else:
+                gs, gts = to_dev(st), to_dev(stt)
+            mir.shampoo_update_stats(gs, gts, LR, b2)
+        torch.cuda.synchronize()
+        outs.append(LR.cpu().numpy())
+    small, big = outs
+    np.testing.assert_array_equal(small, big[:, :v, :v])
+    assert not big[:, v:, :].any() and not big[:, :, v:].any()
+    del gen
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_precondition_vs_oracle(mir, dt):
     import torch
     B, nblk = 256, 3
