@@ -61,7 +61,10 @@ __global__ __launch_bounds__(256) void pack_kernel(const Desc* __restrict__ desc
                                                    const shampoo_block* __restrict__ table, int B,
                                                    int tiles_per_side, E* __restrict__ stack,
                                                    E* __restrict__ stack_t) {
-  __shared__ E tile[64][65];
+  constexpr int VE = 16 / (int)sizeof(E);  // elements per 16-byte access
+  constexpr int CPR = 64 / VE;             // 16-byte chunks per tile row
+  constexpr int RPP = 256 / CPR;           // tile rows per pass
+  __shared__ __attribute__((aligned(16))) E tile[64][64 + VE];
   const int64_t b = blockIdx.y;
   const int tt = blockIdx.x;
   const int tr = tt / tiles_per_side, tc = tt - tr * tiles_per_side;
@@ -69,22 +72,53 @@ __global__ __launch_bounds__(256) void pack_kernel(const Desc* __restrict__ desc
   if (blk.param < 0 || blk.param >= nparams) return;  // uniform per workgroup
   const Desc m = descs[blk.param];
   const E* src = reinterpret_cast<const E*>(desc_data(m));
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const int64_t BB = (int64_t)B * B;
-#pragma unroll 4
-  for (int rr = ty; rr < 64; rr += 4) {
-    const int r = tr * 64 + rr, c = tc * 64 + tx;
-    E v = E(0);
-    if (r < blk.rows && c < blk.cols) v = src[(int64_t)(blk.row0 + r) * m.ld + blk.col0 + c];
-    if (r < B && c < B) stack[b * BB + (int64_t)r * B + c] = v;
-    tile[rr][tx] = v;
+  if (B % 64 != 0 || ((reinterpret_cast<uintptr_t>(stack) | reinterpret_cast<uintptr_t>(stack_t)) & 15) != 0) {
+    // general sides: element-wise copy with bounds checks (uniform branch)
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int rr = ty; rr < 64; rr += 4) {
+      const int r = tr * 64 + rr, c = tc * 64 + tx;
+      E v = E(0);
+      if (r < blk.rows && c < blk.cols) v = src[(int64_t)(blk.row0 + r) * m.ld + blk.col0 + c];
+      if (r < B && c < B) stack[b * BB + (int64_t)r * B + c] = v;
+      tile[rr][tx] = v;
+    }
+    if (!stack_t) return;
+    __syncthreads();
+    for (int cc2 = ty; cc2 < 64; cc2 += 4) {
+      const int c = tc * 64 + cc2, r = tr * 64 + tx;
+      if (r < B && c < B) stack_t[b * BB + (int64_t)c * B + r] = tile[tx][cc2];
+    }
+    return;
+  }
+  // 16-byte source access needs 16-byte aligned rows (uniform per workgroup)
+  const bool vec = ((reinterpret_cast<uintptr_t>(src) | ((uintptr_t)m.ld * sizeof(E)) |
+                     ((uintptr_t)blk.col0 * sizeof(E))) & 15) == 0;
+  const int cc = (int)threadIdx.x % CPR, rq = (int)threadIdx.x / CPR;
+#pragma unroll
+  for (int pass = 0; pass < 64 / RPP; ++pass) {
+    const int rr = pass * RPP + rq, r = tr * 64 + rr, c = tc * 64 + cc * VE;
+    E v[VE];
+    const E* sp = src + (int64_t)(blk.row0 + r) * m.ld + blk.col0 + c;
+    if (vec && r < blk.rows && c + VE <= blk.cols) {
+      *reinterpret_cast<uint4*>(v) = *reinterpret_cast<const uint4*>(sp);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) v[e] = (r < blk.rows && c + e < blk.cols) ? sp[e] : E(0);
+    }
+    *reinterpret_cast<uint4*>(stack + b * BB + (int64_t)r * B + c) = *reinterpret_cast<const uint4*>(v);
+    *reinterpret_cast<uint4*>(&tile[rr][cc * VE]) = *reinterpret_cast<const uint4*>(v);
   }
   if (!stack_t) return;
   __syncthreads();
-#pragma unroll 4
-  for (int cc = ty; cc < 64; cc += 4) {
-    const int c = tc * 64 + cc, r = tr * 64 + tx;
-    if (r < B && c < B) stack_t[b * BB + (int64_t)c * B + r] = tile[tx][cc];
+  // transposed tile: output row (column c of the block), VE consecutive r
+#pragma unroll
+  for (int pass = 0; pass < 64 / RPP; ++pass) {
+    const int ccol = pass * RPP + rq, c = tc * 64 + ccol, r0 = tr * 64 + cc * VE;
+    E v[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) v[e] = tile[cc * VE + e][ccol];
+    *reinterpret_cast<uint4*>(stack_t + b * BB + (int64_t)c * B + r0) = *reinterpret_cast<const uint4*>(v);
   }
 }
 
@@ -144,7 +178,7 @@ template <> struct Quad<double> {
 // frob_partial: grid (P, n).  The valid region is read as rows of ceil(v/4)
 // four-element chunks; part p of matrix b sums the chunks
 // [p total / P, (p + 1) total / P) of that sequence, chunk k going to thread
-// k % 256, 8 chunks in flight per thread.  frob_finish adds the P partial
+// k % 256, 4 chunks in flight per thread.  frob_finish adds the P partial
 // sums of each matrix in order.  The summation order thus depends on the
 // valid side v and on P (a function of the batch size) alone: a padded and
 // an unpadded stack give the same bits.
@@ -153,23 +187,28 @@ template <typename TI>
 __global__ __launch_bounds__(256) void frob_partial_kernel(const TI* __restrict__ in, int B,
                                                            const int32_t* __restrict__ valid, double eps,
                                                            int P, double* __restrict__ part) {
-  constexpr int U = 8;
+  constexpr int U = 4;  // chunks in flight per thread (more costs occupancy)
   __shared__ double red[4];
   const int p = blockIdx.x;
   const int64_t b = blockIdx.y;
   const int v = valid ? min(max(valid[b], 0), B) : B;
   const TI* A = in + b * (int64_t)B * B;
   const int cv = (v + 3) / 4;
+  // row of chunk k: floor(k / cv) through a double reciprocal (exact: the
+  // quotient's distance to an integer, >= 0.5 / cv, dwarfs the rounding)
+  const double icv = 1.0 / (double)max(cv, 1);
   const int64_t total = (int64_t)v * cv;
   const int k0 = (int)(total * p / P), k1 = (int)(total * (p + 1) / P);
-  double acc = 0.0;
+  // one accumulator per element position: four independent chains, added in
+  // a fixed order at the end
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
   for (int base = k0; base < k1; base += 256 * U) {
     double x[U][4];
     int rr[U], cc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = base + u * 256 + (int)threadIdx.x;
-      rr[u] = k / cv;
+      rr[u] = (int)(((double)k + 0.5) * icv);
       cc[u] = 4 * (k - rr[u] * cv);
       if (k < k1) Quad<TI>::load(A + (int64_t)rr[u] * B + cc[u], x[u]);
     }
@@ -181,12 +220,13 @@ __global__ __launch_bounds__(256) void frob_partial_kernel(const TI* __restrict_
         if (cc[u] + e >= v) continue;
         double y = x[u][e];
         if (rr[u] == cc[u] + e) y += eps;
-        acc += y * y;
+        acc[e] += y * y;
       }
     }
   }
-  acc = block_sum256(acc, red);
-  if (threadIdx.x == 0) part[b * P + p] = acc;
+  double t = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  t = block_sum256(t, red);
+  if (threadIdx.x == 0) part[b * P + p] = t;
 }
 
 __global__ __launch_bounds__(256) void frob_finish_kernel(const double* __restrict__ part, int P, int64_t n,
@@ -580,6 +620,35 @@ struct GraftArgs {
   float* scales;     // [nblk]: per-block D_g / D factor
 };
 
+// Four consecutive gradient values (16-byte aligned float32 or 8-byte
+// aligned bfloat16) as float.
+template <typename TG> __device__ __forceinline__ void gload4(const void* g, int64_t i, float* o);
+template <> __device__ __forceinline__ void gload4<float>(const void* g, int64_t i, float* o) {
+  const floatx4 t = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(g) + i);
+  o[0] = t[0]; o[1] = t[1]; o[2] = t[2]; o[3] = t[3];
+}
+template <> __device__ __forceinline__ void gload4<__bf16>(const void* g, int64_t i, float* o) {
+  const u32x2 t = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(g) + i);
+  o[0] = __uint_as_float(t[0] << 16); o[1] = __uint_as_float(t[0] & 0xffff0000u);
+  o[2] = __uint_as_float(t[1] << 16); o[3] = __uint_as_float(t[1] & 0xffff0000u);
+}
+
+// Parameter rows of a block can be read four elements at a time when every
+// row starts 16-byte aligned (uniform per workgroup).
+template <typename TG> __device__ __forceinline__ bool graft_vec(const shampoo_param& P, const shampoo_block& blk) {
+  const uintptr_t al = reinterpret_cast<uintptr_t>(P.w) | reinterpret_cast<uintptr_t>(P.m) |
+                       reinterpret_cast<uintptr_t>(P.v) | ((uintptr_t)P.ld * 4) | ((uintptr_t)blk.col0 * 4);
+  const uintptr_t ag = reinterpret_cast<uintptr_t>(P.g) | ((uintptr_t)P.ld * sizeof(TG)) |
+                       ((uintptr_t)blk.col0 * sizeof(TG));
+  return (al & 15) == 0 && (ag & (4 * sizeof(TG) - 1)) == 0;
+}
+
+// Sums of D^2 and Delta^2 over GRAFT_ROWS rows of a block (Adam: m and v
+// updated in passing).  Work: chunks of 4 columns, chunk k to thread
+// k % 256, GRAFT_U chunks loaded before any is used; one accumulator chain
+// per element position, added in a fixed order at the end.
+constexpr int GRAFT_U = 4;
+
 template <typename TG>
 __global__ __launch_bounds__(256) void graft_partials_kernel(GraftArgs a) {
   __shared__ double red[4];
@@ -589,31 +658,78 @@ __global__ __launch_bounds__(256) void graft_partials_kernel(GraftArgs a) {
   if (blk.param < 0 || blk.param >= a.nparams) return;
   const shampoo_param P = a.params[blk.param];
   const float* D = a.dstack + b * (int64_t)a.B * a.B;
-  double sd = 0.0, sg = 0.0;
+  const bool adam = a.graft == SHAMPOO_GRAFT_ADAM && P.m && P.v;
+  const bool vec = graft_vec<TG>(P, blk);
+  double sd[4] = {0.0, 0.0, 0.0, 0.0}, sg[4] = {0.0, 0.0, 0.0, 0.0};
   const int r0 = ch * GRAFT_ROWS;
   const int r1 = min(blk.rows, r0 + GRAFT_ROWS);
-  for (int r = r0; r < r1; ++r) {
-    const int64_t prow = (int64_t)(blk.row0 + r) * P.ld + blk.col0;
-    for (int c = threadIdx.x; c < blk.cols; c += 256) {
-      const float d = D[(int64_t)r * a.B + c];
-      sd += (double)d * d;
-      const float g = gval<TG>(P.g, prow + c);
-      float delta = g;
-      if (a.graft == SHAMPOO_GRAFT_ADAM && P.m && P.v) {
-        const float m = a.beta1 * P.m[prow + c] + (1.0f - a.beta1) * g;
-        const float v = a.beta2 * P.v[prow + c] + (1.0f - a.beta2) * g * g;
-        P.m[prow + c] = m;
-        P.v[prow + c] = v;
-        delta = (m / a.bc1) / (sqrtf(v / a.bc2) + a.eps);
+  const int cpr = (blk.cols + 3) / 4;
+  const int total = max(r1 - r0, 0) * cpr;
+  for (int base = 0; base < total; base += 256 * GRAFT_U) {
+    float d[GRAFT_U][4], g[GRAFT_U][4], m[GRAFT_U][4], v[GRAFT_U][4];
+    int64_t prow[GRAFT_U];
+    int r[GRAFT_U], c[GRAFT_U], nv[GRAFT_U];  // nv: valid elements of the chunk (0 past the end)
+#pragma unroll
+    for (int u = 0; u < GRAFT_U; ++u) {
+      const int k = base + u * 256 + (int)threadIdx.x;
+      r[u] = r0 + k / cpr;
+      c[u] = (k % cpr) * 4;
+      nv[u] = k < total ? min(4, blk.cols - c[u]) : 0;
+      prow[u] = (int64_t)(blk.row0 + r[u]) * P.ld + blk.col0 + c[u];
+      const float* dp = D + (int64_t)r[u] * a.B + c[u];
+      if (nv[u] == 4 && vec) {
+        const floatx4 d4 = *reinterpret_cast<const floatx4*>(dp);
+        for (int e = 0; e < 4; ++e) d[u][e] = d4[e];
+        gload4<TG>(P.g, prow[u], g[u]);
+        if (adam) {
+          const floatx4 m4 = *reinterpret_cast<const floatx4*>(P.m + prow[u]);
+          const floatx4 v4 = *reinterpret_cast<const floatx4*>(P.v + prow[u]);
+          for (int e = 0; e < 4; ++e) { m[u][e] = m4[e]; v[u][e] = v4[e]; }
+        }
+      } else {
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = e < nv[u];
+          d[u][e] = ok ? dp[e] : 0.f;
+          g[u][e] = ok ? gval<TG>(P.g, prow[u] + e) : 0.f;
+          m[u][e] = ok && adam ? P.m[prow[u] + e] : 0.f;
+          v[u][e] = ok && adam ? P.v[prow[u] + e] : 0.f;
+        }
       }
-      sg += (double)delta * delta;
+    }
+#pragma unroll
+    for (int u = 0; u < GRAFT_U; ++u) {
+      if (nv[u] == 0) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (e >= nv[u]) continue;
+        sd[e] += (double)d[u][e] * d[u][e];
+        float delta = g[u][e];
+        if (adam) {
+          m[u][e] = a.beta1 * m[u][e] + (1.0f - a.beta1) * g[u][e];
+          v[u][e] = a.beta2 * v[u][e] + (1.0f - a.beta2) * g[u][e] * g[u][e];
+          delta = (m[u][e] / a.bc1) / (sqrtf(v[u][e] / a.bc2) + a.eps);
+        }
+        sg[e] += (double)delta * delta;
+      }
+      if (!adam) continue;
+      if (nv[u] == 4 && vec) {
+        *reinterpret_cast<floatx4*>(P.m + prow[u]) = floatx4{m[u][0], m[u][1], m[u][2], m[u][3]};
+        *reinterpret_cast<floatx4*>(P.v + prow[u]) = floatx4{v[u][0], v[u][1], v[u][2], v[u][3]};
+      } else {
+        for (int e = 0; e < nv[u]; ++e) {
+          P.m[prow[u] + e] = m[u][e];
+          P.v[prow[u] + e] = v[u][e];
+        }
+      }
     }
   }
-  sd = block_sum256(sd, red);
-  sg = block_sum256(sg, red);
+  double td = (sd[0] + sd[1]) + (sd[2] + sd[3]);
+  double tg = (sg[0] + sg[1]) + (sg[2] + sg[3]);
+  td = block_sum256(td, red);
+  tg = block_sum256(tg, red);
   if (threadIdx.x == 0) {
-    a.partials[(b * a.nchunk + ch) * 2 + 0] = sd;
-    a.partials[(b * a.nchunk + ch) * 2 + 1] = sg;
+    a.partials[(b * a.nchunk + ch) * 2 + 0] = td;
+    a.partials[(b * a.nchunk + ch) * 2 + 1] = tg;
   }
 }
 
@@ -652,23 +768,65 @@ __global__ __launch_bounds__(256) void graft_update_kernel(GraftArgs a) {
   const shampoo_param P = a.params[blk.param];
   const float* D = a.dstack + b * (int64_t)a.B * a.B;
   const float sc = a.scales[b];
+  const bool mom = a.graft == SHAMPOO_GRAFT_MOMENTUM && P.m;
+  const bool vec = graft_vec<float>(P, blk);
   const int r0 = ch * GRAFT_ROWS;
   const int r1 = min(blk.rows, r0 + GRAFT_ROWS);
-  for (int r = r0; r < r1; ++r) {
-    const int64_t prow = (int64_t)(blk.row0 + r) * P.ld + blk.col0;
-    for (int c = threadIdx.x; c < blk.cols; c += 256) {
-      const float dg = sc * D[(int64_t)r * a.B + c];
-      if (a.graft == SHAMPOO_GRAFT_MOMENTUM && P.m) {
-        const float m = a.momentum * P.m[prow + c] + dg;
-        P.m[prow + c] = m;
-        P.w[prow + c] -= a.lr * m;
+  const int cpr = (blk.cols + 3) / 4;
+  const int total = max(r1 - r0, 0) * cpr;
+  for (int base = 0; base < total; base += 256 * GRAFT_U) {
+    float d[GRAFT_U][4], w[GRAFT_U][4], m[GRAFT_U][4];
+    int64_t prow[GRAFT_U];
+    int nv[GRAFT_U];
+#pragma unroll
+    for (int u = 0; u < GRAFT_U; ++u) {
+      const int k = base + u * 256 + (int)threadIdx.x;
+      const int r = r0 + k / cpr, c = (k % cpr) * 4;
+      nv[u] = k < total ? min(4, blk.cols - c) : 0;
+      prow[u] = (int64_t)(blk.row0 + r) * P.ld + blk.col0 + c;
+      const float* dp = D + (int64_t)r * a.B + c;
+      if (nv[u] == 4 && vec) {
+        const floatx4 d4 = *reinterpret_cast<const floatx4*>(dp);
+        const floatx4 w4 = *reinterpret_cast<const floatx4*>(P.w + prow[u]);
+        for (int e = 0; e < 4; ++e) { d[u][e] = d4[e]; w[u][e] = w4[e]; }
+        if (mom) {
+          const floatx4 m4 = *reinterpret_cast<const floatx4*>(P.m + prow[u]);
+          for (int e = 0; e < 4; ++e) m[u][e] = m4[e];
+        }
       } else {
-        P.w[prow + c] -= a.lr * dg;
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = e < nv[u];
+          d[u][e] = ok ? dp[e] : 0.f;
+          w[u][e] = ok ? P.w[prow[u] + e] : 0.f;
+          m[u][e] = ok && mom ? P.m[prow[u] + e] : 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < GRAFT_U; ++u) {
+      if (nv[u] == 0) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float dg = sc * d[u][e];
+        if (mom) {
+          m[u][e] = a.momentum * m[u][e] + dg;
+          w[u][e] -= a.lr * m[u][e];
+        } else {
+          w[u][e] -= a.lr * dg;
+        }
+      }
+      if (nv[u] == 4 && vec) {
+        *reinterpret_cast<floatx4*>(P.w + prow[u]) = floatx4{w[u][0], w[u][1], w[u][2], w[u][3]};
+        if (mom) *reinterpret_cast<floatx4*>(P.m + prow[u]) = floatx4{m[u][0], m[u][1], m[u][2], m[u][3]};
+      } else {
+        for (int e = 0; e < nv[u]; ++e) {
+          P.w[prow[u] + e] = w[u][e];
+          if (mom) P.m[prow[u] + e] = m[u][e];
+        }
       }
     }
   }
 }
-
 
 // ---------------------------------------------------------------------------
 // Matrix-core throughput: each wave runs `iters` rounds of CHAINS independent

@@ -568,9 +568,10 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
   const size_t bufstride = align_up((size_t)n * BB * sizeof(TS));
   auto buf = [&](int i) -> TS* { return (TS*)(bufbase + (size_t)i * bufstride); };
 
-  // Frobenius norms: P workgroups per matrix (about 2048 in all), partial
-  // sums in the first iterate buffer, which prep overwrites afterwards.
-  const int parts = (int)std::max<int64_t>(1, std::min<int64_t>(32, (2048 + n - 1) / n));
+  // Frobenius norms: P workgroups per matrix (about 4096 in all, two full
+  // rounds of the CUs), partial sums in the first iterate buffer, which prep
+  // overwrites afterwards.
+  const int parts = (int)std::max<int64_t>(1, std::min<int64_t>(32, (4096 + n - 1) / n));
   hipLaunchKernelGGL((frob_partial_kernel<TI>), dim3((unsigned)parts, (unsigned)n), dim3(256), 0, st, (const TI*)in,
                      B, valid, o->eps, parts, (double*)buf(0));
   LAUNCH_CHECK("frob_partial");
