@@ -82,6 +82,31 @@ def time_roots(mir, inp, opts, steps, warmup, timing_cap=0):
     return dt, gemm_ms, nflag, out
 
 
+PARITY_SAMPLE = (0, 511, 1023)
+
+
+def parity_sample(A64, out32, out64):
+    """The oracle's roots of sampled blocks beside the GPU's: relative
+    Frobenius error and the solver residual ||X^4 A - I||_F / sqrt(B) of the
+    float64 and float32 chains and of the oracle's eigendecomposition root."""
+    import numpy as np
+    import oracle
+    rep = {"blocks": list(PARITY_SAMPLE), "oracle_residual": [], "f64_rel_err": [], "f64_residual": [],
+           "f32_finite": [], "f32_residual": []}
+    for k, i in enumerate(PARITY_SAMPLE):
+        A = A64[i]
+        ref = oracle.inverse_root_eigh(A, 4)
+        rep["oracle_residual"].append(oracle.residual(ref, A, 4))
+        if out64 is not None:
+            rep["f64_rel_err"].append(float(np.linalg.norm(out64[k] - ref) / np.linalg.norm(ref)))
+            rep["f64_residual"].append(oracle.residual(out64[k], A, 4))
+        x32 = out32[k].astype(np.float64)
+        fin = bool(np.isfinite(x32).all())
+        rep["f32_finite"].append(fin)
+        rep["f32_residual"].append(oracle.residual(x32, A, 4) if fin else None)
+    return rep
+
+
 def cpu_baseline(sample_f32, budget_s=15.0):
     import numpy as np
     import oracle
@@ -263,7 +288,9 @@ def main():
             o2 = mir.RootOpts(**{**opts.__dict__, "compute": comp})
             x = inp if comp != "f64" else torch.from_numpy(A64).to(dev)
             steps = max(1, args.steps // 2)
-            d2, gm, nf2, _ = time_roots(mir, x, o2, steps, 1, timing_cap=steps * ngemm)
+            d2, gm, nf2, o_var = time_roots(mir, x, o2, steps, 1, timing_cap=steps * ngemm)
+            if comp == "f64":
+                out64_sample = o_var[list(PARITY_SAMPLE)].cpu().numpy()
             peak = PEAK_FP16_MFMA if comp == "f16" else PEAK_FP64_MFMA
             mg = float(np.mean(gm)) * 1e-3
             var[comp] = {"blocks_per_s": round(N_BLOCKS / d2, 2), "ms_per_call": round(d2 * 1e3, 2),
@@ -288,6 +315,9 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp[:256].cpu().numpy())
         log(f"cpu baseline: {result['cpu_baseline']}")
+        result["parity_sample"] = parity_sample(A64, out[list(PARITY_SAMPLE)].cpu().numpy(),
+                                                None if args.no_variants else out64_sample)
+        log(f"parity sample: {result['parity_sample']}")
     print(json.dumps(result), flush=True)
 
 
