@@ -132,7 +132,7 @@ def test_other_orders(mir, p, method):
     assert not fl.any() and worst < 1e-4
 
 
-@pytest.mark.parametrize("degree", [2, 5, 16, 30])
+@pytest.mark.parametrize("degree", [2, 5, 16, 30, 40, 60, 100])
 def test_chebyshev_vs_polynomial_oracle(mir, degree):
     eps = 1e-3
     A = synthetic.spd_stack(8, 6, 128, 1e-4, 1.0).astype(np.float32)
@@ -276,6 +276,23 @@ def test_half_precision_products(mir, method):
     else:
         worst, _ = worst_vs_eigh(X, A, 4)
     log(f"f16 {method}: worst {worst:.2e}")
+    assert not fl.any() and worst < 2e-2
+
+
+@pytest.mark.parametrize("degree", [40, 60])
+def test_mixed_precision_clenshaw_degree_sweep(mir, degree):
+    """Clenshaw with half-precision products and float32 B_k at the higher
+    degrees of the pages' sweep, against the oracle's exact polynomial."""
+    eps = 1e-3
+    A = synthetic.spd_stack(13, 6, 256, 1e-3, 1.0).astype(np.float32)
+    X, s, fl = run_root(mir, A, 4, method="chebyshev", cheb_degree=degree, eps=eps, compute="f16")
+    c = oracle.chebyshev_coefficients(4, degree, eps)
+    worst = 0.0
+    for i in range(A.shape[0]):
+        Ae = A[i].astype(np.float64) + eps * np.eye(256)
+        ref = oracle.chebyshev_matrix_eigh(Ae / float(s[i]), c) * float(s[i]) ** -0.25
+        worst = max(worst, rel_fro(X[i], ref))
+    log(f"f16 Clenshaw d={degree}: worst {worst:.2e}")
     assert not fl.any() and worst < 2e-2
 
 
