@@ -165,3 +165,28 @@ def test_no_cpu_fallback_in_product():
         if f.endswith(".py"):
             src = open(os.path.join(pkg, f)).read()
             assert "torch.linalg" not in src and "np.linalg" not in src and "scipy" not in src, f
+
+
+def test_size_limits_are_rejected(mir):
+    """Documented limits fail before any launch: more than 65535 matrices in
+    one root call, power scaling beyond B = 1024 with 16 vectors, more than
+    32767 blocks in a step, and an unknown fallback."""
+    oc = mir.RootOpts(method="cn", iters=5).c()
+    fake = ctypes.c_void_p(0x1000)
+    st = mir.lib.shampoo_inverse_root(fake, fake, mir.F32, 65536, 64, 4, ctypes.byref(oc), None, None, None, fake,
+                                      1 << 40, None)
+    assert st == mir.E_UNSUPPORTED
+    with pytest.raises(mir.ShampooError) as e:
+        mir.shampoo_inverse_root_workspace(4, 2048, 4, mir.RootOpts(method="cn", iters=5, scaling="power"))
+    assert e.value.status == mir.E_UNSUPPORTED
+    a = mir.StepArgsC()
+    a.nparams, a.B, a.nblk = 1, 128, 40000
+    a.g_dt, a.p = mir.F32, 4
+    a.root = mir.RootOpts(method="cn", iters=10).c()
+    with pytest.raises(mir.ShampooError) as e:
+        mir.shampoo_step_workspace(a)
+    assert e.value.status == mir.E_UNSUPPORTED
+    a.nblk, a.fallback = 2, 7
+    with pytest.raises(mir.ShampooError) as e:
+        mir.shampoo_step_workspace(a)
+    assert e.value.status == mir.E_INVALID
