@@ -8,7 +8,7 @@
 // prep          A_s = (A + eps I)/s with the padding set to the identity (or
 //               to zero for the power iteration), and up to three affine
 //               images alpha A_s + gamma I that seed the solver chains.
-// power_iter    half-precision multi-start power iteration on the Frobenius
+// power_iter_fused  half-precision multi-start power iteration on the Frobenius
 //               scaled matrix, largest Rayleigh quotient ([DASH] "3. Inverse
 //               Root Methods", Power-Iteration).
 // finalize      out = X s^(-1/p) on the valid region, 0 on the padding,
@@ -303,122 +303,124 @@ __global__ __launch_bounds__(256) void prep_kernel(const TI* __restrict__ in, in
 }
 
 // ---------------------------------------------------------------------------
-// Multi-start power iteration, one workgroup (4 waves) per matrix.
-// Af: Frobenius-scaled matrices (padding zero), storage type TS.
-// Each of `iters` rounds normalises the k vectors and multiplies by Af with
+// Multi-start power iteration ([DASH] "3. Inverse Root Methods",
+// Power-Iteration), fused with its scaling and persistent over the matrices.
+// Workgroup w (4 waves) takes matrices w, w + gridDim.x, ...  For each, on
+// A_s = (in + eps I)/s_F (valid region; zero padding) rounded to half:
+// `iters` rounds normalise the k vectors and multiply by A_s with
 // half-precision operands and float32 accumulation (MFMA 16x16x32 f16); a
-// final product gives the Rayleigh quotients of the last normalised vectors.
-// s_out[b] = sf[b] * max_j rq_j (lowest j on ties).
-// Dynamic LDS: Vh half [k16][B + 8], Wf float [k16][B + 4], 2 * k16 floats.
+// final product gives the Rayleigh quotients of the last normalised vectors;
+// s_out[b] = sf[b] * max_j rq_j (lowest j on ties), or sf[b] with
+// PI_FALLBACK when no quotient is positive and finite.
+// Pass 0 computes A_s from `in` (in double, rounded to float, then to half)
+// and stores the half matrix in `hcopy`; later passes read that copy, half
+// the bytes of a float32 matrix.  Each lane reads back exactly the 16 bytes
+// it wrote.  Two workgroups per CU keep few matrices in flight.
+// Dynamic LDS: Vh half [k16][B + 8], Wf float [k16][B + 4], k16 floats.
 // ---------------------------------------------------------------------------
-template <typename TS> struct HalfLoad8;
-template <> struct HalfLoad8<float> {
-  static __device__ __forceinline__ halfx8 load(const float* p) {
-    const floatx4 lo = *reinterpret_cast<const floatx4*>(p);
-    const floatx4 hi = *reinterpret_cast<const floatx4*>(p + 4);
-    halfx8 h;
-    h[0] = (_Float16)lo[0]; h[1] = (_Float16)lo[1]; h[2] = (_Float16)lo[2]; h[3] = (_Float16)lo[3];
-    h[4] = (_Float16)hi[0]; h[5] = (_Float16)hi[1]; h[6] = (_Float16)hi[2]; h[7] = (_Float16)hi[3];
-    return h;
-  }
-};
-template <> struct HalfLoad8<double> {
-  static __device__ __forceinline__ halfx8 load(const double* p) {
-    halfx8 h;
-#pragma unroll
-    for (int q = 0; q < 8; q += 2) {
-      const doublex2 d = *reinterpret_cast<const doublex2*>(p + q);
-      // double -> float -> half is a double rounding; the operands are
-      // Frobenius-scaled values whose float32 rounding error (2^-24
-      // relative) sits far below half precision's (2^-11).
-      h[q] = (_Float16)(float)d[0];
-      h[q + 1] = (_Float16)(float)d[1];
-    }
-    return h;
-  }
-};
-
-template <typename TS, int NVB>
-__global__ __launch_bounds__(256) void power_iter_kernel(const TS* __restrict__ Af, int B, int k,
-                                                         int iters, const float* __restrict__ v0,
-                                                         const double* __restrict__ sf,
-                                                         double* __restrict__ s_out,
-                                                         int32_t* __restrict__ flags) {
+template <typename TI, int NVB>
+__global__ __launch_bounds__(256) void power_iter_fused_kernel(const TI* __restrict__ in, int B, int64_t n,
+                                                               const int32_t* __restrict__ valid, double eps,
+                                                               const double* __restrict__ sf, int k, int iters,
+                                                               const float* __restrict__ v0,
+                                                               _Float16* __restrict__ hcopy,
+                                                               double* __restrict__ s_out,
+                                                               int32_t* __restrict__ flags) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int k16 = NVB * 16;
-  const int VP = B + 8;  // half pitch (elements)
-  const int WP = B + 4;  // float pitch
+  const int VP = B + 8;
+  const int WP = B + 4;
   _Float16* Vh = reinterpret_cast<_Float16*>(smem);
   float* Wf = reinterpret_cast<float*>(smem + (size_t)k16 * VP * 2);
   float* rq = Wf + (size_t)k16 * WP;
-  const int64_t b = blockIdx.x;
-  const TS* A = Af + b * (int64_t)B * B;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, grp = lane >> 4;
-
-  for (int e = tid; e < k16 * B; e += 256) {
-    const int vv = e / B, i = e - vv * B;
-    Wf[vv * WP + i] = vv < k ? v0[(int64_t)vv * B + i] : 0.0f;
-  }
-
-  for (int it = 0; it <= iters; ++it) {
-    __syncthreads();
-    // normalise the columns of W into half-precision V
-    for (int vv = wave; vv < k16; vv += 4) {
-      float ss = 0.0f;
-      for (int i = lane; i < B; i += 64) {
-        const float x = Wf[vv * WP + i];
-        ss += x * x;
-      }
-      ss = wave_sum(ss);
-      const float nrm = sqrtf(ss);
-      const float inv = nrm > 0.0f ? 1.0f / nrm : 1.0f;
-      for (int i = lane; i < B; i += 64) Vh[vv * VP + i] = (_Float16)(Wf[vv * WP + i] * inv);
-    }
-    __syncthreads();
-    // W = A V
-    for (int rb = wave; rb < B / 16; rb += 4) {
-      floatx4 acc[NVB];
-#pragma unroll
-      for (int vb = 0; vb < NVB; ++vb) acc[vb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const TS* arow = A + (int64_t)(rb * 16 + i16) * B + 8 * grp;
-#pragma unroll 4
-      for (int kk = 0; kk < B; kk += 32) {
-        const halfx8 a = HalfLoad8<TS>::load(arow + kk);
-#pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) {
-          const halfx8 bv = *reinterpret_cast<const halfx8*>(Vh + (vb * 16 + i16) * VP + kk + 8 * grp);
-          acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv, acc[vb], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int vb = 0; vb < NVB; ++vb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) Wf[(vb * 16 + i16) * WP + rb * 16 + 4 * grp + v] = acc[vb][v];
-    }
-  }
-  __syncthreads();
-  // Rayleigh quotients of the last normalised (half) vectors
-  for (int vv = wave; vv < k16; vv += 4) {
-    float num = 0.0f, den = 0.0f;
-    for (int i = lane; i < B; i += 64) {
-      const float x = (float)Vh[vv * VP + i];
-      num += x * Wf[vv * WP + i];
-      den += x * x;
-    }
-    num = wave_sum(num);
-    den = wave_sum(den);
-    if (lane == 0) rq[vv] = den > 0.0f ? num / den : 0.0f;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float best = rq[0];
-    for (int vv = 1; vv < k; ++vv)
-      if (rq[vv] > best) best = rq[vv];
+  for (int64_t b = blockIdx.x; b < n; b += gridDim.x) {
+    const TI* A = in + b * (int64_t)B * B;
+    _Float16* H = hcopy + b * (int64_t)B * B;
+    const int v = valid ? min(max(valid[b], 0), B) : B;
     const double sfb = sf[b];
-    const bool ok = best > 0.0f && best < 3.0e38f;
-    s_out[b] = ok ? sfb * (double)best : sfb;
-    if (!ok && flags) atomicOr(flags + b, SHAMPOO_FLAG_PI_FALLBACK);
+    const double inv = (sfb > 0.0 && sfb < 1.0e300) ? 1.0 / sfb : 0.0;
+    __syncthreads();  // the previous matrix's last reads of Wf / Vh are done
+    for (int e = tid; e < k16 * B; e += 256) {
+      const int vv = e / B, i = e - vv * B;
+      Wf[vv * WP + i] = vv < k ? v0[(int64_t)vv * B + i] : 0.0f;
+    }
+    for (int it = 0; it <= iters; ++it) {
+      __syncthreads();
+      for (int vv = wave; vv < k16; vv += 4) {
+        float ss = 0.0f;
+        for (int i = lane; i < B; i += 64) {
+          const float x = Wf[vv * WP + i];
+          ss += x * x;
+        }
+        ss = wave_sum(ss);
+        const float nrm = sqrtf(ss);
+        const float rn = nrm > 0.0f ? 1.0f / nrm : 1.0f;
+        for (int i = lane; i < B; i += 64) Vh[vv * VP + i] = (_Float16)(Wf[vv * WP + i] * rn);
+      }
+      __syncthreads();
+      for (int rb = wave; rb < B / 16; rb += 4) {
+        floatx4 acc[NVB];
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) acc[vb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const int row = rb * 16 + i16;
+#pragma unroll 4
+        for (int kk = 0; kk < B; kk += 32) {
+          const int c0 = kk + 8 * grp;
+          halfx8 a;
+          if (it == 0) {
+            double x[8];
+#pragma unroll
+            for (int q = 0; q < 8; q += 4) Quad<TI>::load(A + (int64_t)row * B + c0 + q, x + q);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const int c = c0 + q;
+              double y = 0.0;
+              if (row < v && c < v) {
+                y = x[q];
+                if (row == c) y += eps;
+                y *= inv;
+              }
+              a[q] = (_Float16)(float)y;
+            }
+            *reinterpret_cast<halfx8*>(H + (int64_t)row * B + c0) = a;
+          } else {
+            a = *reinterpret_cast<const halfx8*>(H + (int64_t)row * B + c0);
+          }
+#pragma unroll
+          for (int vb = 0; vb < NVB; ++vb) {
+            const halfx8 bv = *reinterpret_cast<const halfx8*>(Vh + (vb * 16 + i16) * VP + kk + 8 * grp);
+            acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv, acc[vb], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) Wf[(vb * 16 + i16) * WP + rb * 16 + 4 * grp + q] = acc[vb][q];
+      }
+    }
+    __syncthreads();
+    for (int vv = wave; vv < k16; vv += 4) {
+      float num = 0.0f, den = 0.0f;
+      for (int i = lane; i < B; i += 64) {
+        const float x = (float)Vh[vv * VP + i];
+        num += x * Wf[vv * WP + i];
+        den += x * x;
+      }
+      num = wave_sum(num);
+      den = wave_sum(den);
+      if (lane == 0) rq[vv] = den > 0.0f ? num / den : 0.0f;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float best = rq[0];
+      for (int vv = 1; vv < k; ++vv)
+        if (rq[vv] > best) best = rq[vv];
+      const bool ok = best > 0.0f && best < 3.0e38f;
+      s_out[b] = ok ? sfb * (double)best : sfb;
+      if (!ok && flags) atomicOr(flags + b, SHAMPOO_FLAG_PI_FALLBACK);
+    }
   }
 }
 

@@ -581,18 +581,24 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
   const double* sc = sf;
   if (o->scaling == SHAMPOO_SCALE_POWER) {
     if (!o->pi_start_dev) return fail(SHAMPOO_E_INVALID, "power scaling needs pi_start_dev");
-    PrepOut a{buf(0), 1.0, 0.0}, none{nullptr, 0, 0};
-    HIP_TRY((launch_prep<TI, TS>(in, B, n, valid, o->eps, sf, 0.0, a, none, none, st)));
+    // Power iteration on (in + eps I)/s_F, scaling fused; its half-precision
+    // copy of each scaled matrix lives in the first iterate buffer, which
+    // the chain's prep overwrites afterwards.  Persistent: two workgroups
+    // per CU walk the matrices.
     const int k16 = (o->pi_vectors + 15) / 16 * 16;
     const size_t lds = (size_t)k16 * (B + 8) * 2 + (size_t)k16 * (B + 4) * 4 + (size_t)k16 * 4;
-    HIP_TRY(hipFuncSetAttribute(k16 == 16 ? (const void*)power_iter_kernel<TS, 1> : (const void*)power_iter_kernel<TS, 2>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    const void* pk = k16 == 16 ? (const void*)power_iter_fused_kernel<TI, 1> : (const void*)power_iter_fused_kernel<TI, 2>;
+    HIP_TRY(hipFuncSetAttribute(pk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    int cus = 0;
+    HIP_TRY(cu_count(&cus));
+    const unsigned pgrid = (unsigned)std::min<int64_t>(n, (int64_t)std::max(1, cus) * 2);
+    _Float16* hcopy = (_Float16*)buf(0);
     if (k16 == 16)
-      hipLaunchKernelGGL((power_iter_kernel<TS, 1>), dim3((unsigned)n), dim3(256), lds, st, buf(0), B,
-                         o->pi_vectors, o->pi_iters, o->pi_start_dev, sf, s, flags);
+      hipLaunchKernelGGL((power_iter_fused_kernel<TI, 1>), dim3(pgrid), dim3(256), lds, st, (const TI*)in, B, n, valid,
+                         o->eps, sf, o->pi_vectors, o->pi_iters, o->pi_start_dev, hcopy, s, flags);
     else
-      hipLaunchKernelGGL((power_iter_kernel<TS, 2>), dim3((unsigned)n), dim3(256), lds, st, buf(0), B,
-                         o->pi_vectors, o->pi_iters, o->pi_start_dev, sf, s, flags);
+      hipLaunchKernelGGL((power_iter_fused_kernel<TI, 2>), dim3(pgrid), dim3(256), lds, st, (const TI*)in, B, n, valid,
+                         o->eps, sf, o->pi_vectors, o->pi_iters, o->pi_start_dev, hcopy, s, flags);
     LAUNCH_CHECK("power_iter");
     sc = s;
   }
