@@ -5,8 +5,8 @@
 //     acc  = A_b * op(B_b)
 //     C_b  = alpha * acc + beta * D_b + gamma * I   (D optional)
 //     C2_b = alpha2 * C_b + gamma2 * I              (second output, optional)
-// op(B) = B^T when B is read row-wise ("NT", B_KN = false) and op(B) = B when
-// B is read k-major ("NN", B_KN = true).
+// op(B) = B^T when B is read row-wise ("NT") and op(B) = B when B is read
+// k-major ("NN").
 //
 // NT serves the products of symmetric matrices (coupled Newton, Clenshaw,
 // statistics G G^T): there A * B = A * B^T.  `sym` mode computes only the
@@ -18,13 +18,22 @@
 // idempotent one into one with eigenvalue 1 - (r + 2 + 1/r)/4 for an
 // eigenvalue pair of ratio r^2, unstable once r^2 exceeds about 34.
 //
-// Layout: all operands row-major, side n a multiple of the tile, batch stride
-// `stride` elements.  LDS holds, for both operands, tile rows (m for A, j for
-// B) of 128 bytes of k plus 16 bytes of padding: a row pitch of 9 16-byte
-// bank groups, so the 16 lanes of a b128 fragment read hit distinct banks.
-// NT operands are copied row by row (16-byte global loads, coalesced per
-// 128-byte row segment); an NN B operand is loaded as VE x VE element blocks
-// (VE = elements per 16 bytes) along its rows and transposed in registers.
+// Three kernels, all row-major with batch stride `stride` elements:
+//   gemm_f32_nn256_kernel  float32 NN, n a multiple of 256: 256 x 256 tiles,
+//                          one persistent workgroup of 8 waves per CU.
+//   gemm_p128_kernel       float32 / float64 NT or NN and bfloat16 NT into
+//                          float32, n a multiple of 128: 128 x 128 tiles, two
+//                          persistent workgroups of 4 waves per CU.
+//   gemm_kernel            every other type mix (operands converted while
+//                          staged: f32 -> f16, bf16/f32 -> f64, ...) and
+//                          n = 64 (mod 128): one tile per workgroup,
+//                          register-staged loads.
+// The first two load both operand tiles straight into LDS
+// (global_load_lds_dwordx4) and store results from the accumulators; the
+// third stages tiles through registers into padded LDS rows and its results
+// through LDS.  All three assign k to (lane group, step) the same way and
+// evaluate the epilogue with the same FMAs, so they give bit-identical
+// results on the same operands.
 //
 // Matrix-core mapping (16x16 family):
 //   f32: v_mfma_f32_16x16x4_f32     (lane supplies 1 value of k per operand)
@@ -36,7 +45,8 @@
 // l % 16 and row 4 (l / 16) + v (f32, f16, bf16) or row (l / 16) + 4 v (f64).
 // Logical k is assigned to (group, step) by a permutation applied
 // identically to A and B, chosen so that each lane reads 16 contiguous bytes
-// of its LDS row per fragment read.
+// of its LDS row per fragment read: a stage holds 128 bytes of k per row,
+// round r of a stage gives lane group g the 16-byte chunk 4 r + g.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -253,6 +263,12 @@ template <typename TC> __device__ __forceinline__ void put(TC* p, double v);
 template <> __device__ __forceinline__ void put<float>(float* p, double v) { *p = (float)v; }
 template <> __device__ __forceinline__ void put<double>(double* p, double v) { *p = v; }
 
+// Tiled kernel.  LDS holds, for both operands, tile rows (m for A, j for B)
+// of 128 bytes of k plus 16 bytes of padding: a row pitch of 9 16-byte bank
+// groups, so the 16 lanes of a b128 fragment read hit distinct banks.  NT
+// operands are copied row by row (16-byte global loads, coalesced per
+// 128-byte row segment); an NN B operand is loaded as VE x VE element blocks
+// (VE = elements per 16 bytes) along its rows and transposed in registers.
 template <Mma MM, int T, bool BKN, typename TA, typename TB, typename TC>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   using Tr = MmaTraits<MM>;
