@@ -46,11 +46,11 @@ def gemm_count_ndb(k1, k2):
     return (3 * k1 - 3) + (3 * k2 - 3)
 
 
-def make_stack(dtype):
+def make_stack(dtype, n=None):
     import numpy as np
     import synthetic
     t = time.time()
-    A = synthetic.spd_stack(3, N_BLOCKS, B, 1e-8, 1.0)
+    A = synthetic.spd_stack(3, N_BLOCKS if n is None else n, B, 1e-8, 1.0)
     log(f"generated the SPD stack in {time.time() - t:.1f} s")
     return A
 
@@ -208,6 +208,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-full-step", action="store_true")
+    ap.add_argument("--blocks", type=int, default=None,
+                    help="with --only roots: solve only the first this-many blocks (counter runs whose "
+                         "per-dispatch cycle counts would otherwise overflow 32 bits)")
     ap.add_argument("--only", choices=["roots", "copy", "step", "step5"], default=None,
                     help="profiling runs: only the float32 solve, only a 1 GiB copy, only the decoder-set step or only the bottleneck-50 step")
     args = ap.parse_args()
@@ -240,14 +243,17 @@ def main():
         log(f"bottleneck-50 step {ms:.2f} ms, flags {nf}")
         return
 
-    A64 = make_stack(np.float64)
+    if args.blocks is not None and args.only != "roots":
+        print(json.dumps({"error": "--blocks is for --only roots profiling runs"}))
+        sys.exit(2)
+    A64 = make_stack(np.float64, args.blocks)
     inp = torch.from_numpy(A64.astype(np.float32)).to(dev)
     V0 = torch.from_numpy(synthetic.pi_start_vectors(3, PI_VECTORS, B)).to(dev)
     opts = mir.RootOpts(method="ndb", scaling="power", compute="f32", iters=ITERS1, iters2=ITERS2,
                         pi_vectors=PI_VECTORS, pi_iters=PI_ITERS, pi_start=V0)
     ngemm = gemm_count_ndb(ITERS1, ITERS2)
     dt, gemm_ms, nflag, out = time_roots(mir, inp, opts, args.steps, args.warmup, timing_cap=args.steps * ngemm)
-    value = N_BLOCKS / dt
+    value = inp.shape[0] / dt
     log(f"f32 NDB+PI: {dt * 1e3:.1f} ms per call, {value:.1f} blocks/s, flagged blocks {nflag}")
     if args.only == "roots":
         return
