@@ -143,17 +143,20 @@ def traffic_from_profiles(kernel_tag):
     return rec.get("bytes_per_launch")
 
 
-def full_step_ms(mir, steps, warmup):
+def full_step_ms(mir, steps, warmup, compute="f32", fallback="none"):
     """Full step on the 12-layer decoder set (151 M parameters, block 1024,
     bfloat16 gradients N(0, 0.02^2), beta2 0.999, eps 1e-12, Adam grafting,
-    coupled Newton 34 iterations in float32, roots every step)."""
+    coupled Newton 34 iterations with float32 or half-precision products,
+    roots every step).  Returns the median step time and the number of
+    factors flagged during the timed steps."""
     import numpy as np
     import torch
     import synthetic
     shapes = synthetic.decoder_shapes()
     W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
-    opt = mir.Shampoo(W, block_size=1024, beta2=0.999, eps=1e-12, root=mir.RootOpts(method="cn", iters=34),
-                      graft="adam", lr=1e-3, grad_dtype=torch.bfloat16)
+    opt = mir.Shampoo(W, block_size=1024, beta2=0.999, eps=1e-12,
+                      root=mir.RootOpts(method="cn", iters=34, compute=compute),
+                      graft="adam", lr=1e-3, grad_dtype=torch.bfloat16, fallback=fallback)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(4)
     grads = [[(torch.randn(s, generator=gen, device="cuda") * 0.02).to(torch.bfloat16) for s in shapes]
@@ -161,8 +164,10 @@ def full_step_ms(mir, steps, warmup):
     for i in range(warmup):
         opt.step(grads[i % 2])
     torch.cuda.synchronize()
+    for f in opt.flags():
+        f.zero_()
     times = []
-    for i in range(steps):
+    for i in range(warmup, warmup + steps):
         t0 = time.perf_counter()
         opt.step(grads[i % 2])
         torch.cuda.synchronize()
@@ -191,7 +196,7 @@ def bottleneck_step_ms(mir, steps, warmup, group):
         opt.step(grads[i % 2])
     torch.cuda.synchronize()
     times = []
-    for i in range(steps):
+    for i in range(warmup, warmup + steps):
         t0 = time.perf_counter()
         opt.step(grads[i % 2])
         torch.cuda.synchronize()
@@ -211,8 +216,9 @@ def main():
     ap.add_argument("--blocks", type=int, default=None,
                     help="with --only roots: solve only the first this-many blocks (counter runs whose "
                          "per-dispatch cycle counts would otherwise overflow 32 bits)")
-    ap.add_argument("--only", choices=["roots", "copy", "step", "step5"], default=None,
-                    help="profiling runs: only the float32 solve, only a 1 GiB copy, only the decoder-set step or only the bottleneck-50 step")
+    ap.add_argument("--only", choices=["roots", "copy", "step", "step_f16", "step5"], default=None,
+                    help="profiling runs: only the float32 solve, only a 1 GiB copy, only the decoder-set step "
+                         "(float32 or half-precision products) or only the bottleneck-50 step")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -234,8 +240,9 @@ def main():
         torch.cuda.synchronize()
         log("copied 1 GiB three times")
         return
-    if args.only == "step":
-        ms, nf = full_step_ms(mir, args.steps, args.warmup)
+    if args.only in ("step", "step_f16"):
+        half = args.only == "step_f16"
+        ms, nf = full_step_ms(mir, args.steps, max(1, args.warmup), "f16" if half else "f32", "f64" if half else "none")
         log(f"full step {ms:.2f} ms, flags {nf}")
         return
     if args.only == "step5":
@@ -311,6 +318,14 @@ def main():
         result["full_step"] = {"workload": "decoder_12x(1024x3072,1024x1024,1024x4096,4096x1024)_bf16_adam_cn34_f32",
                                "ms": round(ms, 2), "flagged_factors": nf}
         log(f"full step: {ms:.1f} ms")
+        # the pages' CN-FP16 configuration: half-precision products; the
+        # single-Gram step-1 factors (warm-up) diverge in half precision and
+        # are recomputed by the float64 fallback, later ones converge
+        ms16, nf16 = full_step_ms(mir, max(3, args.steps), 1, "f16", "f64")
+        result["full_step_cn_f16"] = {
+            "workload": "decoder_12x(1024x3072,1024x1024,1024x4096,4096x1024)_bf16_adam_cn34_f16_products_f64_fallback",
+            "ms": round(ms16, 2), "flagged_factors": nf16}
+        log(f"full step, half-precision products: {ms16:.1f} ms (flagged {nf16})")
         msg, nfg = bottleneck_step_ms(mir, max(5, args.steps), 2, True)
         msu, nfu = bottleneck_step_ms(mir, max(5, args.steps), 2, False)
         result["full_step_bottleneck50"] = {

@@ -21,13 +21,15 @@
 // Three kernels, all row-major with batch stride `stride` elements:
 //   gemm_f32_nn256_kernel  float32 NN, n a multiple of 256: 256 x 256 tiles,
 //                          one persistent workgroup of 8 waves per CU.
-//   gemm_p128_kernel       float32 / float64 NT or NN and bfloat16 NT into
-//                          float32, n a multiple of 128: 128 x 128 tiles, two
-//                          persistent workgroups of 4 waves per CU.
+//   gemm_p128_kernel       float32 / float64 NT or NN, and bfloat16 or half
+//                          NT into float32, n a multiple of 128: 128 x 128
+//                          tiles, two persistent workgroups of 4 waves per CU.
 //   gemm_kernel            every other type mix (operands converted while
-//                          staged: f32 -> f16, bf16/f32 -> f64, ...) and
+//                          staged: bf16/f32 -> f64, ...), half NN, and
 //                          n = 64 (mod 128): one tile per workgroup,
 //                          register-staged loads.
+// Products of half operands write float32 results (C, C2) and, where later
+// products read them, half copies (Ch, C2h) rounded through float32.
 // The first two load both operand tiles straight into LDS
 // (global_load_lds_dwordx4) and store results from the accumulators; the
 // third stages tiles through registers into padded LDS rows and its results
@@ -38,7 +40,7 @@
 // Matrix-core mapping (16x16 family):
 //   f32: v_mfma_f32_16x16x4_f32     (lane supplies 1 value of k per operand)
 //   f64: v_mfma_f64_16x16x4_f64
-//   f16: v_mfma_f32_16x16x32_f16    (8 values; f32 operands rounded to half)
+//   f16: v_mfma_f32_16x16x32_f16    (8 values)
 //   bf16: v_mfma_f32_16x16x32_bf16
 // Lane l supplies row (l % 16) of its A fragment and column (l % 16) of its
 // B fragment for k-group (l / 16).  Result element v of lane l is column
@@ -51,6 +53,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace shampoo {
 
@@ -185,19 +189,11 @@ template <> struct Chunk<__bf16, double, 2> {  // bf16 -> f64 (exact)
   }
 };
 
-template <> struct Chunk<float, _Float16, 8> {  // f32 -> f16, round to nearest even
-  floatx4 lo, hi;
-  __device__ __forceinline__ void load(const float* p) {
-    lo = *reinterpret_cast<const floatx4*>(p);
-    hi = *reinterpret_cast<const floatx4*>(p + 4);
-  }
-  __device__ __forceinline__ _Float16 get(int e) const { return (_Float16)(e < 4 ? lo[e] : hi[e - 4]); }
-  __device__ __forceinline__ void store(unsigned char* d) const {
-    halfx8 h;
-    h[0] = (_Float16)lo[0]; h[1] = (_Float16)lo[1]; h[2] = (_Float16)lo[2]; h[3] = (_Float16)lo[3];
-    h[4] = (_Float16)hi[0]; h[5] = (_Float16)hi[1]; h[6] = (_Float16)hi[2]; h[7] = (_Float16)hi[3];
-    *reinterpret_cast<halfx8*>(d) = h;
-  }
+template <> struct Chunk<_Float16, _Float16, 8> {  // f16 -> f16
+  halfx8 w;
+  __device__ __forceinline__ void load(const _Float16* p) { w = *reinterpret_cast<const halfx8*>(p); }
+  __device__ __forceinline__ void store(unsigned char* d) const { *reinterpret_cast<halfx8*>(d) = w; }
+  __device__ __forceinline__ _Float16 get(int e) const { return w[e]; }
 };
 
 template <> struct Chunk<__bf16, __bf16, 8> {  // bf16 -> bf16
@@ -230,8 +226,10 @@ struct GemmArgs {
   const void* A;
   const void* B;
   const void* D;   // may be null (then beta is ignored)
-  void* C;
+  void* C;         // may be null where Ch is set (half operands)
   void* C2;        // may be null
+  void* Ch;        // half copy of C (half operands only; may be null)
+  void* C2h;       // half copy of C2 (half operands only; may be null)
   int n;           // side of every matrix, a multiple of the tile
   int tiles;       // tiles per matrix (n/T)^2, or (n/T)(n/T + 1)/2 in sym mode
   int nt;          // n / T
@@ -262,6 +260,22 @@ __device__ __forceinline__ double epi_c2(double alpha2, double c, double diag2) 
 template <typename TC> __device__ __forceinline__ void put(TC* p, double v);
 template <> __device__ __forceinline__ void put<float>(float* p, double v) { *p = (float)v; }
 template <> __device__ __forceinline__ void put<double>(double* p, double v) { *p = v; }
+
+// Half copies of float32 results (operands of later half-precision
+// products): each value is rounded to float32 first, then to half (nearest
+// even both times), so the copy holds what a float32 iterate rounded to a
+// half operand holds.  The empty asm statement pins the float32 value:
+// without it the compiler merges a preceding double -> float32 conversion
+// and this one into a single double -> half rounding, which differs where
+// the float32 rounding lands on a half-way point.
+__device__ __forceinline__ _Float16 half_of(float f) {
+  asm volatile("" : "+v"(f));
+  return (_Float16)f;
+}
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_h4(_Float16* p, floatx4 v) {
+  *reinterpret_cast<halfx4*>(p) = halfx4{half_of(v[0]), half_of(v[1]), half_of(v[2]), half_of(v[3])};
+}
 
 // Tiled kernel.  LDS holds, for both operands, tile rows (m for A, j for B)
 // of 128 bytes of k plus 16 bytes of padding: a row pitch of 9 16-byte bank
@@ -399,8 +413,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   }
 
   // Epilogue.
-  TC* C = reinterpret_cast<TC*>(g.C) + mat * g.stride;
+  TC* C = g.C ? reinterpret_cast<TC*>(g.C) + mat * g.stride : nullptr;
   TC* C2 = g.C2 ? reinterpret_cast<TC*>(g.C2) + mat * g.stride : nullptr;
+  _Float16* Ch = g.Ch ? reinterpret_cast<_Float16*>(g.Ch) + mat * g.stride : nullptr;
+  _Float16* C2h = g.C2h ? reinterpret_cast<_Float16*>(g.C2h) + mat * g.stride : nullptr;
   const TC* D = g.D ? reinterpret_cast<const TC*>(g.D) + mat * g.stride : nullptr;
   const bool diag = g.sym && ti == tj;
   const bool mirror = g.sym != 0;
@@ -450,12 +466,15 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
           y[q] = epi_c(g.alpha, (double)x[q], D ? g.beta : 0.0, dv[q], R == otj * T + c4 + q ? g.gamma : 0.0);
         }
         if constexpr (sizeof(TC) == 4) {
-          *reinterpret_cast<floatx4*>(C + base) = floatx4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]};
-          if (C2) {
-            float z[4];
+          const floatx4 yf = floatx4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]};
+          if (C) *reinterpret_cast<floatx4*>(C + base) = yf;
+          if (Ch) store_h4(Ch + base, yf);
+          if (C2 || C2h) {
+            floatx4 z;
 #pragma unroll
             for (int q = 0; q < 4; ++q) z[q] = (float)epi_c2(g.alpha2, y[q], R == otj * T + c4 + q ? g.gamma2 : 0.0);
-            *reinterpret_cast<floatx4*>(C2 + base) = floatx4{z[0], z[1], z[2], z[3]};
+            if (C2) *reinterpret_cast<floatx4*>(C2 + base) = z;
+            if (C2h) store_h4(C2h + base, z);
           }
         } else {
 #pragma unroll
@@ -731,8 +750,8 @@ constexpr int P128_TILE_BYTES = P128_T * 128;  // 16 KB per operand and stage
 
 // Operand type EI -> 16-byte fragment, accumulator, output type and the
 // k-steps (MFMAs) one fragment feeds.  float32/float64 fragments hold 4/2
-// consecutive k, one per 16x16x4 MFMA; a bfloat16 fragment holds the 8 k a
-// lane supplies to one 16x16x32 MFMA (NT only).
+// consecutive k, one per 16x16x4 MFMA; a bfloat16 or half fragment holds
+// the 8 k a lane supplies to one 16x16x32 MFMA (NT only).
 template <typename EI> struct P128;
 template <> struct P128<float> {
   using acc_t = floatx4;
@@ -771,6 +790,17 @@ template <> struct P128<__bf16> {
   static __device__ __forceinline__ int arow(int r) { return r; }
 };
 
+template <> struct P128<_Float16> {
+  using acc_t = floatx4;
+  using frag_t = halfx8;
+  using out_t = float;
+  static constexpr int VE = 8, KS = 1;
+  static __device__ __forceinline__ acc_t mma(const frag_t& a, const frag_t& b, int, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int arow(int r) { return r; }
+};
+
 // LDS row -> B-tile row of an NT operand (the inverse of
 // j -> (j & 64) | 16 (j & 3) | ((j >> 2) & 15))
 __device__ __forceinline__ int p128_brow(int rho) { return (rho & 64) | (4 * (rho & 15)) | ((rho >> 4) & 3); }
@@ -784,6 +814,13 @@ template <typename E, int RUN> __device__ __forceinline__ void store_run(E* p, c
     else
       *reinterpret_cast<doublex2*>(p + 2 * s) = doublex2{v[2 * s], v[2 * s + 1]};
   }
+}
+// RUN consecutive half copies of float32 results (4 per 8-byte store)
+template <typename E, int RUN> __device__ __forceinline__ void store_run_h(_Float16* p, const E* v) {
+  static_assert(RUN % 4 == 0, "half runs of 4");
+#pragma unroll
+  for (int s = 0; s < RUN / 4; ++s)
+    store_h4(p + 4 * s, floatx4{(float)v[4 * s], (float)v[4 * s + 1], (float)v[4 * s + 2], (float)v[4 * s + 3]});
 }
 template <typename E, int RUN> __device__ __forceinline__ void load_run(const E* p, E* v) {
 #pragma unroll
@@ -808,6 +845,8 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
   constexpr int RB = T * (int)sizeof(E);  // bytes per k-row of an NN B tile
   constexpr int RUN = NN ? VE : 4;        // consecutive output columns per lane and run
   constexpr bool PREFETCH_D = sizeof(EO) == 4;
+  constexpr bool HALF_OUT = std::is_same<E, _Float16>::value;
+  static_assert(!NN || P::KS > 1, "NN operands need fragments of one k per MFMA");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * SB];
   const int per = gridDim.x >> 3;
   const int x = blockIdx.x & 7, l = blockIdx.x >> 3;
@@ -894,7 +933,7 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
     for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
   const EO* Dg = reinterpret_cast<const EO*>(g.D);
   EO dpre[PREFETCH_D ? 4 : 1][4][4];  // D of the current tile [i][v][jb] (float32)
-  const bool plain = g.alpha == 1.0 && g.gamma == 0.0 && Dg == nullptr && g.C2 == nullptr;
+  const bool plain = g.alpha == 1.0 && g.gamma == 0.0 && Dg == nullptr && g.C2 == nullptr && g.C2h == nullptr;
   const int total_steps = ntile * nst;
   auto dload = [&](int i, EO (*d)[4]) {  // D at the lane's outputs of row block i
 #pragma unroll
@@ -965,8 +1004,12 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
     barrier_no_fence();
     if (++ck < nst) continue;
     ck = 0;
-    EO* C = reinterpret_cast<EO*>(g.C) + cmo;
+    EO* C = g.C ? reinterpret_cast<EO*>(g.C) + cmo : nullptr;
     EO* C2 = g.C2 ? reinterpret_cast<EO*>(g.C2) + cmo : nullptr;
+    // half copies: float32 results of half-operand products only
+    _Float16* Ch = HALF_OUT && g.Ch ? reinterpret_cast<_Float16*>(g.Ch) + cmo : nullptr;
+    _Float16* C2h = HALF_OUT && g.C2h ? reinterpret_cast<_Float16*>(g.C2h) + cmo : nullptr;
+    const bool two = C2 || C2h;
     const int R0 = cti * T + wm * 64, C0 = ctj * T + wn * 64;
     const bool diag = g.sym && cti == ctj;
     const bool mirror = (g.sym && !diag) || g.transC;
@@ -1003,12 +1046,24 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
             if (R > Cc) continue;
             double t;
             const EO y = val(v, j, t);
-            C[(int64_t)R * n + Cc] = y;
-            C[(int64_t)Cc * n + R] = y;
-            if (C2) {
+            if (C) {
+              C[(int64_t)R * n + Cc] = y;
+              C[(int64_t)Cc * n + R] = y;
+            }
+            if (Ch) {
+              Ch[(int64_t)R * n + Cc] = half_of((float)y);
+              Ch[(int64_t)Cc * n + R] = half_of((float)y);
+            }
+            if (two) {
               const EO z = val2(v, j, t);
-              C2[(int64_t)R * n + Cc] = z;
-              C2[(int64_t)Cc * n + R] = z;
+              if (C2) {
+                C2[(int64_t)R * n + Cc] = z;
+                C2[(int64_t)Cc * n + R] = z;
+              }
+              if (C2h) {
+                C2h[(int64_t)R * n + Cc] = half_of((float)z);
+                C2h[(int64_t)Cc * n + R] = half_of((float)z);
+              }
             }
           }
         continue;
@@ -1023,11 +1078,17 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
             double t[RUN];
 #pragma unroll
             for (int e = 0; e < RUN; ++e) y[e] = val(v, h * RUN + e, t[e]);
-            store_run<EO, RUN>(C + at, y);
-            if (C2) {
+            if (C) store_run<EO, RUN>(C + at, y);
+            if constexpr (HALF_OUT) {
+              if (Ch) store_run_h<EO, RUN>(Ch + at, y);
+            }
+            if (two) {
 #pragma unroll
               for (int e = 0; e < RUN; ++e) z[e] = val2(v, h * RUN + e, t[e]);
-              store_run<EO, RUN>(C2 + at, z);
+              if (C2) store_run<EO, RUN>(C2 + at, z);
+              if constexpr (HALF_OUT) {
+                if (C2h) store_run_h<EO, RUN>(C2h + at, z);
+              }
             }
           }
       }
@@ -1039,11 +1100,17 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
           double t[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) y[v] = val(v, j, t[v]);
-          store_run<EO, 4>(C + at, y);
-          if (C2) {
+          if (C) store_run<EO, 4>(C + at, y);
+          if constexpr (HALF_OUT) {
+            if (Ch) store_run_h<EO, 4>(Ch + at, y);
+          }
+          if (two) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) z[v] = val2(v, j, t[v]);
-            store_run<EO, 4>(C2 + at, z);
+            if (C2) store_run<EO, 4>(C2 + at, z);
+            if constexpr (HALF_OUT) {
+              if (C2h) store_run_h<EO, 4>(C2h + at, z);
+            }
           }
         }
       }

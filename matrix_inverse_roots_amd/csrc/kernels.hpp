@@ -244,8 +244,9 @@ __global__ __launch_bounds__(256) void frob_finish_kernel(const double* __restri
 // each thread maps PREP_U four-element chunks of one matrix.
 // ---------------------------------------------------------------------------
 struct PrepOut {
-  void* p;
+  void* p;   // output in the iterate type (may be null)
   double alpha, gamma;
+  void* ph;  // half copy, rounded through float32 (half operands only; may be null)
 };
 constexpr int PREP_U = 4;
 
@@ -264,6 +265,9 @@ __global__ __launch_bounds__(256) void prep_kernel(const TI* __restrict__ in, in
   TS* out[3] = {o0.p ? reinterpret_cast<TS*>(o0.p) + b * BB : nullptr,
                 o1.p ? reinterpret_cast<TS*>(o1.p) + b * BB : nullptr,
                 o2.p ? reinterpret_cast<TS*>(o2.p) + b * BB : nullptr};
+  _Float16* outh[3] = {o0.ph ? reinterpret_cast<_Float16*>(o0.ph) + b * BB : nullptr,
+                       o1.ph ? reinterpret_cast<_Float16*>(o1.ph) + b * BB : nullptr,
+                       o2.ph ? reinterpret_cast<_Float16*>(o2.ph) + b * BB : nullptr};
   const double al[3] = {o0.alpha, o1.alpha, o2.alpha}, ga[3] = {o0.gamma, o1.gamma, o2.gamma};
   const int total = B * cpr;
   double x[PREP_U][4];
@@ -293,11 +297,13 @@ __global__ __launch_bounds__(256) void prep_kernel(const TI* __restrict__ in, in
     }
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
-      if (!out[q]) continue;
+      if (!out[q] && !outh[q]) continue;
       double y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] = al[q] * a[e] + ga[q] * (rr[u] == cc[u] + e ? 1.0 : 0.0);
-      Quad<TS>::store(out[q] + (int64_t)rr[u] * B + cc[u], y);
+      if (out[q]) Quad<TS>::store(out[q] + (int64_t)rr[u] * B + cc[u], y);
+      if (outh[q])
+        store_h4(outh[q] + (int64_t)rr[u] * B + cc[u], floatx4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]});
     }
   }
 }
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const TI* __restrict__ in, in
 // final product gives the Rayleigh quotients of the last normalised vectors;
 // s_out[b] = sf[b] * max_j rq_j (lowest j on ties), or sf[b] with
 // PI_FALLBACK when no quotient is positive and finite.
-// Pass 0 computes A_s from `in` (in double, rounded to float, then to half)
+// Pass 0 computes A_s from `in` (in double, rounded once to half)
 // and stores the half matrix in `hcopy`; later passes read that copy, half
 // the bytes of a float32 matrix.  Each lane reads back exactly the 16 bytes
 // it wrote.  Two workgroups per CU keep few matrices in flight.
@@ -382,7 +388,7 @@ __global__ __launch_bounds__(256) void power_iter_fused_kernel(const TI* __restr
                 if (row == c) y += eps;
                 y *= inv;
               }
-              a[q] = (_Float16)(float)y;
+              a[q] = (_Float16)y;  // one rounding, double -> half
             }
             *reinterpret_cast<halfx8*>(H + (int64_t)row * B + c0) = a;
           } else {

@@ -63,11 +63,13 @@ size_t dtype_size(int dt) {
 // GEMM dispatch
 // ---------------------------------------------------------------------------
 struct GemmCall {
-  const void* A;
-  const void* B;
-  const void* D;
-  void* C;
-  void* C2;
+  const void* A = nullptr;
+  const void* B = nullptr;
+  const void* D = nullptr;
+  void* C = nullptr;
+  void* C2 = nullptr;
+  void* Ch = nullptr;   // half copies (products of half operands)
+  void* C2h = nullptr;
   double alpha = 1.0, beta = 0.0, gamma = 0.0, alpha2 = 0.0, gamma2 = 0.0;
   bool sym = true;
   bool transC = false;
@@ -120,6 +122,8 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
   g.D = c.D;
   g.C = c.C;
   g.C2 = c.C2;
+  g.Ch = c.Ch;
+  g.C2h = c.C2h;
   g.n = n;
   g.nt = n / T;
   g.sym = c.sym ? 1 : 0;
@@ -188,7 +192,19 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
       return hipGetLastError();
     }
   }
-  if constexpr (std::is_same<TB, float>::value || std::is_same<TB, double>::value) {
+  // half operands into float32 (f16 solver chains), NT
+  constexpr bool f16_in = MM == Mma::F16 && std::is_same<TA, _Float16>::value &&
+                          std::is_same<TB, _Float16>::value && std::is_same<TC, float>::value;
+  if constexpr (f16_in) {
+    if (T == P128_T && !c.nn && !c.transC) {
+      int cus = 0;
+      HIP_TRY_ERR(cu_count(&cus));
+      const int64_t wgs = std::min<int64_t>(((g.total + 7) / 8) * 8, std::max(8, (cus / 8) * 8) * 2);
+      hipLaunchKernelGGL((gemm_p128_kernel<_Float16, false>), dim3((unsigned)wgs), dim3(256), 0, st, g);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (std::is_same<TB, float>::value || std::is_same<TB, double>::value || f16_in) {
     if (c.nn) {
       if (T == 128)
         hipLaunchKernelGGL((gemm_kernel<MM, 128, true, TA, TB, TC>), grid, dim3(256), 0, st, g);
@@ -228,7 +244,12 @@ struct Op {
   bool nn = false;  // full product A B in the given order (else symmetric NT)
   double alpha = 1, beta = 0, gamma = 0, alpha2 = 0, gamma2 = 0;
   // FINAL: buffer a -> out
+  // Forms of each output that later ops read (NEED_F32: addend D or final
+  // output; NEED_HALF: product operand); used by half-operand chains.
+  int need[3] = {0, 0, 0};  // PREP outputs
+  int need_c = 0, need_c2 = 0;
 };
+constexpr int NEED_F32 = 1, NEED_HALF = 2;
 
 struct Plan {
   std::vector<Op> ops;
@@ -507,6 +528,34 @@ shampoo_status check_root_args(int64_t n, int32_t B, int32_t p, const shampoo_ro
   return SHAMPOO_OK;
 }
 
+// Which forms of every value the chain reads, by a backward scan: a product
+// reads its operands as half (in half-operand chains) and its addend D in
+// float32; the final pass reads float32.  A buffer written by an op holds a
+// new value, so the needs gathered after it belong to that op's output.
+void mark_needs(Plan& P) {
+  std::vector<int> need(P.peak > 0 ? P.peak : 1, 0);
+  auto take = [&](int b) {
+    const int v = need[b];
+    need[b] = 0;
+    return v;
+  };
+  for (auto it = P.ops.rbegin(); it != P.ops.rend(); ++it) {
+    Op& op = *it;
+    if (op.kind == OP_PREP) {
+      for (int q = 0; q < 3; ++q)
+        if (op.out[q] >= 0) op.need[q] = take(op.out[q]);
+    } else if (op.kind == OP_GEMM) {
+      op.need_c = take(op.c);
+      if (op.c2 >= 0) op.need_c2 = take(op.c2);
+      need[op.a] |= NEED_HALF;
+      need[op.b] |= NEED_HALF;
+      if (op.d >= 0) need[op.d] |= NEED_F32;
+    } else {
+      need[op.a] |= NEED_F32;
+    }
+  }
+}
+
 Plan build_plan(int32_t p, const shampoo_root_opts* o) {
   Plan P;
   switch (o->method) {
@@ -517,13 +566,22 @@ Plan build_plan(int32_t p, const shampoo_root_opts* o) {
       plan_cheb(P, cheb_coeffs(p, o->cheb_degree, N, o->cheb_eps));
     }
   }
+  mark_needs(P);
   return P;
 }
 
+// One iterate buffer: float64 or float32 matrices; half-operand chains add a
+// half copy of each matrix after the float32 part.
+size_t root_slot_f32_bytes(int64_t n, int32_t B, int compute) {
+  return align_up((size_t)n * B * B * (compute == SHAMPOO_F64 ? 8 : 4));
+}
+size_t root_slot_bytes(int64_t n, int32_t B, int compute) {
+  return root_slot_f32_bytes(n, B, compute) + (compute == SHAMPOO_F16 ? align_up((size_t)n * B * B * 2) : 0);
+}
+
 size_t root_ws_bytes(int64_t n, int32_t B, const Plan& P, int compute) {
-  const size_t es = compute == SHAMPOO_F64 ? 8 : 4;
   const int nbuf = P.peak > 1 ? P.peak : 1;  // the power iteration borrows one buffer
-  return 2 * align_up((size_t)n * 8) + (size_t)nbuf * align_up((size_t)n * B * B * es);
+  return 2 * align_up((size_t)n * 8) + (size_t)nbuf * root_slot_bytes(n, B, compute);
 }
 
 // Benchmark timing of the batched products (shampoo_timing_enable).
@@ -565,8 +623,14 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
   double* sf = (double*)w;
   double* s = (double*)(w + align_up((size_t)n * 8));
   unsigned char* bufbase = w + 2 * align_up((size_t)n * 8);
-  const size_t bufstride = align_up((size_t)n * BB * sizeof(TS));
+  // Half-operand chains (f16): every product reads half operands, so a value
+  // is stored as half where products read it and in float32 where it is an
+  // addend or the result (Op::need); each buffer has room for both forms.
+  constexpr bool HALF = MM == Mma::F16;
+  const size_t slot32 = root_slot_f32_bytes(n, B, o->compute);
+  const size_t bufstride = root_slot_bytes(n, B, o->compute);
   auto buf = [&](int i) -> TS* { return (TS*)(bufbase + (size_t)i * bufstride); };
+  auto hbuf = [&](int i) -> _Float16* { return (_Float16*)(bufbase + (size_t)i * bufstride + slot32); };
 
   // Frobenius norms: P workgroups per matrix (about 4096 in all, two full
   // rounds of the CUs), partial sums in the first iterate buffer, which prep
@@ -605,20 +669,35 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
   for (const Op& op : P.ops) {
     if (op.kind == OP_PREP) {
       PrepOut q[3];
-      for (int i = 0; i < 3; ++i) q[i] = PrepOut{op.out[i] >= 0 ? buf(op.out[i]) : nullptr, op.oa[i], op.og[i]};
+      for (int i = 0; i < 3; ++i) {
+        q[i] = PrepOut{nullptr, op.oa[i], op.og[i], nullptr};
+        if (op.out[i] < 0) continue;
+        if (!HALF || (op.need[i] & NEED_F32)) q[i].p = buf(op.out[i]);
+        if (HALF && (op.need[i] & NEED_HALF)) q[i].ph = hbuf(op.out[i]);
+      }
       HIP_TRY((launch_prep<TI, TS>(in, B, n, valid, o->eps, sc, 1.0, q[0], q[1], q[2], st)));
     } else if (op.kind == OP_GEMM) {
       GemmCall c;
-      c.A = buf(op.a);
-      c.B = buf(op.b);
       c.D = op.d >= 0 ? buf(op.d) : nullptr;
-      c.C = buf(op.c);
-      c.C2 = op.c2 >= 0 ? buf(op.c2) : nullptr;
       c.alpha = op.alpha; c.beta = op.beta; c.gamma = op.gamma; c.alpha2 = op.alpha2; c.gamma2 = op.gamma2;
       c.sym = !op.nn;
       c.nn = op.nn;
       HIP_TRY(timing_mark(0, st));
-      HIP_TRY((gemm<MM, TS, TS, TS>(c, B, n, st)));
+      if constexpr (HALF) {
+        c.A = hbuf(op.a);
+        c.B = hbuf(op.b);
+        if (op.need_c & NEED_F32) c.C = buf(op.c);
+        if (op.need_c & NEED_HALF) c.Ch = hbuf(op.c);
+        if (op.c2 >= 0 && (op.need_c2 & NEED_F32)) c.C2 = buf(op.c2);
+        if (op.c2 >= 0 && (op.need_c2 & NEED_HALF)) c.C2h = hbuf(op.c2);
+        HIP_TRY((gemm<MM, _Float16, _Float16, TS>(c, B, n, st)));
+      } else {
+        c.A = buf(op.a);
+        c.B = buf(op.b);
+        c.C = buf(op.c);
+        c.C2 = op.c2 >= 0 ? buf(op.c2) : nullptr;
+        HIP_TRY((gemm<MM, TS, TS, TS>(c, B, n, st)));
+      }
       HIP_TRY(timing_mark(1, st));
       timing_advance();
     } else {

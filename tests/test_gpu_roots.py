@@ -103,14 +103,15 @@ def test_large_and_small_tile_products_bit_identical(mir):
     assert not X2[:, v:, :].any() and not X2[:, :, v:].any()
 
 
-@pytest.mark.parametrize("compute", ["f32", "f64"])
+@pytest.mark.parametrize("compute", ["f32", "f64", "f16"])
 @pytest.mark.parametrize("method", ["cn", "ndb", "chebyshev"])
 def test_product_kernels_bit_identical(mir, method, compute):
     """A 192 x 192 stack runs on the 64-tile product kernel, the same stack
-    padded to 256 (valid = 192) on the persistent kernels (128-tile NT and
-    float64 NN, 256-tile float32 NN); all walk k in the same order and the
-    padding adds exact zeros, so the roots agree bit for bit.  Chebyshev
-    exercises the D operand, Newton-DB p = 4 the second output."""
+    padded to 256 (valid = 192) on the persistent kernels (128-tile NT,
+    float64 NN, 256-tile float32 NN; half NN stays on the tiled kernel); all
+    walk k in the same order and the padding adds exact zeros, so the roots
+    agree bit for bit.  Chebyshev exercises the D operand, Newton-DB p = 4
+    the second output; with half operands both also write half copies."""
     n, v = 5, 192
     A = synthetic.spd_stack(192, n, v, 1e-2, 1.0).astype(np.float32)
     kw = dict(method=method, scaling="frobenius", iters=20, iters2=14, cheb_degree=12, eps=1e-3, compute=compute)

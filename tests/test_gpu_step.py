@@ -291,6 +291,39 @@ def test_decoder_layer_adam_bf16_f32_chain(mir):
     assert all(e < t for e, t in errs)
 
 
+def test_decoder_layer_cn_half_products_with_f64_fallback(mir):
+    """The decoder layer with coupled Newton on half-precision products (the
+    pages' CN-FP16 configuration).  Step 1's factors are single square
+    Gram matrices: their scaled smallest eigenvalues (about 1e-8) sit below
+    the half-precision rounding of the scaled factor, the half chain diverges
+    on all 24 of them, and the float64 fallback recomputes them.  From step
+    2 on the factors are sums of several Gram matrices (condition number 33,
+    then 14) and the half chain converges on every factor.  The parameters
+    stay within the half-precision bar of the oracle at every step."""
+    import torch
+    shapes = synthetic.decoder_shapes(layers=1)
+    grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
+    W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    opt = mir.Shampoo(W, block_size=1024, beta2=0.999, eps=1e-12, root=mir.RootOpts(method="cn", iters=34, compute="f16"),
+                      graft="adam", lr=1e-3, grad_dtype=torch.bfloat16, fallback="f64")
+    orc = oracle.ShampooOracle(shapes, [1024] * len(shapes), beta2=0.999, eps=1e-12, graft="adam", lr=1e-3)
+    Wo = [np.zeros(s) for s in shapes]
+    for t in range(3):
+        for f in opt.flags():
+            f.zero_()
+        opt.step([bf16_tensor(g) for g in grads[t]])
+        orc.step(Wo, [synthetic.bf16_bits_to_f32(g).astype(np.float64) for g in grads[t]])
+        torch.cuda.synchronize()
+        fl = torch.cat(opt.flags()).cpu().numpy()
+        e = max(rel_fro(w.cpu().numpy(), wo) for w, wo in zip(W, Wo))
+        log(f"decoder layer CN f16 step {t + 1}: worst parameter rel err {e:.2e}, flags {np.unique(fl).tolist()}")
+        if t == 0:
+            assert (fl == (mir.FLAG_NONFINITE | mir.FLAG_RECOMPUTED_F64)).all()
+        else:
+            assert not fl.any()
+        assert e < 2e-2
+
+
 def test_bottleneck_subset_chebyshev_momentum(mir):
     """First 12 matrices of the 50-layer bottleneck CNN set (1x1 and 3x3
     kernels as (out, in k k)), block sizes 256 / 1024 by size, ragged edges,
