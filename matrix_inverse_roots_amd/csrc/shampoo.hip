@@ -100,15 +100,16 @@ hipError_t cu_count(int* cus) {
   return hipSuccess;
 }
 
-// The large-tile product needs 128 KB of dynamic LDS, above the default
-// limit; raise the kernel's limit once per device.
-hipError_t nn256_prepare() {
+// The large-tile products need 128 KB of dynamic LDS, above the default
+// limit; raise each kernel's limit once per device (K tells the kernels
+// apart).
+template <int K>
+hipError_t large_lds_prepare(const void* kernel, int bytes) {
   static bool done[MAX_DEVICES] = {false};
   int dev = 0;
   HIP_TRY_ERR(hipGetDevice(&dev));
   if (dev >= 0 && dev < MAX_DEVICES && done[dev]) return hipSuccess;
-  HIP_TRY_ERR(hipFuncSetAttribute((const void*)gemm_f32_nn256_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  NN256_LDS));
+  HIP_TRY_ERR(hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
   if (dev >= 0 && dev < MAX_DEVICES) done[dev] = true;
   return hipSuccess;
 }
@@ -149,7 +150,7 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
       h.total = batch * h.tiles;
       // persistent grid: at most one workgroup per CU, a multiple of the 8 XCDs
       const int64_t wgs = std::min<int64_t>(((h.total + 7) / 8) * 8, std::max(8, (cus / 8) * 8));
-      HIP_TRY_ERR(nn256_prepare());
+      HIP_TRY_ERR(large_lds_prepare<0>((const void*)gemm_f32_nn256_kernel, NN256_LDS));
       hipLaunchKernelGGL(gemm_f32_nn256_kernel, dim3((unsigned)wgs), dim3(512), NN256_LDS, st, h);
       return hipGetLastError();
     }
@@ -196,6 +197,25 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
   constexpr bool f16_in = MM == Mma::F16 && std::is_same<TA, _Float16>::value &&
                           std::is_same<TB, _Float16>::value && std::is_same<TC, float>::value;
   if constexpr (f16_in) {
+    if (n % H256_T == 0 && !c.transC && !(c.nn && (c.sym || c.D))) {
+      int cus = 0;
+      HIP_TRY_ERR(cu_count(&cus));
+      GemmArgs h = g;
+      h.sym = c.nn ? 0 : g.sym;
+      h.nt = n / H256_T;
+      h.tiles = h.sym ? h.nt * (h.nt + 1) / 2 : h.nt * h.nt;
+      h.total = batch * h.tiles;
+      // persistent grid: one workgroup per CU, a multiple of the 8 XCDs
+      const int64_t wgs = std::min<int64_t>(((h.total + 7) / 8) * 8, std::max(8, (cus / 8) * 8));
+      if (c.nn) {
+        HIP_TRY_ERR(large_lds_prepare<1>((const void*)gemm_h256_kernel<true>, H256_LDS));
+        hipLaunchKernelGGL((gemm_h256_kernel<true>), dim3((unsigned)wgs), dim3(512), H256_LDS, st, h);
+      } else {
+        HIP_TRY_ERR(large_lds_prepare<2>((const void*)gemm_h256_kernel<false>, H256_LDS));
+        hipLaunchKernelGGL((gemm_h256_kernel<false>), dim3((unsigned)wgs), dim3(512), H256_LDS, st, h);
+      }
+      return hipGetLastError();
+    }
     if (T == P128_T && !c.nn && !c.transC) {
       int cus = 0;
       HIP_TRY_ERR(cu_count(&cus));

@@ -124,6 +124,27 @@ def test_product_kernels_bit_identical(mir, method, compute):
     assert not X2[:, v:, :].any() and not X2[:, :, v:].any()
 
 
+@pytest.mark.parametrize("method", ["cn", "ndb", "chebyshev"])
+def test_half_products_large_tiles_bit_identical(mir, method):
+    """Half-precision products: a 384 x 384 stack runs on the 128-tile NT
+    kernel (Newton-DB's NN products on the tiled kernel), the same stack
+    padded to 512 (valid = 384) on the 256-tile half kernel, whose matrix
+    cores take the operands in swapped roles and whose NN operand comes
+    through transposed LDS reads; the roots agree bit for bit."""
+    n, v = 4, 384
+    A = synthetic.spd_stack(384, n, v, 1e-2, 1.0).astype(np.float32)
+    kw = dict(method=method, scaling="frobenius", iters=18, iters2=12, cheb_degree=12, eps=1e-3, compute="f16")
+    X1, s1, f1 = run_root(mir, A, 4, **kw)
+    Ap = np.zeros((n, 512, 512), dtype=np.float32)
+    Ap[:, :v, :v] = A
+    X2, s2, f2 = run_root(mir, Ap, 4, valid=[v] * n, **kw)
+    assert not f1.any() and not f2.any()
+    np.testing.assert_array_equal(X1, X2[:, :v, :v])
+    assert not X2[:, v:, :].any() and not X2[:, :, v:].any()
+    worst, _ = worst_vs_eigh(X1, A, 4, eps=1e-3) if method != "chebyshev" else (0.0, None)
+    assert worst < 2e-2
+
+
 @pytest.mark.parametrize("p,method", [(2, "cn"), (8, "cn"), (1, "cn"), (2, "ndb")])
 def test_other_orders(mir, p, method):
     A = synthetic.spd_stack(7, 4, 128, 1e-2, 1.0).astype(np.float32)
