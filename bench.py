@@ -136,9 +136,11 @@ def traffic_from_profiles(kernel_tag):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, "matrix_inverse_roots_amd", "csrc", "gemm.hpp")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("gemm_hpp_sha256") != h:
+    h = hashlib.sha256()
+    for name in rec.get("kernel_sources", []):
+        with open(os.path.join(ROOT, "matrix_inverse_roots_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if not rec.get("kernel_sources") or rec.get("kernel_sources_sha256") != h.hexdigest():
         return None
     return rec.get("bytes_per_launch")
 

@@ -1,54 +1,6 @@
-// Batched square GEMM on CDNA4 matrix cores (gfx950), with the fused
-// epilogues the inverse-root chains need.
-//
-// For every matrix b of a batch of n x n matrices:
-//     acc  = A_b * op(B_b)
-//     C_b  = alpha * acc + beta * D_b + gamma * I   (D optional)
-//     C2_b = alpha2 * C_b + gamma2 * I              (second output, optional)
-// op(B) = B^T when B is read row-wise ("NT") and op(B) = B when B is read
-// k-major ("NN").
-//
-// NT serves the products of symmetric matrices (coupled Newton, Clenshaw,
-// statistics G G^T): there A * B = A * B^T.  `sym` mode computes only the
-// upper-triangular tiles of such a product and writes each twice (in place
-// and mirrored), which keeps the iterate exactly symmetric and skips the
-// lower tiles.  NN serves Newton-DB, whose coupled iterates must be
-// multiplied as they are, in the order of the recurrence: symmetrising its
-// products changes the first-order error map of the iteration from an
-// idempotent one into one with eigenvalue 1 - (r + 2 + 1/r)/4 for an
-// eigenvalue pair of ratio r^2, unstable once r^2 exceeds about 34.
-//
-// Three kernels, all row-major with batch stride `stride` elements:
-//   gemm_f32_nn256_kernel  float32 NN, n a multiple of 256: 256 x 256 tiles,
-//                          one persistent workgroup of 8 waves per CU.
-//   gemm_p128_kernel       float32 / float64 NT or NN, and bfloat16 or half
-//                          NT into float32, n a multiple of 128: 128 x 128
-//                          tiles, two persistent workgroups of 4 waves per CU.
-//   gemm_kernel            every other type mix (operands converted while
-//                          staged: bf16/f32 -> f64, ...), half NN, and
-//                          n = 64 (mod 128): one tile per workgroup,
-//                          register-staged loads.
-// Products of half operands write float32 results (C, C2) and, where later
-// products read them, half copies (Ch, C2h) rounded through float32.
-// The first two load both operand tiles straight into LDS
-// (global_load_lds_dwordx4) and store results from the accumulators; the
-// third stages tiles through registers into padded LDS rows and its results
-// through LDS.  All three assign k to (lane group, step) the same way and
-// evaluate the epilogue with the same FMAs, so they give bit-identical
-// results on the same operands.
-//
-// Matrix-core mapping (16x16 family):
-//   f32: v_mfma_f32_16x16x4_f32     (lane supplies 1 value of k per operand)
-//   f64: v_mfma_f64_16x16x4_f64
-//   f16: v_mfma_f32_16x16x32_f16    (8 values)
-//   bf16: v_mfma_f32_16x16x32_bf16
-// Lane l supplies row (l % 16) of its A fragment and column (l % 16) of its
-// B fragment for k-group (l / 16).  Result element v of lane l is column
-// l % 16 and row 4 (l / 16) + v (f32, f16, bf16) or row (l / 16) + 4 v (f64).
-// Logical k is assigned to (group, step) by a permutation applied
-// identically to A and B, chosen so that each lane reads 16 contiguous bytes
-// of its LDS row per fragment read: a stage holds 128 bytes of k per row,
-// round r of a stage gives lane group g the 16-byte chunk 4 r + g.
+// Batched square products for the solver chains and the statistics: the
+// tiled kernel, the persistent 128-tile kernel and the persistent 256-tile
+// half-operand kernel (the family is described in gemm_common.hpp).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -56,15 +8,9 @@
 
 #include <type_traits>
 
-namespace shampoo {
+#include "gemm_common.hpp"
 
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef double doublex2 __attribute__((ext_vector_type(2)));
-typedef double doublex4 __attribute__((ext_vector_type(4)));
-typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+namespace shampoo {
 
 enum class Mma { F32, F64, F16, BF16 };
 
@@ -221,61 +167,6 @@ template <typename TG, typename TL, int VE> struct BlockKN {
     }
   }
 };
-
-struct GemmArgs {
-  const void* A;
-  const void* B;
-  const void* D;   // may be null (then beta is ignored)
-  void* C;         // may be null where Ch is set (half operands)
-  void* C2;        // may be null
-  void* Ch;        // half copy of C (half operands only; may be null)
-  void* C2h;       // half copy of C2 (half operands only; may be null)
-  int n;           // side of every matrix, a multiple of the tile
-  int tiles;       // tiles per matrix (n/T)^2, or (n/T)(n/T + 1)/2 in sym mode
-  int nt;          // n / T
-  int sym;         // compute upper tiles only and mirror (NT only)
-  int transC;      // write C transposed (no D, no C2, no sym)
-  int64_t stride;  // elements between consecutive matrices
-  int64_t total;   // batch * tiles (= grid size)
-  double alpha, beta, gamma, alpha2, gamma2;
-};
-
-// Workgroup id -> linear work index so that the consecutive work items of one
-// XCD are contiguous: the hardware deals workgroups to the 8 XCDs round-robin,
-// and each XCD has its own L2, so all tiles of a matrix should share an XCD.
-__device__ __forceinline__ int64_t xcd_remap(int64_t w, int64_t total) {
-  const int64_t q = total >> 3, r = total & 7;
-  const int64_t xcd = w & 7, local = w >> 3;
-  return xcd * q + (xcd < r ? xcd : r) + local;
-}
-
-// The fused epilogue's affine maps in double, written as explicit FMAs so
-// that every product kernel rounds them identically:
-//   C  = alpha acc + beta D + gamma [diagonal],   C2 = alpha2 C + gamma2 [diagonal].
-__device__ __forceinline__ double epi_c(double alpha, double acc, double beta, double d, double diag) {
-  return __builtin_fma(alpha, acc, __builtin_fma(beta, d, diag));
-}
-__device__ __forceinline__ double epi_c2(double alpha2, double c, double diag2) { return __builtin_fma(alpha2, c, diag2); }
-
-template <typename TC> __device__ __forceinline__ void put(TC* p, double v);
-template <> __device__ __forceinline__ void put<float>(float* p, double v) { *p = (float)v; }
-template <> __device__ __forceinline__ void put<double>(double* p, double v) { *p = v; }
-
-// Half copies of float32 results (operands of later half-precision
-// products): each value is rounded to float32 first, then to half (nearest
-// even both times), so the copy holds what a float32 iterate rounded to a
-// half operand holds.  The empty asm statement pins the float32 value:
-// without it the compiler merges a preceding double -> float32 conversion
-// and this one into a single double -> half rounding, which differs where
-// the float32 rounding lands on a half-way point.
-__device__ __forceinline__ _Float16 half_of(float f) {
-  asm volatile("" : "+v"(f));
-  return (_Float16)f;
-}
-typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void store_h4(_Float16* p, floatx4 v) {
-  *reinterpret_cast<halfx4*>(p) = halfx4{half_of(v[0]), half_of(v[1]), half_of(v[2]), half_of(v[3])};
-}
 
 // Tiled kernel.  LDS holds, for both operands, tile rows (m for A, j for B)
 // of 128 bytes of k plus 16 bytes of padding: a row pitch of 9 16-byte bank
@@ -525,191 +416,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
           if (C2) put<TC>(C2 + (int64_t)Cc * n + R, x2);
         }
       }
-}
-
-// ---------------------------------------------------------------------------
-// Large-tile float32 NN product (n a multiple of 256, no D operand):
-//     C_b = alpha * A_b B_b + gamma * I,   C2_b = alpha2 * C_b + gamma2 * I.
-//
-// One workgroup per CU (512 threads, 8 waves of 128 x 64 outputs) computes
-// 256 x 256 tiles and walks a strided list of them (persistent grid), so the
-// loads of a tile's first k-stage overlap the previous tile's last stage and
-// its stores overlap the next tile's first.  Per k-stage (32 values of k)
-// both operand tiles (32 KB each) go straight from global memory into LDS
-// with `global_load_lds_dwordx4` (no staging registers, no LDS store
-// instructions); two stage buffers, 128 KB of LDS.  Each wave waits for its
-// own loads (vmcnt) and then meets the others at a plain `s_barrier`: the
-// release fence of __syncthreads() would wait for every outstanding load,
-// including those of the next stage.
-//
-// LDS layouts:
-//   A tile  [256 rows m][128 B of k]: no padding (the DMA writes 1 KB runs);
-//           the 16-byte chunk c of row m sits at position c ^ swz(m), which
-//           spreads a fragment read over all banks.
-//   B tile  [32 rows k][256 columns]: B's own row-major layout, k-major.
-// Fragments: A as in gemm_kernel (lane reads 4 consecutive k of its row);
-// for B, lane (i16, grp) reads the 4 consecutive columns 4 i16 .. 4 i16 + 3
-// of k-row 4 kc + u, one per 16x16 column block.  Output column block j of a
-// wave therefore holds columns wn*64 + 4 (l % 16) + j, and a lane owns 4
-// consecutive columns of each of its rows: the epilogue stores float4 runs
-// straight from the accumulators.  The k order per output element is the
-// same as in gemm_kernel, so the two kernels give bit-identical results.
-// ---------------------------------------------------------------------------
-constexpr int NN256_T = 256;
-constexpr int NN256_BK = 32;
-constexpr int NN256_ABYTES = NN256_T * 128;               // 32 KB
-constexpr int NN256_BBYTES = NN256_BK * NN256_T * 4;      // 32 KB
-constexpr int NN256_LDS = 2 * (NN256_ABYTES + NN256_BBYTES);  // 128 KB
-
-__device__ __forceinline__ int nn256_swz(int m) { return (m & 7) ^ ((m >> 3) & 1); }
-__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x3f70); }  // vmcnt(0) only
-
-__global__ __launch_bounds__(512, 1) void gemm_f32_nn256_kernel(GemmArgs g) {
-  constexpr int T = NN256_T, BK = NN256_BK, SB = NN256_ABYTES + NN256_BBYTES;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  // Tiles of XCD x (blockIdx % 8) form one contiguous range; workgroup l of
-  // that XCD takes every per-th of them.
-  const int per = gridDim.x >> 3;
-  const int x = blockIdx.x & 7, l = blockIdx.x >> 3;
-  const int64_t q = g.total >> 3, r = g.total & 7;
-  const int64_t mine = q + (x < r ? 1 : 0);
-  if (mine <= l) return;
-  const int64_t first = x * q + (x < r ? x : r) + l;
-  const int ntile = (int)((mine - l + per - 1) / per);
-  const int n = g.n, nst = n / BK;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
-  const int i16 = lane & 15, grp = lane >> 4;
-  const float* Ag = reinterpret_cast<const float*>(g.A);
-  const float* Bg = reinterpret_cast<const float*>(g.B);
-
-  // Each wave issues 4 A loads (8 rows x 128 B each) and 4 B loads (one
-  // 1 KB k-row each) per stage; lane offsets in elements.
-  int aoff[4], boff[4];
-#pragma unroll
-  for (int qq = 0; qq < 4; ++qq) {
-    const int row = 8 * (4 * wave + qq) + (lane >> 3), pos = lane & 7;
-    aoff[qq] = row * n + 4 * (pos ^ nn256_swz(row));
-    boff[qq] = (4 * wave + qq) * n + 4 * lane;
-  }
-  auto coords = [&](int it, int64_t& moff, int& ti, int& tj) {
-    const int64_t w = first + (int64_t)it * per;
-    const int64_t mat = w / g.tiles;
-    const int t = (int)(w - mat * g.tiles);
-    ti = t / g.nt;
-    tj = t - ti * g.nt;
-    moff = mat * g.stride;
-  };
-  // load cursor: tile lt, k-stage lk
-  int lt = 0, lk = 0;
-  const float *LA, *LB;
-  {
-    int64_t mo;
-    int ti, tj;
-    coords(0, mo, ti, tj);
-    LA = Ag + mo + (int64_t)ti * T * n;
-    LB = Bg + mo + (int64_t)tj * T;
-  }
-  auto issue = [&](int buf) {
-    unsigned char* sa = smem + buf * SB;
-    unsigned char* sb = sa + NN256_ABYTES;
-    const float* pa = LA + lk * BK;
-    const float* pb = LB + (int64_t)lk * BK * n;
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      __builtin_amdgcn_global_load_lds((const void*)(pa + aoff[qq]), (void*)(sa + (4 * wave + qq) * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(pb + boff[qq]), (void*)(sb + (4 * wave + qq) * 1024), 16, 0, 0);
-    }
-  };
-  auto advance = [&]() {
-    if (++lk == nst) {
-      lk = 0;
-      if (++lt < ntile) {
-        int64_t mo;
-        int ti, tj;
-        coords(lt, mo, ti, tj);
-        LA = Ag + mo + (int64_t)ti * T * n;
-        LB = Bg + mo + (int64_t)tj * T;
-      }
-    }
-  };
-
-  floatx4 acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const bool plain = g.alpha == 1.0 && g.gamma == 0.0 && g.C2 == nullptr;
-  const int total_steps = ntile * nst;
-
-  issue(0);
-  advance();
-  wait_vmcnt0();
-  barrier_no_fence();
-  int ck = 0, ct = 0;
-  for (int step = 0; step < total_steps; ++step) {
-    const bool more = step + 1 < total_steps;
-    if (more) issue((step + 1) & 1);
-    const unsigned char* sa = smem + (step & 1) * SB;
-    const unsigned char* sb = sa + NN256_ABYTES;
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int kc = rr * 4 + grp;
-      floatx4 a[8], b[4];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int m = wm * 128 + i * 16 + i16;
-        a[i] = *reinterpret_cast<const floatx4*>(sa + m * 128 + 16 * (kc ^ nn256_swz(m)));
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        b[u] = *reinterpret_cast<const floatx4*>(sb + (kc * 4 + u) * (T * 4) + wn * 256 + 16 * i16);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][u], b[u][j], acc[i][j], 0, 0, 0);
-    }
-    if (more) advance();
-    wait_vmcnt0();
-    barrier_no_fence();
-    if (++ck < nst) continue;
-    // Tile done: its stores overlap the next tile's first stage.
-    ck = 0;
-    int64_t mo;
-    int ti, tj;
-    coords(ct++, mo, ti, tj);
-    float* C = reinterpret_cast<float*>(g.C) + mo;
-    float* C2 = g.C2 ? reinterpret_cast<float*>(g.C2) + mo : nullptr;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int R = ti * T + wm * 128 + i * 16 + 4 * grp + v;
-        const int c0 = tj * T + wn * 64 + 4 * i16;
-        const int64_t at = (int64_t)R * n + c0;
-        if (plain) {
-          *reinterpret_cast<floatx4*>(C + at) = floatx4{acc[i][0][v], acc[i][1][v], acc[i][2][v], acc[i][3][v]};
-          continue;
-        }
-        double y[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) y[j] = epi_c(g.alpha, (double)acc[i][j][v], 0.0, 0.0, R == c0 + j ? g.gamma : 0.0);
-        *reinterpret_cast<floatx4*>(C + at) = floatx4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]};
-        if (C2) {
-          float z[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) z[j] = (float)epi_c2(g.alpha2, y[j], R == c0 + j ? g.gamma2 : 0.0);
-          *reinterpret_cast<floatx4*>(C2 + at) = floatx4{z[0], z[1], z[2], z[3]};
-        }
-      }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
 }
 
 // ---------------------------------------------------------------------------

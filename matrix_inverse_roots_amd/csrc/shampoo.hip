@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "gemm.hpp"
+#include "gemm_nn256.hpp"
 #include "kernels.hpp"
 #include "shampoo.h"
 
