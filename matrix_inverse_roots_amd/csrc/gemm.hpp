@@ -830,8 +830,9 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// Half-operand 256 x 256-tile product (n a multiple of 256), float32 results
-// and their half copies:
+// 16-bit-operand 256 x 256-tile product (n a multiple of 256; half
+// operands in the solver chains, bfloat16 available), float32 results and,
+// for half operands, their half copies:
 //     NT: C = alpha A B^T + beta D + gamma I, sym (upper tiles, mirrored) or not
 //     NN: C = alpha A B + gamma I (no D, no sym)
 //     C2 = alpha2 C + gamma2 I in both.
@@ -875,8 +876,25 @@ __device__ __forceinline__ int h256_bswz(int k) { return 2 * ((k & 3) | (((k >> 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
 
-template <bool NN>
+// 16-bit operand type -> matrix-core fragment (8 k per lane) and product
+template <typename E> struct H256;
+template <> struct H256<_Float16> {
+  using frag_t = halfx8;
+  static __device__ __forceinline__ floatx4 mma(const frag_t& a, const frag_t& b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct H256<__bf16> {
+  using frag_t = bf16x8;
+  static __device__ __forceinline__ floatx4 mma(const frag_t& a, const frag_t& b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <typename E, bool NN>
 __global__ __launch_bounds__(512, 1) void gemm_h256_kernel(GemmArgs g) {
+  using frag_t = typename H256<E>::frag_t;
+  constexpr bool HALF_OUT = std::is_same<E, _Float16>::value;
   constexpr int T = H256_T, BK = H256_BK, TB = H256_TILE_BYTES, SB = 2 * TB;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int per = gridDim.x >> 3;
@@ -890,8 +908,8 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   const int i16 = lane & 15, grp = lane >> 4;
-  const _Float16* Ag = reinterpret_cast<const _Float16*>(g.A);
-  const _Float16* Bg = reinterpret_cast<const _Float16*>(g.B);
+  const E* Ag = reinterpret_cast<const E*>(g.A);
+  const E* Bg = reinterpret_cast<const E*>(g.B);
 
   // Each wave issues 4 A and 4 B loads of 1 KB per stage; lane offsets in elements.
   int aoff[4], boff[4];
@@ -931,13 +949,13 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_kernel(GemmArgs g) {
   int64_t cmo;
   int cti, ctj;
   coords(0, cmo, cti, ctj);
-  const _Float16* LA = Ag + cmo + (int64_t)cti * T * n;
-  const _Float16* LB = bbase(cmo, ctj);
+  const E* LA = Ag + cmo + (int64_t)cti * T * n;
+  const E* LB = bbase(cmo, ctj);
   auto issue = [&](int buf) {
     unsigned char* sa = smem + buf * SB;
     unsigned char* sb = sa + TB;
-    const _Float16* pa = LA + lk * BK;
-    const _Float16* pb = NN ? LB + (int64_t)lk * BK * n : LB + lk * BK;
+    const E* pa = LA + lk * BK;
+    const E* pb = NN ? LB + (int64_t)lk * BK * n : LB + lk * BK;
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       __builtin_amdgcn_global_load_lds((const void*)(pa + aoff[qq]), (void*)(sa + (4 * wave + qq) * 1024), 16, 0, 0);
@@ -990,11 +1008,11 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_kernel(GemmArgs g) {
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int kc = rr * 4 + grp;
-      halfx8 a[8], b[4];
+      frag_t a[8], b[4];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int m = wm * 128 + i * 16 + i16;
-        a[i] = *reinterpret_cast<const halfx8*>(sa + m * 128 + 16 * (kc ^ nn256_swz(m)));
+        a[i] = *reinterpret_cast<const frag_t*>(sa + m * 128 + 16 * (kc ^ nn256_swz(m)));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -1004,16 +1022,16 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_kernel(GemmArgs g) {
           const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0));
           const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0 + 4 * (T * 2)));
           const shortx8 w = shortx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          b[j] = __builtin_bit_cast(halfx8, w);
+          b[j] = __builtin_bit_cast(frag_t, w);
         } else {
           const int rho = wn * 64 + 16 * j + i16;
-          b[j] = *reinterpret_cast<const halfx8*>(sb + rho * 128 + 16 * (kc ^ nn256_swz(rho)));
+          b[j] = *reinterpret_cast<const frag_t*>(sb + rho * 128 + 16 * (kc ^ nn256_swz(rho)));
         }
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j], a[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) acc[i][j] = H256<E>::mma(b[j], a[i], acc[i][j]);
     }
     if (more) advance();
     wait_vmcnt0();
@@ -1022,8 +1040,8 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_kernel(GemmArgs g) {
     ck = 0;
     float* C = g.C ? reinterpret_cast<float*>(g.C) + cmo : nullptr;
     float* C2 = g.C2 ? reinterpret_cast<float*>(g.C2) + cmo : nullptr;
-    _Float16* Ch = g.Ch ? reinterpret_cast<_Float16*>(g.Ch) + cmo : nullptr;
-    _Float16* C2h = g.C2h ? reinterpret_cast<_Float16*>(g.C2h) + cmo : nullptr;
+    _Float16* Ch = HALF_OUT && g.Ch ? reinterpret_cast<_Float16*>(g.Ch) + cmo : nullptr;
+    _Float16* C2h = HALF_OUT && g.C2h ? reinterpret_cast<_Float16*>(g.C2h) + cmo : nullptr;
     const float* D = Dg ? Dg + cmo : nullptr;
     const bool two = C2 || C2h;
     const int R0 = cti * T + wm * 128, C0 = ctj * T + wn * 64;

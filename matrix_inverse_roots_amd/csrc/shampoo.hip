@@ -209,11 +209,11 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
       // persistent grid: one workgroup per CU, a multiple of the 8 XCDs
       const int64_t wgs = std::min<int64_t>(((h.total + 7) / 8) * 8, std::max(8, (cus / 8) * 8));
       if (c.nn) {
-        HIP_TRY_ERR(large_lds_prepare<1>((const void*)gemm_h256_kernel<true>, H256_LDS));
-        hipLaunchKernelGGL((gemm_h256_kernel<true>), dim3((unsigned)wgs), dim3(512), H256_LDS, st, h);
+        HIP_TRY_ERR(large_lds_prepare<1>((const void*)gemm_h256_kernel<_Float16, true>, H256_LDS));
+        hipLaunchKernelGGL((gemm_h256_kernel<_Float16, true>), dim3((unsigned)wgs), dim3(512), H256_LDS, st, h);
       } else {
-        HIP_TRY_ERR(large_lds_prepare<2>((const void*)gemm_h256_kernel<false>, H256_LDS));
-        hipLaunchKernelGGL((gemm_h256_kernel<false>), dim3((unsigned)wgs), dim3(512), H256_LDS, st, h);
+        HIP_TRY_ERR(large_lds_prepare<2>((const void*)gemm_h256_kernel<_Float16, false>, H256_LDS));
+        hipLaunchKernelGGL((gemm_h256_kernel<_Float16, false>), dim3((unsigned)wgs), dim3(512), H256_LDS, st, h);
       }
       return hipGetLastError();
     }
