@@ -198,7 +198,11 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
   constexpr bool f16_in = MM == Mma::F16 && std::is_same<TA, _Float16>::value &&
                           std::is_same<TB, _Float16>::value && std::is_same<TC, float>::value;
   if constexpr (f16_in) {
-    if (n % H256_T == 0 && !c.transC && !(c.nn && (c.sym || c.D))) {
+    // NN, and NT without symmetry: 256-tile kernel.  Symmetric NT products
+    // stay on 128 tiles, whose diagonal tiles waste half as much work (the
+    // upper tiles are 36 of 64 at n = 1024 against 10 of 16).
+    const bool sym_p128 = c.sym && !c.nn && n % P128_T == 0;
+    if (n % H256_T == 0 && !c.transC && !(c.nn && (c.sym || c.D)) && !sym_p128) {
       int cus = 0;
       HIP_TRY_ERR(cu_count(&cus));
       GemmArgs h = g;
