@@ -83,3 +83,34 @@ def test_grouping_reduces_root_work():
     torch.cuda.synchronize()
     assert int(st.flags.sum().item()) == 0
     assert all(torch.isfinite(w).all().item() for w in W)
+
+
+def test_grouped_roots_with_half_products():
+    """Half-precision Clenshaw products (the pages' mixed-precision
+    Chebyshev) on the same subset: the grouped stacks put factors of side
+    128 .. 1024 on the tiled, 128-tile and 256-tile half kernels; grouped and
+    ungrouped steps agree within half-precision rounding and both match the
+    oracle's exact polynomial within the half-precision bar."""
+    import matrix_inverse_roots_amd as mir
+    shapes = synthetic.bottleneck50_shapes()
+    sel = [0, 1, 2, 3, 4, 14, 24, 40, 41, 52]
+    sh = [shapes[i] for i in sel]
+    bsz = synthetic.bottleneck50_block_sizes(shapes)
+    bs = lambda m, n: 1024 if max(m, n) >= 2048 else 256
+    grads = synthetic.gaussian_grads(5, sh, 2, 0.1)
+    kw = dict(beta2=0.999, eps=1e-12, root=mir.RootOpts(method="chebyshev", cheb_degree=16, compute="f16"),
+              graft="momentum", lr=0.1, momentum=0.9)
+    Wg, og = run(mir, sh, bs, grads, True, **kw)
+    Wu, ou = run(mir, sh, bs, grads, False, **kw)
+    for st in og.stacks + ou.stacks:
+        assert int(st.flags.sum().item()) == 0
+    orc = oracle.ShampooOracle(sh, [bsz[i] for i in sel], beta2=0.999, eps=1e-12, root="chebyshev", cheb_degree=16,
+                               graft="momentum", lr=0.1, momentum=0.9)
+    Wo = [np.zeros(s) for s in sh]
+    for g in grads:
+        orc.step(Wo, [x.astype(np.float64) for x in g])
+    eg = max(rel_fro(a, b) for a, b in zip(Wg, Wo))
+    eu = max(rel_fro(a, b) for a, b in zip(Wu, Wo))
+    d = max(rel_fro(a, b) for a, b in zip(Wg, Wu))
+    log(f"half products: grouped vs oracle {eg:.2e}, ungrouped vs oracle {eu:.2e}, grouped vs ungrouped {d:.2e}")
+    assert eg < 2e-2 and eu < 2e-2 and d < 2e-2
