@@ -141,8 +141,12 @@ typedef struct shampoo_param {
  * method/scaling: shampoo_method / shampoo_scaling.
  * compute: arithmetic of the solver chain.  SHAMPOO_F32: float32 MFMA;
  *   SHAMPOO_F16: half-precision products with float32 accumulation and
- *   float32 iterates ([DASH] "A.3 Numerical Precision"); SHAMPOO_F64:
- *   float64 MFMA (iterates float64).
+ *   float32 iterates ([DASH] "A.3 Numerical Precision"): each product's
+ *   result is rounded to float32, and a value that only later products read
+ *   is kept as its half rounding (what those products would read from the
+ *   float32 iterate), so each iterate buffer of the workspace holds a float32
+ *   and a half part (1.5x the float32 buffers); SHAMPOO_F64: float64 MFMA
+ *   (iterates float64).
  * iters: coupled-Newton iterations, or Newton-DB iterations of the first
  *   call; iters2: Newton-DB iterations of the second call (p = 4 only).
  * pi_vectors (1..32), pi_iters (>= 1): power-iteration start vectors and
@@ -268,7 +272,7 @@ shampoo_status shampoo_inverse_root_workspace(int64_t n, int32_t B, int32_t p,
  * largest Rayleigh quotient of A/||A||_F; A_s = A/s with the padding set to
  * the identity; X = solver(A_s); out = X s^(-1/p).
  * Supported: CN with p in {1, 2, 4, 8}; NDB with p in {2, 4}; Chebyshev with
- * p >= 1 (compute F32 or F64); power scaling with B <= 1024.  B must be a
+ * p >= 1; compute F32, F16 or F64; power scaling with B <= 1024.  B must be a
  * multiple of 64.  Errors: E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP. */
 shampoo_status shampoo_inverse_root(const void* in, void* out, shampoo_dtype io_dt, int64_t n,
                                     int32_t B, int32_t p, const shampoo_root_opts* opts,

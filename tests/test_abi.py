@@ -99,6 +99,13 @@ def test_workspace_queries_and_support_matrix(mir):
     o = mir.RootOpts(method="ndb", iters=28, iters2=17, scaling="power", pi_vectors=16)
     b = mir.shampoo_inverse_root_workspace(1024, 512, 4, o)
     assert b >= 1024 * 512 * 512 * 4 * 3
+    # same plan: iterate buffers of float64 are twice, of half products 1.5 times
+    # the float32 ones (a float32 and a half part); two per-matrix double
+    # arrays (scales) come first
+    head = 2 * 1024 * 8
+    b16 = mir.shampoo_inverse_root_workspace(1024, 512, 4, mir.RootOpts(**{**o.__dict__, "compute": "f16"}))
+    b64 = mir.shampoo_inverse_root_workspace(1024, 512, 4, mir.RootOpts(**{**o.__dict__, "compute": "f64"}))
+    assert 2 * (b16 - head) == 3 * (b - head) and b64 - head == 2 * (b - head)
     for opts, p, status in [
         (mir.RootOpts(method="ndb", iters=5, iters2=5), 3, mir.E_UNSUPPORTED),
         (mir.RootOpts(method="cn", iters=5), 3, mir.E_UNSUPPORTED),
