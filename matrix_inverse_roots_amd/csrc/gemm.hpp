@@ -1,6 +1,6 @@
 // Batched square products for the solver chains and the statistics: the
 // tiled kernel, the persistent 128-tile kernel and the persistent 256-tile
-// half-operand kernel (the family is described in gemm_common.hpp).
+// half-operand NN kernel (the family is described in gemm_common.hpp).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -830,71 +830,46 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// 16-bit-operand 256 x 256-tile product (n a multiple of 256; half
-// operands in the solver chains, bfloat16 available), float32 results and,
-// for half operands, their half copies:
-//     NT: C = alpha A B^T + beta D + gamma I, sym (upper tiles, mirrored) or not
-//     NN: C = alpha A B + gamma I (no D, no sym)
-//     C2 = alpha2 C + gamma2 I in both.
-// A k-stage of 64 halves carries twice the MFMA work of a float32 stage over
-// the same bytes, so half products need the larger tile to stay ahead of the
-// operand traffic: one persistent workgroup of 8 waves (128 x 64 outputs
-// each) per CU, stage loads straight into LDS one stage ahead, 128 KB of LDS
-// (as the float32 NN product).
+// Half-operand NN product with 256 x 256 tiles (n a multiple of 256), the
+// Newton-DB products of the half-precision chains:
+//     C = alpha A B + gamma I,   C2 = alpha2 C + gamma2 I,
+// float32 results and, where later products read them, half copies.  A half
+// k-stage of 64 values carries twice the matrix-core work of a float32 stage
+// over the same bytes, so these products need the larger tile to stay ahead
+// of their operand traffic: one persistent workgroup of 8 waves (128 x 64
+// outputs each) per CU, stage loads straight into LDS one stage ahead,
+// 128 KB of LDS (as the float32 NN product).  (Symmetric NT half products
+// stay on the 128-tile kernel, whose diagonal tiles waste less work.)
 //
 // The matrix-core operands are swapped: the B side feeds the A operand of
 // v_mfma_f32_16x16x32_f16 and the A side its B operand, so that lane
 // (i16, grp) of a 16 x 16 block holds C[row i16][column 4 grp + v]: four
-// consecutive columns.  A's LDS rows are permuted within each group of 64
-// (LDS row 16 b + c holds tile row 4 c + b), so that block i of a wave
-// covers rows 64 (i / 4) + 4 i16 + i % 4: four consecutive rows per lane as
-// well.  Every lane thus owns 4 x 4 sub-blocks and stores float4 runs in both
-// directions (direct output along rows, mirrored output along columns).
+// consecutive columns, stored as one float4 (or 4-half) run.
 //
 // LDS layouts (16-byte chunks, XOR-swizzled so fragment reads spread over
 // all banks):
-//   A      [256 rows][128 B of k], chunk c of LDS row r at c ^ swz(r).
-//   B (NT) [256 rows (output columns)][128 B of k], likewise, unpermuted.
-//   B (NN) [64 k-rows][256 columns], B's own k-major layout, chunk c of
-//          k-row k at c ^ bswz(k).  Fragments come from
-//          ds_read_b64_tr_b16: in each group of 16 lanes, lane 4 i + q
-//          addresses the 4 columns 4 q .. 4 q + 3 of k-row k0 + i, and lane
-//          j receives column j of k-rows k0 .. k0 + 3 (the transposed read
-//          gives lane j element j % 4 of lane 4 i + j / 4).  Two such reads
-//          give a lane the 8 consecutive k of its column.
+//   A [256 rows][128 B of k], chunk c of LDS row r at c ^ nn256_swz(r).
+//   B [64 k-rows][256 columns], B's own k-major layout, chunk c of k-row k
+//     at c ^ bswz(k).  Fragments come from ds_read_b64_tr_b16: in each group
+//     of 16 lanes, lane 4 i + q addresses the 4 columns 4 q .. 4 q + 3 of
+//     k-row k0 + i, and lane j receives column j of k-rows k0 .. k0 + 3 (the
+//     transposed read gives lane j element j % 4 of lane 4 i + j / 4).  Two
+//     such reads give a lane the 8 consecutive k of its column.
 // Lane group grp supplies k 8 grp .. 8 grp + 7 of each 32-k MFMA, as in the
-// other kernels; the per-element k order is the same.
+// other kernels; the per-element k order is the same, and so are the
+// results, bit for bit.
 // ---------------------------------------------------------------------------
 constexpr int H256_T = 256;
 constexpr int H256_BK = 64;
 constexpr int H256_TILE_BYTES = H256_T * 128;              // 32 KB per operand and stage
 constexpr int H256_LDS = 2 * 2 * H256_TILE_BYTES;           // 128 KB
 
-__device__ __forceinline__ int h256_arow(int rho) { return (rho & ~63) | (4 * (rho & 15)) | ((rho >> 4) & 3); }
 __device__ __forceinline__ int h256_bswz(int k) { return 2 * ((k & 3) | (((k >> 3) & 3) << 2)); }
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
 
-// 16-bit operand type -> matrix-core fragment (8 k per lane) and product
-template <typename E> struct H256;
-template <> struct H256<_Float16> {
-  using frag_t = halfx8;
-  static __device__ __forceinline__ floatx4 mma(const frag_t& a, const frag_t& b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-};
-template <> struct H256<__bf16> {
-  using frag_t = bf16x8;
-  static __device__ __forceinline__ floatx4 mma(const frag_t& a, const frag_t& b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <typename E, bool NN>
-__global__ __launch_bounds__(512, 1) void gemm_h256_kernel(GemmArgs g) {
-  using frag_t = typename H256<E>::frag_t;
-  constexpr bool HALF_OUT = std::is_same<E, _Float16>::value;
+__global__ __launch_bounds__(512, 1) void gemm_h256_nn_kernel(GemmArgs g) {
   constexpr int T = H256_T, BK = H256_BK, TB = H256_TILE_BYTES, SB = 2 * TB;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int per = gridDim.x >> 3;
@@ -908,54 +883,39 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   const int i16 = lane & 15, grp = lane >> 4;
-  const E* Ag = reinterpret_cast<const E*>(g.A);
-  const E* Bg = reinterpret_cast<const E*>(g.B);
+  const _Float16* Ag = reinterpret_cast<const _Float16*>(g.A);
+  const _Float16* Bg = reinterpret_cast<const _Float16*>(g.B);
 
-  // Each wave issues 4 A and 4 B loads of 1 KB per stage; lane offsets in elements.
+  // Each wave issues 4 A loads (8 rows x 128 B) and 4 B loads (2 k-rows x
+  // 512 B) of 1 KB per stage; lane offsets in elements.
   int aoff[4], boff[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
     const int I = 4 * wave + qq;
     const int row = 8 * I + (lane >> 3), pos = lane & 7;
-    aoff[qq] = h256_arow(row) * n + 8 * (pos ^ nn256_swz(row));
-    if constexpr (NN) {
-      const int k = 2 * I + (lane >> 5), p = lane & 31;
-      boff[qq] = k * n + 8 * (p ^ h256_bswz(k));
-    } else {
-      boff[qq] = row * n + 8 * (pos ^ nn256_swz(row));
-    }
+    aoff[qq] = row * n + 8 * (pos ^ nn256_swz(row));
+    const int k = 2 * I + (lane >> 5), p = lane & 31;
+    boff[qq] = k * n + 8 * (p ^ h256_bswz(k));
   }
   auto coords = [&](int it, int64_t& moff, int& ti, int& tj) {
     const int64_t w = first + (int64_t)it * per;
     const int64_t mat = w / g.tiles;
-    int t = (int)(w - mat * g.tiles);
-    if (g.sym) {
-      ti = 0;
-      int rowlen = g.nt;
-      while (t >= rowlen) {
-        t -= rowlen;
-        ++ti;
-        --rowlen;
-      }
-      tj = ti + t;
-    } else {
-      ti = t / g.nt;
-      tj = t - ti * g.nt;
-    }
+    const int t = (int)(w - mat * g.tiles);
+    ti = t / g.nt;
+    tj = t - ti * g.nt;
     moff = mat * g.stride;
   };
-  auto bbase = [&](int64_t mo, int tj) { return Bg + mo + (NN ? (int64_t)tj * T : (int64_t)tj * T * n); };
   int lt = 0, lk = 0;
   int64_t cmo;
   int cti, ctj;
   coords(0, cmo, cti, ctj);
-  const E* LA = Ag + cmo + (int64_t)cti * T * n;
-  const E* LB = bbase(cmo, ctj);
+  const _Float16* LA = Ag + cmo + (int64_t)cti * T * n;
+  const _Float16* LB = Bg + cmo + (int64_t)ctj * T;
   auto issue = [&](int buf) {
     unsigned char* sa = smem + buf * SB;
     unsigned char* sb = sa + TB;
-    const E* pa = LA + lk * BK;
-    const E* pb = NN ? LB + (int64_t)lk * BK * n : LB + lk * BK;
+    const _Float16* pa = LA + lk * BK;
+    const _Float16* pb = LB + (int64_t)lk * BK * n;
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       __builtin_amdgcn_global_load_lds((const void*)(pa + aoff[qq]), (void*)(sa + (4 * wave + qq) * 1024), 16, 0, 0);
@@ -970,20 +930,18 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_kernel(GemmArgs g) {
         int ti, tj;
         coords(lt, mo, ti, tj);
         LA = Ag + mo + (int64_t)ti * T * n;
-        LB = bbase(mo, tj);
+        LB = Bg + mo + (int64_t)tj * T;
       }
     }
   };
-  // NN: byte offsets (within a B stage) of this lane's transposed reads for
-  // column block j, first half of k-group (second half: + 4 k-rows)
+  // byte offsets (within a B stage) of this lane's transposed reads for
+  // column block j, first half of its k-group (the second half: + 4 k-rows)
   int troff[4];
-  if constexpr (NN) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = 8 * grp + (i16 >> 2);
-      const int col = wn * 64 + 16 * j + 4 * (i16 & 3);
-      troff[j] = k * (T * 2) + 16 * ((col >> 3) ^ h256_bswz(k)) + 2 * (col & 7);
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int k = 8 * grp + (i16 >> 2);
+    const int col = wn * 64 + 16 * j + 4 * (i16 & 3);
+    troff[j] = k * (T * 2) + 16 * ((col >> 3) ^ h256_bswz(k)) + 2 * (col & 7);
   }
 
   floatx4 acc[8][4];
@@ -991,8 +949,7 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_kernel(GemmArgs g) {
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const float* Dg = reinterpret_cast<const float*>(g.D);
-  const bool plain = g.alpha == 1.0 && g.gamma == 0.0 && Dg == nullptr && g.C2 == nullptr && g.C2h == nullptr;
+  const bool plain = g.alpha == 1.0 && g.gamma == 0.0 && g.C2 == nullptr && g.C2h == nullptr;
   const int total_steps = ntile * nst;
 
   issue(0);
@@ -1008,30 +965,24 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_kernel(GemmArgs g) {
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int kc = rr * 4 + grp;
-      frag_t a[8], b[4];
+      halfx8 a[8], b[4];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int m = wm * 128 + i * 16 + i16;
-        a[i] = *reinterpret_cast<const frag_t*>(sa + m * 128 + 16 * (kc ^ nn256_swz(m)));
+        a[i] = *reinterpret_cast<const halfx8*>(sa + m * 128 + 16 * (kc ^ nn256_swz(m)));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if constexpr (NN) {
-          typedef __attribute__((address_space(3))) shortx4 lds_s4;
-          const unsigned char* p0 = sb + rr * 32 * (T * 2) + troff[j];
-          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0));
-          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0 + 4 * (T * 2)));
-          const shortx8 w = shortx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          b[j] = __builtin_bit_cast(frag_t, w);
-        } else {
-          const int rho = wn * 64 + 16 * j + i16;
-          b[j] = *reinterpret_cast<const frag_t*>(sb + rho * 128 + 16 * (kc ^ nn256_swz(rho)));
-        }
+        typedef __attribute__((address_space(3))) shortx4 lds_s4;
+        const unsigned char* p0 = sb + rr * 32 * (T * 2) + troff[j];
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0));
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0 + 4 * (T * 2)));
+        b[j] = __builtin_bit_cast(halfx8, shortx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = H256<E>::mma(b[j], a[i], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j], a[i], acc[i][j], 0, 0, 0);
     }
     if (more) advance();
     wait_vmcnt0();
@@ -1040,96 +991,30 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_kernel(GemmArgs g) {
     ck = 0;
     float* C = g.C ? reinterpret_cast<float*>(g.C) + cmo : nullptr;
     float* C2 = g.C2 ? reinterpret_cast<float*>(g.C2) + cmo : nullptr;
-    _Float16* Ch = HALF_OUT && g.Ch ? reinterpret_cast<_Float16*>(g.Ch) + cmo : nullptr;
-    _Float16* C2h = HALF_OUT && g.C2h ? reinterpret_cast<_Float16*>(g.C2h) + cmo : nullptr;
-    const float* D = Dg ? Dg + cmo : nullptr;
+    _Float16* Ch = g.Ch ? reinterpret_cast<_Float16*>(g.Ch) + cmo : nullptr;
+    _Float16* C2h = g.C2h ? reinterpret_cast<_Float16*>(g.C2h) + cmo : nullptr;
     const bool two = C2 || C2h;
     const int R0 = cti * T + wm * 128, C0 = ctj * T + wn * 64;
-    const bool diag = g.sym && cti == ctj;
-    auto rowof = [&](int i) { return R0 + 64 * (i >> 2) + 4 * i16 + (i & 3); };
-    auto colof = [&](int j) { return C0 + 16 * j + 4 * grp; };
-    // One 4 x 4 sub-block per (j, h): rows 64 h + 4 i16 + b (b = 0..3, block
-    // i = 4 h + b), columns colof(j) + v.  Written out per (j, h) with
-    // compile-time indices (the accumulators must stay in registers).
-    auto sub = [&](auto jc, auto hc) {
-      constexpr int j = decltype(jc)::value, h = decltype(hc)::value;
-      floatx4 y[4], t2[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) y[b] = acc[4 * h + b][j];
-      if (!plain) {
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int R = rowof(4 * h + b), c0 = colof(j);
-          floatx4 d = floatx4{0.f, 0.f, 0.f, 0.f};
-          if (D && !(diag && R > c0 + 3)) d = *reinterpret_cast<const floatx4*>(D + (int64_t)R * n + c0);
+      for (int j = 0; j < 4; ++j) {
+        const int R = R0 + i * 16 + i16, c0 = C0 + 16 * j + 4 * grp;
+        floatx4 y = acc[i][j], z;
+        if (!plain) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const double t = epi_c(g.alpha, (double)y[b][v], D ? g.beta : 0.0, (double)d[v], R == c0 + v ? g.gamma : 0.0);
-            if (two) t2[b][v] = (float)epi_c2(g.alpha2, t, R == c0 + v ? g.gamma2 : 0.0);
-            y[b][v] = (float)t;
+            const double t = epi_c(g.alpha, (double)acc[i][j][v], 0.0, 0.0, R == c0 + v ? g.gamma : 0.0);
+            if (two) z[v] = (float)epi_c2(g.alpha2, t, R == c0 + v ? g.gamma2 : 0.0);
+            y[v] = (float)t;
           }
         }
+        const int64_t at = (int64_t)R * n + c0;
+        if (C) *reinterpret_cast<floatx4*>(C + at) = y;
+        if (Ch) store_h4(Ch + at, y);
+        if (C2) *reinterpret_cast<floatx4*>(C2 + at) = z;
+        if (C2h) store_h4(C2h + at, z);
       }
-      if (diag) {
-        // diagonal tile: the upper element (R <= Cc) is written in place and mirrored
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int R = rowof(4 * h + b), Cc = colof(j) + v;
-            if (R <= Cc) {
-              if (C) {
-                C[(int64_t)R * n + Cc] = y[b][v];
-                C[(int64_t)Cc * n + R] = y[b][v];
-              }
-              if (Ch) {
-                Ch[(int64_t)R * n + Cc] = half_of(y[b][v]);
-                Ch[(int64_t)Cc * n + R] = half_of(y[b][v]);
-              }
-              if (C2) {
-                C2[(int64_t)R * n + Cc] = t2[b][v];
-                C2[(int64_t)Cc * n + R] = t2[b][v];
-              }
-              if (C2h) {
-                C2h[(int64_t)R * n + Cc] = half_of(t2[b][v]);
-                C2h[(int64_t)Cc * n + R] = half_of(t2[b][v]);
-              }
-            }
-          }
-      } else {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int64_t at = (int64_t)rowof(4 * h + b) * n + colof(j);
-          if (C) *reinterpret_cast<floatx4*>(C + at) = y[b];
-          if (Ch) store_h4(Ch + at, y[b]);
-          if (C2) *reinterpret_cast<floatx4*>(C2 + at) = t2[b];
-          if (C2h) store_h4(C2h + at, t2[b]);
-        }
-        if (g.sym) {
-          // mirrored sub-block: rows R0 + 64 h + 4 i16 .. + 3 of column colof(j) + v
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int64_t at = (int64_t)(colof(j) + v) * n + R0 + 64 * h + 4 * i16;
-            const floatx4 m = floatx4{y[0][v], y[1][v], y[2][v], y[3][v]};
-            if (C) *reinterpret_cast<floatx4*>(C + at) = m;
-            if (Ch) store_h4(Ch + at, m);
-            if (two) {
-              const floatx4 z = floatx4{t2[0][v], t2[1][v], t2[2][v], t2[3][v]};
-              if (C2) *reinterpret_cast<floatx4*>(C2 + at) = z;
-              if (C2h) store_h4(C2h + at, z);
-            }
-          }
-        }
-      }
-    };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-    sub(I0{}, I0{}); sub(I0{}, I1{});
-    sub(I1{}, I0{}); sub(I1{}, I1{});
-    sub(I2{}, I0{}); sub(I2{}, I1{});
-    sub(I3{}, I0{}); sub(I3{}, I1{});
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll

@@ -22,9 +22,9 @@
 //   gemm_f32_nn256_kernel  (gemm_nn256.hpp) float32 NN, n a multiple of 256:
 //                          256 x 256 tiles, one persistent workgroup of 8
 //                          waves per CU.
-//   gemm_h256_kernel       (gemm.hpp) half NT or NN into float32, n a multiple
-//                          of 256: 256 x 256 tiles, one persistent workgroup
-//                          of 8 waves per CU.
+//   gemm_h256_nn_kernel    (gemm.hpp) half NN into float32, n a multiple of
+//                          256: 256 x 256 tiles, one persistent workgroup of
+//                          8 waves per CU.
 //   gemm_p128_kernel       (gemm.hpp) float32 / float64 NT or NN, and bfloat16
 //                          or half NT into float32, n a multiple of 128:
 //                          128 x 128 tiles, two persistent workgroups of 4

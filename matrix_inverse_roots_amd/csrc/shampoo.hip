@@ -198,27 +198,21 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
   constexpr bool f16_in = MM == Mma::F16 && std::is_same<TA, _Float16>::value &&
                           std::is_same<TB, _Float16>::value && std::is_same<TC, float>::value;
   if constexpr (f16_in) {
-    // NN, and NT without symmetry: 256-tile kernel.  Symmetric NT products
-    // stay on 128 tiles, whose diagonal tiles waste half as much work (the
-    // upper tiles are 36 of 64 at n = 1024 against 10 of 16).
-    const bool sym_p128 = c.sym && !c.nn && n % P128_T == 0;
-    if (n % H256_T == 0 && !c.transC && !(c.nn && (c.sym || c.D)) && !sym_p128) {
+    // NN (Newton-DB): 256-tile kernel; NT (symmetric: coupled Newton,
+    // Clenshaw): 128-tile kernel, whose diagonal tiles waste less work
+    // (36 of 64 tiles at n = 1024 against 10 of 16).
+    if (c.nn && n % H256_T == 0 && !c.sym && c.D == nullptr && !c.transC) {
       int cus = 0;
       HIP_TRY_ERR(cu_count(&cus));
       GemmArgs h = g;
-      h.sym = c.nn ? 0 : g.sym;
+      h.sym = 0;
       h.nt = n / H256_T;
-      h.tiles = h.sym ? h.nt * (h.nt + 1) / 2 : h.nt * h.nt;
+      h.tiles = h.nt * h.nt;
       h.total = batch * h.tiles;
       // persistent grid: one workgroup per CU, a multiple of the 8 XCDs
       const int64_t wgs = std::min<int64_t>(((h.total + 7) / 8) * 8, std::max(8, (cus / 8) * 8));
-      if (c.nn) {
-        HIP_TRY_ERR(large_lds_prepare<1>((const void*)gemm_h256_kernel<_Float16, true>, H256_LDS));
-        hipLaunchKernelGGL((gemm_h256_kernel<_Float16, true>), dim3((unsigned)wgs), dim3(512), H256_LDS, st, h);
-      } else {
-        HIP_TRY_ERR(large_lds_prepare<2>((const void*)gemm_h256_kernel<_Float16, false>, H256_LDS));
-        hipLaunchKernelGGL((gemm_h256_kernel<_Float16, false>), dim3((unsigned)wgs), dim3(512), H256_LDS, st, h);
-      }
+      HIP_TRY_ERR(large_lds_prepare<1>((const void*)gemm_h256_nn_kernel, H256_LDS));
+      hipLaunchKernelGGL(gemm_h256_nn_kernel, dim3((unsigned)wgs), dim3(512), H256_LDS, st, h);
       return hipGetLastError();
     }
     if (T == P128_T && !c.nn && !c.transC) {

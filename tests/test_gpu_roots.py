@@ -126,11 +126,12 @@ def test_product_kernels_bit_identical(mir, method, compute):
 
 @pytest.mark.parametrize("method", ["cn", "ndb", "chebyshev"])
 def test_half_products_large_tiles_bit_identical(mir, method):
-    """Half-precision products: a 384 x 384 stack runs on the 128-tile NT
-    kernel (Newton-DB's NN products on the tiled kernel), the same stack
-    padded to 512 (valid = 384) on the 256-tile half kernel, whose matrix
-    cores take the operands in swapped roles and whose NN operand comes
-    through transposed LDS reads; the roots agree bit for bit."""
+    """Half-precision products: Newton-DB's NN products of a 384 x 384 stack
+    run on the tiled kernel, those of the same stack padded to 512 (valid =
+    384) on the 256-tile NN kernel, whose matrix cores take the operands in
+    swapped roles and whose k-major operand comes through transposed LDS
+    reads; coupled Newton and Clenshaw run on the 128-tile kernel at both
+    sides.  The roots agree bit for bit."""
     n, v = 4, 384
     A = synthetic.spd_stack(384, n, v, 1e-2, 1.0).astype(np.float32)
     kw = dict(method=method, scaling="frobenius", iters=18, iters2=12, cheb_degree=12, eps=1e-3, compute="f16")
