@@ -115,9 +115,33 @@ hipError_t large_lds_prepare(const void* kernel, int bytes) {
   return hipSuccess;
 }
 
+// Float32 NT products: the persistent 128-tile kernel runs 2 workgroups per
+// CU, the 64-tile kernel 4.  Measured on MI355X, a round of 128-tile slots
+// costs as much as 2 / 0.88 rounds of 64-tile slots (half the work per round
+// at 88% of the efficiency), so the 64-tile kernel wins when the tiles fill
+// the 128-tile slots poorly: small batches, and tile counts just above a
+// multiple of the slots (171 blocks of 256^2: 513 tiles for 512 slots, two
+// rounds).
+bool prefer_64_tiles(int n, int64_t batch, bool sym, int cus) {
+  const int64_t nt128 = n / 128, nt64 = n / 64;
+  const int64_t t128 = batch * (sym ? nt128 * (nt128 + 1) / 2 : nt128 * nt128);
+  const int64_t t64 = batch * (sym ? nt64 * (nt64 + 1) / 2 : nt64 * nt64);
+  const int64_t s128 = (int64_t)std::max(8, (cus / 8) * 8) * 2, s64 = (int64_t)std::max(1, cus) * 4;
+  const int64_t r128 = (t128 + s128 - 1) / s128, r64 = (t64 + s64 - 1) / s64;
+  return r64 * 100 < r128 * 2 * 88;
+}
+
 template <Mma MM, typename TA, typename TB, typename TC>
 hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
-  const int T = (n % 128 == 0) ? 128 : 64;
+  int T = (n % 128 == 0) ? 128 : 64;
+  if constexpr (MM == Mma::F32 && std::is_same<TA, float>::value && std::is_same<TB, float>::value &&
+                std::is_same<TC, float>::value) {
+    if (T == 128 && !c.nn && batch > 0) {
+      int cus = 0;
+      HIP_TRY_ERR(cu_count(&cus));
+      if (prefer_64_tiles(n, batch, c.sym, cus)) T = 64;
+    }
+  }
   GemmArgs g;
   g.A = c.A;
   g.B = c.B;
