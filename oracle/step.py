@@ -18,6 +18,10 @@ Oracle; test infrastructure only.  float64 numpy throughout.
   lr = 0.1, momentum = 0.9): Delta = G, M <- mu M + D_g, W <- W - lr M.
   Adam: m <- beta1 m + (1 - beta1) G, v <- beta2 v + (1 - beta2) G^2, bias
   corrected, Delta = m_hat / (sqrt(v_hat) + eps_g), W <- W - lr D_g.
+  Options beyond the layer-wise default: block-wise grafting ([DASH] "2.
+  Preliminaries on Shampoo" speaks of block-wise Adam grafting) takes the two
+  norms over each block's slice of D and Delta; graft "none" steps along D
+  itself, W <- W - lr D.
 
 Order inside a step: statistics with G_t first, then roots, then D from G_t.
 """
@@ -75,7 +79,7 @@ class ShampooOracle:
     def __init__(self, shapes, block_sizes, beta2=1.0, eps=1e-12, p=4,
                  root="eigh", cheb_degree=16, cheb_points=None,
                  graft="sgd", lr=0.1, momentum=0.9, beta1=0.9, graft_beta2=0.999,
-                 eps_g=1e-8):
+                 eps_g=1e-8, graft_blockwise=False):
         self.shapes = [reshape_2d(s) for s in shapes]
         self.table = plan_blocks(self.shapes, block_sizes)
         self.beta2, self.eps, self.p = float(beta2), float(eps), int(p)
@@ -84,6 +88,7 @@ class ShampooOracle:
                        if root == "chebyshev" else None)
         self.graft, self.lr, self.momentum = graft, float(lr), float(momentum)
         self.beta1, self.graft_beta2, self.eps_g = float(beta1), float(graft_beta2), float(eps_g)
+        self.graft_blockwise = bool(graft_blockwise)
         self.t = 0
         self.L = []
         self.R = []
@@ -121,11 +126,22 @@ class ShampooOracle:
             D[p][rs, cs] = precondition(Lr, Gb, Rr)
         Dg = []
         for p, s in enumerate(self.shapes):
-            delta = graft_direction(self.graft, G[p], self.state[p], self.t,
-                                    beta1=self.beta1, beta2=self.graft_beta2, eps_g=self.eps_g)
-            nD = np.linalg.norm(D[p])
-            nd = np.linalg.norm(delta)
-            dg = D[p] * (nd / nD) if nD > 0 else np.zeros(s)
+            if self.graft == "none":
+                dg = D[p].copy()
+            else:
+                delta = graft_direction(self.graft, G[p], self.state[p], self.t,
+                                        beta1=self.beta1, beta2=self.graft_beta2, eps_g=self.eps_g)
+                dg = np.zeros(s)
+                if self.graft_blockwise:
+                    groups = [block_slices(self.table, b) for b in range(self.table.shape[0])
+                              if int(self.table[b, 0]) == p]
+                else:
+                    groups = [(slice(None), slice(None))]
+                for rs, cs in groups:
+                    nD = np.linalg.norm(D[p][rs, cs])
+                    nd = np.linalg.norm(delta[rs, cs])
+                    if nD > 0:
+                        dg[rs, cs] = D[p][rs, cs] * (nd / nD)
             Dg.append(dg)
             if self.graft == "momentum":
                 self.state[p]["mom"] = self.momentum * self.state[p]["mom"] + dg

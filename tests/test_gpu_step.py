@@ -377,3 +377,29 @@ def test_step_deterministic_and_infrequent_roots(mir):
     e = max(rel_fro(w.cpu().numpy(), wo) for w, wo in zip(W, Wo))
     log(f"infrequent roots: rel err {e:.2e}")
     assert e < 1e-4
+
+
+@pytest.mark.parametrize("graft,blockwise", [("sgd", True), ("momentum", True), ("adam", True), ("none", False)])
+def test_blockwise_and_no_graft_vs_oracle(mir, graft, blockwise):
+    """Block-wise grafting (norms per block: [DASH] "2. Preliminaries on
+    Shampoo" speaks of block-wise Adam grafting) and graft "none" (W <- W -
+    lr D) on ragged blocks, float64 statistics and chain, 3 steps, against
+    the oracle."""
+    import torch
+    shapes = [(300, 130), (64, 200)]
+    grads = synthetic.gaussian_grads(23, shapes, 3, 0.1)
+    lr = 0.05
+    W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    opt = mir.Shampoo(W, block_size=128, beta2=0.9, eps=1e-3, root=mir.RootOpts(method="cn", iters=30, compute="f64"),
+                      graft=graft, lr=lr, momentum=0.9, graft_blockwise=blockwise, stats_dtype=torch.float64)
+    orc = oracle.ShampooOracle(shapes, [128, 128], beta2=0.9, eps=1e-3, graft=graft, lr=lr, momentum=0.9,
+                               graft_blockwise=blockwise)
+    Wo = [np.zeros(s) for s in shapes]
+    for t in range(3):
+        opt.step([to_dev(g) for g in grads[t]])
+        orc.step(Wo, [g.astype(np.float64) for g in grads[t]])
+        torch.cuda.synchronize()
+        e = max(rel_fro(w.cpu().numpy(), wo) for w, wo in zip(W, Wo))
+        log(f"graft {graft} blockwise={blockwise} step {t + 1}: worst parameter rel err {e:.2e}")
+        assert e < 1e-5
+    assert sum(int(f.sum().item()) for f in opt.flags()) == 0

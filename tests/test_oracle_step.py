@@ -122,6 +122,43 @@ def test_momentum_graft_two_steps():
     assert np.allclose(W[0], -0.1 * Dg1[0] - 0.1 * M, atol=1e-14)
 
 
+def test_blockwise_graft_and_no_graft():
+    """Block-wise grafting: each block's D_g has the norm of its slice of
+    Delta and D's direction; with one block per parameter it is the
+    layer-wise graft.  Graft "none" steps along D itself."""
+    gen = np.random.default_rng(8)
+    shapes = [(10, 7), (5, 12)]
+    G = [gen.standard_normal(s) for s in shapes]
+    for graft in ("sgd", "adam"):
+        opt = oracle.ShampooOracle(shapes, [4, 4], beta2=0.9, eps=1e-6, graft=graft, lr=0.1, graft_blockwise=True)
+        W = [np.zeros(s) for s in shapes]
+        D, Dg = opt.step(W, G)
+        for b in range(opt.table.shape[0]):
+            p = int(opt.table[b, 0])
+            rs, cs = oracle.block_slices(opt.table, b)
+            delta = G[p] if graft == "sgd" else G[p] / (np.abs(G[p]) + 1e-8)
+            assert np.isclose(np.linalg.norm(Dg[p][rs, cs]), np.linalg.norm(delta[rs, cs]), rtol=1e-12)
+            u, v = Dg[p][rs, cs].ravel(), D[p][rs, cs].ravel()
+            assert np.isclose(u @ v, np.linalg.norm(u) * np.linalg.norm(v), rtol=1e-12)
+        for p in range(2):
+            assert np.allclose(W[p], -0.1 * Dg[p], atol=1e-15)
+    # one block per parameter: block-wise = layer-wise
+    one = [oracle.ShampooOracle(shapes, [16, 16], beta2=0.9, eps=1e-6, graft="sgd", lr=0.1, graft_blockwise=bw)
+           for bw in (False, True)]
+    Ws = [[np.zeros(s) for s in shapes] for _ in one]
+    for o, W in zip(one, Ws):
+        o.step(W, G)
+    for p in range(2):
+        np.testing.assert_array_equal(Ws[0][p], Ws[1][p])
+    # graft "none": W <- W - lr D
+    opt = oracle.ShampooOracle(shapes, [4, 4], beta2=0.9, eps=1e-6, graft="none", lr=0.1)
+    W = [np.zeros(s) for s in shapes]
+    D, Dg = opt.step(W, G)
+    for p in range(2):
+        np.testing.assert_array_equal(Dg[p], D[p])
+        assert np.allclose(W[p], -0.1 * D[p], atol=1e-15)
+
+
 def test_chebyshev_step_tends_to_shifted_root():
     # The fit approximates (x + eps)^(-1/4) on the Frobenius-scaled spectrum x of
     # L + eps I: with a large degree the step tends to
