@@ -288,6 +288,25 @@ def test_spd_stack_512_kappa_1e8_newton_db(mir):
     log(f"kappa 1e8 NDB f32: {nbad} of {n} blocks non-finite (flagged)")
 
 
+def test_chebyshev_custom_nodes_and_fit_interval(mir):
+    """Chebyshev with a node count other than 4 (d + 1) and a fit interval
+    [cheb_eps, 1 + cheb_eps] other than the regularisation: the GPU's
+    coefficients (computed by the library from the same rule) give the
+    oracle's polynomial."""
+    eps, ceps, d, N = 1e-4, 5e-3, 12, 19
+    A = synthetic.spd_stack(14, 5, 192, 1e-3, 1.0).astype(np.float32)
+    X, s, fl = run_root(mir, A, 4, method="chebyshev", cheb_degree=d, cheb_points=N, cheb_eps=ceps, eps=eps)
+    assert not fl.any()
+    c = oracle.chebyshev_coefficients(4, d, ceps, N)
+    worst = 0.0
+    for i in range(A.shape[0]):
+        Ae = A[i].astype(np.float64) + eps * np.eye(192)
+        ref = oracle.chebyshev_matrix_eigh(Ae / float(s[i]), c) * float(s[i]) ** -0.25
+        worst = max(worst, rel_fro(X[i], ref))
+    log(f"chebyshev d={d} N={N} fit eps {ceps}: worst {worst:.2e}")
+    assert worst < 1e-4
+
+
 @pytest.mark.parametrize("method", ["cn", "chebyshev", "ndb"])
 def test_half_precision_products(mir, method):
     A = synthetic.spd_stack(12, 6, 256, 1e-2, 1.0).astype(np.float32)

@@ -403,3 +403,25 @@ def test_blockwise_and_no_graft_vs_oracle(mir, graft, blockwise):
         log(f"graft {graft} blockwise={blockwise} step {t + 1}: worst parameter rel err {e:.2e}")
         assert e < 1e-5
     assert sum(int(f.sum().item()) for f in opt.flags()) == 0
+
+
+def test_whole_parameter_blocks(mir):
+    """block_size 0: each parameter is one block of side max(m, n) (ragged,
+    padded to a multiple of 64 in the stack), against the oracle's blocking
+    of the same rule; float64 statistics and chain."""
+    import torch
+    shapes = [(100, 37), (70, 90)]
+    grads = synthetic.gaussian_grads(29, shapes, 2, 0.1)
+    W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    opt = mir.Shampoo(W, block_size=0, beta2=0.9, eps=1e-3, root=mir.RootOpts(method="cn", iters=30, compute="f64"),
+                      graft="sgd", lr=0.1, stats_dtype=torch.float64)
+    orc = oracle.ShampooOracle(shapes, [0, 0], beta2=0.9, eps=1e-3, graft="sgd", lr=0.1)
+    assert orc.table.shape[0] == 2
+    Wo = [np.zeros(s) for s in shapes]
+    for t in range(2):
+        opt.step([to_dev(g) for g in grads[t]])
+        orc.step(Wo, [g.astype(np.float64) for g in grads[t]])
+    torch.cuda.synchronize()
+    e = max(rel_fro(w.cpu().numpy(), wo) for w, wo in zip(W, Wo))
+    log(f"whole-parameter blocks: worst rel err {e:.2e}")
+    assert e < 1e-5
