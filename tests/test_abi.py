@@ -197,3 +197,8 @@ def test_size_limits_are_rejected(mir):
     with pytest.raises(mir.ShampooError) as e:
         mir.shampoo_step_workspace(a)
     assert e.value.status == mir.E_INVALID
+
+
+def test_version_string(mir):
+    v = mir.version()
+    assert "gfx950" in v and v.startswith("shampoo-mi355x")

@@ -348,6 +348,27 @@ def test_zero_and_nonfinite_inputs_are_flagged(mir):
     assert fl[2] & (mir.FLAG_NONFINITE | mir.FLAG_ZERO_SCALE)
 
 
+def test_check_flags_and_product_timing(mir):
+    """shampoo_check_flags maps set flags to E_NONFINITE after a stream
+    synchronisation; the benchmark timing records one duration per batched
+    product of a call (NDB 5 + 4: 3 5 - 3 + 3 4 - 3 = 21 products)."""
+    import torch
+    A = synthetic.spd_stack(15, 3, 128, 1e-2, 1.0).astype(np.float32)
+    A[1] = 0.0
+    inp = to_dev(A)
+    out = torch.empty_like(inp)
+    flags = torch.zeros(3, dtype=torch.int32, device="cuda")
+    mir.shampoo_timing_enable(64)
+    try:
+        mir.shampoo_inverse_root(inp, out, 4, mir.RootOpts(method="ndb", iters=5, iters2=4), flags=flags)
+        ms = mir.shampoo_timing_read(64)
+    finally:
+        mir.shampoo_timing_enable(0)
+    assert len(ms) == 21 and all(m > 0 for m in ms)
+    assert not mir.shampoo_check_flags(flags)
+    assert mir.shampoo_check_flags(flags[[0, 2]].contiguous())
+
+
 def test_deterministic_and_in_place(mir):
     import torch
     A = synthetic.spd_stack(14, 8, 256, 1e-3, 1.0).astype(np.float32)
