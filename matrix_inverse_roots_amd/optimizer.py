@@ -112,7 +112,9 @@ class ShampooStack:
         self.args.params_dev = self.params_dev.data_ptr()
         self._grad_ptrs = ptrs
 
-    def step(self, grads, t, recompute, dstack=None, stream=None):
+    def prepare(self, grads, t, recompute, dstack=None):
+        """Checks the gradients and sets the step's arguments; the gradient
+        descriptors go to the device with a synchronous copy."""
         for g, w in zip(grads, self.weights):
             if g.dtype != self.grad_dtype or tuple(g.shape) != tuple(w.shape) or not g.is_contiguous():
                 raise ValueError("gradient must be a contiguous %s tensor of shape %s" % (self.grad_dtype, tuple(w.shape)))
@@ -120,7 +122,13 @@ class ShampooStack:
         self.args.t = int(t)
         self.args.recompute_roots = 1 if recompute else 0
         self.args.dstack = None if dstack is None else dstack.data_ptr()
+
+    def launch(self, stream=None):
         shampoo_step(self.args, stream)
+
+    def step(self, grads, t, recompute, dstack=None, stream=None):
+        self.prepare(grads, t, recompute, dstack)
+        self.launch(stream)
 
 
 class Shampoo:
@@ -136,6 +144,10 @@ class Shampoo:
     it; keep its previous root; recompute it with the float64 chain).
     group_factors: root each factor in a stack of its own side (rounded up
     to 64) rather than the block size, grouped by side.
+    concurrent_stacks: with more than one stack (parameters of different
+    block sizes), step each stack on its own side stream (default priority),
+    forked from and joined back to the calling stream with events, so that
+    one stack's launches fill the gaps and partly idle rounds of another's.
     Power-iteration scaling draws its start vectors once per stack from
     ``pi_seed``.
     """
@@ -143,7 +155,7 @@ class Shampoo:
     def __init__(self, params, block_size=1024, beta2=1.0, eps=1e-12, p=4, root=None, graft="sgd",
                  lr=0.1, momentum=0.9, beta1=0.9, graft_beta2=0.999, graft_eps=1e-8,
                  graft_blockwise=False, precondition_frequency=1, grad_dtype=None, stats_dtype=None,
-                 pi_seed=0, fallback="none", group_factors=True):
+                 pi_seed=0, fallback="none", group_factors=True, concurrent_stacks=True):
         import torch
         params = list(params)
         if not params:
@@ -181,14 +193,35 @@ class Shampoo:
             self.members.append(idx)
         self.frequency = int(precondition_frequency)
         self.t = 0
+        self.device = params[0].device
+        nside = min(len(self.stacks), 4) if concurrent_stacks and len(self.stacks) > 1 else 0
+        self._side = [torch.cuda.Stream(device=self.device) for _ in range(nside)]
 
     def step(self, grads, stream=None):
         """One step with gradients given per parameter (same order as params)."""
         self.t += 1
         recompute = (self.t - 1) % self.frequency == 0
         views = [g.reshape(v.shape) for g, v in zip(grads, self.views)]
+        if not self._side:
+            for st, idx in zip(self.stacks, self.members):
+                st.step([views[i] for i in idx], self.t, recompute, stream=stream)
+            return
+        torch = self.stacks[0].torch
+        cur = stream if stream is not None else torch.cuda.current_stream(self.device)
         for st, idx in zip(self.stacks, self.members):
-            st.step([views[i] for i in idx], self.t, recompute, stream=stream)
+            st.prepare([views[i] for i in idx], self.t, recompute)
+        fork = torch.cuda.Event()
+        fork.record(cur)
+        joins = []
+        for k, st in enumerate(self.stacks):
+            side = self._side[k % len(self._side)]
+            side.wait_event(fork)
+            st.launch(side)
+            done = torch.cuda.Event()
+            done.record(side)
+            joins.append(done)
+        for done in joins:
+            cur.wait_event(done)
 
     def flags(self):
         return [st.flags for st in self.stacks]
