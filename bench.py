@@ -178,19 +178,20 @@ def full_step_ms(mir, steps, warmup, compute="f32", fallback="none"):
     return float(np.median(times)), nflag
 
 
-def bottleneck_step_ms(mir, steps, warmup, group):
+def bottleneck_step_ms(mir, steps, warmup, group, cheb_eval="clenshaw"):
     """Full step on the bottleneck-50 set (53 matrices, 25.5 M parameters,
     block 1024 if max(m, n) >= 2048 else 256, float32 gradients N(0, 1e-2),
-    beta2 0.999, eps 1e-12, Chebyshev degree 16, momentum grafting), with the
-    roots grouped by factor side or computed at the block size."""
+    beta2 0.999, eps 1e-12, Chebyshev degree 16 summed by Clenshaw's
+    recurrence or by the Paterson-Stockmeyer split, momentum grafting), with
+    the roots grouped by factor side or computed at the block size."""
     import numpy as np
     import torch
     import synthetic
     shapes = synthetic.bottleneck50_shapes()
     W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
     opt = mir.Shampoo(W, block_size=lambda m, n: 1024 if max(m, n) >= 2048 else 256, beta2=0.999, eps=1e-12,
-                      root=mir.RootOpts(method="chebyshev", cheb_degree=16), graft="momentum", lr=0.1,
-                      momentum=0.9, group_factors=group)
+                      root=mir.RootOpts(method="chebyshev", cheb_degree=16, cheb_eval=cheb_eval), graft="momentum",
+                      lr=0.1, momentum=0.9, group_factors=group)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(5)
     grads = [[torch.randn(s, generator=gen, device="cuda") * 0.1 for s in shapes] for _ in range(2)]
@@ -218,9 +219,10 @@ def main():
     ap.add_argument("--blocks", type=int, default=None,
                     help="with --only roots: solve only the first this-many blocks (counter runs whose "
                          "per-dispatch cycle counts would otherwise overflow 32 bits)")
-    ap.add_argument("--only", choices=["roots", "copy", "step", "step_f16", "step5"], default=None,
+    ap.add_argument("--only", choices=["roots", "copy", "step", "step_f16", "step5", "step5_ps"], default=None,
                     help="profiling runs: only the float32 solve, only a 1 GiB copy, only the decoder-set step "
-                         "(float32 or half-precision products) or only the bottleneck-50 step")
+                         "(float32 or half-precision products) or only the bottleneck-50 step (Clenshaw or "
+                         "Paterson-Stockmeyer Chebyshev sums)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -247,8 +249,9 @@ def main():
         ms, nf = full_step_ms(mir, args.steps, max(1, args.warmup), "f16" if half else "f32", "f64" if half else "none")
         log(f"full step {ms:.2f} ms, flags {nf}")
         return
-    if args.only == "step5":
-        ms, nf = bottleneck_step_ms(mir, args.steps, args.warmup, True)
+    if args.only in ("step5", "step5_ps"):
+        ms, nf = bottleneck_step_ms(mir, args.steps, args.warmup, True,
+                                    "ps" if args.only == "step5_ps" else "clenshaw")
         log(f"bottleneck-50 step {ms:.2f} ms, flags {nf}")
         return
 
@@ -330,11 +333,13 @@ def main():
         log(f"full step, half-precision products: {ms16:.1f} ms (flagged {nf16})")
         msg, nfg = bottleneck_step_ms(mir, max(5, args.steps), 2, True)
         msu, nfu = bottleneck_step_ms(mir, max(5, args.steps), 2, False)
+        msp, nfp = bottleneck_step_ms(mir, max(5, args.steps), 2, True, "ps")
         result["full_step_bottleneck50"] = {
             "workload": "bottleneck50_53_matrices_b256_1024_chebyshev16_f32_momentum",
             "ms_grouped_by_factor_side": round(msg, 2), "ms_padded_to_block": round(msu, 2),
-            "flagged_factors": nfg + nfu}
-        log(f"bottleneck-50 step: {msg:.1f} ms grouped, {msu:.1f} ms padded")
+            "ms_grouped_paterson_stockmeyer": round(msp, 2), "flagged_factors": nfg + nfu + nfp}
+        log(f"bottleneck-50 step: {msg:.1f} ms grouped, {msu:.1f} ms padded, {msp:.1f} ms grouped with the "
+            f"Paterson-Stockmeyer sum")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp[:256].cpu().numpy())
         log(f"cpu baseline: {result['cpu_baseline']}")

@@ -26,12 +26,14 @@ STATUS_NAMES = {0: "OK", 1: "E_INVALID", 2: "E_UNSUPPORTED", 3: "E_WORKSPACE", 4
 F32, F16, BF16, F64 = 0, 1, 2, 3
 CN, NDB, CHEBYSHEV = 0, 1, 2
 SCALE_FROBENIUS, SCALE_POWER = 0, 1
+CHEB_CLENSHAW, CHEB_PS = 0, 1
 GRAFT_SGD, GRAFT_MOMENTUM, GRAFT_ADAM, GRAFT_NONE = 0, 1, 2, 3
 FLAG_NONFINITE, FLAG_ZERO_SCALE, FLAG_PI_FALLBACK, FLAG_RECOMPUTED_F64, FLAG_KEPT_PREVIOUS = 1, 2, 4, 8, 16
 FALLBACKS = {"none": 0, "keep": 1, "f64": 2}
 
 METHODS = {"cn": CN, "ndb": NDB, "chebyshev": CHEBYSHEV}
 SCALINGS = {"frobenius": SCALE_FROBENIUS, "power": SCALE_POWER}
+CHEB_EVALS = {"clenshaw": CHEB_CLENSHAW, "ps": CHEB_PS}
 DTYPES = {"f32": F32, "f16": F16, "bf16": BF16, "f64": F64}
 GRAFTS = {"sgd": GRAFT_SGD, "momentum": GRAFT_MOMENTUM, "adam": GRAFT_ADAM, "none": GRAFT_NONE}
 
@@ -64,7 +66,7 @@ class RootOptsC(ctypes.Structure):
     _fields_ = [("method", ctypes.c_int32), ("scaling", ctypes.c_int32), ("compute", ctypes.c_int32),
                 ("iters", ctypes.c_int32), ("iters2", ctypes.c_int32), ("pi_vectors", ctypes.c_int32),
                 ("pi_iters", ctypes.c_int32), ("cheb_degree", ctypes.c_int32),
-                ("cheb_points", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("cheb_points", ctypes.c_int32), ("cheb_eval", ctypes.c_int32),
                 ("eps", ctypes.c_double), ("cheb_eps", ctypes.c_double),
                 ("pi_start_dev", ctypes.c_void_p)]
 
@@ -189,6 +191,7 @@ class RootOpts:
     pi_iters: int = 10
     cheb_degree: int = 16
     cheb_points: int = 0
+    cheb_eval: str = "clenshaw"   # "clenshaw" | "ps" (Paterson-Stockmeyer split)
     eps: float = 0.0
     cheb_eps: Optional[float] = None   # defaults to eps
     pi_start: object = None       # device float32 [pi_vectors, B]
@@ -196,7 +199,7 @@ class RootOpts:
     def c(self):
         return RootOptsC(METHODS[self.method], SCALINGS[self.scaling], DTYPES[self.compute],
                          int(self.iters), int(self.iters2), int(self.pi_vectors), int(self.pi_iters),
-                         int(self.cheb_degree), int(self.cheb_points), 0, float(self.eps),
+                         int(self.cheb_degree), int(self.cheb_points), CHEB_EVALS[self.cheb_eval], float(self.eps),
                          float(self.eps if self.cheb_eps is None else self.cheb_eps),
                          None if self.pi_start is None else self.pi_start.data_ptr())
 

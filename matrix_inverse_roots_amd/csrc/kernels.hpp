@@ -8,6 +8,8 @@
 // prep          A_s = (A + eps I)/s with the padding set to the identity (or
 //               to zero for the power iteration), and up to three affine
 //               images alpha A_s + gamma I that seed the solver chains.
+// comb          linear combinations of chain values (the Chebyshev series
+//               split into baby and giant steps).
 // power_iter_fused  half-precision multi-start power iteration on the Frobenius
 //               scaled matrix, largest Rayleigh quotient ([DASH] "3. Inverse
 //               Root Methods", Power-Iteration).
@@ -321,6 +323,54 @@ __global__ __launch_bounds__(256) void prep_kernel(const TI* __restrict__ in, in
       if (outh[q])
         store_h4(outh[q] + (int64_t)rr[u] * B + cc[u], floatx4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]});
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// comb: out = sum_q w_q in_q + gamma I over whole matrices, evaluated in
+// double and rounded once (as the product epilogue).  The padding is
+// included: every chain value is a polynomial in A_s, whose padding is the
+// identity, so its padding holds that polynomial's value at 1 and a linear
+// combination keeps it so.  An input may be `out` itself (each element is
+// read before it is written, by the same thread).  Grid (chunks, n) as prep.
+// ---------------------------------------------------------------------------
+constexpr int COMB_IN = 4;
+struct CombArgs {
+  const void* in[COMB_IN];  // the first nin are used
+  double w[COMB_IN];
+  int nin;
+  double gamma;
+  void* out;   // iterate type (may be null)
+  void* outh;  // half copy (half operands only; may be null)
+};
+
+template <typename TS>
+__global__ __launch_bounds__(256) void comb_kernel(CombArgs a, int B) {
+  const int64_t b = blockIdx.y;
+  const int64_t BB = (int64_t)B * B;
+  const int cpr = B / 4;
+  const int total = B * cpr;
+  TS* out = a.out ? reinterpret_cast<TS*>(a.out) + b * BB : nullptr;
+  _Float16* outh = a.outh ? reinterpret_cast<_Float16*>(a.outh) + b * BB : nullptr;
+#pragma unroll
+  for (int u = 0; u < PREP_U; ++u) {
+    const int k = ((int)blockIdx.x * PREP_U + u) * 256 + (int)threadIdx.x;
+    if (k >= total) continue;
+    const int r = k / cpr, c = 4 * (k - r * cpr);
+    const int64_t off = b * BB + (int64_t)r * B + c;
+    double y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = (r == c + e) ? a.gamma : 0.0;
+#pragma unroll
+    for (int q = 0; q < COMB_IN; ++q) {
+      if (q >= a.nin) break;
+      double x[4];
+      Quad<TS>::load(reinterpret_cast<const TS*>(a.in[q]) + off, x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] += a.w[q] * x[e];
+    }
+    if (out) Quad<TS>::store(out + (int64_t)r * B + c, y);
+    if (outh) store_h4(outh + (int64_t)r * B + c, floatx4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]});
   }
 }
 

@@ -275,7 +275,7 @@ int64_t gemm_wgs(int n, int64_t batch, bool sym) {
 // records its peak, so the workspace query and the execution run the very
 // same plan.
 // ---------------------------------------------------------------------------
-enum OpKind { OP_PREP, OP_GEMM, OP_FINAL };
+enum OpKind { OP_PREP, OP_GEMM, OP_COMB, OP_FINAL };
 
 struct Op {
   OpKind kind;
@@ -286,6 +286,10 @@ struct Op {
   int a = -1, b = -1, d = -1, c = -1, c2 = -1;
   bool nn = false;  // full product A B in the given order (else symmetric NT)
   double alpha = 1, beta = 0, gamma = 0, alpha2 = 0, gamma2 = 0;
+  // COMB: c = sum_q w[q] in[q] + gamma I (nin <= COMB_IN; an input may be c)
+  int in[COMB_IN] = {-1, -1, -1, -1};
+  double w[COMB_IN] = {0, 0, 0, 0};
+  int nin = 0;
   // FINAL: buffer a -> out
   // Forms of each output that later ops read (NEED_F32: addend D or final
   // output; NEED_HALF: product operand); used by half-operand chains.
@@ -331,6 +335,37 @@ struct Plan {
     op.nn = nn;
     ops.push_back(op);
     ++gemms;
+  }
+  // c = sum_q w_q in_q + gamma I for any number of (buffer, weight) terms:
+  // zero weights are dropped and longer sums are chained through c.
+  void comb(int c, const std::vector<std::pair<int, double>>& terms, double gamma) {
+    // a term that reads c itself goes first, before any chained op writes c
+    std::vector<std::pair<int, double>> t;
+    for (const auto& x : terms)
+      if (x.second != 0.0 && x.first == c) t.push_back(x);
+    for (const auto& x : terms)
+      if (x.second != 0.0 && x.first != c) t.push_back(x);
+    size_t q = 0;
+    bool first = true;
+    do {
+      Op op;
+      op.kind = OP_COMB;
+      op.c = c;
+      op.gamma = first ? gamma : 0.0;
+      if (!first) {
+        op.in[0] = c;
+        op.w[0] = 1.0;
+        op.nin = 1;
+      }
+      while (q < t.size() && op.nin < COMB_IN) {
+        op.in[op.nin] = t[q].first;
+        op.w[op.nin] = t[q].second;
+        ++op.nin;
+        ++q;
+      }
+      ops.push_back(op);
+      first = false;
+    } while (q < t.size());
   }
   void final_(int x) {
     Op op;
@@ -504,6 +539,101 @@ void plan_cheb(Plan& P, const std::vector<double>& c) {
   P.final_(X);
 }
 
+// Products of the Paterson-Stockmeyer split with baby-step size m (see
+// plan_cheb_ps); a constant outer coefficient a_J saves one.
+int cheb_ps_products(int d, int m) { return (m - 1) + d / m - (d % m == 0 ? 1 : 0); }
+
+int cheb_ps_step(int d) {
+  int m = 2;
+  for (int k = 3; k <= d; ++k)
+    if (cheb_ps_products(d, k) < cheb_ps_products(d, m)) m = k;
+  return m;
+}
+
+// The Chebyshev series sum_k c_k T_k(S) by the baby-step/giant-step split of
+// Paterson and Stockmeyer in the Chebyshev basis.  With y = T_m(S):
+// T_(mj)(S) = T_j(y), and for 0 < i < m, T_(mj+i) = 2 T_j(y) T_i - T_(mj-i)
+// (from 2 T_a T_b = T_(a+b) + T_(a-b)).  Applying these from the top degree
+// down (the T_(mj-i) term moves to a lower coefficient) rewrites the series
+// as sum_(j=0..J) T_j(y) a_j(S), J = floor(d/m), a_j = sum_(i<m) al[j][i] T_i.
+// Baby steps: T_2..T_m, one product each (T_2k = 2 T_k^2 - I,
+// T_(2k+1) = 2 T_k T_(k+1) - S).  Giant steps: Clenshaw's recurrence in y
+// with matrix coefficients, B_j = a_j + 2 y B_(j+1) - B_(j+2), result
+// a_0 + y B_1 - B_2; the a_j - B_(j+2) addends are formed by comb passes.
+// Every product is of two polynomials in S, hence symmetric.
+void plan_cheb_ps(Plan& P, const std::vector<double>& c) {
+  const int d = (int)c.size() - 1;
+  const int m = cheb_ps_step(d);
+  const int J = d / m;
+  std::vector<double> cc(c);
+  std::vector<std::vector<double>> al(J + 1, std::vector<double>(m, 0.0));
+  for (int k = d; k >= 0; --k) {
+    const int j = k / m, i = k - j * m;
+    if (j == 0 || i == 0) {
+      al[j][i] += cc[k];
+    } else {
+      al[j][i] += 2.0 * cc[k];
+      cc[m * j - i] -= cc[k];
+    }
+  }
+  // baby steps: T[1] = S from the prep pass, T[k] for 2 <= k <= m
+  std::vector<int> T(m + 1, -1);
+  T[1] = P.get();
+  P.prep(T[1], 2.0, -1.0);
+  for (int k = 2; k <= m; ++k) {
+    T[k] = P.get();
+    if (k % 2 == 0) P.gemm(T[k / 2], T[k / 2], T[k], 2.0, -1.0);
+    else P.gemm(T[k / 2], T[k / 2 + 1], T[k], 2.0, 0.0, T[1], -1.0);
+  }
+  const int y = T[m];
+  // a_j - beta I - (matrix) as comb terms: al[j][0] goes to gamma
+  auto a_terms = [&](int j) {
+    std::vector<std::pair<int, double>> t;
+    for (int i = 1; i < m; ++i) t.push_back({T[i], al[j][i]});
+    return t;
+  };
+  // B_(j+1) and B_(j+2): a buffer, or (buffer -1) the scalar multiple of I in
+  // sc1 / sc2 (B_J when a_J is constant), or absent (scalar 0)
+  int B1 = -1, B2 = -1;
+  double sc1 = 0.0, sc2 = 0.0;
+  bool b1_mat = false;
+  if (d % m == 0) {
+    sc1 = al[J][0];
+  } else {
+    B1 = P.get();
+    P.comb(B1, a_terms(J), al[J][0]);
+    b1_mat = true;
+  }
+  for (int j = J - 1; j >= 0; --j) {
+    const double two = j > 0 ? 2.0 : 1.0;  // the last step is a_0 + y B_1 - B_2
+    std::vector<std::pair<int, double>> t = a_terms(j);
+    double g = al[j][0] - sc2;
+    if (B2 >= 0) t.push_back({B2, -1.0});
+    const int N = P.get();
+    if (!b1_mat) {
+      // B_(j+1) = sc1 I: no product
+      t.push_back({y, two * sc1});
+      P.comb(N, t, g);
+    } else {
+      // the addend a_j - B_(j+2) goes into B_(j+2)'s buffer when there is one
+      const int D = B2 >= 0 ? B2 : P.get();
+      P.comb(D, t, g);
+      P.gemm(y, B1, N, two, 0.0, D, 1.0);
+      P.put(D);
+      B2 = -1;
+    }
+    P.put(B2);
+    B2 = B1;
+    sc2 = b1_mat ? 0.0 : sc1;
+    B1 = N;
+    sc1 = 0.0;
+    b1_mat = true;
+  }
+  for (int k = 1; k <= m; ++k) P.put(T[k]);
+  P.put(B2);
+  P.final_(B1);
+}
+
 // Chebyshev coefficients of x^(-1/p) on [eps, 1 + eps] ([DASH] "A.1/A.2"):
 // N first-kind nodes t_j = cos(theta_j), theta_j = pi (j + 1/2) / N, mapped
 // to x_j = (t_j + 1)/2 + eps; c_k = (2/N) sum_j f(x_j) cos(k theta_j), with
@@ -554,6 +684,8 @@ shampoo_status check_root_args(int64_t n, int32_t B, int32_t p, const shampoo_ro
       const int N = o->cheb_points ? o->cheb_points : 4 * (o->cheb_degree + 1);
       if (N <= o->cheb_degree) return fail(SHAMPOO_E_INVALID, "cheb_points = %d must exceed the degree", N);
       if (!(o->cheb_eps >= 0.0) || !std::isfinite(o->cheb_eps)) return fail(SHAMPOO_E_INVALID, "cheb_eps must be finite and >= 0");
+      if (o->cheb_eval != SHAMPOO_CHEB_CLENSHAW && o->cheb_eval != SHAMPOO_CHEB_PS)
+        return fail(SHAMPOO_E_INVALID, "cheb_eval = %d (CLENSHAW or PS)", o->cheb_eval);
       break;
     }
     default:
@@ -593,6 +725,9 @@ void mark_needs(Plan& P) {
       need[op.a] |= NEED_HALF;
       need[op.b] |= NEED_HALF;
       if (op.d >= 0) need[op.d] |= NEED_F32;
+    } else if (op.kind == OP_COMB) {
+      op.need_c = take(op.c);
+      for (int q = 0; q < op.nin; ++q) need[op.in[q]] |= NEED_F32;
     } else {
       need[op.a] |= NEED_F32;
     }
@@ -606,7 +741,11 @@ Plan build_plan(int32_t p, const shampoo_root_opts* o) {
     case SHAMPOO_NDB: plan_ndb(P, p, o->iters, o->iters2); break;
     default: {
       const int N = o->cheb_points ? o->cheb_points : 4 * (o->cheb_degree + 1);
-      plan_cheb(P, cheb_coeffs(p, o->cheb_degree, N, o->cheb_eps));
+      const int d = o->cheb_degree;
+      if (o->cheb_eval == SHAMPOO_CHEB_PS && d >= 2 && cheb_ps_products(d, cheb_ps_step(d)) < d - 1)
+        plan_cheb_ps(P, cheb_coeffs(p, d, N, o->cheb_eps));
+      else
+        plan_cheb(P, cheb_coeffs(p, d, N, o->cheb_eps));
     }
   }
   mark_needs(P);
@@ -743,6 +882,19 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
       }
       HIP_TRY(timing_mark(1, st));
       timing_advance();
+    } else if (op.kind == OP_COMB) {
+      CombArgs ca{};
+      for (int q = 0; q < op.nin; ++q) {
+        ca.in[q] = buf(op.in[q]);
+        ca.w[q] = op.w[q];
+      }
+      ca.nin = op.nin;
+      ca.gamma = op.gamma;
+      if (!HALF || (op.need_c & NEED_F32)) ca.out = buf(op.c);
+      if (HALF && (op.need_c & NEED_HALF)) ca.outh = hbuf(op.c);
+      const unsigned gx = (unsigned)(((int64_t)B * B / 4 + 256 * PREP_U - 1) / (256 * PREP_U));
+      hipLaunchKernelGGL((comb_kernel<TS>), dim3(gx, (unsigned)n), dim3(256), 0, st, ca, B);
+      LAUNCH_CHECK("comb");
     } else {
       const int tps = B / 64;
       const dim3 fgrid((unsigned)(tps * tps), (unsigned)n);

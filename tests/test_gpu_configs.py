@@ -153,15 +153,16 @@ def test_decoder_set_full_size_cn_half_products(mir):
         assert e < 2e-2
 
 
-def test_bottleneck_set_full_size_chebyshev(mir):
+@pytest.mark.parametrize("cheb_eval", ["clenshaw", "ps"])
+def test_bottleneck_set_full_size_chebyshev(mir, cheb_eval):
     import torch
     shapes = synthetic.bottleneck50_shapes()
     bsz = synthetic.bottleneck50_block_sizes(shapes)
     grads = synthetic.gaussian_grads(5, shapes, 3, 0.1)
     W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
     opt = mir.Shampoo(W, block_size=lambda m, n: 1024 if max(m, n) >= 2048 else 256, beta2=0.999, eps=1e-12,
-                      root=mir.RootOpts(method="chebyshev", cheb_degree=16), graft="momentum", lr=0.1,
-                      momentum=0.9)
+                      root=mir.RootOpts(method="chebyshev", cheb_degree=16, cheb_eval=cheb_eval), graft="momentum",
+                      lr=0.1, momentum=0.9)
     sample = [0, 1, 2, 3, 14, 24, 40, 41, 48, 51, 52]
     sshapes = [shapes[i] for i in sample]
     orc = oracle.ShampooOracle(sshapes, [bsz[i] for i in sample], beta2=0.999, eps=1e-12, root="chebyshev",

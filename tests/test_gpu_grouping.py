@@ -33,7 +33,8 @@ def run(mir, shapes, bs, grads, group, **kw):
     return [w.cpu().numpy() for w in W], opt
 
 
-def test_grouped_and_ungrouped_roots_agree():
+@pytest.mark.parametrize("cheb_eval", ["clenshaw", "ps"])
+def test_grouped_and_ungrouped_roots_agree(cheb_eval):
     import matrix_inverse_roots_amd as mir
     shapes = synthetic.bottleneck50_shapes()
     sel = [0, 1, 2, 3, 4, 14, 24, 40, 41, 52]        # narrow and full factors in the 256 and 1024 stacks
@@ -41,8 +42,8 @@ def test_grouped_and_ungrouped_roots_agree():
     bsz = synthetic.bottleneck50_block_sizes(shapes)
     bs = lambda m, n: 1024 if max(m, n) >= 2048 else 256
     grads = synthetic.gaussian_grads(5, sh, 2, 0.1)
-    kw = dict(beta2=0.999, eps=1e-12, root=mir.RootOpts(method="chebyshev", cheb_degree=16), graft="momentum",
-              lr=0.1, momentum=0.9)
+    kw = dict(beta2=0.999, eps=1e-12, root=mir.RootOpts(method="chebyshev", cheb_degree=16, cheb_eval=cheb_eval),
+              graft="momentum", lr=0.1, momentum=0.9)
     Wg, og = run(mir, sh, bs, grads, True, **kw)
     Wu, ou = run(mir, sh, bs, grads, False, **kw)
     wsg = sum(st.ws.numel() for st in og.stacks)

@@ -172,6 +172,79 @@ def test_chebyshev_vs_polynomial_oracle(mir, degree):
     assert not fl.any() and worst < 1e-4
 
 
+PS_PRODUCTS = {2: 1, 3: 2, 4: 2, 5: 3, 9: 4, 16: 6, 25: 8, 40: 11, 100: 18}
+
+
+@pytest.mark.parametrize("degree", sorted(PS_PRODUCTS))
+@pytest.mark.parametrize("compute", ["f32", "f64"])
+def test_chebyshev_paterson_stockmeyer_vs_polynomial_oracle(mir, degree, compute):
+    """The baby-step/giant-step split sums the same series as Clenshaw's
+    recurrence: against the oracle's exact polynomial (float32 bar 1e-4;
+    float64 chain 1e-6, its result rounded to the float32 output), with
+    fewer products (timed one by one)."""
+    eps = 1e-3
+    A = synthetic.spd_stack(8, 6, 128, 1e-4, 1.0).astype(np.float32)
+    mir.shampoo_timing_enable(256)
+    try:
+        X, s, fl = run_root(mir, A, 4, method="chebyshev", cheb_degree=degree, eps=eps, cheb_eval="ps",
+                            compute=compute)
+        ms = mir.shampoo_timing_read(256)
+    finally:
+        mir.shampoo_timing_enable(0)
+    c = oracle.chebyshev_coefficients(4, degree, eps)
+    worst = 0.0
+    for i in range(A.shape[0]):
+        Ae = A[i].astype(np.float64) + eps * np.eye(128)
+        so = oracle.frobenius_scale(Ae)
+        ref = oracle.chebyshev_matrix_eigh(Ae / so, c) * so ** -0.25
+        worst = max(worst, rel_fro(X[i], ref))
+    log(f"chebyshev PS d={degree} {compute}: {len(ms)} products, worst {worst:.2e}")
+    assert len(ms) == PS_PRODUCTS[degree] and (degree < 4 or len(ms) < degree - 1)
+    assert not fl.any() and worst < (1e-4 if compute == "f32" else 1e-6)
+
+
+@pytest.mark.parametrize("B,valid", [(192, [192, 150, 97]), (256, [256, 200, 129]), (512, [512, 300, 64])])
+@pytest.mark.parametrize("degree", [16, 25])
+def test_chebyshev_paterson_stockmeyer_padded_and_tile_paths(mir, B, valid, degree):
+    """Ragged valid regions (identity padding) and the three product paths
+    (B = 192: 64-tiles; 256 and 512: 128-tile persistent kernel), against
+    the exact polynomial on each valid block and against Clenshaw's sum."""
+    eps = 1e-3
+    A = np.zeros((len(valid), B, B), dtype=np.float32)
+    for i, v in enumerate(valid):
+        A[i, :v, :v] = synthetic.spd_stack(30 + i, 1, v, 1e-4, 1.0)[0]
+    kw = dict(method="chebyshev", cheb_degree=degree, eps=eps)
+    X, s, fl = run_root(mir, A, 4, valid=valid, cheb_eval="ps", **kw)
+    Xc, sc, flc = run_root(mir, A, 4, valid=valid, **kw)
+    c = oracle.chebyshev_coefficients(4, degree, eps)
+    worst = worst_c = 0.0
+    for i, v in enumerate(valid):
+        Ae = A[i, :v, :v].astype(np.float64) + eps * np.eye(v)
+        so = oracle.frobenius_scale(Ae)
+        ref = oracle.chebyshev_matrix_eigh(Ae / so, c) * so ** -0.25
+        worst = max(worst, rel_fro(X[i, :v, :v], ref))
+        worst_c = max(worst_c, rel_fro(Xc[i, :v, :v], ref))
+        assert not X[i, v:, :].any() and not X[i, :, v:].any()
+    log(f"PS B={B} d={degree}: worst {worst:.2e} (Clenshaw {worst_c:.2e})")
+    assert not fl.any() and worst < 1e-4 and worst < 4 * worst_c + 1e-6
+
+
+@pytest.mark.parametrize("degree", [16, 40])
+def test_chebyshev_paterson_stockmeyer_half_products(mir, degree):
+    """Half-precision products with float32 iterates and combinations."""
+    eps = 1e-3
+    A = synthetic.spd_stack(13, 6, 256, 1e-3, 1.0).astype(np.float32)
+    X, s, fl = run_root(mir, A, 4, method="chebyshev", cheb_degree=degree, eps=eps, compute="f16", cheb_eval="ps")
+    c = oracle.chebyshev_coefficients(4, degree, eps)
+    worst = 0.0
+    for i in range(A.shape[0]):
+        Ae = A[i].astype(np.float64) + eps * np.eye(256)
+        ref = oracle.chebyshev_matrix_eigh(Ae / float(s[i]), c) * float(s[i]) ** -0.25
+        worst = max(worst, rel_fro(X[i], ref))
+    log(f"f16 PS d={degree}: worst {worst:.2e}")
+    assert not fl.any() and worst < 2e-2
+
+
 def test_scales_match_oracle(mir):
     B, n = 256, 6
     A = synthetic.spd_stack(9, n, B, 1e-4, 1.0).astype(np.float32)

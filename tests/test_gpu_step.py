@@ -324,7 +324,8 @@ def test_decoder_layer_cn_half_products_with_f64_fallback(mir):
         assert e < 2e-2
 
 
-def test_bottleneck_subset_chebyshev_momentum(mir):
+@pytest.mark.parametrize("cheb_eval", ["clenshaw", "ps"])
+def test_bottleneck_subset_chebyshev_momentum(mir, cheb_eval):
     """First 12 matrices of the 50-layer bottleneck CNN set (1x1 and 3x3
     kernels as (out, in k k)), block sizes 256 / 1024 by size, ragged edges,
     Chebyshev degree 16 in float32, SGD-momentum 0.9 grafting lr 0.1,
@@ -335,7 +336,7 @@ def test_bottleneck_subset_chebyshev_momentum(mir):
     grads = synthetic.gaussian_grads(5, shapes, 3, 0.1)
     errs = run_steps(mir, shapes, bs, grads, 3,
                      dict(beta2=0.999, eps=1e-12, graft="momentum", lr=0.1, momentum=0.9),
-                     dict(method="chebyshev", cheb_degree=16), oracle_root="chebyshev")
+                     dict(method="chebyshev", cheb_degree=16, cheb_eval=cheb_eval), oracle_root="chebyshev")
     assert all(e < 1e-4 for e, _ in errs)
 
 
