@@ -123,8 +123,64 @@ def cpu_baseline(sample_f32, budget_s=15.0):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
+    # the same roots on one thread (a few seconds)
+    one = None
+    try:
+        import threadpoolctl
+        with threadpoolctl.threadpool_limits(1):
+            t1 = time.perf_counter()
+            k = 0
+            while k < sample_f32.shape[0] and (k == 0 or time.perf_counter() - t1 < budget_s / 3):
+                oracle.inverse_root_eigh(sample_f32[k].astype(np.float64), 4)
+                k += 1
+            one = k / (time.perf_counter() - t1)
+    except Exception:
+        pass
     return {"value": done / dt, "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} of the {N_BLOCKS} blocks (512 x 512, float32 input), float64 eigh inverse 4th root each"}
+            "sample": f"{done} of the {N_BLOCKS} blocks (512 x 512, float32 input), float64 eigh inverse 4th root each",
+            "value_1thread": one, "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_full_steps():
+    """The oracle's full step (statistics, float64 eigh or exact-polynomial
+    roots, direction, grafting) on the host, for the two step workloads:
+    one whole bottleneck-50 step, and one of the 12 identical decoder layers
+    scaled by 12 (the layers are independent and equal in shape)."""
+    import numpy as np
+    import oracle
+    import synthetic
+    res = {}
+    shapes = synthetic.bottleneck50_shapes()
+    bsz = synthetic.bottleneck50_block_sizes(shapes)
+    g = synthetic.gaussian_grads(5, shapes, 1, 0.1)[0]
+    orc = oracle.ShampooOracle(shapes, bsz, beta2=0.999, eps=1e-12, root="chebyshev", cheb_degree=16,
+                               graft="momentum", lr=0.1, momentum=0.9)
+    W = [np.zeros(sh) for sh in shapes]
+    t0 = time.perf_counter()
+    orc.step(W, [x.astype(np.float64) for x in g])
+    res["bottleneck50_step_ms"] = round((time.perf_counter() - t0) * 1e3, 1)
+    res["bottleneck50_sample"] = "one whole step, 53 matrices, Chebyshev degree 16 as the exact polynomial"
+    layer = synthetic.decoder_shapes(layers=1)
+    g = synthetic.gaussian_grads(4, layer, 1, 0.02)[0]
+    orc = oracle.ShampooOracle(layer, [1024] * len(layer), beta2=0.999, eps=1e-12, root="eigh", graft="adam",
+                               lr=1e-3)
+    W = [np.zeros(sh) for sh in layer]
+    t0 = time.perf_counter()
+    orc.step(W, [x.astype(np.float64) for x in g])
+    res["decoder12_step_ms"] = round((time.perf_counter() - t0) * 1e3 * 12, 1)
+    res["decoder12_sample"] = "one decoder layer (24 factors of 1024^2, eigh roots) timed, times 12"
+    return res
 
 
 def traffic_from_profiles(kernel_tag):
@@ -176,6 +232,22 @@ def full_step_ms(mir, steps, warmup, compute="f32", fallback="none"):
         times.append((time.perf_counter() - t0) * 1e3)
     nflag = sum(int((f != 0).sum().item()) for f in opt.flags())
     return float(np.median(times)), nflag
+
+
+def bottleneck_root_gflop(mir, products):
+    """Root work per step of the bottleneck-50 set, counted as full products
+    (2 v^3 flop each): on the factors' valid sides, on their grouped sides
+    (valid side rounded up to 64) and padded to the block size."""
+    import numpy as np
+    import synthetic
+    shapes = [(s[0], int(np.prod(s[1:]))) for s in synthetic.bottleneck50_shapes()]
+    bs = [1024 if max(m, n) >= 2048 else 256 for m, n in shapes]
+    table = mir.shampoo_plan_blocks(shapes, bs)
+    v = np.concatenate([table[:, 5], table[:, 6]]).astype(np.float64)
+    blk = np.concatenate([table[:, 7], table[:, 7]]).astype(np.float64)
+    side = np.ceil(v / 64) * 64
+    f = lambda x: round(float(2.0 * products * np.sum(x ** 3)) / 1e9, 1)
+    return {"valid_region": f(v), "grouped_sides": f(side), "padded_to_block": f(blk)}
 
 
 def bottleneck_step_ms(mir, steps, warmup, group, cheb_eval="clenshaw"):
@@ -337,11 +409,15 @@ def main():
         result["full_step_bottleneck50"] = {
             "workload": "bottleneck50_53_matrices_b256_1024_chebyshev16_f32_momentum",
             "ms_grouped_by_factor_side": round(msg, 2), "ms_padded_to_block": round(msu, 2),
-            "ms_grouped_paterson_stockmeyer": round(msp, 2), "flagged_factors": nfg + nfu + nfp}
+            "ms_grouped_paterson_stockmeyer": round(msp, 2), "flagged_factors": nfg + nfu + nfp,
+            "root_gflop_per_step_clenshaw_15_products": bottleneck_root_gflop(mir, 15),
+            "root_gflop_per_step_paterson_stockmeyer_6_products": bottleneck_root_gflop(mir, 6)}
         log(f"bottleneck-50 step: {msg:.1f} ms grouped, {msu:.1f} ms padded, {msp:.1f} ms grouped with the "
             f"Paterson-Stockmeyer sum")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp[:256].cpu().numpy())
+        if not args.no_full_step:
+            result["cpu_baseline"]["full_steps"] = oracle_full_steps()
         log(f"cpu baseline: {result['cpu_baseline']}")
         result["parity_sample"] = parity_sample(A64, out[list(PARITY_SAMPLE)].cpu().numpy(),
                                                 None if args.no_variants else out64_sample)
