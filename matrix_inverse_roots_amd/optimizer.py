@@ -59,6 +59,7 @@ class ShampooStack:
         self.grad_dtype = hp["grad_dtype"]
         self.params_dev = None
         self._grad_ptrs = None
+        self._desc_cache = {}   # gradient pointers -> device descriptor table
         self.args = StepArgsC()
         a = self.args
         a.nparams = len(weights)
@@ -97,28 +98,42 @@ class ShampooStack:
         a.ws = self.ws.data_ptr()
         a.ws_bytes = self.ws.numel()
 
-    def _descriptors(self, grads):
+    def _descriptors(self, grads, stream):
+        """Device table of shampoo_param rows for these gradients.  Tables are
+        kept per set of gradient pointers (a training loop reuses a few
+        gradient buffers), so a step normally uploads nothing; a new set is
+        copied from pinned memory on ``stream``, without blocking the host."""
         torch = self.torch
         ptrs = tuple(g.data_ptr() for g in grads)
         if ptrs == self._grad_ptrs:
             return
-        rows = []
-        for i, (w, g) in enumerate(zip(self.weights, grads)):
-            rows.append([w.data_ptr(), g.data_ptr(),
-                         self.m[i].data_ptr() if self.m is not None else 0,
-                         self.v[i].data_ptr() if self.v is not None else 0,
-                         w.shape[0], w.shape[1], w.stride(0), self.first_block[i]])
-        self.params_dev = torch.tensor(rows, dtype=torch.int64).reshape(-1, 8).to(self.LR.device)
-        self.args.params_dev = self.params_dev.data_ptr()
+        dev = self._desc_cache.get(ptrs)
+        if dev is None:
+            rows = []
+            for i, (w, g) in enumerate(zip(self.weights, grads)):
+                rows.append([w.data_ptr(), g.data_ptr(),
+                             self.m[i].data_ptr() if self.m is not None else 0,
+                             self.v[i].data_ptr() if self.v is not None else 0,
+                             w.shape[0], w.shape[1], w.stride(0), self.first_block[i]])
+            host = torch.tensor(rows, dtype=torch.int64).reshape(-1, 8).pin_memory()
+            dev = torch.empty(host.shape, dtype=torch.int64, device=self.LR.device)
+            with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(self.LR.device)):
+                dev.copy_(host, non_blocking=True)
+            if len(self._desc_cache) >= 8:
+                self._desc_cache.pop(next(iter(self._desc_cache)))
+            self._desc_cache[ptrs] = dev
+        self.params_dev = dev
+        self.args.params_dev = dev.data_ptr()
         self._grad_ptrs = ptrs
 
-    def prepare(self, grads, t, recompute, dstack=None):
-        """Checks the gradients and sets the step's arguments; the gradient
-        descriptors go to the device with a synchronous copy."""
+    def prepare(self, grads, t, recompute, dstack=None, stream=None):
+        """Checks the gradients and sets the step's arguments; a descriptor
+        table not seen before is copied to the device on ``stream`` (default:
+        the current stream), ahead of the work enqueued there afterwards."""
         for g, w in zip(grads, self.weights):
             if g.dtype != self.grad_dtype or tuple(g.shape) != tuple(w.shape) or not g.is_contiguous():
                 raise ValueError("gradient must be a contiguous %s tensor of shape %s" % (self.grad_dtype, tuple(w.shape)))
-        self._descriptors(grads)
+        self._descriptors(grads, stream)
         self.args.t = int(t)
         self.args.recompute_roots = 1 if recompute else 0
         self.args.dstack = None if dstack is None else dstack.data_ptr()
@@ -127,7 +142,7 @@ class ShampooStack:
         shampoo_step(self.args, stream)
 
     def step(self, grads, t, recompute, dstack=None, stream=None):
-        self.prepare(grads, t, recompute, dstack)
+        self.prepare(grads, t, recompute, dstack, stream)
         self.launch(stream)
 
 
@@ -196,6 +211,9 @@ class Shampoo:
         self.device = params[0].device
         nside = min(len(self.stacks), 4) if concurrent_stacks and len(self.stacks) > 1 else 0
         self._side = [torch.cuda.Stream(device=self.device) for _ in range(nside)]
+        # concurrent stacks are enqueued heaviest first (block work ~ nblk B^3),
+        # so that the longest chain starts while the host enqueues the rest
+        self._order = sorted(range(len(self.stacks)), key=lambda k: -self.stacks[k].nblk * self.stacks[k].B ** 3)
 
     def step(self, grads, stream=None):
         """One step with gradients given per parameter (same order as params)."""
@@ -209,12 +227,13 @@ class Shampoo:
         torch = self.stacks[0].torch
         cur = stream if stream is not None else torch.cuda.current_stream(self.device)
         for st, idx in zip(self.stacks, self.members):
-            st.prepare([views[i] for i in idx], self.t, recompute)
+            st.prepare([views[i] for i in idx], self.t, recompute, stream=cur)
         fork = torch.cuda.Event()
         fork.record(cur)
         joins = []
-        for k, st in enumerate(self.stacks):
-            side = self._side[k % len(self._side)]
+        for j, k in enumerate(self._order):
+            st = self.stacks[k]
+            side = self._side[j % len(self._side)]
             side.wait_event(fork)
             st.launch(side)
             done = torch.cuda.Event()
