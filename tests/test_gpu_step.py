@@ -426,3 +426,41 @@ def test_whole_parameter_blocks(mir):
     e = max(rel_fro(w.cpu().numpy(), wo) for w, wo in zip(W, Wo))
     log(f"whole-parameter blocks: worst rel err {e:.2e}")
     assert e < 1e-5
+
+
+def test_reused_gradient_buffers_rewritten_in_place(mir):
+    """Gradient buffers reused across steps (two sets, alternating, refilled in
+    place) and then a set of fresh tensors every step: the device descriptor
+    tables are kept per set of gradient pointers, so reuse uploads nothing and
+    the kernels read the new contents; more than 8 distinct sets evict old
+    tables.  Against the oracle with two stacks stepped concurrently."""
+    import torch
+    shapes = [(256, 384), (64, 200), (512, 128)]
+    bs = {(256, 384): 128, (64, 200): 256, (512, 128): 256}
+    steps = 12
+    grads = synthetic.gaussian_grads(17, shapes, steps, 1.0)
+    W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    opt = mir.Shampoo(W, block_size=lambda m, n: bs[(m, n)], beta2=0.99, eps=1e-2, graft="momentum", lr=0.1,
+                      momentum=0.9, root=mir.RootOpts(method="cn", iters=30))
+    assert len(opt.stacks) == 2
+    orc = oracle.ShampooOracle(shapes, [bs[s] for s in shapes], beta2=0.99, eps=1e-2, root="eigh",
+                               graft="momentum", lr=0.1, momentum=0.9)
+    Wo = [np.zeros(s) for s in shapes]
+    bufs = [[torch.empty(s, dtype=torch.float32, device="cuda") for s in shapes] for _ in range(2)]
+    keep = []
+    for t in range(steps):
+        if t < 6:
+            dg = bufs[t % 2]
+            for d, g in zip(dg, grads[t]):
+                d.copy_(torch.from_numpy(g))
+        else:
+            dg = [to_dev(g) for g in grads[t]]
+            keep.append(dg)  # distinct pointers for every later step
+        opt.step(dg)
+        orc.step(Wo, [g.astype(np.float64) for g in grads[t]])
+        torch.cuda.synchronize()
+        e = max(rel_fro(w.cpu().numpy(), wo) for w, wo in zip(W, Wo))
+        log(f"step {t + 1}: worst parameter rel err {e:.2e}")
+        assert e < 1e-4
+    assert sum(int(f.sum().item()) for f in opt.flags()) == 0
+    assert all(len(st._desc_cache) <= 8 for st in opt.stacks)
