@@ -234,6 +234,45 @@ def full_step_ms(mir, steps, warmup, compute="f32", fallback="none"):
     return float(np.median(times)), nflag
 
 
+def single_step_ms(mir, steps, warmup):
+    """Step on one [256, 128] float32 parameter in two 128-blocks (gradients
+    N(0, 1), statistics summed (beta2 1), eps 1e-12, coupled Newton 30 in
+    float32, SGD grafting lr 0.1): a launch-bound step, timed eagerly and as
+    a graph replay.  Returns (eager ms, replay ms)."""
+    import numpy as np
+    import torch
+    W = [torch.zeros((256, 128), dtype=torch.float32, device="cuda")]
+    opt = mir.Shampoo(W, block_size=128, beta2=1.0, eps=1e-12, root=mir.RootOpts(method="cn", iters=30),
+                      graft="sgd", lr=0.1)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    grads = [[torch.randn((256, 128), generator=gen, device="cuda")] for _ in range(2)]
+    static = [torch.empty((256, 128), device="cuda")]
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        times = []
+        for i in range(warmup, warmup + steps):
+            t0 = time.perf_counter()
+            fn(i)
+            torch.cuda.synchronize()
+            times.append((time.perf_counter() - t0) * 1e3)
+        return float(np.median(times))
+
+    eager = timed(lambda i: opt.step(grads[i % 2]))
+    static[0].copy_(grads[0][0])
+    opt.step(static)
+    replay = opt.capture(static)
+
+    def rep(i):
+        replay()
+
+    graph = timed(rep)
+    return eager, graph
+
+
 def bottleneck_root_gflop(mir, products):
     """Root work per step of the bottleneck-50 set, counted as full products
     (2 v^3 flop each): on the factors' valid sides, on their grouped sides
@@ -291,7 +330,7 @@ def main():
     ap.add_argument("--blocks", type=int, default=None,
                     help="with --only roots: solve only the first this-many blocks (counter runs whose "
                          "per-dispatch cycle counts would otherwise overflow 32 bits)")
-    ap.add_argument("--only", choices=["roots", "copy", "step", "step_f16", "step5", "step5_ps"], default=None,
+    ap.add_argument("--only", choices=["roots", "copy", "step", "step_f16", "step5", "step5_ps", "step1"], default=None,
                     help="profiling runs: only the float32 solve, only a 1 GiB copy, only the decoder-set step "
                          "(float32 or half-precision products) or only the bottleneck-50 step (Clenshaw or "
                          "Paterson-Stockmeyer Chebyshev sums)")
@@ -320,6 +359,10 @@ def main():
         half = args.only == "step_f16"
         ms, nf = full_step_ms(mir, args.steps, max(1, args.warmup), "f16" if half else "f32", "f64" if half else "none")
         log(f"full step {ms:.2f} ms, flags {nf}")
+        return
+    if args.only == "step1":
+        e, gr = single_step_ms(mir, max(args.steps, 20), max(args.warmup, 3))
+        log(f"single-parameter step: {e:.3f} ms eager, {gr:.3f} ms as a graph replay")
         return
     if args.only in ("step5", "step5_ps"):
         ms, nf = bottleneck_step_ms(mir, args.steps, args.warmup, True,
@@ -414,6 +457,11 @@ def main():
             "root_gflop_per_step_paterson_stockmeyer_6_products": bottleneck_root_gflop(mir, 6)}
         log(f"bottleneck-50 step: {msg:.1f} ms grouped, {msu:.1f} ms padded, {msp:.1f} ms grouped with the "
             f"Paterson-Stockmeyer sum")
+        e1, g1 = single_step_ms(mir, 50, 5)
+        result["full_step_single"] = {
+            "workload": "one_256x128_f32_param_b128_sum_stats_cn30_f32_sgd",
+            "ms_eager": round(e1, 3), "ms_graph_replay": round(g1, 3)}
+        log(f"single-parameter step: {e1:.3f} ms eager, {g1:.3f} ms graph replay")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp[:256].cpu().numpy())
         if not args.no_full_step:

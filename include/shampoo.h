@@ -220,7 +220,10 @@ typedef struct shampoo_step_args {
                                        (L: rows, R: cols) rather than B, grouped by that side, and
                                        written back zero-padded to B: the padded work of narrow
                                        blocks disappears ([DASH] "4. Blocking Strategy" groups
-                                       blocks by shape).  The workspace then depends on it. */
+                                       blocks by shape).  The workspace then depends on it.
+                                       The groups are planned on the host from this copy; the
+                                       device orders the factors from table_dev, so the two
+                                       must hold the same rows.  Ignored for B > 8192. */
 } shampoo_step_args;
 
 /* Version string of the library. */

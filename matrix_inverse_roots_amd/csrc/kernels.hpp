@@ -576,6 +576,54 @@ __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
   if (i < n) p[i] = v;
 }
 
+// Factor order of the grouped roots: factor f < nblk is the L factor of block
+// f (side: valid rows), f >= nblk the R factor of block f - nblk (valid
+// columns), side = valid rounded up to 64.  gidx lists the factors by side,
+// ascending, and by index within a side (a stable counting sort), the order
+// the host plans its groups in.  One workgroup of 1024 threads: a histogram
+// of the sides, then for each side that occurs a pass over the factors whose
+// ballot prefix sums place them.  nbins = B / 64 <= GROUP_BINS.
+constexpr int GROUP_BINS = 128;
+__device__ __forceinline__ int factor_bin(const shampoo_block* table, int64_t nblk, int B, int64_t f) {
+  const shampoo_block t = table[f < nblk ? f : f - nblk];
+  const int v = min(max(f < nblk ? t.rows : t.cols, 1), B);
+  return (v + 63) / 64 - 1;
+}
+
+__global__ __launch_bounds__(1024) void group_order_kernel(const shampoo_block* __restrict__ table, int64_t nblk,
+                                                           int B, int32_t* __restrict__ gidx) {
+  __shared__ int hist[GROUP_BINS];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nf = 2 * nblk;
+  const int nbins = B / 64;
+  for (int i = tid; i < GROUP_BINS; i += 1024) hist[i] = 0;
+  __syncthreads();
+  for (int64_t f = tid; f < nf; f += 1024) atomicAdd(&hist[factor_bin(table, nblk, B, f)], 1);
+  __syncthreads();
+  int base = 0;
+  for (int bin = 0; bin < nbins; ++bin) {
+    if (hist[bin] == 0) continue;  // uniform: every thread reads the same count
+    for (int64_t c0 = 0; c0 < nf; c0 += 1024) {
+      const int64_t f = c0 + tid;
+      const bool pred = f < nf && factor_bin(table, nblk, B, f) == bin;
+      const unsigned long long m = __ballot(pred);
+      const int within = __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == 0) wsum[wave] = __popcll(m);
+      __syncthreads();
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        pre += w < wave ? wsum[w] : 0;
+        tot += wsum[w];
+      }
+      if (pred) gidx[base + pre + within] = (int32_t)f;
+      base += tot;
+      __syncthreads();
+    }
+  }
+}
+
 __global__ void gather_i32_kernel(const int32_t* __restrict__ src, const int32_t* __restrict__ idx, int m,
                                   int32_t* __restrict__ dst) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;

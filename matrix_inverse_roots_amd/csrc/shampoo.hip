@@ -1126,7 +1126,7 @@ shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
       side[(size_t)(a->nblk + b)] = (vc + 63) / 64 * 64;
       narrow = narrow || side[(size_t)b] < a->B || side[(size_t)(a->nblk + b)] < a->B;
     }
-    if (narrow) {
+    if (narrow && a->B <= 64 * GROUP_BINS) {
       size_t need_io = 0, need_root = 0;
       for (int sd = 64; sd <= a->B; sd += 64) {
         const int64_t start = (int64_t)L->gorder.size();
@@ -1162,7 +1162,10 @@ shampoo_status step_roots_grouped(const shampoo_step_args* a, const StepLayout& 
   int32_t* gvalid = (int32_t*)(w + L.gvalid);
   int32_t* gflags = (int32_t*)(w + L.gflags);
   const int64_t nf = (int64_t)L.gorder.size();
-  HIP_TRY(hipMemcpyAsync(gidx, L.gorder.data(), (size_t)nf * 4, hipMemcpyHostToDevice, st));
+  // the same order as L.gorder, computed on the device from the device table
+  // (no host copy: the step stays capturable in a graph)
+  hipLaunchKernelGGL(group_order_kernel, dim3(1), dim3(1024), 0, st, a->table_dev, a->nblk, B, gidx);
+  LAUNCH_CHECK("group_order");
   hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, st, gflags, nf, 0);
   LAUNCH_CHECK("fill");
   for (size_t g = 0; g < L.gside.size(); ++g) {

@@ -242,5 +242,44 @@ class Shampoo:
         for done in joins:
             cur.wait_event(done)
 
+    def capture(self, grads):
+        """Record one step on the gradient buffers ``grads`` into a graph and
+        return a function that replays it (and advances the step count).
+        Refill the buffers in place before each replay.  The graph replays
+        the launches of an eager step with the same arguments, so it needs a
+        step whose kernels do not change with the step count: SGD, momentum
+        or no grafting (Adam's bias correction depends on it), roots every
+        step, and fallback "none" or "keep" (the float64 fallback counts the
+        failed factors on the host).  Take at least one eager step first, so
+        that one-time set-up (kernel attributes, descriptor tables of these
+        buffers) happens outside the capture."""
+        torch = self.stacks[0].torch
+        if self.hp["graft"] == "adam":
+            raise ValueError("capture: Adam grafting depends on the step count")
+        if self.frequency != 1:
+            raise ValueError("capture: roots must be recomputed every step")
+        if self.hp["fallback"] == "f64":
+            raise ValueError("capture: the float64 fallback synchronises with the host")
+        if self.t < 1:
+            raise ValueError("capture: take one eager step first")
+        views = [g.reshape(v.shape) for g, v in zip(grads, self.views)]
+        # descriptor tables of these buffers, uploaded before the capture
+        cur = torch.cuda.current_stream(self.device)
+        for st, idx in zip(self.stacks, self.members):
+            st.prepare([views[i] for i in idx], self.t + 1, True, stream=cur)
+        torch.cuda.synchronize(self.device)
+        graph = torch.cuda.CUDAGraph()
+        t_saved = self.t
+        with torch.cuda.graph(graph):
+            self.step(grads)
+        self.t = t_saved
+
+        def replay():
+            self.t += 1
+            graph.replay()
+
+        replay.graph = graph
+        return replay
+
     def flags(self):
         return [st.flags for st in self.stacks]
