@@ -586,7 +586,8 @@ void plan_cheb_ps(Plan& P, const std::vector<double>& c) {
     else P.gemm(T[k / 2], T[k / 2 + 1], T[k], 2.0, 0.0, T[1], -1.0);
   }
   const int y = T[m];
-  // a_j - beta I - (matrix) as comb terms: al[j][0] goes to gamma
+  // the matrix terms of a_j (on T_1 .. T_(m-1)); its constant al[j][0] goes
+  // into the comb's multiple of I
   auto a_terms = [&](int j) {
     std::vector<std::pair<int, double>> t;
     for (int i = 1; i < m; ++i) t.push_back({T[i], al[j][i]});
