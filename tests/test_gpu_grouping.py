@@ -115,3 +115,26 @@ def test_grouped_roots_with_half_products():
     d = max(rel_fro(a, b) for a, b in zip(Wg, Wu))
     log(f"half products: grouped vs oracle {eg:.2e}, ungrouped vs oracle {eu:.2e}, grouped vs ungrouped {d:.2e}")
     assert eg < 2e-2 and eu < 2e-2 and d < 2e-2
+
+
+def test_device_factor_order_many_factors_and_sides():
+    """150 parameters of (512 + r, 512 + c), r, c in 1..511, block 512: 600
+    blocks and 1200 factors over all 8 sides 64..512 (more than one pass of
+    the ordering kernel's 1024 threads).  Grouped roots, ordered on the
+    device, give the same bits as roots at the block size."""
+    import torch
+    import matrix_inverse_roots_amd as mir
+    rng = np.random.default_rng(44)
+    shapes = [(512 + int(r), 512 + int(c)) for r, c in rng.integers(1, 512, size=(150, 2))]
+    grads = synthetic.gaussian_grads(45, shapes, 2, 1.0)
+    kw = dict(beta2=0.99, eps=1e-3, root=mir.RootOpts(method="cn", iters=12), graft="sgd", lr=0.1)
+    Wg, og = run(mir, shapes, 512, grads, True, **kw)
+    Wu, ou = run(mir, shapes, 512, grads, False, **kw)
+    sides = set()
+    for st in og.stacks:
+        t = st.table
+        sides |= {int(-(-v // 64) * 64) for v in np.concatenate([t[:, 5], t[:, 6]])}
+    nf = sum(2 * st.nblk for st in og.stacks)
+    log(f"{nf} factors, sides {sorted(sides)}")
+    assert nf > 1024 and sides == set(range(64, 513, 64))
+    assert all(np.array_equal(a, b) for a, b in zip(Wg, Wu))
