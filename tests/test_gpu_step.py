@@ -464,3 +464,44 @@ def test_reused_gradient_buffers_rewritten_in_place(mir):
         assert e < 1e-4
     assert sum(int(f.sum().item()) for f in opt.flags()) == 0
     assert all(len(st._desc_cache) <= 8 for st in opt.stacks)
+
+
+@pytest.mark.parametrize("eps", [1e-2, 0.0])
+def test_zero_gradient_parameter(mir, eps):
+    """A parameter whose gradient is zero for the first two steps: its
+    statistics stay 0, D = 0 and the grafted step is 0 (norm rule for
+    ||D|| = 0), so its weights stay exactly 0.  With eps = 0 the zero
+    statistics have no scale and their factors are flagged ZERO_SCALE with a
+    zero root; with eps > 0 (1e-2, which keeps the square Gaussian blocks of
+    the other parameter well conditioned in float32) the whole run matches
+    the oracle."""
+    import torch
+    shapes = [(128, 256), (64, 64)]
+    grads = synthetic.gaussian_grads(23, shapes, 4, 1.0)
+    for t in (0, 1):
+        grads[t][1][:] = 0.0
+    W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    opt = mir.Shampoo(W, block_size=128, beta2=0.99, eps=eps, graft="momentum", lr=0.1, momentum=0.9,
+                      root=mir.RootOpts(method="cn", iters=25))
+    orc = oracle.ShampooOracle(shapes, [128, 128], beta2=0.99, eps=eps, root="eigh", graft="momentum", lr=0.1,
+                               momentum=0.9)
+    Wo = [np.zeros(s) for s in shapes]
+    stack1 = [k for k, st in enumerate(opt.stacks) if st.B == 64][0]
+    for t in range(4):
+        opt.step([to_dev(g) for g in grads[t]])
+        torch.cuda.synchronize()
+        w1 = W[1].cpu().numpy()
+        fl = opt.flags()[stack1].cpu().numpy()
+        if t < 2:
+            assert not w1.any()
+            if eps == 0.0:
+                assert (fl & mir.FLAG_ZERO_SCALE).all()
+            else:
+                assert not fl.any()
+        if eps > 0.0:
+            orc.step(Wo, [g.astype(np.float64) for g in grads[t]])
+            e = max(rel_fro(w.cpu().numpy(), wo) if np.abs(wo).sum() else float(np.abs(w.cpu().numpy()).max())
+                    for w, wo in zip(W, Wo))
+            log(f"eps {eps} step {t + 1}: worst rel err {e:.2e}")
+            assert e < 1e-4
+    assert np.isfinite(W[0].cpu().numpy()).all() and np.isfinite(W[1].cpu().numpy()).all()
