@@ -203,6 +203,25 @@ def test_chebyshev_paterson_stockmeyer_vs_polynomial_oracle(mir, degree, compute
     assert not fl.any() and worst < (1e-4 if compute == "f32" else 1e-6)
 
 
+@pytest.mark.parametrize("p", [1, 2, 3, 8])
+@pytest.mark.parametrize("cheb_eval", ["clenshaw", "ps"])
+def test_chebyshev_other_orders(mir, p, cheb_eval):
+    """x^(-1/p) fits for p other than 4, summed both ways, against the oracle's
+    exact polynomial of the same fit (float32 bar 1e-4)."""
+    eps, degree = 1e-3, 20
+    A = synthetic.spd_stack(9, 4, 128, 1e-3, 1.0).astype(np.float32)
+    X, s, fl = run_root(mir, A, p, method="chebyshev", cheb_degree=degree, eps=eps, cheb_eval=cheb_eval)
+    c = oracle.chebyshev_coefficients(p, degree, eps)
+    worst = 0.0
+    for i in range(A.shape[0]):
+        Ae = A[i].astype(np.float64) + eps * np.eye(128)
+        so = oracle.frobenius_scale(Ae)
+        ref = oracle.chebyshev_matrix_eigh(Ae / so, c) * so ** (-1.0 / p)
+        worst = max(worst, rel_fro(X[i], ref))
+    log(f"chebyshev {cheb_eval} p={p} d={degree}: worst {worst:.2e}")
+    assert not fl.any() and worst < 1e-4
+
+
 @pytest.mark.parametrize("B,valid", [(192, [192, 150, 97]), (256, [256, 200, 129]), (512, [512, 300, 64])])
 @pytest.mark.parametrize("degree", [16, 25])
 def test_chebyshev_paterson_stockmeyer_padded_and_tile_paths(mir, B, valid, degree):
