@@ -268,6 +268,9 @@ class Shampoo:
         for st, idx in zip(self.stacks, self.members):
             st.prepare([views[i] for i in idx], self.t + 1, True, stream=cur)
         torch.cuda.synchronize(self.device)
+        # the graph reads these descriptor tables: the replay function owns
+        # them, so that later eager steps cannot evict and free them
+        tables = [st.params_dev for st in self.stacks]
         graph = torch.cuda.CUDAGraph()
         t_saved = self.t
         with torch.cuda.graph(graph):
@@ -279,6 +282,7 @@ class Shampoo:
             graph.replay()
 
         replay.graph = graph
+        replay.tables = tables
         return replay
 
     def flags(self):

@@ -81,3 +81,36 @@ def test_capture_rejects_unsupported(mir):
     opt = mir.Shampoo(W, block_size=128)
     with pytest.raises(ValueError):
         opt.capture(g)   # no eager step yet
+
+
+def test_replay_after_many_eager_gradient_sets(mir):
+    """Eager steps on more distinct gradient buffer sets than the descriptor
+    cache holds, between replays: the captured graph keeps its own
+    descriptor tables, and replays still match eager steps bit for bit."""
+    import torch
+    shapes = [(256, 128), (64, 96)]
+    grads = synthetic.gaussian_grads(31, shapes, 16, 1.0)
+    kw = dict(block_size=128, beta2=0.99, eps=1e-3, graft="momentum", lr=0.05, root=mir.RootOpts(method="cn", iters=20))
+    Wa = [torch.zeros(s, device="cuda") for s in shapes]
+    Wb = [torch.zeros(s, device="cuda") for s in shapes]
+    opt_a, opt_b = mir.Shampoo(Wa, **kw), mir.Shampoo(Wb, **kw)
+    static = [torch.empty(s, device="cuda") for s in shapes]
+    for d, g in zip(static, grads[0]):
+        d.copy_(torch.from_numpy(g))
+    opt_a.step([to_dev(g) for g in grads[0]])
+    opt_b.step(static)
+    replay = opt_b.capture(static)
+    held = []
+    for t in range(1, 16):
+        dg = [to_dev(g) for g in grads[t]]
+        held.append(dg)
+        if t % 5 == 0:
+            for d, g in zip(static, dg):
+                d.copy_(g)
+            replay()
+        else:
+            opt_b.step(dg)   # a new buffer set every step: the cache evicts
+        opt_a.step(dg)
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(Wa, Wb)), t
+    assert all(len(st._desc_cache) <= 8 for st in opt_b.stacks)
