@@ -201,11 +201,11 @@ def traffic_from_profiles(kernel_tag):
     return rec.get("bytes_per_launch")
 
 
-def full_step_ms(mir, steps, warmup, compute="f32", fallback="none"):
+def full_step_ms(mir, steps, warmup, compute="f32", fallback="none", tol=0.0):
     """Full step on the 12-layer decoder set (151 M parameters, block 1024,
     bfloat16 gradients N(0, 0.02^2), beta2 0.999, eps 1e-12, Adam grafting,
     coupled Newton 34 iterations with float32 or half-precision products,
-    roots every step).  Returns the median step time and the number of
+    or stopping at a tolerance, roots every step).  Returns the median step time and the number of
     factors flagged during the timed steps."""
     import numpy as np
     import torch
@@ -213,7 +213,7 @@ def full_step_ms(mir, steps, warmup, compute="f32", fallback="none"):
     shapes = synthetic.decoder_shapes()
     W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
     opt = mir.Shampoo(W, block_size=1024, beta2=0.999, eps=1e-12,
-                      root=mir.RootOpts(method="cn", iters=34, compute=compute),
+                      root=mir.RootOpts(method="cn", iters=34, compute=compute, tol=tol),
                       graft="adam", lr=1e-3, grad_dtype=torch.bfloat16, fallback=fallback)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(4)
@@ -330,7 +330,8 @@ def main():
     ap.add_argument("--blocks", type=int, default=None,
                     help="with --only roots: solve only the first this-many blocks (counter runs whose "
                          "per-dispatch cycle counts would otherwise overflow 32 bits)")
-    ap.add_argument("--only", choices=["roots", "copy", "step", "step_f16", "step5", "step5_ps", "step1"], default=None,
+    ap.add_argument("--only", choices=["roots", "copy", "step", "step_f16", "step_tol", "step5", "step5_ps", "step1"],
+                    default=None,
                     help="profiling runs: only the float32 solve, only a 1 GiB copy, only the decoder-set step "
                          "(float32 or half-precision products) or only the bottleneck-50 step (Clenshaw or "
                          "Paterson-Stockmeyer Chebyshev sums)")
@@ -359,6 +360,10 @@ def main():
         half = args.only == "step_f16"
         ms, nf = full_step_ms(mir, args.steps, max(1, args.warmup), "f16" if half else "f32", "f64" if half else "none")
         log(f"full step {ms:.2f} ms, flags {nf}")
+        return
+    if args.only == "step_tol":
+        ms, nf = full_step_ms(mir, args.steps, max(1, args.warmup), "f32", "none", 1e-6)
+        log(f"full step, Newton tolerance 1e-6: {ms:.2f} ms, flags {nf}")
         return
     if args.only == "step1":
         e, gr = single_step_ms(mir, max(args.steps, 20), max(args.warmup, 3))
@@ -446,6 +451,11 @@ def main():
             "workload": "decoder_12x(1024x3072,1024x1024,1024x4096,4096x1024)_bf16_adam_cn34_f16_products_f64_fallback",
             "ms": round(ms16, 2), "flagged_factors": nf16}
         log(f"full step, half-precision products: {ms16:.1f} ms (flagged {nf16})")
+        mst, nft = full_step_ms(mir, max(3, args.steps), 2, "f32", "none", 1e-6)
+        result["full_step_cn_tol"] = {
+            "workload": "decoder_12x(1024x3072,1024x1024,1024x4096,4096x1024)_bf16_adam_cn_tol1e-6_max34_f32",
+            "ms": round(mst, 2), "flagged_factors": nft}
+        log(f"full step, Newton tolerance 1e-6 (at most 34 iterations): {mst:.1f} ms (flagged {nft})")
         msg, nfg = bottleneck_step_ms(mir, max(5, args.steps), 2, True)
         msu, nfu = bottleneck_step_ms(mir, max(5, args.steps), 2, False)
         msp, nfp = bottleneck_step_ms(mir, max(5, args.steps), 2, True, "ps")

@@ -172,7 +172,13 @@ typedef struct shampoo_param {
  *   cheb_eps: the fit interval is [cheb_eps, 1 + cheb_eps]; cheb_eval:
  *   shampoo_cheb_eval, how the series is summed.
  * eps: added to the diagonal of each matrix's valid region before scaling
- *   ([DASH] "2. Preliminaries on Shampoo"; added once, see [DASH] "B.1"). */
+ *   ([DASH] "2. Preliminaries on Shampoo"; added once, see [DASH] "B.1").
+ * tol: coupled Newton only, compute F32 or F64; 0 runs exactly `iters`
+ *   iterations (the fixed count of [3DS] "Hyperparameters", fix_iter).
+ *   tol > 0 stops early once every matrix has ||M - I||_F <= tol sqrt(v)
+ *   (v its valid size), checked after each M update; X then takes its
+ *   last update and is final.  Each check synchronises the stream with
+ *   the host (one flag read); `iters` stays the upper bound. */
 typedef struct shampoo_root_opts {
   int32_t method;
   int32_t scaling;
@@ -187,6 +193,7 @@ typedef struct shampoo_root_opts {
   double eps;
   double cheb_eps;
   const float* pi_start_dev;
+  double tol;
 } shampoo_root_opts;
 
 /* Arguments of one shampoo_step over one stack (one block size B). */

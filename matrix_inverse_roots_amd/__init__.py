@@ -68,7 +68,7 @@ class RootOptsC(ctypes.Structure):
                 ("pi_iters", ctypes.c_int32), ("cheb_degree", ctypes.c_int32),
                 ("cheb_points", ctypes.c_int32), ("cheb_eval", ctypes.c_int32),
                 ("eps", ctypes.c_double), ("cheb_eps", ctypes.c_double),
-                ("pi_start_dev", ctypes.c_void_p)]
+                ("pi_start_dev", ctypes.c_void_p), ("tol", ctypes.c_double)]
 
 
 class StepArgsC(ctypes.Structure):
@@ -195,13 +195,14 @@ class RootOpts:
     eps: float = 0.0
     cheb_eps: Optional[float] = None   # defaults to eps
     pi_start: object = None       # device float32 [pi_vectors, B]
+    tol: float = 0.0              # coupled Newton: stop once ||M - I||_F <= tol sqrt(v) (0: run iters)
 
     def c(self):
         return RootOptsC(METHODS[self.method], SCALINGS[self.scaling], DTYPES[self.compute],
                          int(self.iters), int(self.iters2), int(self.pi_vectors), int(self.pi_iters),
                          int(self.cheb_degree), int(self.cheb_points), CHEB_EVALS[self.cheb_eval], float(self.eps),
                          float(self.eps if self.cheb_eps is None else self.cheb_eps),
-                         None if self.pi_start is None else self.pi_start.data_ptr())
+                         None if self.pi_start is None else self.pi_start.data_ptr(), float(self.tol))
 
 
 # ---------------------------------------------------------------------------

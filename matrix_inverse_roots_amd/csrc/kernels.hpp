@@ -375,6 +375,30 @@ __global__ __launch_bounds__(256) void comb_kernel(CombArgs a, int B) {
 }
 
 // ---------------------------------------------------------------------------
+// Convergence check of coupled Newton: one workgroup per matrix sums
+// (M - I)^2 over the valid region in a fixed order; a matrix whose
+// ||M - I||_F exceeds tol sqrt(v) (or is not finite) sets *notdone.
+// ---------------------------------------------------------------------------
+template <typename TS>
+__global__ __launch_bounds__(256) void identity_gap_kernel(const TS* __restrict__ M, int B,
+                                                           const int32_t* __restrict__ valid, double tol,
+                                                           int32_t* __restrict__ notdone) {
+  __shared__ double red[4];
+  const int64_t b = blockIdx.x;
+  const int v = valid ? min(max(valid[b], 0), B) : B;
+  const TS* A = M + b * (int64_t)B * B;
+  double acc = 0.0;
+  const int64_t total = (int64_t)v * v;
+  for (int64_t k = threadIdx.x; k < total; k += 256) {
+    const int r = (int)(k / v), c = (int)(k - (int64_t)r * v);
+    const double d = (double)A[(int64_t)r * B + c] - (r == c ? 1.0 : 0.0);
+    acc += d * d;
+  }
+  acc = block_sum256(acc, red);
+  if (threadIdx.x == 0 && v > 0 && !(acc <= tol * tol * (double)v)) atomicOr(notdone, 1);
+}
+
+// ---------------------------------------------------------------------------
 // Multi-start power iteration ([DASH] "3. Inverse Root Methods",
 // Power-Iteration), fused with its scaling and persistent over the matrices.
 // Workgroup w (4 waves) takes matrices w, w + gridDim.x, ...  For each, on

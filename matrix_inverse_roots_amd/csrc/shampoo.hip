@@ -275,7 +275,7 @@ int64_t gemm_wgs(int n, int64_t batch, bool sym) {
 // records its peak, so the workspace query and the execution run the very
 // same plan.
 // ---------------------------------------------------------------------------
-enum OpKind { OP_PREP, OP_GEMM, OP_COMB, OP_FINAL };
+enum OpKind { OP_PREP, OP_GEMM, OP_COMB, OP_CHECK, OP_FINAL };
 
 struct Op {
   OpKind kind;
@@ -286,6 +286,8 @@ struct Op {
   int a = -1, b = -1, d = -1, c = -1, c2 = -1;
   bool nn = false;  // full product A B in the given order (else symmetric NT)
   double alpha = 1, beta = 0, gamma = 0, alpha2 = 0, gamma2 = 0;
+  // CHECK: stop once every matrix of buffer a is within the tolerance of I;
+  // the next op (X T) then gives the result, which is finalised
   // COMB: c = sum_q w[q] in[q] + gamma I (nin <= COMB_IN; an input may be c)
   int in[COMB_IN] = {-1, -1, -1, -1};
   double w[COMB_IN] = {0, 0, 0, 0};
@@ -302,6 +304,7 @@ struct Plan {
   std::vector<Op> ops;
   int peak = 0;
   int gemms = 0;
+  bool checks = false;  // the chain holds convergence checks (needs their scratch)
   bool sym_out = false;  // finalize returns the symmetric part (X + X^T)/2
   std::vector<bool> used;
   int get() {
@@ -367,6 +370,13 @@ struct Plan {
       first = false;
     } while (q < t.size());
   }
+  void check(int m) {
+    Op op;
+    op.kind = OP_CHECK;
+    op.a = m;
+    ops.push_back(op);
+    checks = true;
+  }
   void final_(int x) {
     Op op;
     op.kind = OP_FINAL;
@@ -380,7 +390,7 @@ struct Plan {
 // X <- X T; M <- T^p M.  X_1 = T_1 comes from the prep pass; the last
 // iteration updates X only, and the one before it produces only the T the
 // last one needs.  T^p by repeated squaring (p a power of two).
-void plan_cn(Plan& P, int p, int iters) {
+void plan_cn(Plan& P, int p, int iters, bool check) {
   const double ap = -1.0 / p, gp = (p + 1.0) / p;
   int M = P.get(), T = P.get(), X = P.get();
   P.prep(M, 1.0, 0.0, T, ap, gp, X, ap, gp);
@@ -415,6 +425,8 @@ void plan_cn(Plan& P, int p, int iters) {
       P.put(M);
       M = Mn;
       T = Tn;
+      // converged: the next op, X T with this T, is the last update of X
+      if (check) P.check(M);
     }
   }
   P.final_(X);
@@ -670,6 +682,11 @@ shampoo_status check_root_args(int64_t n, int32_t B, int32_t p, const shampoo_ro
   if (o->compute != SHAMPOO_F32 && o->compute != SHAMPOO_F16 && o->compute != SHAMPOO_F64)
     return fail(SHAMPOO_E_UNSUPPORTED, "compute dtype %d not supported (F32, F16, F64)", o->compute);
   if (!(o->eps >= 0.0) || !std::isfinite(o->eps)) return fail(SHAMPOO_E_INVALID, "eps must be finite and >= 0");
+  if (!(o->tol >= 0.0) || !std::isfinite(o->tol)) return fail(SHAMPOO_E_INVALID, "tol must be finite and >= 0");
+  if (o->tol > 0.0 && o->method != SHAMPOO_CN)
+    return fail(SHAMPOO_E_INVALID, "tol applies to coupled Newton only");
+  if (o->tol > 0.0 && o->compute == SHAMPOO_F16)
+    return fail(SHAMPOO_E_UNSUPPORTED, "tol needs float32 or float64 iterates (compute F32 or F64)");
   switch (o->method) {
     case SHAMPOO_CN:
       if (!pow2_in(p, 8)) return fail(SHAMPOO_E_UNSUPPORTED, "coupled Newton supports p in {1, 2, 4, 8}, got %d", p);
@@ -729,6 +746,8 @@ void mark_needs(Plan& P) {
     } else if (op.kind == OP_COMB) {
       op.need_c = take(op.c);
       for (int q = 0; q < op.nin; ++q) need[op.in[q]] |= NEED_F32;
+    } else if (op.kind == OP_CHECK) {
+      need[op.a] |= NEED_F32;
     } else {
       need[op.a] |= NEED_F32;
     }
@@ -738,7 +757,7 @@ void mark_needs(Plan& P) {
 Plan build_plan(int32_t p, const shampoo_root_opts* o) {
   Plan P;
   switch (o->method) {
-    case SHAMPOO_CN: plan_cn(P, p, o->iters); break;
+    case SHAMPOO_CN: plan_cn(P, p, o->iters, o->tol > 0.0); break;
     case SHAMPOO_NDB: plan_ndb(P, p, o->iters, o->iters2); break;
     default: {
       const int N = o->cheb_points ? o->cheb_points : 4 * (o->cheb_degree + 1);
@@ -764,7 +783,7 @@ size_t root_slot_bytes(int64_t n, int32_t B, int compute) {
 
 size_t root_ws_bytes(int64_t n, int32_t B, const Plan& P, int compute) {
   const int nbuf = P.peak > 1 ? P.peak : 1;  // the power iteration borrows one buffer
-  return 2 * align_up((size_t)n * 8) + (size_t)nbuf * root_slot_bytes(n, B, compute);
+  return 2 * align_up((size_t)n * 8) + (size_t)nbuf * root_slot_bytes(n, B, compute) + (P.checks ? ALIGN : 0);
 }
 
 // Benchmark timing of the batched products (shampoo_timing_enable).
@@ -849,7 +868,7 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
     LAUNCH_CHECK("power_iter");
     sc = s;
   }
-  for (const Op& op : P.ops) {
+  auto exec = [&](const Op& op) -> shampoo_status {
     if (op.kind == OP_PREP) {
       PrepOut q[3];
       for (int i = 0; i < 3; ++i) {
@@ -912,6 +931,35 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
       }
       LAUNCH_CHECK("finalize");
     }
+      return SHAMPOO_OK;
+  };
+  // convergence checks (coupled Newton with a tolerance): a device flag after
+  // the iterate buffers, read back by the host
+  int32_t* notdone = (int32_t*)(bufbase + (size_t)(P.peak > 1 ? P.peak : 1) * bufstride);
+  for (size_t oi = 0; oi < P.ops.size(); ++oi) {
+    const Op& op = P.ops[oi];
+    if (op.kind != OP_CHECK) {
+      shampoo_status r = exec(op);
+      if (r != SHAMPOO_OK) return r;
+      continue;
+    }
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, notdone, (int64_t)1, 0);
+    LAUNCH_CHECK("fill");
+    hipLaunchKernelGGL((identity_gap_kernel<TS>), dim3((unsigned)n), dim3(256), 0, st, (const TS*)buf(op.a), B, valid,
+                       o->tol, notdone);
+    LAUNCH_CHECK("identity_gap");
+    int32_t h = 1;
+    HIP_TRY(hipMemcpyAsync(&h, notdone, 4, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    if (h != 0) continue;
+    // every matrix has converged: the next op (X T) is X's last update
+    if (oi + 1 >= P.ops.size() || P.ops[oi + 1].kind != OP_GEMM || P.ops.back().kind != OP_FINAL)
+      return fail(SHAMPOO_E_INVALID, "internal: convergence check placement");
+    shampoo_status r = exec(P.ops[oi + 1]);
+    if (r != SHAMPOO_OK) return r;
+    Op fin = P.ops.back();
+    fin.a = P.ops[oi + 1].c;
+    return exec(fin);
   }
   return SHAMPOO_OK;
 }

@@ -249,8 +249,9 @@ class Shampoo:
         the launches of an eager step with the same arguments, so it needs a
         step whose kernels do not change with the step count: SGD, momentum
         or no grafting (Adam's bias correction depends on it), roots every
-        step, and fallback "none" or "keep" (the float64 fallback counts the
-        failed factors on the host).  Take at least one eager step first, so
+        step, fallback "none" or "keep" (the float64 fallback counts the
+        failed factors on the host) and no Newton tolerance (its checks read
+        a flag on the host).  Take at least one eager step first, so
         that one-time set-up (kernel attributes, descriptor tables of these
         buffers) happens outside the capture."""
         torch = self.stacks[0].torch
@@ -260,6 +261,8 @@ class Shampoo:
             raise ValueError("capture: roots must be recomputed every step")
         if self.hp["fallback"] == "f64":
             raise ValueError("capture: the float64 fallback synchronises with the host")
+        if self.hp["root"].tol > 0:
+            raise ValueError("capture: a coupled-Newton tolerance synchronises with the host")
         if self.t < 1:
             raise ValueError("capture: take one eager step first")
         views = [g.reshape(v.shape) for g, v in zip(grads, self.views)]

@@ -146,6 +146,22 @@ def test_chebyshev_split_workspace_and_validation(mir):
     assert b"cheb_eval" in mir.lib.shampoo_last_error()
 
 
+def test_newton_tolerance_workspace_and_validation(mir):
+    """A coupled-Newton tolerance adds one 256-byte flag slot to the
+    workspace; it is rejected for other methods, for half-precision chains
+    and when negative."""
+    a = mir.shampoo_inverse_root_workspace(64, 256, 4, mir.RootOpts(method="cn", iters=20))
+    b = mir.shampoo_inverse_root_workspace(64, 256, 4, mir.RootOpts(method="cn", iters=20, tol=1e-6))
+    assert b - a == 256
+    for opts, status in [(mir.RootOpts(method="ndb", iters=5, iters2=5, tol=1e-6), mir.E_INVALID),
+                         (mir.RootOpts(method="chebyshev", tol=1e-6), mir.E_INVALID),
+                         (mir.RootOpts(method="cn", iters=5, tol=-1.0), mir.E_INVALID),
+                         (mir.RootOpts(method="cn", iters=5, tol=1e-6, compute="f16"), mir.E_UNSUPPORTED)]:
+        with pytest.raises(mir.ShampooError) as e:
+            mir.shampoo_inverse_root_workspace(4, 128, 4, opts)
+        assert e.value.status == status, opts
+
+
 def test_invalid_calls_fail_before_launch(mir):
     oc = mir.RootOpts(method="cn", iters=5).c()
     # null input

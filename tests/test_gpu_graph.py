@@ -73,7 +73,8 @@ def test_capture_rejects_unsupported(mir):
     import torch
     W = [torch.zeros((128, 128), device="cuda")]
     g = [torch.zeros((128, 128), device="cuda")]
-    for kw in (dict(graft="adam"), dict(precondition_frequency=2), dict(fallback="f64")):
+    for kw in (dict(graft="adam"), dict(precondition_frequency=2), dict(fallback="f64"),
+               dict(root=mir.RootOpts(method="cn", iters=10, tol=1e-6))):
         opt = mir.Shampoo(W, block_size=128, **kw)
         opt.step(g)
         with pytest.raises(ValueError):

@@ -291,6 +291,25 @@ def test_decoder_layer_adam_bf16_f32_chain(mir):
     assert all(e < t for e, t in errs)
 
 
+@pytest.mark.parametrize("chain", ["f32", "f64"])
+def test_decoder_layer_newton_tolerance(mir, chain):
+    """The decoder layer with coupled Newton stopping at a tolerance (1e-6
+    in float32, 1e-12 with float64 statistics and chain) instead of the
+    fixed 34 iterations: the same bars as the fixed-count runs (the float32
+    floor of each step's factors; 1e-4 in float64)."""
+    shapes = synthetic.decoder_shapes(layers=1)
+    grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
+    hp = dict(beta2=0.999, eps=1e-12, graft="adam", lr=1e-3)
+    if chain == "f32":
+        errs = run_steps(mir, shapes, 1024, grads, 3, hp, dict(method="cn", iters=34, tol=1e-6), grad_bf16=True,
+                         check_every=True, floor=True)
+    else:
+        errs = run_steps(mir, shapes, 1024, grads, 3, hp, dict(method="cn", iters=34, tol=1e-12, compute="f64"),
+                         grad_bf16=True, check_every=True, stats64=True)
+    log(f"decoder layer, Newton tolerance ({chain}), (error, tolerance) per step: {errs}")
+    assert all(e < t for e, t in errs)
+
+
 def test_decoder_layer_cn_half_products_with_f64_fallback(mir):
     """The decoder layer with coupled Newton on half-precision products (the
     pages' CN-FP16 configuration).  Step 1's factors are single square
