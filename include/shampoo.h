@@ -175,10 +175,14 @@ typedef struct shampoo_param {
  *   ([DASH] "2. Preliminaries on Shampoo"; added once, see [DASH] "B.1").
  * tol: coupled Newton only, compute F32 or F64; 0 runs exactly `iters`
  *   iterations (the fixed count of [3DS] "Hyperparameters", fix_iter).
- *   tol > 0 stops early once every matrix has ||M - I||_F <= tol sqrt(v)
- *   (v its valid size), checked after each M update; X then takes its
- *   last update and is final.  Each check synchronises the stream with
- *   the host (one flag read); `iters` stays the upper bound. */
+ *   tol > 0 stops early once every matrix has ||M - I||_F <= tol over its
+ *   valid region, which bounds every eigenvalue of M = X^p A_s within tol
+ *   of 1; checked after each M update, X then takes its last update and is
+ *   final.  Rounding keeps ||M - I||_F near u sqrt(v) .. u v (u the unit
+ *   roundoff, v the valid size), so tol must lie above that: 1e-4 suits
+ *   float32 up to v = 1024.  Each check synchronises the stream with the
+ *   host (one flag read); `iters` stays the upper bound; the float64
+ *   recomputation of shampoo_step's fallback runs the full count. */
 typedef struct shampoo_root_opts {
   int32_t method;
   int32_t scaling;

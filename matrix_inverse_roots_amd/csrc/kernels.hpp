@@ -377,7 +377,8 @@ __global__ __launch_bounds__(256) void comb_kernel(CombArgs a, int B) {
 // ---------------------------------------------------------------------------
 // Convergence check of coupled Newton: one workgroup per matrix sums
 // (M - I)^2 over the valid region in a fixed order; a matrix whose
-// ||M - I||_F exceeds tol sqrt(v) (or is not finite) sets *notdone.
+// ||M - I||_F exceeds tol (or is not finite) sets *notdone.  The Frobenius
+// norm bounds every eigenvalue's distance from 1.
 // ---------------------------------------------------------------------------
 template <typename TS>
 __global__ __launch_bounds__(256) void identity_gap_kernel(const TS* __restrict__ M, int B,
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(256) void identity_gap_kernel(const TS* __restrict_
     acc += d * d;
   }
   acc = block_sum256(acc, red);
-  if (threadIdx.x == 0 && v > 0 && !(acc <= tol * tol * (double)v)) atomicOr(notdone, 1);
+  if (threadIdx.x == 0 && v > 0 && !(acc <= tol * tol)) atomicOr(notdone, 1);
 }
 
 // ---------------------------------------------------------------------------

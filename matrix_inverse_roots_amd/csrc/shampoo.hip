@@ -686,7 +686,8 @@ shampoo_status check_root_args(int64_t n, int32_t B, int32_t p, const shampoo_ro
   if (o->tol > 0.0 && o->method != SHAMPOO_CN)
     return fail(SHAMPOO_E_INVALID, "tol applies to coupled Newton only");
   if (o->tol > 0.0 && o->compute == SHAMPOO_F16)
-    return fail(SHAMPOO_E_UNSUPPORTED, "tol needs float32 or float64 iterates (compute F32 or F64)");
+    return fail(SHAMPOO_E_UNSUPPORTED, "tol needs float32 or float64 iterates: half products leave ||M - I||_F near "
+                "half resolution times the matrix size");
   switch (o->method) {
     case SHAMPOO_CN:
       if (!pow2_in(p, 8)) return fail(SHAMPOO_E_UNSUPPORTED, "coupled Newton supports p in {1, 2, 4, 8}, got %d", p);
@@ -1291,6 +1292,7 @@ shampoo_status step_roots(const shampoo_step_args* a, const StepLayout& L, unsig
       LAUNCH_CHECK("fill");
       shampoo_root_opts o64 = a->root;
       o64.compute = SHAMPOO_F64;
+      o64.tol = 0.0;  // the recomputation runs the full iteration count
       r = inverse_root_impl(w + L.fin, w + L.fout, a->stats_dt, m, B, a->p, &o64, fvalid, nullptr, fflags,
                             w + L.froot, L.froot_bytes, st, true);
       if (r != SHAMPOO_OK) return r;

@@ -264,13 +264,13 @@ def test_chebyshev_paterson_stockmeyer_half_products(mir, degree):
     assert not fl.any() and worst < 2e-2
 
 
-@pytest.mark.parametrize("compute,lo,tol,bar", [("f32", 1e-2, 1e-6, 1e-4), ("f32", 1e-4, 1e-6, 1e-4),
-                                                 ("f64", 1e-6, 1e-12, 1e-6)])
+@pytest.mark.parametrize("compute,lo,tol,bar", [("f32", 1e-2, 1e-4, 1e-4), ("f32", 1e-4, 1e-4, 1e-4),
+                                                 ("f64", 1e-6, 1e-10, 1e-6)])
 def test_coupled_newton_tolerance(mir, compute, lo, tol, bar):
-    """Coupled Newton with a tolerance stops once every ||M - I||_F <=
-    tol sqrt(B), with fewer products than the fixed count, and the same
-    root within the bar against the oracle (float32: the stated 1e-4;
-    float64 at kappa 1e6: 1e-6, rounded to the float32 output)."""
+    """Coupled Newton with a tolerance stops once every ||M - I||_F <= tol,
+    with fewer products than the fixed count, and the same root within the
+    bar against the oracle (float32: the stated 1e-4; float64 at kappa 1e6:
+    1e-6, rounded to the float32 output)."""
     A = synthetic.spd_stack(17, 6, 128, lo, 1.0).astype(np.float32)
     iters = 40
     mir.shampoo_timing_enable(512)

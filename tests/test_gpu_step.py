@@ -203,7 +203,7 @@ def test_float64_statistics_and_direction(mir, gdt):
 
 
 def run_steps(mir, shapes, block_sizes, grads, steps, hp, root_kw, oracle_root="eigh", grad_bf16=False,
-              cheb_degree=16, check_every=True, floor=False, stats64=False):
+              cheb_degree=16, check_every=True, floor=False, stats64=False, allow_flags=False):
     """Run the GPU optimizer and the oracle side by side; return per-step
     (error, tolerance).  The tolerance is 1e-4, or with ``floor`` the larger of
     1e-4 and 4x the float32 rounding floor of the directions so far
@@ -240,7 +240,7 @@ def run_steps(mir, shapes, block_sizes, grads, steps, hp, root_kw, oracle_root="
             fl = sum(int(f.sum().item()) for f in opt.flags())
             errs.append((e, tol))
             log(f"step {t + 1}: worst parameter rel err {e:.2e} (tolerance {tol:.2e}), flags {fl}")
-            assert fl == 0
+            assert allow_flags or fl == 0
     return errs
 
 
@@ -293,18 +293,18 @@ def test_decoder_layer_adam_bf16_f32_chain(mir):
 
 @pytest.mark.parametrize("chain", ["f32", "f64"])
 def test_decoder_layer_newton_tolerance(mir, chain):
-    """The decoder layer with coupled Newton stopping at a tolerance (1e-6
-    in float32, 1e-12 with float64 statistics and chain) instead of the
-    fixed 34 iterations: the same bars as the fixed-count runs (the float32
-    floor of each step's factors; 1e-4 in float64)."""
+    """The decoder layer with coupled Newton stopping at a tolerance
+    (||M - I||_F <= 1e-4 in float32, 1e-9 with float64 statistics and chain)
+    instead of the fixed 34 iterations: the same bars as the fixed-count
+    runs (the float32 floor of each step's factors; 1e-4 in float64)."""
     shapes = synthetic.decoder_shapes(layers=1)
     grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
     hp = dict(beta2=0.999, eps=1e-12, graft="adam", lr=1e-3)
     if chain == "f32":
-        errs = run_steps(mir, shapes, 1024, grads, 3, hp, dict(method="cn", iters=34, tol=1e-6), grad_bf16=True,
+        errs = run_steps(mir, shapes, 1024, grads, 3, hp, dict(method="cn", iters=34, tol=1e-4), grad_bf16=True,
                          check_every=True, floor=True)
     else:
-        errs = run_steps(mir, shapes, 1024, grads, 3, hp, dict(method="cn", iters=34, tol=1e-12, compute="f64"),
+        errs = run_steps(mir, shapes, 1024, grads, 3, hp, dict(method="cn", iters=34, tol=1e-9, compute="f64"),
                          grad_bf16=True, check_every=True, stats64=True)
     log(f"decoder layer, Newton tolerance ({chain}), (error, tolerance) per step: {errs}")
     assert all(e < t for e, t in errs)
