@@ -375,28 +375,13 @@ __global__ __launch_bounds__(256) void comb_kernel(CombArgs a, int B) {
 }
 
 // ---------------------------------------------------------------------------
-// Convergence check of coupled Newton: one workgroup per matrix sums
-// (M - I)^2 over the valid region in a fixed order; a matrix whose
-// ||M - I||_F exceeds tol (or is not finite) sets *notdone.  The Frobenius
-// norm bounds every eigenvalue's distance from 1.
+// Convergence check of coupled Newton: ||M - I||_F per matrix comes from the
+// Frobenius kernels with eps = -1; a matrix above tol (or not finite) sets
+// *notdone.  The Frobenius norm bounds every eigenvalue's distance from 1.
 // ---------------------------------------------------------------------------
-template <typename TS>
-__global__ __launch_bounds__(256) void identity_gap_kernel(const TS* __restrict__ M, int B,
-                                                           const int32_t* __restrict__ valid, double tol,
-                                                           int32_t* __restrict__ notdone) {
-  __shared__ double red[4];
-  const int64_t b = blockIdx.x;
-  const int v = valid ? min(max(valid[b], 0), B) : B;
-  const TS* A = M + b * (int64_t)B * B;
-  double acc = 0.0;
-  const int64_t total = (int64_t)v * v;
-  for (int64_t k = threadIdx.x; k < total; k += 256) {
-    const int r = (int)(k / v), c = (int)(k - (int64_t)r * v);
-    const double d = (double)A[(int64_t)r * B + c] - (r == c ? 1.0 : 0.0);
-    acc += d * d;
-  }
-  acc = block_sum256(acc, red);
-  if (threadIdx.x == 0 && v > 0 && !(acc <= tol * tol)) atomicOr(notdone, 1);
+__global__ void above_tol_kernel(const double* __restrict__ norms, int64_t n, double tol, int32_t* __restrict__ notdone) {
+  const int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (b < n && !(norms[b] <= tol)) atomicOr(notdone, 1);
 }
 
 // ---------------------------------------------------------------------------

@@ -782,9 +782,17 @@ size_t root_slot_bytes(int64_t n, int32_t B, int compute) {
   return root_slot_f32_bytes(n, B, compute) + (compute == SHAMPOO_F16 ? align_up((size_t)n * B * B * 2) : 0);
 }
 
+// Frobenius partial sums per matrix: about 4096 workgroups in all, at most 32
+// per matrix.
+int frob_parts(int64_t n) { return (int)std::max<int64_t>(1, std::min<int64_t>(32, (4096 + n - 1) / n)); }
+
+// Convergence checks: partial sums, per-matrix norms and the flag, after the
+// iterate buffers.
+size_t check_bytes(int64_t n) { return align_up((size_t)frob_parts(n) * n * 8) + align_up((size_t)n * 8) + ALIGN; }
+
 size_t root_ws_bytes(int64_t n, int32_t B, const Plan& P, int compute) {
   const int nbuf = P.peak > 1 ? P.peak : 1;  // the power iteration borrows one buffer
-  return 2 * align_up((size_t)n * 8) + (size_t)nbuf * root_slot_bytes(n, B, compute) + (P.checks ? ALIGN : 0);
+  return 2 * align_up((size_t)n * 8) + (size_t)nbuf * root_slot_bytes(n, B, compute) + (P.checks ? check_bytes(n) : 0);
 }
 
 // Benchmark timing of the batched products (shampoo_timing_enable).
@@ -838,7 +846,7 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
   // Frobenius norms: P workgroups per matrix (about 4096 in all, two full
   // rounds of the CUs), partial sums in the first iterate buffer, which prep
   // overwrites afterwards.
-  const int parts = (int)std::max<int64_t>(1, std::min<int64_t>(32, (4096 + n - 1) / n));
+  const int parts = frob_parts(n);
   hipLaunchKernelGGL((frob_partial_kernel<TI>), dim3((unsigned)parts, (unsigned)n), dim3(256), 0, st, (const TI*)in,
                      B, valid, o->eps, parts, (double*)buf(0));
   LAUNCH_CHECK("frob_partial");
@@ -936,7 +944,10 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
   };
   // convergence checks (coupled Newton with a tolerance): a device flag after
   // the iterate buffers, read back by the host
-  int32_t* notdone = (int32_t*)(bufbase + (size_t)(P.peak > 1 ? P.peak : 1) * bufstride);
+  unsigned char* chk = bufbase + (size_t)(P.peak > 1 ? P.peak : 1) * bufstride;
+  double* cpart = (double*)chk;
+  double* cnorm = (double*)(chk + align_up((size_t)parts * n * 8));
+  int32_t* notdone = (int32_t*)(chk + align_up((size_t)parts * n * 8) + align_up((size_t)n * 8));
   for (size_t oi = 0; oi < P.ops.size(); ++oi) {
     const Op& op = P.ops[oi];
     if (op.kind != OP_CHECK) {
@@ -944,11 +955,18 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
       if (r != SHAMPOO_OK) return r;
       continue;
     }
+    // ||M - I||_F: the Frobenius sums of M + eps I with eps = -1
+    hipLaunchKernelGGL((frob_partial_kernel<TS>), dim3((unsigned)parts, (unsigned)n), dim3(256), 0, st,
+                       (const TS*)buf(op.a), B, valid, -1.0, parts, cpart);
+    LAUNCH_CHECK("frob_partial");
+    hipLaunchKernelGGL(frob_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const double*)cpart,
+                       parts, n, cnorm);
+    LAUNCH_CHECK("frob_finish");
     hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, notdone, (int64_t)1, 0);
     LAUNCH_CHECK("fill");
-    hipLaunchKernelGGL((identity_gap_kernel<TS>), dim3((unsigned)n), dim3(256), 0, st, (const TS*)buf(op.a), B, valid,
+    hipLaunchKernelGGL(above_tol_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const double*)cnorm, n,
                        o->tol, notdone);
-    LAUNCH_CHECK("identity_gap");
+    LAUNCH_CHECK("above_tol");
     int32_t h = 1;
     HIP_TRY(hipMemcpyAsync(&h, notdone, 4, hipMemcpyDeviceToHost, st));
     HIP_TRY(hipStreamSynchronize(st));
