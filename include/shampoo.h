@@ -181,8 +181,9 @@ typedef struct shampoo_param {
  *   final.  Rounding keeps ||M - I||_F near u sqrt(v) .. u v (u the unit
  *   roundoff, v the valid size), so tol must lie above that: 1e-4 suits
  *   float32 up to v = 1024.  Each check synchronises the stream with the
- *   host (one flag read); `iters` stays the upper bound; the float64
- *   recomputation of shampoo_step's fallback runs the full count. */
+ *   host (one flag read), so work queued after it on other streams is not
+ *   enqueued until the solve ends; `iters` stays the upper bound; the
+ *   float64 recomputation of shampoo_step's fallback runs the full count. */
 typedef struct shampoo_root_opts {
   int32_t method;
   int32_t scaling;

@@ -942,8 +942,9 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
     }
       return SHAMPOO_OK;
   };
-  // convergence checks (coupled Newton with a tolerance): a device flag after
-  // the iterate buffers, read back by the host
+  // convergence checks (coupled Newton with a tolerance): scratch after the
+  // iterate buffers for the Frobenius partial sums, the per-matrix norms and
+  // a flag that the host reads back
   unsigned char* chk = bufbase + (size_t)(P.peak > 1 ? P.peak : 1) * bufstride;
   double* cpart = (double*)chk;
   double* cnorm = (double*)(chk + align_up((size_t)parts * n * 8));
