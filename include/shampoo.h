@@ -173,12 +173,14 @@ typedef struct shampoo_param {
  *   shampoo_cheb_eval, how the series is summed.
  * eps: added to the diagonal of each matrix's valid region before scaling
  *   ([DASH] "2. Preliminaries on Shampoo"; added once, see [DASH] "B.1").
- * tol: coupled Newton only, compute F32 or F64; 0 runs exactly `iters`
- *   iterations (the fixed count of [3DS] "Hyperparameters", fix_iter).
- *   tol > 0 stops early once every matrix has ||M - I||_F <= tol over its
- *   valid region, which bounds every eigenvalue of M = X^p A_s within tol
- *   of 1; checked after each M update, X then takes its last update and is
- *   final.  Rounding keeps ||M - I||_F near u sqrt(v) .. u v (u the unit
+ * tol: the Newton iterations (CN, NDB), compute F32 or F64; 0 runs
+ *   exactly `iters` (and `iters2`) iterations (the fixed count of [3DS]
+ *   "Hyperparameters", fix_iter).  tol > 0 stops early once every matrix is
+ *   within tol over its valid region: coupled Newton ||M - I||_F <= tol
+ *   (every eigenvalue of M = X^p A_s within tol of 1), checked after each M
+ *   update, X then taking its last update; Newton-DB ||ZY - I||_F <= tol in
+ *   each call, checked after each T product, the call then ending with that
+ *   iteration as its last (the chain is planned again with that count).  Rounding keeps ||M - I||_F near u sqrt(v) .. u v (u the unit
  *   roundoff, v the valid size), so tol must lie above that: 1e-4 suits
  *   float32 up to v = 1024.  Each check synchronises the stream with the
  *   host (one flag read), so work queued after it on other streams is not

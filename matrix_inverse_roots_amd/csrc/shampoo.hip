@@ -286,8 +286,11 @@ struct Op {
   int a = -1, b = -1, d = -1, c = -1, c2 = -1;
   bool nn = false;  // full product A B in the given order (else symmetric NT)
   double alpha = 1, beta = 0, gamma = 0, alpha2 = 0, gamma2 = 0;
-  // CHECK: stop once every matrix of buffer a is within the tolerance of I;
-  // the next op (X T) then gives the result, which is finalised
+  // CHECK: stop once every matrix of buffer a is within alpha * tol of I.
+  // Coupled Newton (b = 0): the next op (X T) then gives the result, which
+  // is finalised.  Newton-DB (b = call 1 or 2, c = iteration): the chain is
+  // planned again with that call ending at this iteration, and runs on from
+  // the same point of the new plan.
   // COMB: c = sum_q w[q] in[q] + gamma I (nin <= COMB_IN; an input may be c)
   int in[COMB_IN] = {-1, -1, -1, -1};
   double w[COMB_IN] = {0, 0, 0, 0};
@@ -370,10 +373,13 @@ struct Plan {
       first = false;
     } while (q < t.size());
   }
-  void check(int m) {
+  void check(int m, double scale = 1.0, int call = 0, int iter = 0) {
     Op op;
     op.kind = OP_CHECK;
     op.a = m;
+    op.alpha = scale;
+    op.b = call;
+    op.c = iter;
     ops.push_back(op);
     checks = true;
   }
@@ -439,7 +445,7 @@ void plan_cn(Plan& P, int p, int iters, bool check) {
 // On return *Yo / *Zo hold the requested final iterates and *Tn the seed
 // 1.5 I - 0.5 Y of a following call.
 void ndb_call(Plan& P, int Y, int T0, int iters, bool needY, bool needZ, bool wantTn, int* Yo, int* Zo,
-              int* Tn) {
+              int* Tn, int call = 0) {
   int Z = -1;
   *Tn = -1;
   // k = 1
@@ -464,6 +470,8 @@ void ndb_call(Plan& P, int Y, int T0, int iters, bool needY, bool needZ, bool wa
     const bool last = (k == iters);
     const int T = P.get();
     P.gemm(Z, Y, T, -0.5, 1.5, -1, 0.0, -1, 0.0, 0.0, true);
+    // ||ZY - I||_F = 2 ||T - I||_F
+    if (call > 0) P.check(T, 0.5, call, k);
     if (!last || needY || wantTn) {
       const int Yn = P.get();
       int t = -1;
@@ -497,19 +505,23 @@ void ndb_call(Plan& P, int Y, int T0, int iters, bool needY, bool needZ, bool wa
 // (see gemm.hpp: symmetrising them destabilises the coupled iteration); the
 // converged root is returned as its symmetric part, which is at least as
 // close as X itself to the symmetric exact root.
-void plan_ndb(Plan& P, int p, int iters1, int iters2) {
+// With `check`, each iteration's T is checked for convergence (calls 1, 2):
+// the ops up to any iteration are the same whatever the counts, so a call
+// that has converged at iteration k continues in the plan whose count for
+// that call is k.
+void plan_ndb(Plan& P, int p, int iters1, int iters2, bool check = false) {
   P.sym_out = true;
   const int Y0 = P.get(), T0 = P.get();
   P.prep(Y0, 1.0, 0.0, T0, -0.5, 1.5);
   int Y, Z, Tn;
   if (p == 2) {
-    ndb_call(P, Y0, T0, iters1, false, true, false, &Y, &Z, &Tn);
+    ndb_call(P, Y0, T0, iters1, false, true, false, &Y, &Z, &Tn, check ? 1 : 0);
     P.final_(Z);
     return;
   }
-  ndb_call(P, Y0, T0, iters1, true, false, true, &Y, &Z, &Tn);
+  ndb_call(P, Y0, T0, iters1, true, false, true, &Y, &Z, &Tn, check ? 1 : 0);
   int Y2, Z2, T2;
-  ndb_call(P, Y, Tn, iters2, false, true, false, &Y2, &Z2, &T2);
+  ndb_call(P, Y, Tn, iters2, false, true, false, &Y2, &Z2, &T2, check ? 2 : 0);
   P.final_(Z2);
 }
 
@@ -683,8 +695,8 @@ shampoo_status check_root_args(int64_t n, int32_t B, int32_t p, const shampoo_ro
     return fail(SHAMPOO_E_UNSUPPORTED, "compute dtype %d not supported (F32, F16, F64)", o->compute);
   if (!(o->eps >= 0.0) || !std::isfinite(o->eps)) return fail(SHAMPOO_E_INVALID, "eps must be finite and >= 0");
   if (!(o->tol >= 0.0) || !std::isfinite(o->tol)) return fail(SHAMPOO_E_INVALID, "tol must be finite and >= 0");
-  if (o->tol > 0.0 && o->method != SHAMPOO_CN)
-    return fail(SHAMPOO_E_INVALID, "tol applies to coupled Newton only");
+  if (o->tol > 0.0 && o->method == SHAMPOO_CHEBYSHEV)
+    return fail(SHAMPOO_E_INVALID, "tol applies to the Newton iterations (CN, NDB), not to Chebyshev");
   if (o->tol > 0.0 && o->compute == SHAMPOO_F16)
     return fail(SHAMPOO_E_UNSUPPORTED, "tol needs float32 or float64 iterates: half products leave ||M - I||_F near "
                 "half resolution times the matrix size");
@@ -759,7 +771,7 @@ Plan build_plan(int32_t p, const shampoo_root_opts* o) {
   Plan P;
   switch (o->method) {
     case SHAMPOO_CN: plan_cn(P, p, o->iters, o->tol > 0.0); break;
-    case SHAMPOO_NDB: plan_ndb(P, p, o->iters, o->iters2); break;
+    case SHAMPOO_NDB: plan_ndb(P, p, o->iters, o->iters2, o->tol > 0.0); break;
     default: {
       const int N = o->cheb_points ? o->cheb_points : 4 * (o->cheb_degree + 1);
       const int d = o->cheb_degree;
@@ -949,11 +961,17 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
   double* cpart = (double*)chk;
   double* cnorm = (double*)(chk + align_up((size_t)parts * n * 8));
   int32_t* notdone = (int32_t*)(chk + align_up((size_t)parts * n * 8) + align_up((size_t)n * 8));
-  for (size_t oi = 0; oi < P.ops.size(); ++oi) {
-    const Op& op = P.ops[oi];
+  // Newton-DB re-plans at convergence: `cur` is the plan being run, `gemms`
+  // the products run so far, used1 the iterations of call 1 once it ended
+  const Plan* cur = &P;
+  Plan replanned;
+  int gemms = 0, used1 = o->iters;
+  for (size_t oi = 0; oi < cur->ops.size(); ++oi) {
+    const Op& op = cur->ops[oi];
     if (op.kind != OP_CHECK) {
       shampoo_status r = exec(op);
       if (r != SHAMPOO_OK) return r;
+      if (op.kind == OP_GEMM) ++gemms;
       continue;
     }
     // ||M - I||_F: the Frobenius sums of M + eps I with eps = -1
@@ -966,20 +984,38 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
     hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, notdone, (int64_t)1, 0);
     LAUNCH_CHECK("fill");
     hipLaunchKernelGGL(above_tol_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const double*)cnorm, n,
-                       o->tol, notdone);
+                       o->tol * op.alpha, notdone);
     LAUNCH_CHECK("above_tol");
     int32_t h = 1;
     HIP_TRY(hipMemcpyAsync(&h, notdone, 4, hipMemcpyDeviceToHost, st));
     HIP_TRY(hipStreamSynchronize(st));
     if (h != 0) continue;
-    // every matrix has converged: the next op (X T) is X's last update
-    if (oi + 1 >= P.ops.size() || P.ops[oi + 1].kind != OP_GEMM || P.ops.back().kind != OP_FINAL)
-      return fail(SHAMPOO_E_INVALID, "internal: convergence check placement");
-    shampoo_status r = exec(P.ops[oi + 1]);
-    if (r != SHAMPOO_OK) return r;
-    Op fin = P.ops.back();
-    fin.a = P.ops[oi + 1].c;
-    return exec(fin);
+    if (op.b == 0) {
+      // coupled Newton has converged: the next op (X T) is X's last update
+      if (oi + 1 >= cur->ops.size() || cur->ops[oi + 1].kind != OP_GEMM || cur->ops.back().kind != OP_FINAL)
+        return fail(SHAMPOO_E_INVALID, "internal: convergence check placement");
+      shampoo_status r = exec(cur->ops[oi + 1]);
+      if (r != SHAMPOO_OK) return r;
+      Op fin = cur->ops.back();
+      fin.a = cur->ops[oi + 1].c;
+      return exec(fin);
+    }
+    // Newton-DB call op.b has converged at iteration op.c: continue in the
+    // plan where that call ends there, after its gemms-th product
+    const int it1 = op.b == 1 ? op.c : used1, it2 = op.b == 2 ? op.c : o->iters2;
+    if (op.b == 1) used1 = op.c;
+    Plan next;
+    plan_ndb(next, p, it1, it2, true);
+    mark_needs(next);
+    if (next.peak > P.peak) return fail(SHAMPOO_E_INVALID, "internal: re-planned chain needs more buffers");
+    size_t j = 0;
+    for (int g = 0; j < next.ops.size(); ++j)
+      if (next.ops[j].kind == OP_GEMM && ++g == gemms) break;
+    if (j >= next.ops.size()) return fail(SHAMPOO_E_INVALID, "internal: re-planned chain is shorter");
+    replanned = std::move(next);
+    cur = &replanned;
+    oi = j;  // the loop's ++oi moves to the op after that product
+    if (oi + 1 < cur->ops.size() && cur->ops[oi + 1].kind == OP_CHECK) ++oi;  // already checked
   }
   return SHAMPOO_OK;
 }

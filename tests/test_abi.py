@@ -147,15 +147,18 @@ def test_chebyshev_split_workspace_and_validation(mir):
 
 
 def test_newton_tolerance_workspace_and_validation(mir):
-    """A coupled-Newton tolerance adds the check's scratch to the workspace
+    """A Newton tolerance adds the check's scratch to the workspace
     (Frobenius partial sums, 32 per matrix for 64 matrices; the norms; a
-    flag slot); it is rejected for other methods, for half-precision chains
-    and when negative."""
+    flag slot); it is rejected for Chebyshev, for half-precision chains and
+    when negative."""
     a = mir.shampoo_inverse_root_workspace(64, 256, 4, mir.RootOpts(method="cn", iters=20))
     b = mir.shampoo_inverse_root_workspace(64, 256, 4, mir.RootOpts(method="cn", iters=20, tol=1e-6))
     assert b - a == 32 * 64 * 8 + 64 * 8 + 256
-    for opts, status in [(mir.RootOpts(method="ndb", iters=5, iters2=5, tol=1e-6), mir.E_INVALID),
-                         (mir.RootOpts(method="chebyshev", tol=1e-6), mir.E_INVALID),
+    c = mir.shampoo_inverse_root_workspace(64, 256, 4, mir.RootOpts(method="ndb", iters=9, iters2=7))
+    d = mir.shampoo_inverse_root_workspace(64, 256, 4, mir.RootOpts(method="ndb", iters=9, iters2=7, tol=1e-6))
+    assert d - c == b - a
+    for opts, status in [(mir.RootOpts(method="chebyshev", tol=1e-6), mir.E_INVALID),
+                         (mir.RootOpts(method="ndb", iters=5, iters2=5, tol=1e-4, compute="f16"), mir.E_UNSUPPORTED),
                          (mir.RootOpts(method="cn", iters=5, tol=-1.0), mir.E_INVALID),
                          (mir.RootOpts(method="cn", iters=5, tol=1e-4, compute="f16"), mir.E_UNSUPPORTED)]:
         with pytest.raises(mir.ShampooError) as e:

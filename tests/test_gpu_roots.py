@@ -264,27 +264,30 @@ def test_chebyshev_paterson_stockmeyer_half_products(mir, degree):
     assert not fl.any() and worst < 2e-2
 
 
+@pytest.mark.parametrize("method,p", [("cn", 4), ("ndb", 4), ("ndb", 2)])
 @pytest.mark.parametrize("compute,lo,tol,bar", [("f32", 1e-2, 1e-4, 1e-4), ("f32", 1e-4, 1e-4, 1e-4),
                                                  ("f64", 1e-6, 1e-10, 1e-6)])
-def test_coupled_newton_tolerance(mir, compute, lo, tol, bar):
-    """Coupled Newton with a tolerance stops once every ||M - I||_F <= tol,
-    with fewer products than the fixed count, and the same root within the
-    bar against the oracle (float32: the stated 1e-4; float64 at kappa 1e6:
-    1e-6, rounded to the float32 output)."""
+def test_newton_tolerance(mir, method, p, compute, lo, tol, bar):
+    """Coupled Newton (||M - I||_F <= tol) and Newton-DB (||ZY - I||_F <= tol
+    in each call, the chain re-planned at convergence) stop with fewer
+    products than the fixed counts and the same root within the bar against
+    the oracle (float32: the stated 1e-4; float64 at kappa 1e6: 1e-6,
+    rounded to the float32 output)."""
     A = synthetic.spd_stack(17, 6, 128, lo, 1.0).astype(np.float32)
-    iters = 40
+    kw = dict(method=method, iters=40, iters2=30, compute=compute)
+    fixed = 4 * 40 - 4 if method == "cn" else (3 * 40 - 3) + (3 * 30 - 3 if p == 4 else 0)
     mir.shampoo_timing_enable(512)
     try:
-        X, _, fl = run_root(mir, A, 4, method="cn", iters=iters, tol=tol, compute=compute)
+        X, _, fl = run_root(mir, A, p, tol=tol, **kw)
         ms = mir.shampoo_timing_read(512)
     finally:
         mir.shampoo_timing_enable(0)
-    Xf, _, _ = run_root(mir, A, 4, method="cn", iters=iters, compute=compute)
-    worst, _ = worst_vs_eigh(X, A, 4)
-    worst_f, _ = worst_vs_eigh(Xf, A, 4)
-    log(f"CN {compute} lambda >= {lo} tol {tol}: {len(ms)} products (fixed {4 * iters - 4}), worst {worst:.2e} "
+    Xf, _, _ = run_root(mir, A, p, **kw)
+    worst, _ = worst_vs_eigh(X, A, p)
+    worst_f, _ = worst_vs_eigh(Xf, A, p)
+    log(f"{method} p={p} {compute} lambda >= {lo} tol {tol}: {len(ms)} products (fixed {fixed}), worst {worst:.2e} "
         f"(fixed count {worst_f:.2e})")
-    assert not fl.any() and worst < bar and len(ms) < 4 * iters - 4
+    assert not fl.any() and worst < bar and len(ms) < fixed
 
 
 def test_scales_match_oracle(mir):
