@@ -180,7 +180,9 @@ typedef struct shampoo_param {
  *   (every eigenvalue of M = X^p A_s within tol of 1), checked after each M
  *   update, X then taking its last update; Newton-DB ||ZY - I||_F <= tol in
  *   each call, checked after each T product, the call then ending with that
- *   iteration as its last (the chain is planned again with that count).  Rounding keeps ||M - I||_F near u sqrt(v) .. u v (u the unit
+ *   iteration as its last (the chain is planned again with that count).
+ *   Matrices that cannot converge are not waited for: an iterate turned
+ *   NaN, or a scale that is zero or not finite (the final pass flags them).  Rounding keeps ||M - I||_F near u sqrt(v) .. u v (u the unit
  *   roundoff, v the valid size), so tol must lie above that: 1e-4 suits
  *   float32 up to v = 1024.  Each check synchronises the stream with the
  *   host (one flag read), so work queued after it on other streams is not

@@ -375,13 +375,16 @@ __global__ __launch_bounds__(256) void comb_kernel(CombArgs a, int B) {
 }
 
 // ---------------------------------------------------------------------------
-// Convergence check of coupled Newton: ||M - I||_F per matrix comes from the
-// Frobenius kernels with eps = -1; a matrix above tol (or not finite) sets
+// Convergence check of the Newton iterations: ||M - I||_F per matrix comes
+// from the Frobenius kernels with eps = -1; a matrix above tol sets
 // *notdone.  The Frobenius norm bounds every eigenvalue's distance from 1.
+// Matrices that cannot converge do not hold the others back: a NaN norm, or
+// a scale that is zero or not finite (the final pass zeroes and flags them).
 // ---------------------------------------------------------------------------
-__global__ void above_tol_kernel(const double* __restrict__ norms, int64_t n, double tol, int32_t* __restrict__ notdone) {
+__global__ void above_tol_kernel(const double* __restrict__ norms, const double* __restrict__ scale, int64_t n,
+                                 double tol, int32_t* __restrict__ notdone) {
   const int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (b < n && !(norms[b] <= tol)) atomicOr(notdone, 1);
+  if (b < n && scale[b] > 0.0 && scale[b] < 1.0e300 && norms[b] > tol) atomicOr(notdone, 1);
 }
 
 // ---------------------------------------------------------------------------

@@ -983,8 +983,8 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
     LAUNCH_CHECK("frob_finish");
     hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, notdone, (int64_t)1, 0);
     LAUNCH_CHECK("fill");
-    hipLaunchKernelGGL(above_tol_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const double*)cnorm, n,
-                       o->tol * op.alpha, notdone);
+    hipLaunchKernelGGL(above_tol_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const double*)cnorm, sc,
+                       n, o->tol * op.alpha, notdone);
     LAUNCH_CHECK("above_tol");
     int32_t h = 1;
     HIP_TRY(hipMemcpyAsync(&h, notdone, 4, hipMemcpyDeviceToHost, st));

@@ -290,6 +290,29 @@ def test_newton_tolerance(mir, method, p, compute, lo, tol, bar):
     assert not fl.any() and worst < bar and len(ms) < fixed
 
 
+@pytest.mark.parametrize("bad", ["nan", "zero"])
+def test_newton_tolerance_does_not_wait_for_failures(mir, bad):
+    """A matrix with a NaN entry, or all zero (zero scale without eps),
+    cannot converge: the others stop at the tolerance all the same, and the
+    failed matrix is flagged."""
+    A = synthetic.spd_stack(19, 4, 128, 1e-2, 1.0).astype(np.float32)
+    if bad == "nan":
+        A[2, 5, 7] = np.nan
+    else:
+        A[2] = 0.0
+    mir.shampoo_timing_enable(256)
+    try:
+        X, _, fl = run_root(mir, A, 4, method="cn", iters=40, tol=1e-4)
+        ms = mir.shampoo_timing_read(256)
+    finally:
+        mir.shampoo_timing_enable(0)
+    good = [0, 1, 3]
+    worst, _ = worst_vs_eigh(X[good], A[good], 4)
+    log(f"{bad} matrix among 4: {len(ms)} products (fixed 156), worst of the others {worst:.2e}, flags {fl}")
+    assert fl[2] & (mir.FLAG_NONFINITE | mir.FLAG_ZERO_SCALE) and not fl[good].any()
+    assert worst < 1e-4 and len(ms) < 156
+
+
 def test_scales_match_oracle(mir):
     B, n = 256, 6
     A = synthetic.spd_stack(9, n, B, 1e-4, 1.0).astype(np.float32)
