@@ -313,6 +313,27 @@ def test_newton_tolerance_does_not_wait_for_failures(mir, bad):
     assert worst < 1e-4 and len(ms) < 156
 
 
+@pytest.mark.parametrize("cheb_eval", ["clenshaw", "ps"])
+def test_chebyshev_with_power_scaling(mir, cheb_eval):
+    """Chebyshev after power-iteration scaling: the scaled spectrum may reach
+    slightly past 1, where the fit is extrapolated; against the oracle's
+    exact polynomial at the GPU's own scale (float32 bar 1e-4)."""
+    eps, degree = 1e-3, 16
+    A = synthetic.spd_stack(27, 6, 256, 1e-3, 1.0).astype(np.float32)
+    X, s, fl = run_root(mir, A, 4, method="chebyshev", cheb_degree=degree, eps=eps, scaling="power",
+                        cheb_eval=cheb_eval)
+    c = oracle.chebyshev_coefficients(4, degree, eps)
+    worst = 0.0
+    for i in range(A.shape[0]):
+        Ae = A[i].astype(np.float64) + eps * np.eye(256)
+        lmax = np.linalg.eigvalsh(Ae)[-1]
+        assert abs(float(s[i]) - lmax) / lmax < 2e-2      # the power scale estimates the top eigenvalue
+        ref = oracle.chebyshev_matrix_eigh(Ae / float(s[i]), c) * float(s[i]) ** -0.25
+        worst = max(worst, rel_fro(X[i], ref))
+    log(f"chebyshev {cheb_eval} with power scaling: worst {worst:.2e}")
+    assert not fl.any() and worst < 1e-4
+
+
 def test_scales_match_oracle(mir):
     B, n = 256, 6
     A = synthetic.spd_stack(9, n, B, 1e-4, 1.0).astype(np.float32)
