@@ -234,6 +234,44 @@ def full_step_ms(mir, steps, warmup, compute="f32", fallback="none", tol=0.0):
     return float(np.median(times)), nflag
 
 
+def chebyshev_sweep(mir, degrees=(16, 40, 60, 100)):
+    """Chebyshev inverse 4th roots of 288 SPD matrices 1024 x 1024 (the
+    decoder set's factor stack; A = X X^T / 1024 + 1e-3 I with X N(0, 1) drawn
+    on the device), Frobenius scaling, for the degree sweep: float32 and
+    half-precision products, Clenshaw's recurrence and the Paterson-Stockmeyer
+    split.  Returns {(degree, compute, eval): (ms per call, products)}."""
+    import torch
+    n, B = 288, 1024
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    A = torch.empty((n, B, B), device="cuda")
+    for i in range(0, n, 32):
+        X = torch.randn((32, B, B), generator=gen, device="cuda")
+        A[i:i + 32] = torch.bmm(X, X.transpose(1, 2).contiguous()) / B
+    A += 1e-3 * torch.eye(B, device="cuda")
+    out = torch.empty_like(A)
+    res = {}
+    for d in degrees:
+        for compute in ("f32", "f16"):
+            for ev in ("clenshaw", "ps"):
+                opts = mir.RootOpts(method="chebyshev", cheb_degree=d, cheb_eval=ev, compute=compute, eps=1e-3)
+                ws = torch.empty(mir.shampoo_inverse_root_workspace(n, B, 4, opts), dtype=torch.uint8, device="cuda")
+                mir.shampoo_inverse_root(A, out, 4, opts, ws=ws)
+                torch.cuda.synchronize()
+                mir.shampoo_timing_enable(512)
+                t0 = time.perf_counter()
+                for _ in range(2):
+                    mir.shampoo_inverse_root(A, out, 4, opts, ws=ws)
+                torch.cuda.synchronize()
+                ms = (time.perf_counter() - t0) / 2 * 1e3
+                prods = len(mir.shampoo_timing_read(512)) // 2
+                mir.shampoo_timing_enable(0)
+                res[(d, compute, ev)] = (ms, prods)
+                log(f"chebyshev d={d} {compute} {ev}: {ms:.1f} ms per call, {prods} products")
+                del ws
+    return res
+
+
 def single_step_ms(mir, steps, warmup):
     """Step on one [256, 128] float32 parameter in two 128-blocks (gradients
     N(0, 1), statistics summed (beta2 1), eps 1e-12, coupled Newton 30 in
@@ -330,7 +368,8 @@ def main():
     ap.add_argument("--blocks", type=int, default=None,
                     help="with --only roots: solve only the first this-many blocks (counter runs whose "
                          "per-dispatch cycle counts would otherwise overflow 32 bits)")
-    ap.add_argument("--only", choices=["roots", "copy", "step", "step_f16", "step_tol", "step5", "step5_ps", "step1"],
+    ap.add_argument("--only", choices=["roots", "copy", "step", "step_f16", "step_tol", "step5", "step5_ps", "step1",
+                                       "cheb_sweep"],
                     default=None,
                     help="profiling runs: only the float32 solve, only a 1 GiB copy, only the decoder-set step "
                          "(float32 or half-precision products) or only the bottleneck-50 step (Clenshaw or "
@@ -360,6 +399,9 @@ def main():
         half = args.only == "step_f16"
         ms, nf = full_step_ms(mir, args.steps, max(1, args.warmup), "f16" if half else "f32", "f64" if half else "none")
         log(f"full step {ms:.2f} ms, flags {nf}")
+        return
+    if args.only == "cheb_sweep":
+        chebyshev_sweep(mir)
         return
     if args.only == "step_tol":
         ms, nf = full_step_ms(mir, args.steps, max(1, args.warmup), "f32", "none", 1e-4)

@@ -375,6 +375,60 @@ __global__ __launch_bounds__(256) void comb_kernel(CombArgs a, int B) {
 }
 
 // ---------------------------------------------------------------------------
+// mcomb: several linear combinations of the same inputs in one pass,
+// out_j = sum_q w[j][q] in_q + gamma_j I: every input is read once.  Same
+// arithmetic as comb (double, one rounding), grid (chunks, n) as prep.
+// ---------------------------------------------------------------------------
+constexpr int MCOMB_IN = 12, MCOMB_OUT = 12;
+struct MCombArgs {
+  const void* in[MCOMB_IN];
+  void* out[MCOMB_OUT];   // iterate type (may be null)
+  void* outh[MCOMB_OUT];  // half copies (half operands only; may be null)
+  double w[MCOMB_OUT][MCOMB_IN];
+  double gamma[MCOMB_OUT];
+  int nin, nout;
+};
+
+template <typename TS>
+__global__ __launch_bounds__(256) void mcomb_kernel(MCombArgs a, int B) {
+  const int64_t b = blockIdx.y;
+  const int64_t BB = (int64_t)B * B;
+  const int cpr = B / 4;
+  const int total = B * cpr;
+  const int k = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (k >= total) return;
+  const int r = k / cpr, c = 4 * (k - r * cpr);
+  const int64_t off = b * BB + (int64_t)r * B + c;
+  // predicated, fully unrolled loops: every array index is a constant, so
+  // the inputs stay in registers
+  double x[MCOMB_IN][4];
+#pragma unroll
+  for (int q = 0; q < MCOMB_IN; ++q) {
+    if (q < a.nin) {
+      Quad<TS>::load(reinterpret_cast<const TS*>(a.in[q]) + off, x[q]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[q][e] = 0.0;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < MCOMB_OUT; ++j) {
+    if (j < a.nout) {
+      double y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = (r == c + e) ? a.gamma[j] : 0.0;
+#pragma unroll
+      for (int q = 0; q < MCOMB_IN; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] += a.w[j][q] * x[q][e];
+      if (a.out[j]) Quad<TS>::store(reinterpret_cast<TS*>(a.out[j]) + off, y);
+      if (a.outh[j])
+        store_h4(reinterpret_cast<_Float16*>(a.outh[j]) + off, floatx4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]});
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Convergence check of the Newton iterations: ||M - I||_F per matrix comes
 // from the Frobenius kernels with eps = -1; a matrix above tol sets
 // *notdone.  The Frobenius norm bounds every eigenvalue's distance from 1.

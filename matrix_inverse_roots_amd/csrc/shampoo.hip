@@ -275,7 +275,7 @@ int64_t gemm_wgs(int n, int64_t batch, bool sym) {
 // records its peak, so the workspace query and the execution run the very
 // same plan.
 // ---------------------------------------------------------------------------
-enum OpKind { OP_PREP, OP_GEMM, OP_COMB, OP_CHECK, OP_FINAL };
+enum OpKind { OP_PREP, OP_GEMM, OP_COMB, OP_MCOMB, OP_CHECK, OP_FINAL };
 
 struct Op {
   OpKind kind;
@@ -295,6 +295,10 @@ struct Op {
   int in[COMB_IN] = {-1, -1, -1, -1};
   double w[COMB_IN] = {0, 0, 0, 0};
   int nin = 0;
+  // MCOMB: mout[j] = sum_q mw[j][q] min[q] + mg[j] I, every input read once
+  std::vector<int> min, mout, mneed;
+  std::vector<std::vector<double>> mw;
+  std::vector<double> mg;
   // FINAL: buffer a -> out
   // Forms of each output that later ops read (NEED_F32: addend D or final
   // output; NEED_HALF: product operand); used by half-operand chains.
@@ -382,6 +386,17 @@ struct Plan {
     op.c = iter;
     ops.push_back(op);
     checks = true;
+  }
+  void mcomb(const std::vector<int>& in, const std::vector<int>& out, const std::vector<std::vector<double>>& w,
+             const std::vector<double>& g) {
+    Op op;
+    op.kind = OP_MCOMB;
+    op.min = in;
+    op.mout = out;
+    op.mw = w;
+    op.mg = g;
+    op.mneed.assign(out.size(), 0);
+    ops.push_back(op);
   }
   void final_(int x) {
     Op op;
@@ -610,7 +625,50 @@ void plan_cheb_ps(Plan& P, const std::vector<double>& c) {
     else P.gemm(T[k / 2], T[k / 2 + 1], T[k], 2.0, 0.0, T[1], -1.0);
   }
   const int y = T[m];
-  // the matrix terms of a_j (on T_1 .. T_(m-1)); its constant al[j][0] goes
+  const bool aJ_const = d % m == 0;
+  if ((m - 1) + (aJ_const ? 1 : 0) <= MCOMB_IN && J + (aJ_const ? 0 : 1) <= MCOMB_OUT) {
+    // Every a_j from one pass over T_1 .. T_(m-1) (and y): A[j] = a_j, with
+    // the known multiples of I folded in.  With a_J = al[J][0] I constant,
+    // A[J-1] is B_(J-1) = a_(J-1) + 2 al[J][0] y (or + al[J][0] y when J = 1,
+    // the last step), and A[J-2] carries - B_J = - al[J][0] I.  Otherwise
+    // A[J] = a_J = B_J.  The giant steps then need one in-place pass each,
+    // A[j] - B_(j+2), before their product.
+    std::vector<int> in;
+    for (int i = 1; i < m; ++i) in.push_back(T[i]);
+    if (aJ_const) in.push_back(y);
+    const int nA = aJ_const ? J : J + 1;
+    std::vector<int> A(nA);
+    std::vector<std::vector<double>> w(nA, std::vector<double>(in.size(), 0.0));
+    std::vector<double> g(nA, 0.0);
+    for (int j = 0; j < nA; ++j) {
+      A[j] = P.get();
+      for (int i = 1; i < m; ++i) w[j][i - 1] = al[j][i];
+      g[j] = al[j][0];
+    }
+    if (aJ_const) {
+      w[J - 1][m - 1] = (J - 1 > 0 ? 2.0 : 1.0) * al[J][0];
+      if (J >= 2) g[J - 2] -= al[J][0];
+    }
+    P.mcomb(in, A, w, g);
+    for (int k = 1; k < m; ++k) P.put(T[k]);  // only y is multiplied from here on
+    int B1 = aJ_const ? A[J - 1] : A[J];  // B_(j+1) for the first product
+    int B2 = -1;                          // B_(j+2), once it is a matrix
+    for (int j = aJ_const ? J - 2 : J - 1; j >= 0; --j) {
+      if (B2 >= 0) P.comb(A[j], {{A[j], 1.0}, {B2, -1.0}}, 0.0);
+      const int N = P.get();
+      P.gemm(y, B1, N, j > 0 ? 2.0 : 1.0, 0.0, A[j], 1.0);
+      P.put(A[j]);
+      P.put(B2);
+      B2 = B1;
+      B1 = N;
+    }
+    P.put(y);
+    P.put(B2);
+    P.final_(B1);
+    return;
+  }
+  // Too many terms for one pass: each addend is formed by chained comb passes.
+  // The matrix terms of a_j (on T_1 .. T_(m-1)); its constant al[j][0] goes
   // into the comb's multiple of I
   auto a_terms = [&](int j) {
     std::vector<std::pair<int, double>> t;
@@ -759,6 +817,9 @@ void mark_needs(Plan& P) {
     } else if (op.kind == OP_COMB) {
       op.need_c = take(op.c);
       for (int q = 0; q < op.nin; ++q) need[op.in[q]] |= NEED_F32;
+    } else if (op.kind == OP_MCOMB) {
+      for (size_t j = 0; j < op.mout.size(); ++j) op.mneed[j] = take(op.mout[j]);
+      for (int b : op.min) need[b] |= NEED_F32;
     } else if (op.kind == OP_CHECK) {
       need[op.a] |= NEED_F32;
     } else {
@@ -923,6 +984,20 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
       }
       HIP_TRY(timing_mark(1, st));
       timing_advance();
+    } else if (op.kind == OP_MCOMB) {
+      MCombArgs ma{};
+      ma.nin = (int)op.min.size();
+      ma.nout = (int)op.mout.size();
+      for (int q = 0; q < ma.nin; ++q) ma.in[q] = buf(op.min[q]);
+      for (int j = 0; j < ma.nout; ++j) {
+        if (!HALF || (op.mneed[j] & NEED_F32)) ma.out[j] = buf(op.mout[j]);
+        if (HALF && (op.mneed[j] & NEED_HALF)) ma.outh[j] = hbuf(op.mout[j]);
+        for (int q = 0; q < ma.nin; ++q) ma.w[j][q] = op.mw[j][q];
+        ma.gamma[j] = op.mg[j];
+      }
+      const unsigned gx = (unsigned)(((int64_t)B * B / 4 + 255) / 256);
+      hipLaunchKernelGGL((mcomb_kernel<TS>), dim3(gx, (unsigned)n), dim3(256), 0, st, ma, B);
+      LAUNCH_CHECK("mcomb");
     } else if (op.kind == OP_COMB) {
       CombArgs ca{};
       for (int q = 0; q < op.nin; ++q) {

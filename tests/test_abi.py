@@ -124,15 +124,15 @@ def test_workspace_queries_and_support_matrix(mir):
 
 
 def test_chebyshev_split_workspace_and_validation(mir):
-    """The Paterson-Stockmeyer split at degree 16 (m = 4) keeps S, T_2, T_3,
-    T_4 and three giant-step values live (7 iterate buffers) where Clenshaw
-    keeps 4; an unknown cheb_eval is rejected."""
+    """The Paterson-Stockmeyer split at degree 16 (m = 4) forms a_0 .. a_3
+    in one pass while S, T_2, T_3 and T_4 are live (8 iterate buffers) where
+    Clenshaw keeps 4; an unknown cheb_eval is rejected."""
     head = 2 * 94 * 8
     slot = 94 * 1024 * 1024 * 4
     cl = mir.shampoo_inverse_root_workspace(94, 1024, 4, mir.RootOpts(method="chebyshev", cheb_degree=16))
     ps = mir.shampoo_inverse_root_workspace(94, 1024, 4, mir.RootOpts(method="chebyshev", cheb_degree=16,
                                                                        cheb_eval="ps"))
-    assert head <= 2 * 1024 and cl - 4 * slot <= 2 * 1024 and ps - 7 * slot == cl - 4 * slot
+    assert head <= 2 * 1024 and cl - 4 * slot <= 2 * 1024 and ps - 8 * slot == cl - 4 * slot
     # up to degree 3 the split saves no product and Clenshaw's plan is used
     for d in (0, 1, 2, 3):
         a = mir.shampoo_inverse_root_workspace(8, 128, 4, mir.RootOpts(method="chebyshev", cheb_degree=d))
