@@ -352,25 +352,35 @@ __global__ __launch_bounds__(256) void comb_kernel(CombArgs a, int B) {
   const int total = B * cpr;
   TS* out = a.out ? reinterpret_cast<TS*>(a.out) + b * BB : nullptr;
   _Float16* outh = a.outh ? reinterpret_cast<_Float16*>(a.outh) + b * BB : nullptr;
+  // All loads of the thread's chunks come before any store: an input may be
+  // `out` itself, so loads placed after a store could not be moved ahead of
+  // it, and the chunks would be read one at a time.
+  double y[PREP_U][4];
+#pragma unroll
+  for (int u = 0; u < PREP_U; ++u) {
+    const int k = ((int)blockIdx.x * PREP_U + u) * 256 + (int)threadIdx.x;
+    const int r = k / cpr, c = 4 * (k - r * cpr);
+    const int64_t off = b * BB + (int64_t)r * B + c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[u][e] = (r == c + e) ? a.gamma : 0.0;
+    if (k >= total) continue;
+#pragma unroll
+    for (int q = 0; q < COMB_IN; ++q) {
+      if (q < a.nin) {
+        double x[4];
+        Quad<TS>::load(reinterpret_cast<const TS*>(a.in[q]) + off, x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[u][e] += a.w[q] * x[e];
+      }
+    }
+  }
 #pragma unroll
   for (int u = 0; u < PREP_U; ++u) {
     const int k = ((int)blockIdx.x * PREP_U + u) * 256 + (int)threadIdx.x;
     if (k >= total) continue;
     const int r = k / cpr, c = 4 * (k - r * cpr);
-    const int64_t off = b * BB + (int64_t)r * B + c;
-    double y[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = (r == c + e) ? a.gamma : 0.0;
-#pragma unroll
-    for (int q = 0; q < COMB_IN; ++q) {
-      if (q >= a.nin) break;
-      double x[4];
-      Quad<TS>::load(reinterpret_cast<const TS*>(a.in[q]) + off, x);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] += a.w[q] * x[e];
-    }
-    if (out) Quad<TS>::store(out + (int64_t)r * B + c, y);
-    if (outh) store_h4(outh + (int64_t)r * B + c, floatx4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]});
+    if (out) Quad<TS>::store(out + (int64_t)r * B + c, y[u]);
+    if (outh) store_h4(outh + (int64_t)r * B + c, floatx4{(float)y[u][0], (float)y[u][1], (float)y[u][2], (float)y[u][3]});
   }
 }
 
