@@ -327,19 +327,21 @@ def bottleneck_root_gflop(mir, products):
     return {"valid_region": f(v), "grouped_sides": f(side), "padded_to_block": f(blk)}
 
 
-def bottleneck_step_ms(mir, steps, warmup, group, cheb_eval="clenshaw"):
+def bottleneck_step_ms(mir, steps, warmup, group, cheb_eval="clenshaw", compute="f32"):
     """Full step on the bottleneck-50 set (53 matrices, 25.5 M parameters,
     block 1024 if max(m, n) >= 2048 else 256, float32 gradients N(0, 1e-2),
     beta2 0.999, eps 1e-12, Chebyshev degree 16 summed by Clenshaw's
-    recurrence or by the Paterson-Stockmeyer split, momentum grafting), with
-    the roots grouped by factor side or computed at the block size."""
+    recurrence or by the Paterson-Stockmeyer split, float32 or half-precision
+    products, momentum grafting), with the roots grouped by factor side or
+    computed at the block size."""
     import numpy as np
     import torch
     import synthetic
     shapes = synthetic.bottleneck50_shapes()
     W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
     opt = mir.Shampoo(W, block_size=lambda m, n: 1024 if max(m, n) >= 2048 else 256, beta2=0.999, eps=1e-12,
-                      root=mir.RootOpts(method="chebyshev", cheb_degree=16, cheb_eval=cheb_eval), graft="momentum",
+                      root=mir.RootOpts(method="chebyshev", cheb_degree=16, cheb_eval=cheb_eval, compute=compute),
+                      graft="momentum",
                       lr=0.1, momentum=0.9, group_factors=group)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(5)
@@ -501,14 +503,16 @@ def main():
         msg, nfg = bottleneck_step_ms(mir, max(5, args.steps), 2, True)
         msu, nfu = bottleneck_step_ms(mir, max(5, args.steps), 2, False)
         msp, nfp = bottleneck_step_ms(mir, max(5, args.steps), 2, True, "ps")
+        msh, nfh = bottleneck_step_ms(mir, max(5, args.steps), 2, True, "ps", "f16")
         result["full_step_bottleneck50"] = {
             "workload": "bottleneck50_53_matrices_b256_1024_chebyshev16_f32_momentum",
             "ms_grouped_by_factor_side": round(msg, 2), "ms_padded_to_block": round(msu, 2),
-            "ms_grouped_paterson_stockmeyer": round(msp, 2), "flagged_factors": nfg + nfu + nfp,
+            "ms_grouped_paterson_stockmeyer": round(msp, 2),
+            "ms_grouped_paterson_stockmeyer_f16_products": round(msh, 2), "flagged_factors": nfg + nfu + nfp + nfh,
             "root_gflop_per_step_clenshaw_15_products": bottleneck_root_gflop(mir, 15),
             "root_gflop_per_step_paterson_stockmeyer_6_products": bottleneck_root_gflop(mir, 6)}
         log(f"bottleneck-50 step: {msg:.1f} ms grouped, {msu:.1f} ms padded, {msp:.1f} ms grouped with the "
-            f"Paterson-Stockmeyer sum")
+            f"Paterson-Stockmeyer sum, {msh:.1f} ms with half-precision products")
         e1, g1 = single_step_ms(mir, 50, 5)
         result["full_step_single"] = {
             "workload": "one_256x128_f32_param_b128_sum_stats_cn30_f32_sgd",

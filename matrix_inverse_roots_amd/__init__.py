@@ -195,7 +195,7 @@ class RootOpts:
     eps: float = 0.0
     cheb_eps: Optional[float] = None   # defaults to eps
     pi_start: object = None       # device float32 [pi_vectors, B]
-    tol: float = 0.0              # coupled Newton: stop once ||M - I||_F <= tol sqrt(v) (0: run iters)
+    tol: float = 0.0              # CN / NDB, f32 or f64: stop once ||M - I||_F <= tol (0: run iters)
 
     def c(self):
         return RootOptsC(METHODS[self.method], SCALINGS[self.scaling], DTYPES[self.compute],

@@ -346,22 +346,26 @@ def test_decoder_layer_cn_half_products_with_f64_fallback(mir):
         assert e < 2e-2
 
 
-@pytest.mark.parametrize("cheb_eval,stats64", [("clenshaw", False), ("ps", False), ("ps", True)])
-def test_bottleneck_subset_chebyshev_momentum(mir, cheb_eval, stats64):
+@pytest.mark.parametrize("cheb_eval,compute", [("clenshaw", "f32"), ("ps", "f32"), ("ps", "f64"),
+                                               ("clenshaw", "f16"), ("ps", "f16")])
+def test_bottleneck_subset_chebyshev_momentum(mir, cheb_eval, compute):
     """First 12 matrices of the 50-layer bottleneck CNN set (1x1 and 3x3
     kernels as (out, in k k)), block sizes 256 / 1024 by size, ragged edges,
-    Chebyshev degree 16 in float32, SGD-momentum 0.9 grafting lr 0.1,
-    gradients variance 1e-2, 3 steps; the oracle evaluates the same fitted
-    polynomial exactly."""
+    Chebyshev degree 16 (float32, half-precision or float64 products),
+    SGD-momentum 0.9 grafting lr 0.1, gradients variance 1e-2, 3 steps; the
+    oracle evaluates the same fitted polynomial exactly."""
+    stats64 = compute == "f64"
     shapes = synthetic.bottleneck50_shapes()[:12]
     bs = dict(zip(shapes, synthetic.bottleneck50_block_sizes(shapes)))
     grads = synthetic.gaussian_grads(5, shapes, 3, 0.1)
     errs = run_steps(mir, shapes, bs, grads, 3,
                      dict(beta2=0.999, eps=1e-12, graft="momentum", lr=0.1, momentum=0.9),
-                     dict(method="chebyshev", cheb_degree=16, cheb_eval=cheb_eval,
-                          compute="f64" if stats64 else "f32"), oracle_root="chebyshev", stats64=stats64)
-    # float64 statistics and chain: the error is the float32 weights' rounding
-    assert all(e < (1e-6 if stats64 else 1e-4) for e, _ in errs)
+                     dict(method="chebyshev", cheb_degree=16, cheb_eval=cheb_eval, compute=compute),
+                     oracle_root="chebyshev", stats64=stats64)
+    # float64 statistics and chain: the error is the float32 weights' rounding;
+    # half-precision products take the half-precision bar
+    bar = {"f64": 1e-6, "f32": 1e-4, "f16": 2e-2}[compute]
+    assert all(e < bar for e, _ in errs)
 
 
 def test_step_deterministic_and_infrequent_roots(mir):
