@@ -174,8 +174,11 @@ template <typename TG, typename TL, int VE> struct BlockKN {
 // operands are copied row by row (16-byte global loads, coalesced per
 // 128-byte row segment); an NN B operand is loaded as VE x VE element blocks
 // (VE = elements per 16 bytes) along its rows and transposed in registers.
+// kext, when set, gives each matrix's inner extent: the k-stages past it are
+// skipped.  That is exact only where both operands are zero beyond the
+// extent (ragged blocks zero-padded on packing).
 template <Mma MM, int T, bool BKN, typename TA, typename TB, typename TC>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, const int32_t* __restrict__ kext) {
   using Tr = MmaTraits<MM>;
   using L = typename Tr::lds_t;
   using acc_t = typename Tr::acc_t;
@@ -276,7 +279,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   gload(0);
   sstore(0);
   __syncthreads();
-  const int nstage = n / BK;
+  int nstage = n / BK;
+  if (kext) nstage = min(nstage, max(0, (kext[mat] + BK - 1) / BK));
   for (int s = 0; s < nstage; ++s) {
     const int cur = s & 1;
     if (s + 1 < nstage) gload((s + 1) * BK);

@@ -75,6 +75,10 @@ struct GemmCall {
   bool sym = true;
   bool transC = false;
   bool nn = false;  // B read k-major: C = A B (no symmetry assumed)
+  // Per-matrix inner extent, or null for n.  Only the tiled kernel uses it;
+  // the others run the full n, which gives the same result because the
+  // operands are zero beyond it.
+  const int32_t* kext = nullptr;
 };
 
 #define HIP_TRY_ERR(expr)         \
@@ -250,17 +254,17 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
   if constexpr (std::is_same<TB, float>::value || std::is_same<TB, double>::value || f16_in) {
     if (c.nn) {
       if (T == 128)
-        hipLaunchKernelGGL((gemm_kernel<MM, 128, true, TA, TB, TC>), grid, dim3(256), 0, st, g);
+        hipLaunchKernelGGL((gemm_kernel<MM, 128, true, TA, TB, TC>), grid, dim3(256), 0, st, g, c.kext);
       else
-        hipLaunchKernelGGL((gemm_kernel<MM, 64, true, TA, TB, TC>), grid, dim3(256), 0, st, g);
+        hipLaunchKernelGGL((gemm_kernel<MM, 64, true, TA, TB, TC>), grid, dim3(256), 0, st, g, c.kext);
       return hipGetLastError();
     }
   }
   if (c.nn) return hipErrorInvalidValue;
   if (T == 128)
-    hipLaunchKernelGGL((gemm_kernel<MM, 128, false, TA, TB, TC>), grid, dim3(256), 0, st, g);
+    hipLaunchKernelGGL((gemm_kernel<MM, 128, false, TA, TB, TC>), grid, dim3(256), 0, st, g, c.kext);
   else
-    hipLaunchKernelGGL((gemm_kernel<MM, 64, false, TA, TB, TC>), grid, dim3(256), 0, st, g);
+    hipLaunchKernelGGL((gemm_kernel<MM, 64, false, TA, TB, TC>), grid, dim3(256), 0, st, g, c.kext);
   return hipGetLastError();
 }
 
@@ -1157,7 +1161,7 @@ shampoo_status pack_impl(const shampoo_matrix* mats, int32_t nparams, const sham
 }
 
 shampoo_status stats_impl(const void* g, const void* gt, shampoo_dtype gdt, int64_t nblk, int32_t B, void* LR,
-                          shampoo_dtype sdt, double beta2, hipStream_t st) {
+                          shampoo_dtype sdt, double beta2, hipStream_t st, const int32_t* valid = nullptr) {
   if (nblk < 0) return fail(SHAMPOO_E_INVALID, "nblk < 0");
   if (B < 64 || B % 64 != 0) return fail(SHAMPOO_E_UNSUPPORTED, "B = %d: must be a positive multiple of 64", B);
   if (!(beta2 >= 0.0 && beta2 <= 1.0)) return fail(SHAMPOO_E_INVALID, "beta2 = %g not in [0, 1]", beta2);
@@ -1174,6 +1178,13 @@ shampoo_status stats_impl(const void* g, const void* gt, shampoo_dtype gdt, int6
   cl.A = g; cl.B = g; cl.D = LR; cl.C = LR; cl.C2 = nullptr; cl.alpha = a; cl.beta = b; cl.sym = true;
   GemmCall cr = cl;
   cr.A = gt; cr.B = gt; cr.D = (unsigned char*)LR + half; cr.C = (unsigned char*)LR + half;
+  // With the blocks' valid sizes (rows in valid[0, nblk), columns in
+  // valid[nblk, 2 nblk)), each product stops at the block's inner extent:
+  // G G^T sums over G's columns, G^T G over its rows.
+  if (valid) {
+    cl.kext = valid + nblk;
+    cr.kext = valid;
+  }
   if (sdt == SHAMPOO_F64) {
     if (gdt == SHAMPOO_F32) {
       HIP_TRY((gemm<Mma::F64, float, float, double>(cl, B, nblk, st)));
@@ -1475,7 +1486,7 @@ shampoo_status step_impl(const shampoo_step_args* a, hipStream_t st) {
     LAUNCH_CHECK("valid");
   }
   // 2. statistics
-  r = stats_impl(g, gt, a->g_dt, nblk, B, a->LR, a->stats_dt, a->beta2, st);
+  r = stats_impl(g, gt, a->g_dt, nblk, B, a->LR, a->stats_dt, a->beta2, st, valid);
   if (r != SHAMPOO_OK) return r;
   // 3. inverse roots of the 2 nblk factors
   if (a->recompute_roots) {
