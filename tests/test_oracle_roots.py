@@ -84,6 +84,41 @@ def test_power_iteration_bounds_and_exactness():
         assert abs(rhoh - lmax) / lmax < 0.2
 
 
+def test_power_iteration_half_branch_hand_rounded():
+    """The half-precision branch on a 3 x 3 case rounded by hand.
+
+    IEEE half keeps 11 significant bits, so x in [2^e, 2^(e+1)) rounds to a
+    multiple of 2^(e-10), ties to even.  The matrix entries:
+      0.1 in [2^-4, 2^-3): 0.1 * 2^14 = 1638.4 -> 1638 / 2^14 = 819 / 8192;
+      0.3 in [2^-2, 2^-1): 0.3 * 2^12 = 1228.8 -> 1229 / 4096;
+      1, 0.5 and 0.25 are exact.
+    Start vector (1, 2, 3) / sqrt(14) = (0.26726, 0.53452, 0.80178):
+      0.26726 * 2^12 = 1094.70 -> 1095 / 4096;
+      0.53452 * 2^11 = 1094.70 -> 1095 / 2048;
+      0.80178 * 2^11 = 1642.05 -> 1642 / 2048 = 821 / 1024.
+    One product with the rounded matrix, normalised, gives
+    (0.44530, 0.74214, 0.50093), rounded in turn:
+      0.44530 * 2^12 = 1823.95 -> 1824 / 4096 = 57 / 128;
+      0.74214 * 2^11 = 1519.90 -> 1520 / 2048 = 95 / 128;
+      0.50093 * 2^11 = 1025.91 -> 1026 / 2048 = 513 / 1024.
+    The Rayleigh quotient of that rounded vector with the rounded matrix is
+    the oracle's answer.  Without the roundings it differs by 2e-5, so a
+    rounding skipped or taken in another place fails the 1e-13 check."""
+    A = np.array([[1.0, 0.1, 0.0], [0.1, 0.5, 0.3], [0.0, 0.3, 0.25]])
+    Am = np.array([[1.0, 819 / 8192, 0.0], [819 / 8192, 0.5, 1229 / 4096], [0.0, 1229 / 4096, 0.25]])
+    v0 = np.array([1095 / 4096, 1095 / 2048, 821 / 1024])
+    v1 = Am @ v0
+    v1 = v1 / np.linalg.norm(v1)
+    assert np.allclose(v1, [0.44530, 0.74214, 0.50093], atol=5e-6)  # the values rounded above
+    v1h = np.array([57 / 128, 95 / 128, 513 / 1024])
+    w = Am @ v1h
+    want = float(v1h @ w / (v1h @ v1h))
+    rho, j, rq = oracle.power_iteration(A, np.array([[1.0, 2.0, 3.0]]), 1, half_operands=True)
+    assert j == 0 and abs(rho - want) <= 1e-13 * want
+    rho_full, _, _ = oracle.power_iteration(A, np.array([[1.0, 2.0, 3.0]]), 1, half_operands=False)
+    assert abs(rho_full - want) > 1e-5 * want
+
+
 @pytest.mark.parametrize("p", [2, 4])
 def test_cn_scalar_and_matrix(p):
     a = np.logspace(-6, 0, 25)

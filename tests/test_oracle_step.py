@@ -109,6 +109,51 @@ def test_adam_graft_step1_and_norm_invariant():
         assert np.allclose(W[p], -1e-3 * Dg[p], atol=1e-18)
 
 
+def test_adam_graft_constant_gradient_every_step():
+    """A constant gradient G gives m_t = (1 - beta1^t) G and v_t = (1 - beta2^t)
+    G^2, so the bias-corrected direction is G / (|G| + eps_g) at every t.  A
+    state that is not carried between steps, or a bias correction taken at a
+    fixed t, leaves m_hat != G from t = 2 on."""
+    gen = np.random.default_rng(9)
+    G = gen.standard_normal((4, 6))
+    want = G / (np.abs(G) + 1e-8)
+    state = {"m": np.zeros((4, 6)), "v": np.zeros((4, 6))}
+    for t in range(1, 6):
+        d = oracle.graft_direction("adam", G, state, t, beta1=0.9, beta2=0.999, eps_g=1e-8)
+        assert np.allclose(d, want, rtol=1e-12, atol=0)
+    # through the step: the grafted norm is ||G / (|G| + eps_g)|| at every step
+    opt = oracle.ShampooOracle([(4, 6)], [8], beta2=0.999, eps=1e-12, graft="adam", lr=1e-3)
+    W = [np.zeros((4, 6))]
+    for t in range(5):
+        _, Dg = opt.step(W, [G])
+        assert np.isclose(np.linalg.norm(Dg[0]), np.linalg.norm(want), rtol=1e-12)
+
+
+def test_adam_graft_two_steps_hand_computed():
+    """Two steps with different gradients, beta1 = 1/2, beta2 = 3/4, eps_g = 0:
+    m_1 = G_1/2 = (1, -1/2), v_1 = G_1^2/4 = (1, 1/4);
+    m_2 = m_1/2 + G_2/2 = (5/2, 5/4), v_2 = 3 v_1/4 + G_2^2/4 = (19/4, 39/16);
+    m_hat = m_2 / (1 - 1/4) = (10/3, 5/3), v_hat = v_2 / (1 - 9/16) = (76/7, 39/7);
+    Delta_2 = m_hat / sqrt(v_hat)."""
+    G1, G2 = np.array([[2.0, -1.0]]), np.array([[4.0, 3.0]])
+    state = {"m": np.zeros((1, 2)), "v": np.zeros((1, 2))}
+    d1 = oracle.graft_direction("adam", G1, state, 1, beta1=0.5, beta2=0.75, eps_g=0.0)
+    assert np.allclose(d1, [[1.0, -1.0]], rtol=1e-15)
+    d2 = oracle.graft_direction("adam", G2, state, 2, beta1=0.5, beta2=0.75, eps_g=0.0)
+    want = np.array([[(10 / 3) / np.sqrt(76 / 7), (5 / 3) / np.sqrt(39 / 7)]])
+    assert np.allclose(d2, want, rtol=1e-14, atol=0)
+    assert np.allclose(state["m"], [[2.5, 1.25]], rtol=1e-15) and np.allclose(state["v"], [[4.75, 2.4375]], rtol=1e-15)
+    # the same two steps through the oracle's step: the grafted step has
+    # ||Delta_2|| as its norm and D's direction
+    opt = oracle.ShampooOracle([(1, 2)], [2], beta2=0.999, eps=1e-12, graft="adam", lr=1.0, beta1=0.5,
+                               graft_beta2=0.75, eps_g=0.0)
+    W = [np.zeros((1, 2))]
+    opt.step(W, [G1])
+    D, Dg = opt.step(W, [G2])
+    assert np.isclose(np.linalg.norm(Dg[0]), np.linalg.norm(want), rtol=1e-13)
+    assert np.allclose(Dg[0] / np.linalg.norm(Dg[0]), D[0] / np.linalg.norm(D[0]), atol=1e-14)
+
+
 def test_momentum_graft_two_steps():
     gen = np.random.default_rng(7)
     shapes = [(5, 8)]
