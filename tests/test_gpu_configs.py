@@ -1,9 +1,12 @@
-"""GPU parity at the full workload sizes, checked on sampled outputs.
+"""GPU parity at the full workload sizes.
 
 * 1024 SPD blocks 512 x 512 with lambda in [1e-8, 1] (the benchmark input),
   Newton-DB 28 + 17 with power-iteration scaling, in the launch configuration
-  the benchmark times: float64 to 1e-4 on sampled blocks; float32 blocks are
-  either flagged non-finite or match on the eigen-directions float32 resolves.
+  the benchmark times: the float64 chain against the oracle on every one of
+  the 1024 blocks, to the stated 1e-4.  Float32 and half-precision products
+  are diagnostics there (float32 cannot resolve condition number 1e8): their
+  non-finite blocks must be flagged, and finite float32 blocks must match on
+  the eigen-directions float32 resolves.
 * The 12-layer decoder set (151 M parameters, 144 blocks of 1024): all
   parameters stepped on the GPU, the oracle run on sampled parameters (grafting
   is per parameter and blocks are independent, so a sampled parameter's
@@ -19,7 +22,7 @@ import pytest
 
 import oracle
 import synthetic
-from helpers import rel_fro, to_dev, bf16_tensor, log, f32_direction_floor
+from helpers import rel_fro, to_dev, bf16_tensor, log
 
 pytestmark = pytest.mark.gpu
 
@@ -28,6 +31,21 @@ pytestmark = pytest.mark.gpu
 def mir():
     import matrix_inverse_roots_amd as m
     return m
+
+
+def all_blocks_vs_oracle(X, A64):
+    """Relative Frobenius error of every block against the oracle's eigh root,
+    the blocks spread over the host's cores (one BLAS thread each)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    import threadpoolctl
+
+    def one(i):
+        return rel_fro(X[i], oracle.inverse_root_eigh(A64[i], 4))
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with threadpoolctl.threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        return np.array(list(ex.map(one, range(A64.shape[0]))))
 
 
 def test_spd_stack_1024x512_newton_db_full_size(mir):
@@ -45,11 +63,14 @@ def test_spd_stack_1024x512_newton_db_full_size(mir):
     mir.shampoo_inverse_root(inp, out, 4, opts, flags=flags)
     torch.cuda.synchronize()
     assert int(flags.sum().item()) == 0
-    X = out[sample].cpu().numpy()
+    X = out.cpu().numpy()
     del inp, out
-    worst = max(rel_fro(X[k], oracle.inverse_root_eigh(A64[i], 4)) for k, i in enumerate(sample))
-    log(f"1024 x 512^2 f64 NDB: worst sampled rel err {worst:.2e}")
-    assert worst < 1e-4
+    errs = all_blocks_vs_oracle(X, A64)
+    del X
+    worst = int(np.argmax(errs))
+    log(f"1024 x 512^2 f64 NDB: all {n} blocks vs the oracle, worst rel err {errs[worst]:.2e} (block {worst}), "
+        f"median {np.median(errs):.2e}")
+    assert errs.max() < 1e-4
     # float32 chain: non-finite blocks must be flagged, finite ones checked on
     # the eigen-directions float32 can resolve
     A32 = A64.astype(np.float32)
@@ -82,43 +103,59 @@ def test_spd_stack_1024x512_newton_db_full_size(mir):
     log(f"1024 x 512^2 f16 NDB: {int((~finite).sum())} of {n} blocks non-finite, all flagged")
 
 
-def _decoder_run(mir, compute, stats64, sample):
+def _decoder_run(mir, compute, stats64, sample, fallback="none", **root_kw):
     import torch
     shapes = synthetic.decoder_shapes()
     grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
     W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
-    opt = mir.Shampoo(W, block_size=1024, beta2=0.999, eps=1e-12, root=mir.RootOpts(method="cn", iters=34, compute=compute),
-                      graft="adam", lr=1e-3, grad_dtype=torch.bfloat16,
+    opt = mir.Shampoo(W, block_size=1024, beta2=0.999, eps=1e-12,
+                      root=mir.RootOpts(method="cn", iters=34, compute=compute, **root_kw),
+                      graft="adam", lr=1e-3, grad_dtype=torch.bfloat16, fallback=fallback,
                       stats_dtype=torch.float64 if stats64 else torch.float32)
     sshapes = [shapes[i] for i in sample]
     orc = oracle.ShampooOracle(sshapes, [1024] * len(sample), beta2=0.999, eps=1e-12, graft="adam", lr=1e-3)
     Wo = [np.zeros(s) for s in sshapes]
     errs = []
-    tol = 1e-4
     for t in range(3):
+        for f in opt.flags():
+            f.zero_()
         opt.step([bf16_tensor(g) for g in grads[t]])
         orc.step(Wo, [synthetic.bf16_bits_to_f32(grads[t][i]).astype(np.float64) for i in sample])
-        if not stats64:
-            for b in range(orc.table.shape[0]):
-                tol = max(tol, 4 * f32_direction_floor(orc.L[b], orc.R[b], eps=1e-12))
         torch.cuda.synchronize()
         e = max(rel_fro(W[i].cpu().numpy(), Wo[k]) for k, i in enumerate(sample))
-        nflag = sum(int(f.sum().item()) for f in opt.flags())
-        log(f"decoder set ({compute}, stats {'f64' if stats64 else 'f32'}) step {t + 1}: sampled rel err {e:.2e} "
-            f"(tolerance {tol:.2e}), flags {nflag}")
-        assert nflag == 0
-        errs.append((e, tol))
+        fl = torch.cat(opt.flags()).cpu().numpy()
+        log(f"decoder set ({compute}, stats {'f64' if stats64 else 'f32'}, {root_kw}) step {t + 1}: sampled rel err "
+            f"{e:.2e}, flags {np.unique(fl).tolist()} ({int((fl != 0).sum())} factors)")
+        if fallback == "none":
+            assert not fl.any()
+        else:
+            assert not (fl & (mir.FLAG_NONFINITE | mir.FLAG_KEPT_PREVIOUS)).any()
+        errs.append(e)
     return errs
 
 
 def test_decoder_set_full_size_f64(mir):
+    """Float64 statistics, chain and products: the stated 1e-4."""
     errs = _decoder_run(mir, "f64", True, sample=[0, 1, 2, 3, 46, 47])
-    assert all(e < t for e, t in errs)
+    assert all(e < 1e-4 for e in errs)
 
 
-def test_decoder_set_full_size_f32(mir):
+def test_decoder_set_full_size_f32_chain_residual_checked(mir):
+    """Float64 statistics, a float32 coupled Newton chain stopping at
+    ||M - I||_F <= 1e-4, its device residual checked against 1e-4 and the
+    float64 recomputation as fallback (step 1's factors fail the check):
+    the stated 1e-4."""
+    errs = _decoder_run(mir, "f32", True, sample=[0, 1, 2, 3, 46, 47], fallback="f64", tol=1e-4,
+                        residual_bound=1e-4)
+    assert all(e < 1e-4 for e in errs)
+
+
+def test_decoder_set_full_size_f32_diagnostic(mir):
+    """Float32 diagnostic, not a parity test: float32 statistics of the
+    step-1 single-Gram factors (condition number about 4e6) cannot reach
+    1e-4 (measured 3.0e-2, 2.5e-2, 2.2e-2); fixed ceiling 5e-2."""
     errs = _decoder_run(mir, "f32", False, sample=[0, 3, 45])
-    assert all(e < t for e, t in errs)
+    assert all(e < 5e-2 for e in errs)
 
 
 def test_decoder_set_full_size_cn_half_products(mir):

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synthetic
-from helpers import rel_fro, to_dev, bf16_tensor, log, f32_direction_floor
+from helpers import rel_fro, to_dev, bf16_tensor, log
 
 pytestmark = pytest.mark.gpu
 
@@ -203,12 +203,10 @@ def test_float64_statistics_and_direction(mir, gdt):
 
 
 def run_steps(mir, shapes, block_sizes, grads, steps, hp, root_kw, oracle_root="eigh", grad_bf16=False,
-              cheb_degree=16, check_every=True, floor=False, stats64=False, allow_flags=False):
-    """Run the GPU optimizer and the oracle side by side; return per-step
-    (error, tolerance).  The tolerance is 1e-4, or with ``floor`` the larger of
-    1e-4 and 4x the float32 rounding floor of the directions so far
-    (helpers.f32_direction_floor over every block's factors).  ``stats64``
-    keeps statistics, roots and preconditioning products in float64."""
+              cheb_degree=16, check_every=True, stats64=False, allow_flags=False):
+    """Run the GPU optimizer and the oracle side by side; return the worst
+    parameter relative error after each checked step.  ``stats64`` keeps
+    statistics, roots and preconditioning products in float64."""
     import torch
     W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
     opt = mir.Shampoo(W, block_size=(lambda m, n: block_sizes[(m, n)]) if isinstance(block_sizes, dict) else block_sizes,
@@ -220,7 +218,6 @@ def run_steps(mir, shapes, block_sizes, grads, steps, hp, root_kw, oracle_root="
                                momentum=hp.get("momentum", 0.9))
     Wo = [np.zeros(s) for s in shapes]
     errs = []
-    tol = 1e-4
     for t in range(steps):
         gs = grads[t]
         if grad_bf16:
@@ -231,86 +228,124 @@ def run_steps(mir, shapes, block_sizes, grads, steps, hp, root_kw, oracle_root="
             hg = [g.astype(np.float64) for g in gs]
         opt.step(dg)
         orc.step(Wo, hg)
-        if floor:
-            for b in range(orc.table.shape[0]):
-                tol = max(tol, 4 * f32_direction_floor(orc.L[b], orc.R[b], eps=hp["eps"]))
         if check_every or t == steps - 1:
             torch.cuda.synchronize()
             e = max(rel_fro(w.cpu().numpy(), wo) for w, wo in zip(W, Wo))
             fl = sum(int(f.sum().item()) for f in opt.flags())
-            errs.append((e, tol))
-            log(f"step {t + 1}: worst parameter rel err {e:.2e} (tolerance {tol:.2e}), flags {fl}")
+            errs.append(e)
+            log(f"step {t + 1}: worst parameter rel err {e:.2e}, flags {fl}")
             assert allow_flags or fl == 0
     return errs
 
 
-@pytest.mark.parametrize("compute", ["f32", "f64"])
-def test_single_matrix_ten_steps(mir, compute):
+def test_single_matrix_ten_steps(mir):
     """One 256 x 128 float32 parameter, block 128 (2 blocks), N(0,1) gradients
     from seed 0, 10 steps, beta2 = 1, eps = 1e-12, SGD grafting lr 0.1;
     coupled Newton 30 iterations.  The step-1 factors of a square Gaussian
-    block have condition numbers up to 1e6: float32 (statistics and chain) is
-    held to its floor, the float64 path (statistics, chain and products) to
-    1e-4."""
+    block have condition numbers up to 1e6; the float64 path (statistics,
+    chain and products) meets the stated 1e-4 at every step."""
     grads = synthetic.gaussian_grads(0, [(256, 128)], 10, 1.0)
     errs = run_steps(mir, [(256, 128)], 128, grads, 10,
-                     dict(beta2=1.0, eps=1e-12, graft="sgd", lr=0.1), dict(method="cn", iters=30, compute=compute),
-                     floor=(compute == "f32"), stats64=(compute == "f64"))
-    assert all(e < t for e, t in errs)
+                     dict(beta2=1.0, eps=1e-12, graft="sgd", lr=0.1), dict(method="cn", iters=30, compute="f64"),
+                     stats64=True)
+    assert all(e < 1e-4 for e in errs)
+
+
+def test_single_matrix_ten_steps_f32_diagnostic(mir):
+    """Float32 diagnostic, not a parity test: the same ten steps with float32
+    statistics and chain.  Float32 rounding of the step-1 factors (condition
+    number 1e6) already moves the direction by about 5e-4, so this path misses
+    the stated 1e-4 (measured 6.3e-4 at step 1, 2.0e-4 at step 10); a fixed
+    ceiling of 1e-3 guards against regressions."""
+    grads = synthetic.gaussian_grads(0, [(256, 128)], 10, 1.0)
+    errs = run_steps(mir, [(256, 128)], 128, grads, 10,
+                     dict(beta2=1.0, eps=1e-12, graft="sgd", lr=0.1), dict(method="cn", iters=30, compute="f32"))
+    log(f"single parameter, float32 diagnostic, error per step: {errs}")
+    assert all(e < 1e-3 for e in errs)
 
 
 @pytest.mark.parametrize("tol", [0.0, 1e-4])
 def test_ragged_blocks_momentum_and_ndb(mir, tol):
     """Ragged blocks (grouped roots), Newton-DB with power scaling, momentum
-    grafting; with a tolerance each group's calls stop at convergence."""
+    grafting, float32; with a tolerance each group's calls stop at
+    convergence.  eps = 1e-3 bounds the factors' condition numbers, and the
+    float32 path meets the stated 1e-4."""
     shapes = [(300, 130), (64, 64), (5, 200)]
     grads = synthetic.gaussian_grads(21, shapes, 3, 0.1)
     errs = run_steps(mir, shapes, 128, grads, 3,
                      dict(beta2=0.999, eps=1e-3, graft="momentum", lr=0.1, momentum=0.9),
-                     dict(method="ndb", scaling="power", iters=24, iters2=16, tol=tol), floor=True)
-    assert all(e < t for e, t in errs)
+                     dict(method="ndb", scaling="power", iters=24, iters2=16, tol=tol))
+    assert all(e < 1e-4 for e in errs)
 
 
 def test_decoder_layer_adam_bf16(mir):
     """One decoder layer of the d_model 1024 / MLP 4096 set (QKV, out, MLP up,
     MLP down), bfloat16 gradients N(0, 0.02^2), beta2 = 0.999, eps = 1e-12,
     Adam grafting lr 1e-3, block 1024, 3 steps; coupled Newton 34 iterations
-    with statistics, chain and products in float64 (the float32 path's floor
-    on the step-1 factors, whose condition number is about 4 B^2, is checked
-    by the float32 variant below)."""
+    with statistics, chain and products in float64: the stated 1e-4."""
     shapes = synthetic.decoder_shapes(layers=1)
     grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
     errs = run_steps(mir, shapes, 1024, grads, 3, dict(beta2=0.999, eps=1e-12, graft="adam", lr=1e-3),
                      dict(method="cn", iters=34, compute="f64"), grad_bf16=True, check_every=True, stats64=True)
-    assert all(e < 1e-4 for e, _ in errs)
+    assert all(e < 1e-4 for e in errs)
 
 
-def test_decoder_layer_adam_bf16_f32_chain(mir):
+def test_decoder_layer_adam_bf16_f32_diagnostic(mir):
+    """Float32 diagnostic, not a parity test: the decoder layer with float32
+    statistics and chain.  The step-1 factors are single Gram matrices of
+    square Gaussian blocks (condition number about 4 B^2 = 4e6), beyond what
+    float32 statistics resolve, so this path misses 1e-4 (measured 3.1e-2);
+    fixed ceiling 5e-2."""
     shapes = synthetic.decoder_shapes(layers=1)
     grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
     errs = run_steps(mir, shapes, 1024, grads, 3, dict(beta2=0.999, eps=1e-12, graft="adam", lr=1e-3),
-                     dict(method="cn", iters=34), grad_bf16=True, check_every=True, floor=True)
-    log(f"decoder layer f32 chain (error, tolerance) per step: {errs}")
-    assert all(e < t for e, t in errs)
+                     dict(method="cn", iters=34), grad_bf16=True, check_every=True)
+    log(f"decoder layer float32 diagnostic, error per step: {errs}")
+    assert all(e < 5e-2 for e in errs)
 
 
-@pytest.mark.parametrize("chain", ["f32", "f64"])
-def test_decoder_layer_newton_tolerance(mir, chain):
-    """The decoder layer with coupled Newton stopping at a tolerance
-    (||M - I||_F <= 1e-4 in float32, 1e-9 with float64 statistics and chain)
-    instead of the fixed 34 iterations: the same bars as the fixed-count
-    runs (the float32 floor of each step's factors; 1e-4 in float64)."""
+def test_decoder_layer_newton_tolerance(mir):
+    """The decoder layer with float64 statistics and a float64 coupled Newton
+    chain stopping at ||M - I||_F <= 1e-9 instead of the fixed 34
+    iterations: the stated 1e-4."""
     shapes = synthetic.decoder_shapes(layers=1)
     grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
     hp = dict(beta2=0.999, eps=1e-12, graft="adam", lr=1e-3)
-    if chain == "f32":
-        errs = run_steps(mir, shapes, 1024, grads, 3, hp, dict(method="cn", iters=34, tol=1e-4), grad_bf16=True,
-                         check_every=True, floor=True)
-    else:
-        errs = run_steps(mir, shapes, 1024, grads, 3, hp, dict(method="cn", iters=34, tol=1e-9, compute="f64"),
-                         grad_bf16=True, check_every=True, stats64=True)
-    log(f"decoder layer, Newton tolerance ({chain}), (error, tolerance) per step: {errs}")
-    assert all(e < t for e, t in errs)
+    errs = run_steps(mir, shapes, 1024, grads, 3, hp, dict(method="cn", iters=34, tol=1e-9, compute="f64"),
+                     grad_bf16=True, check_every=True, stats64=True)
+    log(f"decoder layer, Newton tolerance (float64), error per step: {errs}")
+    assert all(e < 1e-4 for e in errs)
+
+
+def test_decoder_layer_newton_tolerance_f32_diagnostic(mir):
+    """Float32 diagnostic, not a parity test: float32 statistics and chain
+    stopping at ||M - I||_F <= 1e-4; the same float32 limit as the fixed
+    count (measured 3.1e-2), fixed ceiling 5e-2."""
+    shapes = synthetic.decoder_shapes(layers=1)
+    grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
+    hp = dict(beta2=0.999, eps=1e-12, graft="adam", lr=1e-3)
+    errs = run_steps(mir, shapes, 1024, grads, 3, hp, dict(method="cn", iters=34, tol=1e-4), grad_bf16=True,
+                     check_every=True)
+    log(f"decoder layer, Newton tolerance (float32 diagnostic), error per step: {errs}")
+    assert all(e < 5e-2 for e in errs)
+
+
+@pytest.mark.parametrize("tol", [0.0, 1e-4])
+def test_decoder_layer_f32_chain_residual_checked(mir, tol):
+    """The decoder layer with float64 statistics and a float32 coupled Newton
+    chain (fixed 34 iterations, or stopping at ||M - I||_F <= 1e-4) whose
+    device residual is checked against 1e-4, with the float64 recomputation
+    as fallback: step 1's single-Gram factors fail the check and are
+    recomputed in float64, later factors (condition number 33, then 14) keep
+    their float32 roots.  The stated 1e-4 at every step."""
+    shapes = synthetic.decoder_shapes(layers=1)
+    grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
+    errs = run_steps(mir, shapes, 1024, grads, 3,
+                     dict(beta2=0.999, eps=1e-12, graft="adam", lr=1e-3, fallback="f64", residuals=True),
+                     dict(method="cn", iters=34, tol=tol, residual_bound=1e-4), grad_bf16=True, check_every=True,
+                     stats64=True, allow_flags=True)
+    log(f"decoder layer, float32 chain checked by its residual (tol {tol}), error per step: {errs}")
+    assert all(e < 1e-4 for e in errs)
 
 
 def test_decoder_layer_cn_half_products_with_f64_fallback(mir):
@@ -365,7 +400,7 @@ def test_bottleneck_subset_chebyshev_momentum(mir, cheb_eval, compute):
     # float64 statistics and chain: the error is the float32 weights' rounding;
     # half-precision products take the half-precision bar
     bar = {"f64": 1e-6, "f32": 1e-4, "f16": 2e-2}[compute]
-    assert all(e < bar for e, _ in errs)
+    assert all(e < bar for e in errs)
 
 
 def test_step_deterministic_and_infrequent_roots(mir):
