@@ -107,19 +107,24 @@ typedef enum shampoo_graft {
                                          recomputed with the float64 chain */
 #define SHAMPOO_FLAG_KEPT_PREVIOUS 16 /* shampoo_step fallback: the factor's
                                          previous root was kept */
+#define SHAMPOO_FLAG_RESIDUAL 32  /* the solver residual exceeded
+                                     shampoo_root_opts.residual_bound (or was
+                                     not finite) */
 
-/* What shampoo_step does with a factor whose new root is not finite (or
- * whose scale is zero).  [DIST] abstract: the distributed implementation
- * retries a failed lower-precision root computation at higher precision. */
+/* What shampoo_step does with a factor whose new root failed: not finite,
+ * a zero scale, or (when root.residual_bound > 0) a solver residual above the
+ * bound.  [NOTES] "Spreading the preconditioners across GPUs ...": a root
+ * whose float32 eigendecomposition fails is computed again in float64. */
 typedef enum shampoo_fallback {
   SHAMPOO_FALLBACK_NONE = 0,     /* write the root as computed and flag it */
   SHAMPOO_FALLBACK_KEEP = 1,     /* keep the factor's previous root */
-  SHAMPOO_FALLBACK_F64 = 2       /* recompute the non-finite factors with the
-                                    float64 chain (same method and counts),
-                                    keeping the previous root where that also
-                                    fails (and for zero scales); synchronises
-                                    the stream to count them; as KEEP when
-                                    root.compute is already F64 */
+  SHAMPOO_FALLBACK_F64 = 2       /* recompute the non-finite and residual-
+                                    flagged factors with the float64 chain
+                                    (same method and counts, no residual
+                                    check), keeping the previous root where
+                                    that is not finite (and for zero scales);
+                                    synchronises the stream to count them; as
+                                    KEEP when root.compute is already F64 */
 } shampoo_fallback;
 
 /* One row of a block table (32 bytes, plain old data).  [DASH] "4. Blocking
@@ -187,7 +192,19 @@ typedef struct shampoo_param {
  *   float32 up to v = 1024.  Each check synchronises the stream with the
  *   host (one flag read), so work queued after it on other streams is not
  *   enqueued until the solve ends; `iters` stays the upper bound; the
- *   float64 recomputation of shampoo_step's fallback runs the full count. */
+ *   float64 recomputation of shampoo_step's fallback runs the full count.
+ * residual_out_dev, residual_bound: the solver residual ||X^p A_s - I||_F /
+ *   sqrt(v) of each matrix's chain result X (before unscaling; equal to
+ *   ||out^p (in + eps I) - I||_F / sqrt(v)), v the valid size, from p - 1
+ *   or log2(p) full products and one with the regenerated A_s, all in the
+ *   chain's iterate precision (float32 for F32 and F16 chains, float64 for
+ *   F64), and one Frobenius pass.  It is computed when residual_out_dev
+ *   (device float32 [n]) is non-NULL or residual_bound > 0; residual_bound > 0
+ *   sets SHAMPOO_FLAG_RESIDUAL on matrices whose residual exceeds it or is
+ *   not finite (matrices with a zero scale are left to ZERO_SCALE).  The
+ *   products need up to three iterate buffers beside the result, which the
+ *   workspace query includes.  For Chebyshev the residual also measures the
+ *   fit's own error (the polynomial approximates (A_s + cheb_eps I)^(-1/p)). */
 typedef struct shampoo_root_opts {
   int32_t method;
   int32_t scaling;
@@ -203,6 +220,8 @@ typedef struct shampoo_root_opts {
   double cheb_eps;
   const float* pi_start_dev;
   double tol;
+  float* residual_out_dev;
+  double residual_bound;
 } shampoo_root_opts;
 
 /* Arguments of one shampoo_step over one stack (one block size B). */

@@ -29,6 +29,7 @@ SCALE_FROBENIUS, SCALE_POWER = 0, 1
 CHEB_CLENSHAW, CHEB_PS = 0, 1
 GRAFT_SGD, GRAFT_MOMENTUM, GRAFT_ADAM, GRAFT_NONE = 0, 1, 2, 3
 FLAG_NONFINITE, FLAG_ZERO_SCALE, FLAG_PI_FALLBACK, FLAG_RECOMPUTED_F64, FLAG_KEPT_PREVIOUS = 1, 2, 4, 8, 16
+FLAG_RESIDUAL = 32
 FALLBACKS = {"none": 0, "keep": 1, "f64": 2}
 
 METHODS = {"cn": CN, "ndb": NDB, "chebyshev": CHEBYSHEV}
@@ -68,7 +69,8 @@ class RootOptsC(ctypes.Structure):
                 ("pi_iters", ctypes.c_int32), ("cheb_degree", ctypes.c_int32),
                 ("cheb_points", ctypes.c_int32), ("cheb_eval", ctypes.c_int32),
                 ("eps", ctypes.c_double), ("cheb_eps", ctypes.c_double),
-                ("pi_start_dev", ctypes.c_void_p), ("tol", ctypes.c_double)]
+                ("pi_start_dev", ctypes.c_void_p), ("tol", ctypes.c_double),
+                ("residual_out_dev", ctypes.c_void_p), ("residual_bound", ctypes.c_double)]
 
 
 class StepArgsC(ctypes.Structure):
@@ -196,13 +198,17 @@ class RootOpts:
     cheb_eps: Optional[float] = None   # defaults to eps
     pi_start: object = None       # device float32 [pi_vectors, B]
     tol: float = 0.0              # CN / NDB, f32 or f64: stop once ||M - I||_F <= tol (0: run iters)
+    residual_out: object = None   # device float32 [n]: ||X^p A_s - I||_F / sqrt(v) per matrix
+    residual_bound: float = 0.0   # > 0: FLAG_RESIDUAL where the residual exceeds it
 
     def c(self):
         return RootOptsC(METHODS[self.method], SCALINGS[self.scaling], DTYPES[self.compute],
                          int(self.iters), int(self.iters2), int(self.pi_vectors), int(self.pi_iters),
                          int(self.cheb_degree), int(self.cheb_points), CHEB_EVALS[self.cheb_eval], float(self.eps),
                          float(self.eps if self.cheb_eps is None else self.cheb_eps),
-                         None if self.pi_start is None else self.pi_start.data_ptr(), float(self.tol))
+                         None if self.pi_start is None else self.pi_start.data_ptr(), float(self.tol),
+                         None if self.residual_out is None else self.residual_out.data_ptr(),
+                         float(self.residual_bound))
 
 
 # ---------------------------------------------------------------------------

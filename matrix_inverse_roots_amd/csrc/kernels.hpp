@@ -452,6 +452,29 @@ __global__ void above_tol_kernel(const double* __restrict__ norms, const double*
 }
 
 // ---------------------------------------------------------------------------
+// Solver residual ||X^p A_s - I||_F / sqrt(v) per matrix, from the Frobenius
+// norm of the product X^p A_s - I over the valid region (frob kernels with
+// eps = 0).  A matrix whose residual exceeds `bound` (> 0), or is not
+// finite, is flagged RESIDUAL unless its scale is zero or not finite (its
+// root is then set to 0 and flagged ZERO_SCALE by the final pass).
+// ---------------------------------------------------------------------------
+__global__ void residual_kernel(const double* __restrict__ norms, const double* __restrict__ scale,
+                                const int32_t* __restrict__ valid, int64_t n, int B, double bound,
+                                float* __restrict__ out, int32_t* __restrict__ flags) {
+  const int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (b >= n) return;
+  const int v = valid ? min(max(valid[b], 0), B) : B;
+  const double r = v > 0 ? norms[b] / sqrt((double)v) : 0.0;
+  if (out) out[b] = (float)r;
+  const bool scaled = scale[b] > 0.0 && scale[b] < 1.0e300;
+  if (flags && bound > 0.0 && scaled && !(r <= bound)) atomicOr(flags + b, SHAMPOO_FLAG_RESIDUAL);
+}
+
+// A root computed but not to be committed: not finite, zero scale, or a
+// residual above the bound.
+constexpr int32_t FAILED_ROOT = SHAMPOO_FLAG_NONFINITE | SHAMPOO_FLAG_ZERO_SCALE | SHAMPOO_FLAG_RESIDUAL;
+
+// ---------------------------------------------------------------------------
 // Multi-start power iteration ([DASH] "3. Inverse Root Methods",
 // Power-Iteration), fused with its scaling and persistent over the matrices.
 // Workgroup w (4 waves) takes matrices w, w + gridDim.x, ...  For each, on
@@ -580,8 +603,8 @@ __global__ __launch_bounds__(256) void power_iter_fused_kernel(const TI* __restr
 // access is a coalesced row segment; one flag update per workgroup.
 // ---------------------------------------------------------------------------
 // mode FIN_WRITE: write and flag; FIN_CHECK: flag only (out unused);
-// FIN_COMMIT: write only matrices whose flags show neither NONFINITE nor
-// ZERO_SCALE (set by a FIN_CHECK pass), flags untouched.
+// FIN_COMMIT: write only matrices whose flags show none of NONFINITE,
+// ZERO_SCALE (set by a FIN_CHECK pass) and RESIDUAL, flags untouched.
 enum { FIN_WRITE = 0, FIN_CHECK = 1, FIN_COMMIT = 2 };
 
 template <typename TS, typename TO>
@@ -593,7 +616,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const TS* __restrict__ X,
   __shared__ TS mir_tile[64][65];
   const int tps = B / 64;
   const int64_t b = blockIdx.y;
-  if (mode == FIN_COMMIT && (flags[b] & (SHAMPOO_FLAG_NONFINITE | SHAMPOO_FLAG_ZERO_SCALE))) return;  // uniform
+  if (mode == FIN_COMMIT && (flags[b] & FAILED_ROOT)) return;  // uniform
   const int tr = blockIdx.x / tps, tc = blockIdx.x - (blockIdx.x / tps) * tps;
   const int64_t BB = (int64_t)B * B;
   const TS* Xb = X + b * BB;
@@ -738,7 +761,7 @@ __global__ __launch_bounds__(256) void scatter_matrices_kernel(const unsigned ch
 // Factor-side groups.  gather_sub: dst[i] (s x s) = leading s x s block of
 // the B x B matrix src[idx[i]]; scatter_sub: the B x B matrix dst[idx[i]] =
 // src[i] (s x s) zero-padded to B, skipped where keep is set and flags[i]
-// shows NONFINITE or ZERO_SCALE.  E: raw element type (bit copies); s and B
+// shows a failed root (NONFINITE, ZERO_SCALE or RESIDUAL).  E: raw element type (bit copies); s and B
 // multiples of 64; grid (chunks, m).
 template <typename E>
 __global__ __launch_bounds__(256) void gather_sub_kernel(const E* __restrict__ src, E* __restrict__ dst,
@@ -760,7 +783,7 @@ __global__ __launch_bounds__(256) void scatter_sub_kernel(const E* __restrict__ 
                                                           const int32_t* __restrict__ flags, int keep) {
   constexpr int V = 16 / sizeof(E);
   const int64_t i = blockIdx.y;
-  if (keep && (flags[i] & (SHAMPOO_FLAG_NONFINITE | SHAMPOO_FLAG_ZERO_SCALE))) return;  // uniform
+  if (keep && (flags[i] & FAILED_ROOT)) return;  // uniform
   const E* a = src + i * (int64_t)s * s;
   E* d = dst + (int64_t)idx[i] * B * B;
   const int cpr = B / V;
@@ -779,15 +802,21 @@ __global__ void or_flags_kernel(const int32_t* __restrict__ src, const int32_t* 
   if (i < m) dst[idx[i]] |= src[i];
 }
 
-// Step flags after the fallback: a factor flagged NONFINITE or ZERO_SCALE
-// that was not recomputed kept its previous root; the result is OR-ed into
-// the caller's flags.
+// dst[idx[i]] = src[i] (distinct indices)
+__global__ void scatter_f32_kernel(const float* __restrict__ src, const int32_t* __restrict__ idx, int m,
+                                   float* __restrict__ dst) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < m) dst[idx[i]] = src[i];
+}
+
+// Step flags after the fallback: a factor whose root failed (NONFINITE,
+// ZERO_SCALE or RESIDUAL) and was not recomputed kept its previous root; the
+// result is OR-ed into the caller's flags.
 __global__ void merge_fallback_flags_kernel(const int32_t* __restrict__ fl, int64_t n, int32_t* __restrict__ out) {
   const int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (b >= n) return;
   int32_t f = fl[b];
-  if ((f & (SHAMPOO_FLAG_NONFINITE | SHAMPOO_FLAG_ZERO_SCALE)) && !(f & SHAMPOO_FLAG_RECOMPUTED_F64))
-    f |= SHAMPOO_FLAG_KEPT_PREVIOUS;
+  if ((f & FAILED_ROOT) && !(f & SHAMPOO_FLAG_RECOMPUTED_F64)) f |= SHAMPOO_FLAG_KEPT_PREVIOUS;
   out[b] |= f;
 }
 

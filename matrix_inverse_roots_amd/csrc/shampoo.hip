@@ -317,6 +317,7 @@ struct Plan {
   int gemms = 0;
   bool checks = false;  // the chain holds convergence checks (needs their scratch)
   bool sym_out = false;  // finalize returns the symmetric part (X + X^T)/2
+  bool resid = false;    // the solver residual is computed before the final pass
   std::vector<bool> used;
   int get() {
     for (size_t i = 0; i < used.size(); ++i)
@@ -757,6 +758,8 @@ shampoo_status check_root_args(int64_t n, int32_t B, int32_t p, const shampoo_ro
     return fail(SHAMPOO_E_UNSUPPORTED, "compute dtype %d not supported (F32, F16, F64)", o->compute);
   if (!(o->eps >= 0.0) || !std::isfinite(o->eps)) return fail(SHAMPOO_E_INVALID, "eps must be finite and >= 0");
   if (!(o->tol >= 0.0) || !std::isfinite(o->tol)) return fail(SHAMPOO_E_INVALID, "tol must be finite and >= 0");
+  if (!(o->residual_bound >= 0.0) || !std::isfinite(o->residual_bound))
+    return fail(SHAMPOO_E_INVALID, "residual_bound must be finite and >= 0");
   if (o->tol > 0.0 && o->method == SHAMPOO_CHEBYSHEV)
     return fail(SHAMPOO_E_INVALID, "tol applies to the Newton iterations (CN, NDB), not to Chebyshev");
   if (o->tol > 0.0 && o->compute == SHAMPOO_F16)
@@ -832,6 +835,12 @@ void mark_needs(Plan& P) {
   }
 }
 
+// The solver residual ||X^p A_s - I||_F / sqrt(v) is computed on request:
+// A_s regenerated by a prep pass, X^p by repeated squaring (p a power of two)
+// or repeated multiplication, then X^p A_s - I.  Three buffers besides X.
+constexpr int RESID_BUFS = 3;
+bool want_residual(const shampoo_root_opts* o) { return o->residual_out_dev != nullptr || o->residual_bound > 0.0; }
+
 Plan build_plan(int32_t p, const shampoo_root_opts* o) {
   Plan P;
   switch (o->method) {
@@ -847,6 +856,13 @@ Plan build_plan(int32_t p, const shampoo_root_opts* o) {
     }
   }
   mark_needs(P);
+  if (want_residual(o)) {
+    // the residual products run after the chain, in any three buffers other
+    // than the result, with the Frobenius scratch of the checks
+    P.resid = true;
+    P.checks = true;
+    P.peak = std::max(P.peak, 1 + RESID_BUFS);
+  }
   return P;
 }
 
@@ -899,9 +915,10 @@ hipError_t launch_prep(const void* in, int B, int64_t n, const int32_t* valid, d
   return hipGetLastError();
 }
 
-// keep_flagged: the final pass first only flags (NONFINITE, ZERO_SCALE) and
-// then writes just the matrices left unflagged, so a flagged matrix keeps the
-// previous content of `out` (flags must then be non-null and start at 0).
+// keep_flagged: the final pass first only flags (NONFINITE, ZERO_SCALE; the
+// residual pass before it sets RESIDUAL) and then writes just the matrices
+// left unflagged, so a flagged matrix keeps the previous content of `out`
+// (flags must then be non-null and start at 0).
 template <typename TI, typename TS, Mma MM>
 shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t p, const shampoo_root_opts* o,
                         const Plan& P, const int32_t* valid, float* scale_out, int32_t* flags, void* ws,
@@ -954,6 +971,64 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
     LAUNCH_CHECK("power_iter");
     sc = s;
   }
+  // convergence checks (Newton tolerance) and the solver residual: scratch
+  // after the iterate buffers for the Frobenius partial sums, the per-matrix
+  // norms and a flag that the host reads back
+  unsigned char* chk = bufbase + (size_t)(P.peak > 1 ? P.peak : 1) * bufstride;
+  double* cpart = (double*)chk;
+  double* cnorm = (double*)(chk + align_up((size_t)parts * n * 8));
+  int32_t* notdone = (int32_t*)(chk + align_up((size_t)parts * n * 8) + align_up((size_t)n * 8));
+  // Solver residual of the chain result in buffer x: A_s regenerated from the
+  // input, X^p by repeated squaring (p a power of two) or multiplication,
+  // R = X^p A_s - I, all full products in the iterate precision (the float32
+  // part of half-operand chains); then ||R||_F / sqrt(v) and the flag.
+  auto residual = [&](int x) -> shampoo_status {
+    int fb[RESID_BUFS], nfb = 0;
+    for (int i = 0; i < std::max(P.peak, 1) && nfb < RESID_BUFS; ++i)
+      if (i != x) fb[nfb++] = i;
+    if (nfb < RESID_BUFS) return fail(SHAMPOO_E_INVALID, "internal: residual buffers");
+    const int As = fb[0], t0 = fb[1], t1 = fb[2];
+    const PrepOut q0{buf(As), 1.0, 0.0, nullptr}, none{nullptr, 0.0, 0.0, nullptr};
+    HIP_TRY((launch_prep<TI, TS>(in, B, n, valid, o->eps, sc, 1.0, q0, none, none, st)));
+    constexpr Mma RM = std::is_same<TS, double>::value ? Mma::F64 : Mma::F32;
+    auto mul = [&](int a, int b, int c, double gamma) -> hipError_t {
+      GemmCall g;
+      g.A = buf(a);
+      g.B = buf(b);
+      g.C = buf(c);
+      g.sym = false;
+      g.nn = true;
+      g.gamma = gamma;
+      return gemm<RM, TS, TS, TS>(g, B, n, st);
+    };
+    int cur = x;
+    auto other = [&]() { return cur == t0 ? t1 : t0; };
+    if ((p & (p - 1)) == 0) {
+      for (int q = 1; q < p; q *= 2) {
+        const int t = other();
+        HIP_TRY(mul(cur, cur, t, 0.0));
+        cur = t;
+      }
+    } else {
+      for (int q = 1; q < p; ++q) {
+        const int t = other();
+        HIP_TRY(mul(cur, x, t, 0.0));
+        cur = t;
+      }
+    }
+    const int R = other();
+    HIP_TRY(mul(cur, As, R, -1.0));
+    hipLaunchKernelGGL((frob_partial_kernel<TS>), dim3((unsigned)parts, (unsigned)n), dim3(256), 0, st,
+                       (const TS*)buf(R), B, valid, 0.0, parts, cpart);
+    LAUNCH_CHECK("frob_partial");
+    hipLaunchKernelGGL(frob_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const double*)cpart,
+                       parts, n, cnorm);
+    LAUNCH_CHECK("frob_finish");
+    hipLaunchKernelGGL(residual_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const double*)cnorm, sc,
+                       valid, n, B, o->residual_bound, o->residual_out_dev, flags);
+    LAUNCH_CHECK("residual");
+    return SHAMPOO_OK;
+  };
   auto exec = [&](const Op& op) -> shampoo_status {
     if (op.kind == OP_PREP) {
       PrepOut q[3];
@@ -1016,6 +1091,10 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
       hipLaunchKernelGGL((comb_kernel<TS>), dim3(gx, (unsigned)n), dim3(256), 0, st, ca, B);
       LAUNCH_CHECK("comb");
     } else {
+      if (P.resid) {
+        shampoo_status rr = residual(op.a);
+        if (rr != SHAMPOO_OK) return rr;
+      }
       const int tps = B / 64;
       const dim3 fgrid((unsigned)(tps * tps), (unsigned)n);
       const int sym = P.sym_out ? 1 : 0;
@@ -1033,13 +1112,6 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
     }
       return SHAMPOO_OK;
   };
-  // convergence checks (coupled Newton with a tolerance): scratch after the
-  // iterate buffers for the Frobenius partial sums, the per-matrix norms and
-  // a flag that the host reads back
-  unsigned char* chk = bufbase + (size_t)(P.peak > 1 ? P.peak : 1) * bufstride;
-  double* cpart = (double*)chk;
-  double* cnorm = (double*)(chk + align_up((size_t)parts * n * 8));
-  int32_t* notdone = (int32_t*)(chk + align_up((size_t)parts * n * 8) + align_up((size_t)n * 8));
   // Newton-DB re-plans at convergence: `cur` is the plan being run, `gemms`
   // the products run so far, used1 the iterations of call 1 once it ended
   const Plan* cur = &P;
@@ -1253,7 +1325,7 @@ struct StepLayout {
   std::vector<int> gside;
   std::vector<int64_t> gstart, gcount;
   std::vector<int32_t> gorder;
-  size_t gidx, gvalid, gflags, gin, gout;
+  size_t gidx, gvalid, gflags, gres, gin, gout;
 };
 
 shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
@@ -1301,7 +1373,7 @@ shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
     L->fout = off; off += align_up((size_t)nf * mb);
     L->froot = off; off += L->froot_bytes;
   }
-  L->gidx = L->gvalid = L->gflags = L->gin = L->gout = 0;
+  L->gidx = L->gvalid = L->gflags = L->gres = L->gin = L->gout = 0;
   L->gside.clear();
   L->gstart.clear();
   L->gcount.clear();
@@ -1335,6 +1407,7 @@ shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
       L->gidx = off; off += align_up((size_t)nf * 4);
       L->gvalid = off; off += align_up((size_t)nf * 4);
       L->gflags = off; off += align_up((size_t)nf * 4);
+      L->gres = off; off += align_up((size_t)nf * 4);
       L->gin = off; off += need_io;
       L->gout = off; off += need_io;
     }
@@ -1371,9 +1444,18 @@ shampoo_status step_roots_grouped(const shampoo_step_args* a, const StepLayout& 
     hipLaunchKernelGGL((gather_sub_kernel<E>), dim3(gchunks, (unsigned)m), dim3(256), 0, st, (const E*)a->LR,
                        (E*)(w + L.gin), idx, B, sd);
     LAUNCH_CHECK("gather_sub");
-    shampoo_status r = inverse_root_impl(w + L.gin, w + L.gout, a->stats_dt, m, sd, a->p, &a->root, gv, nullptr, gf,
+    // the group's residuals (if requested) in group order, scattered below
+    shampoo_root_opts og = a->root;
+    float* gr = (float*)(w + L.gres) + L.gstart[g];
+    if (og.residual_out_dev) og.residual_out_dev = gr;
+    shampoo_status r = inverse_root_impl(w + L.gin, w + L.gout, a->stats_dt, m, sd, a->p, &og, gv, nullptr, gf,
                                          w + L.root, L.root_bytes, st, keep_flagged);
     if (r != SHAMPOO_OK) return r;
+    if (a->root.residual_out_dev) {
+      hipLaunchKernelGGL(scatter_f32_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, (const float*)gr, idx,
+                         m, a->root.residual_out_dev);
+      LAUNCH_CHECK("scatter_residual");
+    }
     const unsigned schunks = (unsigned)std::min<int64_t>(64, ((int64_t)B * B / (16 / sizeof(E)) + 255) / 256);
     hipLaunchKernelGGL((scatter_sub_kernel<E>), dim3(schunks, (unsigned)m), dim3(256), 0, st, (const E*)(w + L.gout),
                        (E*)a->roots, idx, B, sd, gf, keep_flagged ? 1 : 0);
@@ -1410,12 +1492,13 @@ shampoo_status step_roots(const shampoo_step_args* a, const StepLayout& L, unsig
   shampoo_status r = roots_of_factors(a, L, w, valid, fl, true, st);
   if (r != SHAMPOO_OK) return r;
   if (L.redo64) {
-    // count the flagged factors on the host, then recompute them in float64
+    // count the failed factors (non-finite, or residual above the bound) on
+    // the host, then recompute them in float64
     std::vector<int32_t> hf((size_t)nf), idx;
     HIP_TRY(hipMemcpyAsync(hf.data(), fl, (size_t)nf * 4, hipMemcpyDeviceToHost, st));
     HIP_TRY(hipStreamSynchronize(st));
     for (int64_t b = 0; b < nf; ++b)
-      if (hf[(size_t)b] & SHAMPOO_FLAG_NONFINITE) idx.push_back((int32_t)b);
+      if (hf[(size_t)b] & (SHAMPOO_FLAG_NONFINITE | SHAMPOO_FLAG_RESIDUAL)) idx.push_back((int32_t)b);
     const int m = (int)idx.size();
     if (m > 0) {
       int32_t* fidx = (int32_t*)(w + L.fidx);
@@ -1423,6 +1506,9 @@ shampoo_status step_roots(const shampoo_step_args* a, const StepLayout& L, unsig
       int32_t* fflags = (int32_t*)(w + L.fflags);
       const int64_t mbytes = (int64_t)B * B * (int64_t)dtype_size(a->stats_dt);
       HIP_TRY(hipMemcpyAsync(fidx, idx.data(), (size_t)m * 4, hipMemcpyHostToDevice, st));
+      // the pageable index vector must outlive its copy, also on the error
+      // returns below: wait for it here (the stream is idle up to it anyway)
+      HIP_TRY(hipStreamSynchronize(st));
       const unsigned chunks = (unsigned)std::min<int64_t>(64, (mbytes / 16 + 255) / 256);
       hipLaunchKernelGGL(gather_matrices_kernel, dim3(chunks, (unsigned)m), dim3(256), 0, st,
                          (const unsigned char*)a->LR, w + L.fin, fidx, mbytes);
@@ -1434,14 +1520,14 @@ shampoo_status step_roots(const shampoo_step_args* a, const StepLayout& L, unsig
       shampoo_root_opts o64 = a->root;
       o64.compute = SHAMPOO_F64;
       o64.tol = 0.0;  // the recomputation runs the full iteration count
+      o64.residual_out_dev = nullptr;  // and keeps its result without a residual check
+      o64.residual_bound = 0.0;
       r = inverse_root_impl(w + L.fin, w + L.fout, a->stats_dt, m, B, a->p, &o64, fvalid, nullptr, fflags,
                             w + L.froot, L.froot_bytes, st, true);
       if (r != SHAMPOO_OK) return r;
       hipLaunchKernelGGL(scatter_matrices_kernel, dim3(chunks, (unsigned)m), dim3(256), 0, st,
                          (const unsigned char*)(w + L.fout), (unsigned char*)a->roots, fidx, fflags, mbytes, fl);
       LAUNCH_CHECK("scatter");
-      // the pageable index vector must outlive its copy
-      HIP_TRY(hipStreamSynchronize(st));
     }
   }
   if (a->flags_dev) {

@@ -53,6 +53,9 @@ class ShampooStack:
         self.LR = torch.zeros((2 * self.nblk, self.B, self.B), dtype=sdt, device=device)
         self.roots = torch.zeros_like(self.LR)
         self.flags = torch.zeros(2 * self.nblk, dtype=torch.int32, device=device)
+        # solver residual of each factor's latest root (NaN until computed)
+        self.residuals = (torch.full((2 * self.nblk,), float("nan"), dtype=torch.float32, device=device)
+                          if hp["residuals"] else None)
         g = hp["graft"]
         self.m = [torch.zeros_like(w) for w in weights] if g in ("momentum", "adam") else None
         self.v = [torch.zeros_like(w) for w in weights] if g == "adam" else None
@@ -80,6 +83,8 @@ class ShampooStack:
             gen.manual_seed(hp["pi_seed"] + self.B)
             self.pi_start = torch.randn((ro.pi_vectors, self.B), generator=gen, device=device, dtype=torch.float32)
             ro = RootOpts(**{**ro.__dict__, "pi_start": self.pi_start})
+        if self.residuals is not None:
+            ro = RootOpts(**{**ro.__dict__, "residual_out": self.residuals})
         a.root = ro.c()
         a.graft = GRAFTS[g]
         a.graft_blockwise = 1 if hp["graft_blockwise"] else 0
@@ -164,13 +169,16 @@ class Shampoo:
     forked from and joined back to the calling stream with events, so that
     one stack's launches fill the gaps and partly idle rounds of another's.
     Power-iteration scaling draws its start vectors once per stack from
-    ``pi_seed``.
+    ``pi_seed``.  residuals: keep each factor's solver residual
+    ||X^p A_s - I||_F / sqrt(v) of its latest root (``residuals()``); with
+    ``root.residual_bound`` > 0 a root above the bound is flagged RESIDUAL
+    and handled by ``fallback`` like a non-finite one.
     """
 
     def __init__(self, params, block_size=1024, beta2=1.0, eps=1e-12, p=4, root=None, graft="sgd",
                  lr=0.1, momentum=0.9, beta1=0.9, graft_beta2=0.999, graft_eps=1e-8,
                  graft_blockwise=False, precondition_frequency=1, grad_dtype=None, stats_dtype=None,
-                 pi_seed=0, fallback="none", group_factors=True, concurrent_stacks=True):
+                 pi_seed=0, fallback="none", group_factors=True, concurrent_stacks=True, residuals=False):
         import torch
         params = list(params)
         if not params:
@@ -188,7 +196,8 @@ class Shampoo:
                        graft_eps=float(graft_eps), graft_blockwise=bool(graft_blockwise),
                        grad_dtype=grad_dtype if grad_dtype is not None else torch.float32,
                        stats_dtype=stats_dtype if stats_dtype is not None else torch.float32,
-                       pi_seed=int(pi_seed), fallback=str(fallback), group_factors=bool(group_factors))
+                       pi_seed=int(pi_seed), fallback=str(fallback), group_factors=bool(group_factors),
+                       residuals=bool(residuals))
         if fallback not in FALLBACKS:
             raise ValueError("fallback must be one of %s" % sorted(FALLBACKS))
         bs_of = block_size if callable(block_size) else (lambda m, n, b=int(block_size): b)
@@ -290,3 +299,8 @@ class Shampoo:
 
     def flags(self):
         return [st.flags for st in self.stacks]
+
+    def residuals(self):
+        """Per stack: the solver residual of each factor's latest root (L
+        factors, then R factors), or None without ``residuals=True``."""
+        return [st.residuals for st in self.stacks]
