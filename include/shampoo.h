@@ -335,6 +335,26 @@ shampoo_status shampoo_inverse_root(const void* in, void* out, shampoo_dtype io_
                                     int32_t* flags_dev, void* ws, size_t ws_bytes,
                                     hipStream_t stream);
 
+/* shampoo_inverse_root without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture into a graph, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, steps,
+ * kernels, results and errors as shampoo_inverse_root; the workspace is a
+ * 64 MiB device array inside the library (one copy per device, allocated
+ * when the library's device code is loaded on that device and held until
+ * the process ends).  Calls needing more scratch than that (the
+ * shampoo_inverse_root_workspace size) fail with E_WORKSPACE before any
+ * launch; e.g. 64 matrices 128 x 128 by coupled Newton or Newton-DB need 20
+ * MiB in float32 and 40 MiB in float64.  Nothing in the scratch needs to
+ * start at zero.
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents: calls that overlap on one device (on different streams,
+ * or from different threads, without ordering between them) race on it.
+ * Calls no hipMalloc, hipFree or allocating library routine. */
+shampoo_status shampoo_inverse_root_noalloc(const void* in, void* out, shampoo_dtype io_dt, int64_t n,
+                                            int32_t B, int32_t p, const shampoo_root_opts* opts,
+                                            const int32_t* valid_dev, float* scale_out_dev,
+                                            int32_t* flags_dev, hipStream_t stream);
+
 /* Workspace bytes for shampoo_precondition: nblk * B * B * sizeof(roots_dt). */
 shampoo_status shampoo_precondition_workspace(int64_t nblk, int32_t B, shampoo_dtype roots_dt,
                                               size_t* bytes);

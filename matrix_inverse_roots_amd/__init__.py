@@ -91,7 +91,8 @@ class StepArgsC(ctypes.Structure):
 EXPORTS = [
     "shampoo_version", "shampoo_last_error", "shampoo_plan_blocks", "shampoo_pack_blocks",
     "shampoo_unpack_blocks", "shampoo_update_stats", "shampoo_inverse_root_workspace",
-    "shampoo_inverse_root", "shampoo_precondition_workspace", "shampoo_precondition",
+    "shampoo_inverse_root", "shampoo_inverse_root_noalloc", "shampoo_precondition_workspace",
+    "shampoo_precondition",
     "shampoo_step_workspace", "shampoo_step", "shampoo_check_flags", "shampoo_timing_enable",
     "shampoo_timing_read", "shampoo_mfma_peak",
 ]
@@ -119,6 +120,8 @@ def _load():
         "shampoo_inverse_root_workspace": ([i64, i32, i32, P(RootOptsC), P(sz)], ctypes.c_int),
         "shampoo_inverse_root": ([vp, vp, ctypes.c_int, i64, i32, i32, P(RootOptsC), vp, vp, vp, vp, sz, vp],
                                  ctypes.c_int),
+        "shampoo_inverse_root_noalloc": ([vp, vp, ctypes.c_int, i64, i32, i32, P(RootOptsC), vp, vp, vp, vp],
+                                         ctypes.c_int),
         "shampoo_precondition_workspace": ([i64, i32, ctypes.c_int, P(sz)], ctypes.c_int),
         "shampoo_precondition": ([vp, ctypes.c_int, vp, ctypes.c_int, i64, i32, vp, vp, sz, vp], ctypes.c_int),
         "shampoo_step_workspace": ([P(StepArgsC), P(sz)], ctypes.c_int),
@@ -297,6 +300,20 @@ def shampoo_inverse_root(inp, out, p, opts, valid=None, scale_out=None, flags=No
     _check(lib.shampoo_inverse_root(_ptr(inp), _ptr(out), _dtype_code(inp), n, B, int(p), ctypes.byref(oc),
                                     _ptr(valid), _ptr(scale_out), _ptr(flags), _ptr(ws), ws.numel(),
                                     _stream(stream)))
+    return out
+
+
+def shampoo_inverse_root_noalloc(inp, out, p, opts, valid=None, scale_out=None, flags=None, stream=None):
+    """shampoo_inverse_root with the library's own fixed device scratch
+    (no workspace, no allocation); calls on one device must not overlap."""
+    for t, nm in ((inp, "inp"), (out, "out"), (valid, "valid"), (scale_out, "scale_out"), (flags, "flags")):
+        _dev(t, nm)
+    n, B = inp.shape[0], inp.shape[1]
+    if out.dtype != inp.dtype or out.shape != inp.shape:
+        raise ValueError("out must match inp")
+    oc = opts.c()
+    _check(lib.shampoo_inverse_root_noalloc(_ptr(inp), _ptr(out), _dtype_code(inp), n, B, int(p), ctypes.byref(oc),
+                                            _ptr(valid), _ptr(scale_out), _ptr(flags), _stream(stream)))
     return out
 
 

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 #include <vector>
@@ -1204,6 +1205,49 @@ shampoo_status inverse_root_impl(const void* in, void* out, shampoo_dtype io_dt,
 }
 
 // ---------------------------------------------------------------------------
+// Allocation-free inverse roots: the workspace lives in a file-scope device
+// array (one copy per device, held until the process ends).  Host code never
+// passes the array's name to a kernel or a copy: in host code it stands for a
+// host-side shadow, not a device address.  Each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+// ---------------------------------------------------------------------------
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** ptr) {
+  static void* addr[MAX_DEVICES] = {nullptr};
+  static std::mutex mu;
+  int dev = 0;
+  HIP_TRY_ERR(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    HIP_TRY_ERR(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
+shampoo_status inverse_root_noalloc_impl(const void* in, void* out, shampoo_dtype io_dt, int64_t n, int32_t B,
+                                         int32_t p, const shampoo_root_opts* o, const int32_t* valid,
+                                         float* scale_out, int32_t* flags, hipStream_t st) {
+  shampoo_status r = check_root_args(n, B, p, o);
+  if (r != SHAMPOO_OK) return r;
+  const size_t need = root_ws_bytes(n, B, build_plan(p, o), o->compute);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(SHAMPOO_E_WORKSPACE,
+                "these arguments need %zu bytes of scratch; the allocation-free entry point holds %zu (use "
+                "shampoo_inverse_root with a workspace)", need, NOALLOC_SCRATCH_BYTES);
+  if (n == 0) return inverse_root_impl(in, out, io_dt, n, B, p, o, valid, scale_out, flags, nullptr, 0, st);
+  void* ws = nullptr;
+  HIP_TRY(noalloc_scratch(&ws));
+  return inverse_root_impl(in, out, io_dt, n, B, p, o, valid, scale_out, flags, ws, NOALLOC_SCRATCH_BYTES, st);
+}
+
+// ---------------------------------------------------------------------------
 // pack, statistics, preconditioning
 // ---------------------------------------------------------------------------
 template <typename E>
@@ -1711,6 +1755,12 @@ shampoo_status shampoo_inverse_root(const void* in, void* out, shampoo_dtype io_
                                     const shampoo_root_opts* opts, const int32_t* valid_dev, float* scale_out_dev,
                                     int32_t* flags_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
   return inverse_root_impl(in, out, io_dt, n, B, p, opts, valid_dev, scale_out_dev, flags_dev, ws, ws_bytes, stream);
+}
+
+shampoo_status shampoo_inverse_root_noalloc(const void* in, void* out, shampoo_dtype io_dt, int64_t n, int32_t B,
+                                            int32_t p, const shampoo_root_opts* opts, const int32_t* valid_dev,
+                                            float* scale_out_dev, int32_t* flags_dev, hipStream_t stream) {
+  return inverse_root_noalloc_impl(in, out, io_dt, n, B, p, opts, valid_dev, scale_out_dev, flags_dev, stream);
 }
 
 shampoo_status shampoo_precondition_workspace(int64_t nblk, int32_t B, shampoo_dtype roots_dt, size_t* bytes) {
