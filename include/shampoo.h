@@ -247,7 +247,9 @@ typedef struct shampoo_step_args {
   float beta1, graft_beta2, graft_eps; /* ADAM */
   int32_t t;                        /* 1-based step count (Adam bias correction) */
   int32_t* flags_dev;               /* device int32 [2 nblk] or NULL */
-  float* dstack;                    /* device f32 [nblk, B, B] or NULL: receives D (ungrafted) */
+  float* dstack;                    /* device f32 [nblk, B, B] or NULL: receives D (ungrafted) on each
+                                       block's valid region (the padding too, unless table_host marks
+                                       ragged blocks) */
   void* ws;
   size_t ws_bytes;
   const shampoo_block* table_host;  /* host copy of table_dev, or NULL.  When given, each factor's
@@ -258,7 +260,13 @@ typedef struct shampoo_step_args {
                                        blocks by shape).  The workspace then depends on it.
                                        The groups are planned on the host from this copy; the
                                        device orders the factors from table_dev, so the two
-                                       must hold the same rows.  Ignored for B > 8192. */
+                                       must hold the same rows.  Ignored for B > 8192.  When some
+                                       block is narrower than B, the statistics and preconditioning
+                                       products also skip each block's padding ([DASH] "4. Blocking
+                                       Strategy": no padded work): L and R are computed on the valid
+                                       rows x rows and cols x cols regions (their padding stays as it
+                                       was, zero from the caller's initialisation), and D on the valid
+                                       rows x cols region, in 64 x 64 tiles. */
 } shampoo_step_args;
 
 /* Version string of the library. */

@@ -174,11 +174,21 @@ template <typename TG, typename TL, int VE> struct BlockKN {
 // operands are copied row by row (16-byte global loads, coalesced per
 // 128-byte row segment); an NN B operand is loaded as VE x VE element blocks
 // (VE = elements per 16 bytes) along its rows and transposed in registers.
-// kext, when set, gives each matrix's inner extent: the k-stages past it are
-// skipped.  That is exact only where both operands are zero beyond the
-// extent (ragged blocks zero-padded on packing).
+// Per-matrix extents (each pointer may be null): a tile whose first row is
+// at or past r[b], or whose first column is at or past c[b], is neither
+// loaded, computed nor written (its workgroup returns at once); k-stages past
+// k[b] are skipped.  Rows and columns refer to the product as computed,
+// before a transposed store.  Exact where both operands are zero beyond the
+// inner extent (ragged blocks zero-padded on packing) and the caller reads
+// only the r x c region (plus partial tiles, which are computed in full).
+struct Extents {
+  const int32_t* r;
+  const int32_t* c;
+  const int32_t* k;
+};
+
 template <Mma MM, int T, bool BKN, typename TA, typename TB, typename TC>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, const int32_t* __restrict__ kext) {
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, Extents ext) {
   using Tr = MmaTraits<MM>;
   using L = typename Tr::lds_t;
   using acc_t = typename Tr::acc_t;
@@ -213,6 +223,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, const int32_t*
     ti = t / g.nt;
     tj = t - ti * g.nt;
   }
+  // tiles outside the matrix's row / column extent: nothing to do (uniform)
+  if ((ext.r && ti * T >= ext.r[mat]) || (ext.c && tj * T >= ext.c[mat])) return;
   const int n = g.n;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -280,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, const int32_t*
   sstore(0);
   __syncthreads();
   int nstage = n / BK;
-  if (kext) nstage = min(nstage, max(0, (kext[mat] + BK - 1) / BK));
+  if (ext.k) nstage = min(nstage, max(0, (ext.k[mat] + BK - 1) / BK));
   for (int s = 0; s < nstage; ++s) {
     const int cur = s & 1;
     if (s + 1 < nstage) gload((s + 1) * BK);

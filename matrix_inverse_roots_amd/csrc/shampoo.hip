@@ -76,9 +76,11 @@ struct GemmCall {
   bool sym = true;
   bool transC = false;
   bool nn = false;  // B read k-major: C = A B (no symmetry assumed)
-  // Per-matrix inner extent, or null for n.  Only the tiled kernel uses it;
-  // the others run the full n, which gives the same result because the
-  // operands are zero beyond it.
+  // Per-matrix row, column and inner extents (gemm_kernel's Extents), or
+  // null for n.  With any of them set the product runs on the 64-tile tiled
+  // kernel, which skips the tiles and k-stages outside them.
+  const int32_t* rext = nullptr;
+  const int32_t* cext = nullptr;
   const int32_t* kext = nullptr;
 };
 
@@ -120,8 +122,8 @@ hipError_t large_lds_prepare(const void* kernel, int bytes) {
   return hipSuccess;
 }
 
-// Float32 NT products: the persistent 128-tile kernel runs 2 workgroups per
-// CU, the 64-tile kernel 4.  Measured on MI355X, a round of 128-tile slots
+// Float32 and float64 NT products: the persistent 128-tile kernel runs 2
+// workgroups per CU, the 64-tile kernel 4.  Measured on MI355X, a round of 128-tile slots
 // costs as much as 2 / 0.88 rounds of 64-tile slots (half the work per round
 // at 88% of the efficiency), so the 64-tile kernel wins when the tiles fill
 // the 128-tile slots poorly: small batches, and tile counts just above a
@@ -138,9 +140,13 @@ bool prefer_64_tiles(int n, int64_t batch, bool sym, int cus) {
 
 template <Mma MM, typename TA, typename TB, typename TC>
 hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
-  int T = (n % 128 == 0) ? 128 : 64;
-  if constexpr (MM == Mma::F32 && std::is_same<TA, float>::value && std::is_same<TB, float>::value &&
-                std::is_same<TC, float>::value) {
+  const bool ext = c.rext || c.cext || c.kext;
+  const Extents ex{c.rext, c.cext, c.kext};
+  int T = (n % 128 == 0 && !ext) ? 128 : 64;
+  if constexpr ((MM == Mma::F32 && std::is_same<TA, float>::value && std::is_same<TB, float>::value &&
+                 std::is_same<TC, float>::value) ||
+                (MM == Mma::F64 && std::is_same<TA, double>::value && std::is_same<TB, double>::value &&
+                 std::is_same<TC, double>::value)) {
     if (T == 128 && !c.nn && batch > 0) {
       int cus = 0;
       HIP_TRY_ERR(cu_count(&cus));
@@ -171,7 +177,7 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
   dim3 grid((unsigned)g.total);
   if constexpr (MM == Mma::F32 && std::is_same<TA, float>::value && std::is_same<TB, float>::value &&
                 std::is_same<TC, float>::value) {
-    if (c.nn && n % NN256_T == 0 && c.D == nullptr && !c.transC) {
+    if (c.nn && n % NN256_T == 0 && c.D == nullptr && !c.transC && !ext) {
       int cus = 0;
       HIP_TRY_ERR(cu_count(&cus));
       GemmArgs h = g;
@@ -230,7 +236,7 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
     // NN (Newton-DB): 256-tile kernel; NT (symmetric: coupled Newton,
     // Clenshaw): 128-tile kernel, whose diagonal tiles waste less work
     // (36 of 64 tiles at n = 1024 against 10 of 16).
-    if (c.nn && n % H256_T == 0 && !c.sym && c.D == nullptr && !c.transC) {
+    if (c.nn && n % H256_T == 0 && !c.sym && c.D == nullptr && !c.transC && !ext) {
       int cus = 0;
       HIP_TRY_ERR(cu_count(&cus));
       GemmArgs h = g;
@@ -255,17 +261,17 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
   if constexpr (std::is_same<TB, float>::value || std::is_same<TB, double>::value || f16_in) {
     if (c.nn) {
       if (T == 128)
-        hipLaunchKernelGGL((gemm_kernel<MM, 128, true, TA, TB, TC>), grid, dim3(256), 0, st, g, c.kext);
+        hipLaunchKernelGGL((gemm_kernel<MM, 128, true, TA, TB, TC>), grid, dim3(256), 0, st, g, ex);
       else
-        hipLaunchKernelGGL((gemm_kernel<MM, 64, true, TA, TB, TC>), grid, dim3(256), 0, st, g, c.kext);
+        hipLaunchKernelGGL((gemm_kernel<MM, 64, true, TA, TB, TC>), grid, dim3(256), 0, st, g, ex);
       return hipGetLastError();
     }
   }
   if (c.nn) return hipErrorInvalidValue;
   if (T == 128)
-    hipLaunchKernelGGL((gemm_kernel<MM, 128, false, TA, TB, TC>), grid, dim3(256), 0, st, g, c.kext);
+    hipLaunchKernelGGL((gemm_kernel<MM, 128, false, TA, TB, TC>), grid, dim3(256), 0, st, g, ex);
   else
-    hipLaunchKernelGGL((gemm_kernel<MM, 64, false, TA, TB, TC>), grid, dim3(256), 0, st, g, c.kext);
+    hipLaunchKernelGGL((gemm_kernel<MM, 64, false, TA, TB, TC>), grid, dim3(256), 0, st, g, ex);
   return hipGetLastError();
 }
 
@@ -1295,10 +1301,13 @@ shampoo_status stats_impl(const void* g, const void* gt, shampoo_dtype gdt, int6
   GemmCall cr = cl;
   cr.A = gt; cr.B = gt; cr.D = (unsigned char*)LR + half; cr.C = (unsigned char*)LR + half;
   // With the blocks' valid sizes (rows in valid[0, nblk), columns in
-  // valid[nblk, 2 nblk)), each product stops at the block's inner extent:
-  // G G^T sums over G's columns, G^T G over its rows.
+  // valid[nblk, 2 nblk)), each product covers only the block's valid region:
+  // L (rows x rows) sums over G's columns, R (cols x cols) over its rows;
+  // tiles past the valid side are not computed (their zeros stay).
   if (valid) {
+    cl.rext = cl.cext = valid;
     cl.kext = valid + nblk;
+    cr.rext = cr.cext = valid + nblk;
     cr.kext = valid;
   }
   if (sdt == SHAMPOO_F64) {
@@ -1320,7 +1329,8 @@ shampoo_status stats_impl(const void* g, const void* gt, shampoo_dtype gdt, int6
 }
 
 shampoo_status precond_impl(const void* roots, shampoo_dtype rdt, const void* g, shampoo_dtype gdt, int64_t nblk,
-                            int32_t B, float* dstack, void* ws, size_t ws_bytes, hipStream_t st) {
+                            int32_t B, float* dstack, void* ws, size_t ws_bytes, hipStream_t st,
+                            const int32_t* valid = nullptr) {
   if (nblk < 0) return fail(SHAMPOO_E_INVALID, "nblk < 0");
   if (B < 64 || B % 64 != 0) return fail(SHAMPOO_E_UNSUPPORTED, "B = %d: must be a positive multiple of 64", B);
   if (gdt != SHAMPOO_F32 && gdt != SHAMPOO_BF16) return fail(SHAMPOO_E_UNSUPPORTED, "gradient dtype %d (F32, BF16)", (int)gdt);
@@ -1338,6 +1348,15 @@ shampoo_status precond_impl(const void* roots, shampoo_dtype rdt, const void* g,
   c1.A = g; c1.B = Rr; c1.D = nullptr; c1.C = ws; c1.C2 = nullptr; c1.sym = false; c1.transC = true;
   GemmCall c2;
   c2.A = Lr; c2.B = ws; c2.D = nullptr; c2.C = dstack; c2.C2 = nullptr; c2.sym = false;
+  // With the blocks' valid sizes, both products cover only the rows x cols
+  // valid region of E and D (inner extents cols and rows); the roots' and
+  // G's zero padding makes the partial tiles at the edges exact.
+  if (valid) {
+    c1.rext = c2.rext = valid;
+    c1.cext = c2.cext = valid + nblk;
+    c1.kext = valid + nblk;
+    c2.kext = valid;
+  }
   if (rdt == SHAMPOO_F64) {
     if (gdt == SHAMPOO_F32) HIP_TRY((gemm<Mma::F64, float, double, double>(c1, B, nblk, st)));
     else HIP_TRY((gemm<Mma::F64, __bf16, double, double>(c1, B, nblk, st)));
@@ -1363,6 +1382,9 @@ struct StepLayout {
   size_t fl, fidx, fvalid, fflags, fin, fout, froot;
   size_t froot_bytes;
   bool redo64;
+  // some block is narrower than B (from table_host): the statistics and
+  // preconditioning products then skip the padding of each block
+  bool ragged;
   // factor-side groups (table_host given and some factor narrower than B):
   // group g roots gcount[g] factors, listed in gorder from gstart[g], in a
   // stack of side gside[g]; their chains use the root region
@@ -1418,6 +1440,10 @@ shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
     L->froot = off; off += L->froot_bytes;
   }
   L->gidx = L->gvalid = L->gflags = L->gres = L->gin = L->gout = 0;
+  L->ragged = false;
+  if (a->table_host)
+    for (int64_t b = 0; b < a->nblk && !L->ragged; ++b)
+      L->ragged = a->table_host[b].rows < a->B || a->table_host[b].cols < a->B;
   L->gside.clear();
   L->gstart.clear();
   L->gcount.clear();
@@ -1616,7 +1642,7 @@ shampoo_status step_impl(const shampoo_step_args* a, hipStream_t st) {
     LAUNCH_CHECK("valid");
   }
   // 2. statistics
-  r = stats_impl(g, gt, a->g_dt, nblk, B, a->LR, a->stats_dt, a->beta2, st, valid);
+  r = stats_impl(g, gt, a->g_dt, nblk, B, a->LR, a->stats_dt, a->beta2, st, L.ragged ? valid : nullptr);
   if (r != SHAMPOO_OK) return r;
   // 3. inverse roots of the 2 nblk factors
   if (a->recompute_roots) {
@@ -1627,7 +1653,7 @@ shampoo_status step_impl(const shampoo_step_args* a, hipStream_t st) {
   const size_t ebytes = align_up((size_t)nblk * BB * dtype_size(a->stats_dt));
   void* Et = root;
   float* D = a->dstack ? a->dstack : (float*)(root + ebytes);
-  r = precond_impl(a->roots, a->stats_dt, g, a->g_dt, nblk, B, D, Et, ebytes, st);
+  r = precond_impl(a->roots, a->stats_dt, g, a->g_dt, nblk, B, D, Et, ebytes, st, L.ragged ? valid : nullptr);
   if (r != SHAMPOO_OK) return r;
   // 5. grafting and update
   GraftArgs ga;
