@@ -188,7 +188,8 @@ struct Extents {
 };
 
 template <Mma MM, int T, bool BKN, typename TA, typename TB, typename TC>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, Extents ext) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Extents& ext, int64_t mat, int ti, int tj,
+                                          unsigned char* smem) {
   using Tr = MmaTraits<MM>;
   using L = typename Tr::lds_t;
   using acc_t = typename Tr::acc_t;
@@ -206,23 +207,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, Extents ext) {
 
   // Two stages of A and B tiles (double buffering: one barrier per k-stage);
   // the epilogue reuses the same bytes to stage the C tile.
-  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * T * ROWB];
   auto sA = [&](int buf) { return smem + buf * T * ROWB; };
   auto sB = [&](int buf) { return smem + (2 + buf) * T * ROWB; };
 
-  const int64_t w = xcd_remap((int64_t)blockIdx.x, g.total);
-  const int64_t mat = w / g.tiles;
-  int t = (int)(w - mat * g.tiles);
-  int ti, tj;
-  if (g.sym) {
-    ti = 0;
-    int rowlen = g.nt;
-    while (t >= rowlen) { t -= rowlen; ++ti; --rowlen; }
-    tj = ti + t;
-  } else {
-    ti = t / g.nt;
-    tj = t - ti * g.nt;
-  }
   // tiles outside the matrix's row / column extent: nothing to do (uniform)
   if ((ext.r && ti * T >= ext.r[mat]) || (ext.c && tj * T >= ext.c[mat])) return;
   const int n = g.n;
@@ -432,6 +419,144 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, Extents ext) {
           if (C2) put<TC>(C2 + (int64_t)Cc * n + R, x2);
         }
       }
+}
+
+// Tile lists: the tiles of a product with extents, listed matrix by matrix
+// and cut into 8 contiguous ranges of about equal cost (see
+// tile_list_kernel); range x goes to XCD x (the hardware deals workgroups to
+// the XCDs round-robin), whose workgroups walk it.  Packed tile:
+// matrix << 16 | ti << 8 | tj.
+struct TileList {
+  const int32_t* tiles;
+  const int32_t* cut;  // [9]
+};
+
+template <Mma MM, int T, bool BKN, typename TA, typename TB, typename TC>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, Extents ext, TileList tl) {
+  using L = typename MmaTraits<MM>::lds_t;
+  constexpr int ROWB = MmaTraits<MM>::BK * (int)sizeof(L) + 16;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * T * ROWB];
+  if (tl.tiles) {
+    const int x = blockIdx.x & 7, l = blockIdx.x >> 3, per = gridDim.x >> 3;
+    for (int i = tl.cut[x] + l; i < tl.cut[x + 1]; i += per) {
+      const int32_t p = tl.tiles[i];
+      gemm_tile<MM, T, BKN, TA, TB, TC>(g, ext, p >> 16, (p >> 8) & 255, p & 255, smem);
+      __syncthreads();  // the epilogue's reads of LDS end before the next tile's stage stores
+    }
+    return;
+  }
+  const int64_t w = xcd_remap((int64_t)blockIdx.x, g.total);
+  const int64_t mat = w / g.tiles;
+  int t = (int)(w - mat * g.tiles);
+  int ti, tj;
+  if (g.sym) {
+    ti = 0;
+    int rowlen = g.nt;
+    while (t >= rowlen) { t -= rowlen; ++ti; --rowlen; }
+    tj = ti + t;
+  } else {
+    ti = t / g.nt;
+    tj = t - ti * g.nt;
+  }
+  gemm_tile<MM, T, BKN, TA, TB, TC>(g, ext, mat, ti, tj, smem);
+}
+
+// Builds up to 4 tile lists for products with extents, one workgroup of
+// 1024 threads per list.  A matrix b contributes the tiles (ti, tj) with
+// ti T < r[b] and tj T < c[b] (and ti <= tj with sym), row-major; a tile
+// costs its k-stages, min(n / BK, ceil(k[b] / BK)), at least 1.  Prefix
+// sums of tile counts and costs over the matrices (chunk sums, a scan of
+// the 1024 chunk sums in LDS, chunk walks) give each matrix's first list
+// slot and cost offset; cut[x] is the first tile whose cost offset reaches
+// x C / 8 (C the total cost), found by binary search over the matrices.
+struct TileListSpec {
+  const int32_t* r;
+  const int32_t* c;
+  const int32_t* k;
+  int sym;
+  int32_t* tiles;  // [matrices * (n/T)^2]
+  int32_t* cut;    // [9]
+  int32_t* tpre;   // [matrices] scratch: first list slot of each matrix
+  int64_t* cpre;   // [matrices] scratch: cost before each matrix
+};
+struct TileListArgs {
+  TileListSpec s[4];
+  int64_t nmat;
+  int n, T, BK;
+};
+
+__global__ __launch_bounds__(1024) void tile_list_kernel(TileListArgs a) {
+  const TileListSpec sp = a.s[blockIdx.x];
+  __shared__ int32_t tsum[1024];
+  __shared__ int64_t csum[1024];
+  const int tid = threadIdx.x;
+  const int nt = a.n / a.T, nsmax = a.n / a.BK;
+  const int64_t ch = (a.nmat + 1023) / 1024;
+  const int64_t m0 = min(a.nmat, (int64_t)tid * ch), m1 = min(a.nmat, m0 + ch);
+  auto info = [&](int64_t m, int& cnt, int& rt, int& ct, int& nst) {
+    rt = sp.r ? min(nt, (max(sp.r[m], 0) + a.T - 1) / a.T) : nt;
+    ct = sp.c ? min(nt, (max(sp.c[m], 0) + a.T - 1) / a.T) : nt;
+    if (sp.sym) {
+      const int rr = min(rt, ct);
+      cnt = rr * ct - rr * (rr - 1) / 2;  // sum over ti < rr of (ct - ti)
+    } else {
+      cnt = rt * ct;
+    }
+    nst = sp.k ? min(nsmax, max(1, (max(sp.k[m], 0) + a.BK - 1) / a.BK)) : nsmax;
+  };
+  int32_t ts = 0;
+  int64_t cs = 0;
+  for (int64_t m = m0; m < m1; ++m) {
+    int cnt, rt, ct, nst;
+    info(m, cnt, rt, ct, nst);
+    ts += cnt;
+    cs += (int64_t)cnt * nst;
+  }
+  tsum[tid] = ts;
+  csum[tid] = cs;
+  __syncthreads();
+  // inclusive scan of the chunk sums (Hillis-Steele)
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t tv = tid >= off ? tsum[tid - off] : 0;
+    const int64_t cv = tid >= off ? csum[tid - off] : 0;
+    __syncthreads();
+    tsum[tid] += tv;
+    csum[tid] += cv;
+    __syncthreads();
+  }
+  int32_t tp = tsum[tid] - ts;
+  int64_t cp = csum[tid] - cs;
+  for (int64_t m = m0; m < m1; ++m) {
+    int cnt, rt, ct, nst;
+    info(m, cnt, rt, ct, nst);
+    sp.tpre[m] = tp;
+    sp.cpre[m] = cp;
+    for (int ti = 0, j = 0; ti < rt; ++ti)
+      for (int tj = sp.sym ? ti : 0; tj < ct; ++tj, ++j) sp.tiles[tp + j] = (int32_t)((m << 16) | (ti << 8) | tj);
+    tp += cnt;
+    cp += (int64_t)cnt * nst;
+  }
+  __syncthreads();  // tpre / cpre of every matrix written
+  const int32_t N = tsum[1023];
+  const int64_t C = csum[1023];
+  if (tid <= 8) {
+    int32_t cut = tid == 0 ? 0 : N;
+    if (tid > 0 && tid < 8 && a.nmat > 0) {
+      const int64_t target = C * tid / 8;
+      // last matrix whose cost offset is <= target
+      int64_t lo = 0, hi = a.nmat - 1;
+      while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) / 2;
+        if (sp.cpre[mid] <= target) lo = mid;
+        else hi = mid - 1;
+      }
+      int cnt, rt, ct, nst;
+      info(lo, cnt, rt, ct, nst);
+      const int64_t j = min((int64_t)cnt, (target - sp.cpre[lo] + nst - 1) / nst);
+      cut = (int32_t)(sp.tpre[lo] + j);
+    }
+    sp.cut[tid] = cut;
+  }
 }
 
 // ---------------------------------------------------------------------------

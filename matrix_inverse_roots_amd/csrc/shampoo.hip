@@ -82,6 +82,10 @@ struct GemmCall {
   const int32_t* rext = nullptr;
   const int32_t* cext = nullptr;
   const int32_t* kext = nullptr;
+  // Optional work-balanced list of the tiles inside the extents
+  // (tile_list_kernel): the tiled kernel then walks it with a fixed grid.
+  const int32_t* tiles = nullptr;
+  const int32_t* cut = nullptr;
 };
 
 #define HIP_TRY_ERR(expr)         \
@@ -175,6 +179,13 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
   g.gamma2 = c.gamma2;
   if (g.total == 0) return hipSuccess;
   dim3 grid((unsigned)g.total);
+  const TileList tl{c.tiles, c.cut};
+  if (c.tiles) {
+    // a fixed grid of 4 workgroups per CU (a multiple of the 8 XCDs) walks the list
+    int cus = 0;
+    HIP_TRY_ERR(cu_count(&cus));
+    grid = dim3((unsigned)(std::max(8, (cus / 8) * 8) * 4));
+  }
   if constexpr (MM == Mma::F32 && std::is_same<TA, float>::value && std::is_same<TB, float>::value &&
                 std::is_same<TC, float>::value) {
     if (c.nn && n % NN256_T == 0 && c.D == nullptr && !c.transC && !ext) {
@@ -261,17 +272,17 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
   if constexpr (std::is_same<TB, float>::value || std::is_same<TB, double>::value || f16_in) {
     if (c.nn) {
       if (T == 128)
-        hipLaunchKernelGGL((gemm_kernel<MM, 128, true, TA, TB, TC>), grid, dim3(256), 0, st, g, ex);
+        hipLaunchKernelGGL((gemm_kernel<MM, 128, true, TA, TB, TC>), grid, dim3(256), 0, st, g, ex, tl);
       else
-        hipLaunchKernelGGL((gemm_kernel<MM, 64, true, TA, TB, TC>), grid, dim3(256), 0, st, g, ex);
+        hipLaunchKernelGGL((gemm_kernel<MM, 64, true, TA, TB, TC>), grid, dim3(256), 0, st, g, ex, tl);
       return hipGetLastError();
     }
   }
   if (c.nn) return hipErrorInvalidValue;
   if (T == 128)
-    hipLaunchKernelGGL((gemm_kernel<MM, 128, false, TA, TB, TC>), grid, dim3(256), 0, st, g, ex);
+    hipLaunchKernelGGL((gemm_kernel<MM, 128, false, TA, TB, TC>), grid, dim3(256), 0, st, g, ex, tl);
   else
-    hipLaunchKernelGGL((gemm_kernel<MM, 64, false, TA, TB, TC>), grid, dim3(256), 0, st, g, ex);
+    hipLaunchKernelGGL((gemm_kernel<MM, 64, false, TA, TB, TC>), grid, dim3(256), 0, st, g, ex, tl);
   return hipGetLastError();
 }
 
@@ -1282,8 +1293,16 @@ shampoo_status pack_impl(const shampoo_matrix* mats, int32_t nparams, const sham
   return SHAMPOO_OK;
 }
 
+// Work-balanced tile lists of the four products with extents (statistics L
+// and R, preconditioning E^T and D), built on the device by tile_list_kernel.
+struct ProductTiles {
+  const int32_t* tiles[4] = {nullptr, nullptr, nullptr, nullptr};
+  const int32_t* cut[4] = {nullptr, nullptr, nullptr, nullptr};
+};
+
 shampoo_status stats_impl(const void* g, const void* gt, shampoo_dtype gdt, int64_t nblk, int32_t B, void* LR,
-                          shampoo_dtype sdt, double beta2, hipStream_t st, const int32_t* valid = nullptr) {
+                          shampoo_dtype sdt, double beta2, hipStream_t st, const int32_t* valid = nullptr,
+                          const ProductTiles* pt = nullptr) {
   if (nblk < 0) return fail(SHAMPOO_E_INVALID, "nblk < 0");
   if (B < 64 || B % 64 != 0) return fail(SHAMPOO_E_UNSUPPORTED, "B = %d: must be a positive multiple of 64", B);
   if (!(beta2 >= 0.0 && beta2 <= 1.0)) return fail(SHAMPOO_E_INVALID, "beta2 = %g not in [0, 1]", beta2);
@@ -1309,6 +1328,12 @@ shampoo_status stats_impl(const void* g, const void* gt, shampoo_dtype gdt, int6
     cl.kext = valid + nblk;
     cr.rext = cr.cext = valid + nblk;
     cr.kext = valid;
+    if (pt) {
+      cl.tiles = pt->tiles[0];
+      cl.cut = pt->cut[0];
+      cr.tiles = pt->tiles[1];
+      cr.cut = pt->cut[1];
+    }
   }
   if (sdt == SHAMPOO_F64) {
     if (gdt == SHAMPOO_F32) {
@@ -1330,7 +1355,7 @@ shampoo_status stats_impl(const void* g, const void* gt, shampoo_dtype gdt, int6
 
 shampoo_status precond_impl(const void* roots, shampoo_dtype rdt, const void* g, shampoo_dtype gdt, int64_t nblk,
                             int32_t B, float* dstack, void* ws, size_t ws_bytes, hipStream_t st,
-                            const int32_t* valid = nullptr) {
+                            const int32_t* valid = nullptr, const ProductTiles* pt = nullptr) {
   if (nblk < 0) return fail(SHAMPOO_E_INVALID, "nblk < 0");
   if (B < 64 || B % 64 != 0) return fail(SHAMPOO_E_UNSUPPORTED, "B = %d: must be a positive multiple of 64", B);
   if (gdt != SHAMPOO_F32 && gdt != SHAMPOO_BF16) return fail(SHAMPOO_E_UNSUPPORTED, "gradient dtype %d (F32, BF16)", (int)gdt);
@@ -1356,6 +1381,12 @@ shampoo_status precond_impl(const void* roots, shampoo_dtype rdt, const void* g,
     c1.cext = c2.cext = valid + nblk;
     c1.kext = valid + nblk;
     c2.kext = valid;
+    if (pt) {
+      c1.tiles = pt->tiles[2];
+      c1.cut = pt->cut[2];
+      c2.tiles = pt->tiles[3];
+      c2.cut = pt->cut[3];
+    }
   }
   if (rdt == SHAMPOO_F64) {
     if (gdt == SHAMPOO_F32) HIP_TRY((gemm<Mma::F64, float, double, double>(c1, B, nblk, st)));
@@ -1385,6 +1416,8 @@ struct StepLayout {
   // some block is narrower than B (from table_host): the statistics and
   // preconditioning products then skip the padding of each block
   bool ragged;
+  size_t tl;        // the four product tile lists (ragged only)
+  size_t tl_each;   // bytes per list
   // factor-side groups (table_host given and some factor narrower than B):
   // group g roots gcount[g] factors, listed in gorder from gstart[g], in a
   // stack of side gside[g]; their chains use the root region
@@ -1441,9 +1474,17 @@ shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
   }
   L->gidx = L->gvalid = L->gflags = L->gres = L->gin = L->gout = 0;
   L->ragged = false;
-  if (a->table_host)
+  if (a->table_host && a->B <= 64 * 128)
     for (int64_t b = 0; b < a->nblk && !L->ragged; ++b)
       L->ragged = a->table_host[b].rows < a->B || a->table_host[b].cols < a->B;
+  L->tl = L->tl_each = 0;
+  if (L->ragged) {
+    const int64_t nt = a->B / 64;
+    L->tl_each = align_up((size_t)a->nblk * nt * nt * 4) + align_up((size_t)a->nblk * 4) +
+                 align_up((size_t)a->nblk * 8) + ALIGN;
+    L->tl = off;
+    off += 4 * L->tl_each;
+  }
   L->gside.clear();
   L->gstart.clear();
   L->gcount.clear();
@@ -1641,8 +1682,38 @@ shampoo_status step_impl(const shampoo_step_args* a, hipStream_t st) {
                        nblk, valid);
     LAUNCH_CHECK("valid");
   }
+  // work-balanced tile lists of the products that skip the blocks' padding
+  ProductTiles pt;
+  if (L.ragged) {
+    TileListArgs ta{};
+    const int32_t* vr = valid;
+    const int32_t* vc = valid + nblk;
+    const int32_t* spec[4][3] = {{vr, vr, vc}, {vc, vc, vr}, {vr, vc, vc}, {vr, vc, vr}};
+    for (int q = 0; q < 4; ++q) {
+      unsigned char* base = w + L.tl + (size_t)q * L.tl_each;
+      const size_t tb = align_up((size_t)nblk * (B / 64) * (B / 64) * 4);
+      TileListSpec& sp = ta.s[q];
+      sp.r = spec[q][0];
+      sp.c = spec[q][1];
+      sp.k = spec[q][2];
+      sp.sym = q < 2 ? 1 : 0;
+      sp.tiles = (int32_t*)base;
+      sp.tpre = (int32_t*)(base + tb);
+      sp.cpre = (int64_t*)(base + tb + align_up((size_t)nblk * 4));
+      sp.cut = (int32_t*)(base + tb + align_up((size_t)nblk * 4) + align_up((size_t)nblk * 8));
+      pt.tiles[q] = sp.tiles;
+      pt.cut[q] = sp.cut;
+    }
+    ta.nmat = nblk;
+    ta.n = B;
+    ta.T = 64;
+    ta.BK = 32;
+    hipLaunchKernelGGL(tile_list_kernel, dim3(4), dim3(1024), 0, st, ta);
+    LAUNCH_CHECK("tile_list");
+  }
   // 2. statistics
-  r = stats_impl(g, gt, a->g_dt, nblk, B, a->LR, a->stats_dt, a->beta2, st, L.ragged ? valid : nullptr);
+  r = stats_impl(g, gt, a->g_dt, nblk, B, a->LR, a->stats_dt, a->beta2, st, L.ragged ? valid : nullptr,
+                 L.ragged ? &pt : nullptr);
   if (r != SHAMPOO_OK) return r;
   // 3. inverse roots of the 2 nblk factors
   if (a->recompute_roots) {
@@ -1653,7 +1724,8 @@ shampoo_status step_impl(const shampoo_step_args* a, hipStream_t st) {
   const size_t ebytes = align_up((size_t)nblk * BB * dtype_size(a->stats_dt));
   void* Et = root;
   float* D = a->dstack ? a->dstack : (float*)(root + ebytes);
-  r = precond_impl(a->roots, a->stats_dt, g, a->g_dt, nblk, B, D, Et, ebytes, st, L.ragged ? valid : nullptr);
+  r = precond_impl(a->roots, a->stats_dt, g, a->g_dt, nblk, B, D, Et, ebytes, st, L.ragged ? valid : nullptr,
+                   L.ragged ? &pt : nullptr);
   if (r != SHAMPOO_OK) return r;
   // 5. grafting and update
   GraftArgs ga;
