@@ -569,8 +569,10 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(TileListArgs a) {
 // of 4 waves per CU, 64 KB of LDS each), direct-to-LDS stage loads one stage
 // ahead, fence-free barriers, vector stores straight from the accumulators.
 // A stage holds 128 B of k per operand row (32 floats or 16 doubles):
-//   A tile  [128 rows][128 B], swizzled as in the NN product.
-//   B (NT)  [128 rows][128 B], swizzled, with the LDS row order permuted:
+//   A tile  [128 rows][128 B], chunks swizzled by P::aswz: lds_swz, or
+//           lds_swz_t for float64, whose A fragments take the rows of a
+//           16-row group in the order 4 (i & 3) + (i >> 2).
+//   B (NT)  [128 rows][128 B], swizzled by lds_swz, with the LDS row order permuted:
 //           output column wn*64 + 4 c + jb (lane c, column block jb) comes
 //           from B-tile row wn*64 + 4 c + jb, stored at LDS row
 //           wn*64 + 16 jb + c, so a fragment read covers 16 consecutive LDS
@@ -612,6 +614,7 @@ template <> struct P128<float> {
     return mma_s(a[u], b[u], c);
   }
   static __device__ __forceinline__ int arow(int r) { return r; }
+  static __device__ __forceinline__ int aswz(int m) { return lds_swz(m); }
 };
 template <> struct P128<double> {
   using acc_t = doublex4;
@@ -625,6 +628,7 @@ template <> struct P128<double> {
     return mma_s(a[u], b[u], c);
   }
   static __device__ __forceinline__ int arow(int r) { return 4 * (r & 3) + (r >> 2); }
+  static __device__ __forceinline__ int aswz(int m) { return lds_swz_t(m); }
 };
 template <> struct P128<__bf16> {
   using acc_t = floatx4;
@@ -635,6 +639,7 @@ template <> struct P128<__bf16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ int arow(int r) { return r; }
+  static __device__ __forceinline__ int aswz(int m) { return lds_swz(m); }
 };
 
 template <> struct P128<_Float16> {
@@ -646,6 +651,7 @@ template <> struct P128<_Float16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ int arow(int r) { return r; }
+  static __device__ __forceinline__ int aswz(int m) { return lds_swz(m); }
 };
 
 // LDS row -> B-tile row of an NT operand (the inverse of
@@ -715,12 +721,12 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
     const int row = 8 * (4 * wave + qq) + (lane >> 3), pos = lane & 7;
-    aoff[qq] = row * n + VE * (pos ^ nn256_swz(row));
+    aoff[qq] = row * n + VE * (pos ^ P::aswz(row));
     if constexpr (NN) {
       const int byte = (4 * wave + qq) * 1024 + 16 * lane;
       boff[qq] = (byte / RB) * n + (byte % RB) / (int)sizeof(E);
     } else {
-      boff[qq] = p128_brow(row) * n + VE * (pos ^ nn256_swz(row));
+      boff[qq] = p128_brow(row) * n + VE * (pos ^ lds_swz(row));
     }
   }
   auto coords = [&](int it, int64_t& moff, int& ti, int& tj) {
@@ -815,7 +821,7 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = wm * 64 + i * 16 + P::arow(i16);
-        a[i] = *reinterpret_cast<const frag_t*>(sa + m * 128 + 16 * (kc ^ nn256_swz(m)));
+        a[i] = *reinterpret_cast<const frag_t*>(sa + m * 128 + 16 * (kc ^ P::aswz(m)));
       }
       if constexpr (NN) {
         // b[u * (4 / VE) + h]: k-row kc VE + u, columns wn*64 + h 16 VE + VE i16 ..
@@ -836,7 +842,7 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int rho = wn * 64 + 16 * j + i16;
-          b[j] = *reinterpret_cast<const frag_t*>(sb + rho * 128 + 16 * (kc ^ nn256_swz(rho)));
+          b[j] = *reinterpret_cast<const frag_t*>(sb + rho * 128 + 16 * (kc ^ lds_swz(rho)));
         }
 #pragma unroll
         for (int u = 0; u < P::KS; ++u)
@@ -989,7 +995,7 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
 //
 // LDS layouts (16-byte chunks, XOR-swizzled so fragment reads spread over
 // all banks):
-//   A [256 rows][128 B of k], chunk c of LDS row r at c ^ nn256_swz(r).
+//   A [256 rows][128 B of k], chunk c of LDS row r at c ^ lds_swz(r).
 //   B [64 k-rows][256 columns], B's own k-major layout, chunk c of k-row k
 //     at c ^ bswz(k).  Fragments come from ds_read_b64_tr_b16: in each group
 //     of 16 lanes, lane 4 i + q addresses the 4 columns 4 q .. 4 q + 3 of
@@ -1041,7 +1047,7 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_nn_kernel(GemmArgs g) {
   for (int qq = 0; qq < 4; ++qq) {
     const int I = 4 * wave + qq;
     const int row = 8 * I + (lane >> 3), pos = lane & 7;
-    aoff[qq] = row * n + 8 * (pos ^ nn256_swz(row));
+    aoff[qq] = row * n + 8 * (pos ^ lds_swz(row));
     const int k = 2 * I + (lane >> 5), p = lane & 31;
     boff[qq] = k * n + 8 * (p ^ h256_bswz(k));
   }
@@ -1122,7 +1128,7 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_nn_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int m = wm * 128 + i * 16 + i16;
-        a[i] = *reinterpret_cast<const halfx8*>(sa + m * 128 + 16 * (kc ^ nn256_swz(m)));
+        a[i] = *reinterpret_cast<const halfx8*>(sa + m * 128 + 16 * (kc ^ lds_swz(m)));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {

@@ -124,9 +124,19 @@ __device__ __forceinline__ void store_h4(_Float16* p, floatx4 v) {
   *reinterpret_cast<halfx4*>(p) = halfx4{half_of(v[0]), half_of(v[1]), half_of(v[2]), half_of(v[3])};
 }
 
-// A tile row of 128 bytes (8 chunks of 16 bytes): chunk c of LDS row m sits
-// at position c ^ nn256_swz(m), which spreads a fragment read over all banks.
-__device__ __forceinline__ int nn256_swz(int m) { return (m & 7) ^ ((m >> 3) & 1); }
+// LDS tile rows of 128 bytes (8 chunks of 16 bytes): chunk c of LDS row m
+// sits at position c ^ swz(m).  A fragment read (ds_read_b128) has lane
+// (i16, grp) read chunk 4 rr + grp of row r0 + rho(i16), r0 a multiple of 16.
+// Which swizzle keeps such a read free of bank conflicts depends on rho; on
+// MI355X (SQ_LDS_BANK_CONFLICT over SQ_LDS_IDX_ACTIVE, 4 active cycles per
+// conflict-free read):
+//   rho(i) = i (rows in lane order):    lds_swz, conflict-free; the form
+//     (m & 7) ^ ((m >> 3) & 1) doubles the cycles of every read (40% of the
+//     float32 NN product's LDS cycles, 50% of the half NT product's);
+//   rho(i) = 4 (i & 3) + (i >> 2) (the float64 A fragments): lds_swz_t,
+//     conflict-free; lds_swz costs 1.5x there.
+__device__ __forceinline__ int lds_swz(int m) { return (m & 3) | (((m >> 3) & 1) << 2); }
+__device__ __forceinline__ int lds_swz_t(int m) { return (m & 7) ^ ((m >> 3) & 1); }
 
 // Stage barriers of the persistent kernels: each wave waits for its own
 // direct-to-LDS loads (vmcnt) and then meets the others at a plain

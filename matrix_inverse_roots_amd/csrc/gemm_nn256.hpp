@@ -68,7 +68,7 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_nn256_kernel(GemmArgs g) {
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
     const int row = 8 * (4 * wave + qq) + (lane >> 3), pos = lane & 7;
-    aoff[qq] = row * n + 4 * (pos ^ nn256_swz(row));
+    aoff[qq] = row * n + 4 * (pos ^ lds_swz(row));
     boff[qq] = (4 * wave + qq) * n + 4 * lane;
   }
   auto coords = [&](int it, int64_t& moff, int& ti, int& tj) {
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(512, 1) void gemm_f32_nn256_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int m = wm * 128 + i * 16 + i16;
-        a[i] = *reinterpret_cast<const floatx4*>(sa + m * 128 + 16 * (kc ^ nn256_swz(m)));
+        a[i] = *reinterpret_cast<const floatx4*>(sa + m * 128 + 16 * (kc ^ lds_swz(m)));
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
