@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libshampoo.so")
 SOURCES = [os.path.join(PKG, "csrc", "shampoo.hip")]
-HEADERS = [os.path.join(PKG, "csrc", f) for f in ("gemm_common.hpp", "gemm.hpp", "gemm_nn256.hpp", "kernels.hpp")] + [
+HEADERS = [os.path.join(PKG, "csrc", f) for f in ("gemm_common.hpp", "gemm.hpp", "gemm_hsym.hpp", "gemm_nn256.hpp",
+                                                  "kernels.hpp")] + [
     os.path.join(ROOT, "include", "shampoo.h")]
 
 FLAGS = [

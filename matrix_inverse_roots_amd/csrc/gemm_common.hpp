@@ -18,10 +18,13 @@
 // idempotent one into one with eigenvalue 1 - (r + 2 + 1/r)/4 for an
 // eigenvalue pair of ratio r^2, unstable once r^2 exceeds about 34.
 //
-// Four kernels, all row-major with batch stride `stride` elements:
+// Five kernels, all row-major with batch stride `stride` elements:
 //   gemm_f32_nn256_kernel  (gemm_nn256.hpp) float32 NN, n a multiple of 256:
 //                          256 x 256 tiles, one persistent workgroup of 8
 //                          waves per CU.
+//   gemm_h256_sym_kernel   (gemm_hsym.hpp) half symmetric NT, n a multiple of
+//                          256: 256 x 256 tiles, one persistent workgroup of
+//                          8 waves per CU, k-stages of 32 in 4 buffers.
 //   gemm_h256_nn_kernel    (gemm.hpp) half NN into float32, n a multiple of
 //                          256: 256 x 256 tiles, one persistent workgroup of
 //                          8 waves per CU.

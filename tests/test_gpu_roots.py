@@ -129,8 +129,10 @@ def test_half_products_large_tiles_bit_identical(mir, method):
     run on the tiled kernel, those of the same stack padded to 512 (valid =
     384) on the 256-tile NN kernel, whose matrix cores take the operands in
     swapped roles and whose k-major operand comes through transposed LDS
-    reads; coupled Newton and Clenshaw run on the 128-tile kernel at both
-    sides.  The roots agree bit for bit."""
+    reads.  Coupled Newton's products with half outputs only run on the
+    128-tile kernel at 384 and on the 256-tile symmetric kernel (8 waves,
+    k-stages of 32) at 512; Clenshaw (float32 outputs) on the 128-tile
+    kernel at both sides.  The roots agree bit for bit."""
     n, v = 4, 384
     A = synthetic.spd_stack(384, n, v, 1e-2, 1.0).astype(np.float32)
     kw = dict(method=method, scaling="frobenius", iters=18, iters2=12, cheb_degree=12, eps=1e-3, compute="f16")
