@@ -986,7 +986,8 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
 // of their operand traffic: one persistent workgroup of 8 waves (128 x 64
 // outputs each) per CU, stage loads straight into LDS one stage ahead,
 // 128 KB of LDS (as the float32 NN product).  (Symmetric NT half products
-// stay on the 128-tile kernel, whose diagonal tiles waste less work.)
+// with half outputs only run on gemm_h256_sym_kernel, the others on the
+// 128-tile kernel.)
 //
 // The matrix-core operands are swapped: the B side feeds the A operand of
 // v_mfma_f32_16x16x32_f16 and the A side its B operand, so that lane

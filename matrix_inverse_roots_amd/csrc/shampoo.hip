@@ -245,9 +245,8 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
   constexpr bool f16_in = MM == Mma::F16 && std::is_same<TA, _Float16>::value &&
                           std::is_same<TB, _Float16>::value && std::is_same<TC, float>::value;
   if constexpr (f16_in) {
-    // NN (Newton-DB): 256-tile kernel; NT (symmetric: coupled Newton,
-    // Clenshaw): 128-tile kernel, whose diagonal tiles waste less work
-    // (36 of 64 tiles at n = 1024 against 10 of 16).
+    // NN (Newton-DB): 256-tile kernel; symmetric NT with half outputs only:
+    // 256-tile symmetric kernel; the other NT products: 128-tile kernel.
     if (c.nn && n % H256_T == 0 && !c.sym && c.D == nullptr && !c.transC && !ext) {
       int cus = 0;
       HIP_TRY_ERR(cu_count(&cus));
