@@ -10,11 +10,13 @@
 namespace shampoo {
 
 // ---------------------------------------------------------------------------
-// Symmetric half NT product, n a multiple of 256: every epilogue form of
-// the family (C, C2, their half copies, D), upper tiles only, each written
-// in place and mirrored.  The library routes the products with half outputs
-// only here (the squarings and updates of the half-precision coupled-Newton
-// chains); with float32 outputs the 128-tile kernel is faster (measured).
+// Symmetric half NT product, n a multiple of 256, half outputs only:
+//     Ch = alpha A B^T + gamma I,   C2h = alpha2 (alpha A B^T + gamma I) + gamma2 I
+// (C2h optional), upper tiles only, each written in place and mirrored.  The
+// library routes the symmetric products whose results are read only as
+// half operands here (the squarings and updates of the half-precision
+// coupled-Newton chains); products with float32 outputs or an addend run on
+// the 128-tile kernel.
 //
 // One persistent workgroup per CU of 8 waves, two per SIMD: a single wave
 // per SIMD issues matrix-core instructions at about 60% of the rate two
@@ -31,10 +33,25 @@ namespace shampoo {
 // a row at c ^ hs_swz(row).  The matrix-core operands are swapped (the B
 // side feeds the A operand), so that lane (i16, grp) holds, in value v of
 // block (i, 4 gj + jj), C[R0 + i][C0 + jj] with R0 = 64 wm + 4 i16 and
-// C0 = 128 wn + 64 gj + 16 grp + 4 v (wave w = 2 wm + wn): 4 x 4
-// sub-blocks, stored as 8-byte runs along rows in place and along columns
-// mirrored; diagonal sub-blocks element by element; on diagonal tiles the
-// waves below the diagonal store nothing.
+// C0 = 128 wn + 64 gj + 16 grp + 4 v (wave w = 2 wm + wn).
+//
+// Stores.  A wave's outputs form two 64 x 64 blocks (gj = 0, 1).  A block
+// above the diagonal of the matrix is written
+//   * in place as rows: lanes i16 and i16 ^ 1 (rows 4 apart) swap half of
+//     their 16 columns of a row with a DPP lane swap, so that each 16-byte
+//     store instruction writes 8 complete 128-byte row segments;
+//   * mirrored as columns: a lane's 4 consecutive rows of one column become
+//     8 bytes of a row of the transposed block, 16 lanes one 128-byte
+//     segment.
+// Stores that leave partial segments (8-byte pieces of 16 rows per
+// instruction, the earlier in-place form) were written back to memory
+// before the segments were complete: 1.33-1.45x the output bytes for one
+// output and 2.2x for two, and about a quarter of the kernel's time.  With
+// the swap the writes are 1.05x (one output) and the squaring of 288 x 1024^2
+// takes 485 us instead of 623 (measured in isolation).  A block on the
+// diagonal is written 4 x 4 sub-block by sub-block: its upper sub-blocks in
+// place (8-byte rows) and mirrored, the diagonal sub-blocks element by
+// element; blocks below the diagonal store nothing.
 //
 // The k order per output element (k-groups of 8 in the order of the other
 // kernels' two rounds per 64-k stage) is the same as in every product
@@ -142,8 +159,7 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_sym_kernel(GemmArgs g) {
   const int bfr = (wn * 128 + i16) * 64 + 16 * (grp ^ hs_swz(i16));
 
   floatx4 acc[4][8];
-  const float* Dg = reinterpret_cast<const float*>(g.D);
-  const bool plain = g.alpha == 1.0 && g.gamma == 0.0 && Dg == nullptr && g.C2 == nullptr && g.C2h == nullptr;
+  const bool plain = g.alpha == 1.0 && g.gamma == 0.0 && g.C2h == nullptr;
   const int total_steps = ntile * nst;  // >= 8 (n >= 256)
 
   issue(0);
@@ -202,13 +218,11 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_sym_kernel(GemmArgs g) {
     // epilogue of tile ct: lane (i16, grp) holds, in value v of block
     // (i, 4 gj + jj), C[R0 + i][C0 + jj] with R0 = 64 wm + 4 i16 and
     // C0 = 128 wn + 64 gj + 16 grp + 4 v (tile coordinates)
-    float* C = g.C ? reinterpret_cast<float*>(g.C) + cmo : nullptr;
-    float* C2 = g.C2 ? reinterpret_cast<float*>(g.C2) + cmo : nullptr;
-    _Float16* Ch = g.Ch ? reinterpret_cast<_Float16*>(g.Ch) + cmo : nullptr;
+    _Float16* Ch = reinterpret_cast<_Float16*>(g.Ch) + cmo;
     _Float16* C2h = g.C2h ? reinterpret_cast<_Float16*>(g.C2h) + cmo : nullptr;
-    const float* D = Dg ? Dg + cmo : nullptr;
-    const bool two = C2 || C2h;
-    const bool diag = cti == ctj;
+    const bool two = C2h != nullptr;
+    // a 4 x 4 sub-block of a block on the diagonal: upper sub-blocks rows in
+    // place and columns mirrored, diagonal ones element by element
     auto sub = [&](int gj, int v, const float (&av)[4][4]) {
       const int R0 = cti * T + wm * 64 + 4 * i16;
       const int C0 = ctj * T + wn * 128 + 64 * gj + 16 * grp + 4 * v;
@@ -216,78 +230,117 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_sym_kernel(GemmArgs g) {
       if (rel > 0) return;
       float y[4][4], z[4][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        double d[4] = {0.0, 0.0, 0.0, 0.0};
-        if (D) {
-          const floatx4 d4 = *reinterpret_cast<const floatx4*>(D + (int64_t)(R0 + i) * n + C0);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) d[j] = (double)d4[j];
-        }
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const bool dg = R0 + i == C0 + j;
-          const double t = epi_c(g.alpha, (double)av[i][j], D ? g.beta : 0.0, d[j], dg ? g.gamma : 0.0);
+          const double t = epi_c(g.alpha, (double)av[i][j], 0.0, 0.0, dg ? g.gamma : 0.0);
           y[i][j] = plain ? av[i][j] : (float)t;
           z[i][j] = two ? (float)epi_c2(g.alpha2, t, dg ? g.gamma2 : 0.0) : 0.f;
         }
-      }
       if (rel < 0) {
-        // strictly above the diagonal: rows in place, columns mirrored
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t at = (int64_t)(R0 + i) * n + C0;
-          const floatx4 yr = floatx4{y[i][0], y[i][1], y[i][2], y[i][3]};
-          if (C) *reinterpret_cast<floatx4*>(C + at) = yr;
-          if (Ch) store_h4(Ch + at, yr);
-          if (two) {
-            const floatx4 zr = floatx4{z[i][0], z[i][1], z[i][2], z[i][3]};
-            if (C2) *reinterpret_cast<floatx4*>(C2 + at) = zr;
-            if (C2h) store_h4(C2h + at, zr);
-          }
+          store_h4(Ch + at, floatx4{y[i][0], y[i][1], y[i][2], y[i][3]});
+          if (two) store_h4(C2h + at, floatx4{z[i][0], z[i][1], z[i][2], z[i][3]});
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int64_t at = (int64_t)(C0 + j) * n + R0;
-          const floatx4 yc = floatx4{y[0][j], y[1][j], y[2][j], y[3][j]};
-          if (C) *reinterpret_cast<floatx4*>(C + at) = yc;
-          if (Ch) store_h4(Ch + at, yc);
-          if (two) {
-            const floatx4 zc = floatx4{z[0][j], z[1][j], z[2][j], z[3][j]};
-            if (C2) *reinterpret_cast<floatx4*>(C2 + at) = zc;
-            if (C2h) store_h4(C2h + at, zc);
-          }
+          store_h4(Ch + at, floatx4{y[0][j], y[1][j], y[2][j], y[3][j]});
+          if (two) store_h4(C2h + at, floatx4{z[0][j], z[1][j], z[2][j], z[3][j]});
         }
       } else {
-        // a diagonal 4 x 4 sub-block: its upper triangle in place and mirrored
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             if (i > j) continue;
             const int64_t a1 = (int64_t)(R0 + i) * n + C0 + j, a2 = (int64_t)(C0 + j) * n + R0 + i;
-            if (C) {
-              C[a1] = y[i][j];
-              C[a2] = y[i][j];
-            }
-            if (Ch) {
-              Ch[a1] = half_of(y[i][j]);
-              Ch[a2] = half_of(y[i][j]);
-            }
-            if (C2) {
-              C2[a1] = z[i][j];
-              C2[a2] = z[i][j];
-            }
-            if (C2h) {
+            Ch[a1] = half_of(y[i][j]);
+            Ch[a2] = half_of(y[i][j]);
+            if (two) {
               C2h[a1] = half_of(z[i][j]);
               C2h[a2] = half_of(z[i][j]);
             }
           }
       }
     };
-    // on diagonal tiles, waves with wm >= 2 wn + 2 lie below the diagonal and
-    // store nothing; every other wave issues at least 64 stores
-    if (!(diag && wm >= 2 * wn + 2)) {
-      young = 64;
+    // a 64 x 64 block above the diagonal (no element on it): rows in place
+    // with the DPP swap, then the mirrored columns
+    const int odd = i16 & 1;
+    auto upper = [&](int gj) {
+      const int R0 = cti * T + wm * 64 + 4 * i16;
+      const int Cg = ctj * T + wn * 128 + 64 * gj + 16 * grp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // qy[v]: the 4 halves of row R0 + i, columns Cg + 4 v .. Cg + 4 v + 3
+        u32x2 qy[4], qz[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          halfx4 hy, hz;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float a_ = acc[i][4 * gj + jj][v];
+            const double t = epi_c(g.alpha, (double)a_, 0.0, 0.0, 0.0);
+            hy[jj] = half_of(plain ? a_ : (float)t);
+            hz[jj] = two ? half_of((float)epi_c2(g.alpha2, t, 0.0)) : (_Float16)0.f;
+          }
+          qy[v] = __builtin_bit_cast(u32x2, hy);
+          qz[v] = __builtin_bit_cast(u32x2, hz);
+        }
+        // the even lane keeps columns 0..7 of its row and sends 8..15; the
+        // odd lane keeps 8..15 of its row and sends 0..7.  Store 1 writes
+        // the even lane's row, store 2 the odd lane's row (4 rows below).
+        const int row1 = R0 + i - 4 * odd, row2 = row1 + 4, col = Cg + 8 * odd;
+        auto put = [&](_Float16* O, const u32x2 (&q)[4]) {
+          uint32_t r_[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t snd = odd ? q[e >> 1][e & 1] : q[2 + (e >> 1)][e & 1];
+            r_[e] = (uint32_t)__builtin_amdgcn_mov_dpp((int)snd, 0xB1, 0xF, 0xF, false);  // lanes i ^ 1
+          }
+          const u32x4 rv = u32x4{r_[0], r_[1], r_[2], r_[3]};
+          const u32x4 lo = u32x4{q[0][0], q[0][1], q[1][0], q[1][1]};
+          const u32x4 hi = u32x4{q[2][0], q[2][1], q[3][0], q[3][1]};
+          *reinterpret_cast<u32x4*>(O + (int64_t)row1 * n + col) = odd ? rv : lo;
+          *reinterpret_cast<u32x4*>(O + (int64_t)row2 * n + col) = odd ? hi : rv;
+        };
+        put(Ch, qy);
+        if (two) put(C2h, qz);
+      }
+      asm volatile("" ::: "memory");
+      // mirrored: column Cg + 4 v + jj, rows R0 .. R0 + 3
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          halfx4 hy, hz;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float a_ = acc[i][4 * gj + jj][v];
+            asm volatile("" : "+v"(a_));  // recomputed here rather than kept live from the rows
+            const double t = epi_c(g.alpha, (double)a_, 0.0, 0.0, 0.0);
+            hy[i] = half_of(plain ? a_ : (float)t);
+            hz[i] = two ? half_of((float)epi_c2(g.alpha2, t, 0.0)) : (_Float16)0.f;
+          }
+          const int64_t at = (int64_t)(Cg + 4 * v + jj) * n + R0;
+          *reinterpret_cast<halfx4*>(Ch + at) = hy;
+          if (two) *reinterpret_cast<halfx4*>(C2h + at) = hz;
+        }
+      asm volatile("" ::: "memory");
+    };
+    // 64-row block of this wave against the two 64-column blocks
+    const int rb = cti * 4 + wm;
+    int stores = 0;  // store instructions issued (a lower bound: per output)
+#pragma unroll
+    for (int gj = 0; gj < 2; ++gj) {
+      const int cb = ctj * 4 + 2 * wn + gj;
+      if (rb < cb) {
+        upper(gj);
+        stores += 24;
+      } else if (rb == cb) {
 #define HS_SUB(GJ, V)                                                                 \
   {                                                                                   \
     float av[4][4];                                                                   \
@@ -296,10 +349,13 @@ __global__ __launch_bounds__(512, 1) void gemm_h256_sym_kernel(GemmArgs g) {
     sub(GJ, V, av);                                                                   \
     asm volatile("" ::: "memory");                                                    \
   }
-      HS_SUB(0, 0) HS_SUB(0, 1) HS_SUB(0, 2) HS_SUB(0, 3)
-      HS_SUB(1, 0) HS_SUB(1, 1) HS_SUB(1, 2) HS_SUB(1, 3)
+        HS_SUB(gj, 0) HS_SUB(gj, 1) HS_SUB(gj, 2) HS_SUB(gj, 3)
 #undef HS_SUB
+        // every sub-block call has a lane with rel < 0: 4 rows and 4 columns
+        stores += 32;
+      }
     }
+    young = stores;
     if (ct + 1 < ntile) coords(ct + 1, cmo, cti, ctj);
   }
 #undef HS_BODY

@@ -876,9 +876,28 @@ template <typename TG> __device__ __forceinline__ bool graft_vec(const shampoo_p
 
 // Sums of D^2 and Delta^2 over GRAFT_ROWS rows of a block (Adam: m and v
 // updated in passing).  Work: chunks of 4 columns, chunk k to thread
-// k % 256, GRAFT_U chunks loaded before any is used; one accumulator chain
-// per element position, added in a fixed order at the end.
+// k % 256, visited in increasing k; one accumulator chain per element
+// position, added in a fixed order at the end.  Blocks whose rows are
+// 16-byte aligned and a multiple of 4 wide take the vector path (GRAFT_U
+// chunks loaded before any is used); the others one chunk at a time with
+// scalar accesses.  The scalar path is kept out of the unrolled loop so that
+// it does not set the register count: the vector kernels then run 4 (norms)
+// and 6 (update) waves per SIMD instead of 3 and 2.  Both paths visit the
+// same chunks in the same order, so the sums are the same bit for bit.
 constexpr int GRAFT_U = 4;
+
+// the per-element Adam step and the two squares added to the chains
+__device__ __forceinline__ void graft_elem(const GraftArgs& a, bool adam, float d, float g, float& m, float& v,
+                                           double& sd, double& sg) {
+  sd += (double)d * d;
+  float delta = g;
+  if (adam) {
+    m = a.beta1 * m + (1.0f - a.beta1) * g;
+    v = a.beta2 * v + (1.0f - a.beta2) * g * g;
+    delta = (m / a.bc1) / (sqrtf(v / a.bc2) + a.eps);
+  }
+  sg += (double)delta * delta;
+}
 
 template <typename TG>
 __global__ __launch_bounds__(256) void graft_partials_kernel(GraftArgs a) {
@@ -890,66 +909,57 @@ __global__ __launch_bounds__(256) void graft_partials_kernel(GraftArgs a) {
   const shampoo_param P = a.params[blk.param];
   const float* D = a.dstack + b * (int64_t)a.B * a.B;
   const bool adam = a.graft == SHAMPOO_GRAFT_ADAM && P.m && P.v;
-  const bool vec = graft_vec<TG>(P, blk);
   double sd[4] = {0.0, 0.0, 0.0, 0.0}, sg[4] = {0.0, 0.0, 0.0, 0.0};
   const int r0 = ch * GRAFT_ROWS;
   const int r1 = min(blk.rows, r0 + GRAFT_ROWS);
   const int cpr = (blk.cols + 3) / 4;
   const int total = max(r1 - r0, 0) * cpr;
-  for (int base = 0; base < total; base += 256 * GRAFT_U) {
-    float d[GRAFT_U][4], g[GRAFT_U][4], m[GRAFT_U][4], v[GRAFT_U][4];
-    int64_t prow[GRAFT_U];
-    int r[GRAFT_U], c[GRAFT_U], nv[GRAFT_U];  // nv: valid elements of the chunk (0 past the end)
+  if (graft_vec<TG>(P, blk) && (blk.cols & 3) == 0) {
+    for (int base = (int)threadIdx.x; base < total; base += 256 * GRAFT_U) {
+      floatx4 d[GRAFT_U], m[GRAFT_U], v[GRAFT_U];
+      float g[GRAFT_U][4];
+      int64_t prow[GRAFT_U];
 #pragma unroll
-    for (int u = 0; u < GRAFT_U; ++u) {
-      const int k = base + u * 256 + (int)threadIdx.x;
-      r[u] = r0 + k / cpr;
-      c[u] = (k % cpr) * 4;
-      nv[u] = k < total ? min(4, blk.cols - c[u]) : 0;
-      prow[u] = (int64_t)(blk.row0 + r[u]) * P.ld + blk.col0 + c[u];
-      const float* dp = D + (int64_t)r[u] * a.B + c[u];
-      if (nv[u] == 4 && vec) {
-        const floatx4 d4 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(dp));
-        for (int e = 0; e < 4; ++e) d[u][e] = d4[e];
+      for (int u = 0; u < GRAFT_U; ++u) {
+        const int k = base + u * 256;
+        if (k >= total) continue;
+        const int rr = k / cpr, c = (k - rr * cpr) * 4;
+        prow[u] = (int64_t)(blk.row0 + r0 + rr) * P.ld + blk.col0 + c;
+        d[u] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(D + (int64_t)(r0 + rr) * a.B + c));
         gload4<TG>(P.g, prow[u], g[u]);
         if (adam) {
-          const floatx4 m4 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(P.m + prow[u]));
-          const floatx4 v4 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(P.v + prow[u]));
-          for (int e = 0; e < 4; ++e) { m[u][e] = m4[e]; v[u][e] = v4[e]; }
+          m[u] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(P.m + prow[u]));
+          v[u] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(P.v + prow[u]));
         }
-      } else {
+      }
+#pragma unroll
+      for (int u = 0; u < GRAFT_U; ++u) {
+        if (base + u * 256 >= total) continue;
+        float mm[4], vv[4];
+#pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool ok = e < nv[u];
-          d[u][e] = ok ? dp[e] : 0.f;
-          g[u][e] = ok ? gval<TG>(P.g, prow[u] + e) : 0.f;
-          m[u][e] = ok && adam ? P.m[prow[u] + e] : 0.f;
-          v[u][e] = ok && adam ? P.v[prow[u] + e] : 0.f;
+          mm[e] = adam ? m[u][e] : 0.f;
+          vv[e] = adam ? v[u][e] : 0.f;
+          graft_elem(a, adam, d[u][e], g[u][e], mm[e], vv[e], sd[e], sg[e]);
+        }
+        if (adam) {
+          __builtin_nontemporal_store(floatx4{mm[0], mm[1], mm[2], mm[3]}, reinterpret_cast<floatx4*>(P.m + prow[u]));
+          __builtin_nontemporal_store(floatx4{vv[0], vv[1], vv[2], vv[3]}, reinterpret_cast<floatx4*>(P.v + prow[u]));
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < GRAFT_U; ++u) {
-      if (nv[u] == 0) continue;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (e >= nv[u]) continue;
-        sd[e] += (double)d[u][e] * d[u][e];
-        float delta = g[u][e];
+  } else {
+    for (int k = (int)threadIdx.x; k < total; k += 256) {
+      const int rr = k / cpr, c = (k - rr * cpr) * 4;
+      const int nv = min(4, blk.cols - c);
+      const int64_t prow = (int64_t)(blk.row0 + r0 + rr) * P.ld + blk.col0 + c;
+      const float* dp = D + (int64_t)(r0 + rr) * a.B + c;
+      for (int e = 0; e < nv; ++e) {
+        float mm = adam ? P.m[prow + e] : 0.f, vv = adam ? P.v[prow + e] : 0.f;
+        graft_elem(a, adam, dp[e], gval<TG>(P.g, prow + e), mm, vv, sd[e], sg[e]);
         if (adam) {
-          m[u][e] = a.beta1 * m[u][e] + (1.0f - a.beta1) * g[u][e];
-          v[u][e] = a.beta2 * v[u][e] + (1.0f - a.beta2) * g[u][e] * g[u][e];
-          delta = (m[u][e] / a.bc1) / (sqrtf(v[u][e] / a.bc2) + a.eps);
-        }
-        sg[e] += (double)delta * delta;
-      }
-      if (!adam) continue;
-      if (nv[u] == 4 && vec) {
-        __builtin_nontemporal_store(floatx4{m[u][0], m[u][1], m[u][2], m[u][3]}, reinterpret_cast<floatx4*>(P.m + prow[u]));
-        __builtin_nontemporal_store(floatx4{v[u][0], v[u][1], v[u][2], v[u][3]}, reinterpret_cast<floatx4*>(P.v + prow[u]));
-      } else {
-        for (int e = 0; e < nv[u]; ++e) {
-          P.m[prow[u] + e] = m[u][e];
-          P.v[prow[u] + e] = v[u][e];
+          P.m[prow + e] = mm;
+          P.v[prow + e] = vv;
         }
       }
     }
@@ -1000,60 +1010,59 @@ __global__ __launch_bounds__(256) void graft_update_kernel(GraftArgs a) {
   const float* D = a.dstack + b * (int64_t)a.B * a.B;
   const float sc = a.scales[b];
   const bool mom = a.graft == SHAMPOO_GRAFT_MOMENTUM && P.m;
-  const bool vec = graft_vec<float>(P, blk);
   const int r0 = ch * GRAFT_ROWS;
   const int r1 = min(blk.rows, r0 + GRAFT_ROWS);
   const int cpr = (blk.cols + 3) / 4;
   const int total = max(r1 - r0, 0) * cpr;
-  for (int base = 0; base < total; base += 256 * GRAFT_U) {
-    float d[GRAFT_U][4], w[GRAFT_U][4], m[GRAFT_U][4];
-    int64_t prow[GRAFT_U];
-    int nv[GRAFT_U];
+  // w -= lr * D_g (plain) or m = mu m + D_g, w -= lr * m (momentum)
+  auto elem = [&](float d, float& w, float& m) {
+    const float dg = sc * d;
+    if (mom) {
+      m = a.momentum * m + dg;
+      w -= a.lr * m;
+    } else {
+      w -= a.lr * dg;
+    }
+  };
+  if (graft_vec<float>(P, blk) && (blk.cols & 3) == 0) {
+    for (int base = (int)threadIdx.x; base < total; base += 256 * GRAFT_U) {
+      floatx4 d[GRAFT_U], w[GRAFT_U], m[GRAFT_U];
+      int64_t prow[GRAFT_U];
 #pragma unroll
-    for (int u = 0; u < GRAFT_U; ++u) {
-      const int k = base + u * 256 + (int)threadIdx.x;
-      const int r = r0 + k / cpr, c = (k % cpr) * 4;
-      nv[u] = k < total ? min(4, blk.cols - c) : 0;
-      prow[u] = (int64_t)(blk.row0 + r) * P.ld + blk.col0 + c;
-      const float* dp = D + (int64_t)r * a.B + c;
-      if (nv[u] == 4 && vec) {
-        const floatx4 d4 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(dp));
-        const floatx4 w4 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(P.w + prow[u]));
-        for (int e = 0; e < 4; ++e) { d[u][e] = d4[e]; w[u][e] = w4[e]; }
-        if (mom) {
-          const floatx4 m4 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(P.m + prow[u]));
-          for (int e = 0; e < 4; ++e) m[u][e] = m4[e];
-        }
-      } else {
+      for (int u = 0; u < GRAFT_U; ++u) {
+        const int k = base + u * 256;
+        if (k >= total) continue;
+        const int rr = k / cpr, c = (k - rr * cpr) * 4;
+        prow[u] = (int64_t)(blk.row0 + r0 + rr) * P.ld + blk.col0 + c;
+        d[u] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(D + (int64_t)(r0 + rr) * a.B + c));
+        w[u] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(P.w + prow[u]));
+        if (mom) m[u] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(P.m + prow[u]));
+      }
+#pragma unroll
+      for (int u = 0; u < GRAFT_U; ++u) {
+        if (base + u * 256 >= total) continue;
+        float ww[4], mm[4];
+#pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool ok = e < nv[u];
-          d[u][e] = ok ? dp[e] : 0.f;
-          w[u][e] = ok ? P.w[prow[u] + e] : 0.f;
-          m[u][e] = ok && mom ? P.m[prow[u] + e] : 0.f;
+          ww[e] = w[u][e];
+          mm[e] = mom ? m[u][e] : 0.f;
+          elem(d[u][e], ww[e], mm[e]);
         }
+        __builtin_nontemporal_store(floatx4{ww[0], ww[1], ww[2], ww[3]}, reinterpret_cast<floatx4*>(P.w + prow[u]));
+        if (mom) __builtin_nontemporal_store(floatx4{mm[0], mm[1], mm[2], mm[3]}, reinterpret_cast<floatx4*>(P.m + prow[u]));
       }
     }
-#pragma unroll
-    for (int u = 0; u < GRAFT_U; ++u) {
-      if (nv[u] == 0) continue;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float dg = sc * d[u][e];
-        if (mom) {
-          m[u][e] = a.momentum * m[u][e] + dg;
-          w[u][e] -= a.lr * m[u][e];
-        } else {
-          w[u][e] -= a.lr * dg;
-        }
-      }
-      if (nv[u] == 4 && vec) {
-        __builtin_nontemporal_store(floatx4{w[u][0], w[u][1], w[u][2], w[u][3]}, reinterpret_cast<floatx4*>(P.w + prow[u]));
-        if (mom) __builtin_nontemporal_store(floatx4{m[u][0], m[u][1], m[u][2], m[u][3]}, reinterpret_cast<floatx4*>(P.m + prow[u]));
-      } else {
-        for (int e = 0; e < nv[u]; ++e) {
-          P.w[prow[u] + e] = w[u][e];
-          if (mom) P.m[prow[u] + e] = m[u][e];
-        }
+  } else {
+    for (int k = (int)threadIdx.x; k < total; k += 256) {
+      const int rr = k / cpr, c = (k - rr * cpr) * 4;
+      const int nv = min(4, blk.cols - c);
+      const int64_t prow = (int64_t)(blk.row0 + r0 + rr) * P.ld + blk.col0 + c;
+      const float* dp = D + (int64_t)(r0 + rr) * a.B + c;
+      for (int e = 0; e < nv; ++e) {
+        float ww = P.w[prow + e], mm = mom ? P.m[prow + e] : 0.f;
+        elem(dp[e], ww, mm);
+        P.w[prow + e] = ww;
+        if (mom) P.m[prow + e] = mm;
       }
     }
   }

@@ -264,7 +264,7 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
     // symmetric NT with half outputs only, n a multiple of 256: 256-tiles of
     // 8 waves (1.07x - 1.23x faster than the 128-tile kernel on 288 x 1024^2)
     if (!c.nn && c.sym && !c.transC && n % HS_T == 0 && !ext && c.C == nullptr && c.C2 == nullptr &&
-        c.D == nullptr) {
+        c.D == nullptr && c.Ch != nullptr) {
       int cus = 0;
       HIP_TRY_ERR(cu_count(&cus));
       GemmArgs h = g;
