@@ -123,8 +123,9 @@ def test_product_kernels_bit_identical(mir, method, compute):
     assert not X2[:, v:, :].any() and not X2[:, :, v:].any()
 
 
+@pytest.mark.parametrize("v,side", [(384, 512), (896, 1024)])
 @pytest.mark.parametrize("method", ["cn", "ndb", "chebyshev"])
-def test_half_products_large_tiles_bit_identical(mir, method):
+def test_half_products_large_tiles_bit_identical(mir, method, v, side):
     """Half-precision products: Newton-DB's NN products of a 384 x 384 stack
     run on the tiled kernel, those of the same stack padded to 512 (valid =
     384) on the 256-tile NN kernel, whose matrix cores take the operands in
@@ -132,12 +133,16 @@ def test_half_products_large_tiles_bit_identical(mir, method):
     reads.  Coupled Newton's products with half outputs only run on the
     128-tile kernel at 384 and on the 256-tile symmetric kernel (8 waves,
     k-stages of 32) at 512; Clenshaw (float32 outputs) on the 128-tile
-    kernel at both sides.  The roots agree bit for bit."""
-    n, v = 4, 384
-    A = synthetic.spd_stack(384, n, v, 1e-2, 1.0).astype(np.float32)
+    kernel at both sides.  The roots agree bit for bit.  At 1024 the
+    symmetric kernel's 4 x 4 tiles put blocks above, on and below the
+    diagonal in every position of a workgroup's waves (rows above the
+    diagonal leave through the lane-swap store path, diagonal blocks
+    through the sub-block path)."""
+    n = 4 if side == 512 else 2
+    A = synthetic.spd_stack(v, n, v, 1e-2, 1.0).astype(np.float32)
     kw = dict(method=method, scaling="frobenius", iters=18, iters2=12, cheb_degree=12, eps=1e-3, compute="f16")
     X1, s1, f1 = run_root(mir, A, 4, **kw)
-    Ap = np.zeros((n, 512, 512), dtype=np.float32)
+    Ap = np.zeros((n, side, side), dtype=np.float32)
     Ap[:, :v, :v] = A
     X2, s2, f2 = run_root(mir, Ap, 4, valid=[v] * n, **kw)
     assert not f1.any() and not f2.any()
