@@ -688,8 +688,14 @@ template <typename E, int RUN> __device__ __forceinline__ void load_run(const E*
   }
 }
 
-template <typename E, bool NN>
-__global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
+// TL: the workgroups walk a tile list (products whose blocks have valid
+// extents: the list holds only the tiles inside each block's rows and
+// columns, cut into 8 ranges of equal cost, one per XCD), and each tile's
+// k-loop stops at its matrix's inner extent (kext, in elements; the zero
+// padding beyond it makes that exact).  Partial tiles at the extents' edges
+// are computed whole: their padding rows and columns come out zero.
+template <typename E, bool NN, bool TL>
+__global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g, TileList tl, const int32_t* kext) {
   using P = P128<E>;
   using EO = typename P::out_t;  // C, D, C2
   using acc_t = typename P::acc_t;
@@ -703,11 +709,20 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * SB];
   const int per = gridDim.x >> 3;
   const int x = blockIdx.x & 7, l = blockIdx.x >> 3;
-  const int64_t q = g.total >> 3, r = g.total & 7;
-  const int64_t mine = q + (x < r ? 1 : 0);
-  if (mine <= l) return;
-  const int64_t first = x * q + (x < r ? x : r) + l;
-  const int ntile = (int)((mine - l + per - 1) / per);
+  int64_t first;
+  int ntile;
+  if constexpr (TL) {
+    const int c0 = tl.cut[x], c1 = tl.cut[x + 1];
+    if (c0 + l >= c1) return;
+    first = c0 + l;
+    ntile = (c1 - c0 - l + per - 1) / per;
+  } else {
+    const int64_t q = g.total >> 3, r = g.total & 7;
+    const int64_t mine = q + (x < r ? 1 : 0);
+    if (mine <= l) return;
+    first = x * q + (x < r ? x : r) + l;
+    ntile = (int)((mine - l + per - 1) / per);
+  }
   const int n = g.n, nst = n / BK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -729,7 +744,18 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
       boff[qq] = p128_brow(row) * n + VE * (pos ^ lds_swz(row));
     }
   }
-  auto coords = [&](int it, int64_t& moff, int& ti, int& tj) {
+  // tile it of this workgroup: matrix offset, tile indices and k-stages
+  auto coords = [&](int it, int64_t& moff, int& ti, int& tj, int& ns) {
+    ns = nst;
+    if constexpr (TL) {
+      const int32_t pk = tl.tiles[first + (int64_t)it * per];
+      const int64_t mat = pk >> 16;
+      ti = (pk >> 8) & 255;
+      tj = pk & 255;
+      moff = mat * g.stride;
+      if (kext) ns = min(nst, max(1, (max(kext[mat], 0) + BK - 1) / BK));
+      return;
+    }
     const int64_t w = first + (int64_t)it * per;
     const int64_t mat = w / g.tiles;
     int t = (int)(w - mat * g.tiles);
@@ -750,9 +776,10 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
   };
   auto bbase = [&](int64_t mo, int tj) { return Bg + mo + (NN ? (int64_t)tj * T : (int64_t)tj * T * n); };
   int lt = 0, lk = 0;
-  int64_t cmo;  // compute cursor: the current tile's matrix offset and tile indices
-  int cti, ctj;
-  coords(0, cmo, cti, ctj);
+  int64_t cmo;  // compute cursor: the current tile's matrix offset, tile indices and k-stages
+  int cti, ctj, cns;
+  coords(0, cmo, cti, ctj, cns);
+  int lns = cns;  // k-stages of the tile being loaded
   const E* LA = Ag + cmo + (int64_t)cti * T * n;
   const E* LB = bbase(cmo, ctj);
   auto issue = [&](int buf) {
@@ -767,12 +794,12 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
     }
   };
   auto advance = [&]() {
-    if (++lk == nst) {
+    if (++lk == lns) {
       lk = 0;
       if (++lt < ntile) {
         int64_t mo;
         int ti, tj;
-        coords(lt, mo, ti, tj);
+        coords(lt, mo, ti, tj, lns);
         LA = Ag + mo + (int64_t)ti * T * n;
         LB = bbase(mo, tj);
       }
@@ -787,7 +814,18 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
   const EO* Dg = reinterpret_cast<const EO*>(g.D);
   EO dpre[PREFETCH_D ? 4 : 1][4][4];  // D of the current tile [i][v][jb] (float32)
   const bool plain = g.alpha == 1.0 && g.gamma == 0.0 && Dg == nullptr && g.C2 == nullptr && g.C2h == nullptr;
-  const int total_steps = ntile * nst;
+  int total_steps = ntile * nst;
+  if constexpr (TL) {
+    if (kext) {
+      total_steps = 0;
+      for (int it = 0; it < ntile; ++it) {
+        int64_t mo;
+        int ti, tj, ns;
+        coords(it, mo, ti, tj, ns);
+        total_steps += ns;
+      }
+    }
+  }
   auto dload = [&](int i, EO (*d)[4]) {  // D at the lane's outputs of row block i
 #pragma unroll
     for (int v = 0; v < 4; ++v)
@@ -807,7 +845,7 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
     const bool more = step + 1 < total_steps;
     if (more) issue((step + 1) & 1);
     if constexpr (PREFETCH_D) {
-      if (Dg && ck == nst - 1) {
+      if (Dg && ck == cns - 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dload(i, dpre[i]);
       }
@@ -855,7 +893,7 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
     if (more) advance();
     wait_vmcnt0();
     barrier_no_fence();
-    if (++ck < nst) continue;
+    if (++ck < cns) continue;
     ck = 0;
     EO* C = g.C ? reinterpret_cast<EO*>(g.C) + cmo : nullptr;
     EO* C2 = g.C2 ? reinterpret_cast<EO*>(g.C2) + cmo : nullptr;
@@ -972,7 +1010,7 @@ __global__ __launch_bounds__(256, 2) void gemm_p128_kernel(GemmArgs g) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
-    if (++ct < ntile) coords(ct, cmo, cti, ctj);
+    if (++ct < ntile) coords(ct, cmo, cti, ctj, cns);
   }
 }
 

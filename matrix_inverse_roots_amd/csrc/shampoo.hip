@@ -87,6 +87,7 @@ struct GemmCall {
   // (tile_list_kernel): the tiled kernel then walks it with a fixed grid.
   const int32_t* tiles = nullptr;
   const int32_t* cut = nullptr;
+  int tile = 64;  // tile side of that list: 64 (tiled kernel) or 128 (persistent 128-tile kernel)
 };
 
 #define HIP_TRY_ERR(expr)         \
@@ -147,6 +148,14 @@ template <Mma MM, typename TA, typename TB, typename TC>
 hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
   const bool ext = c.rext || c.cext || c.kext;
   const Extents ex{c.rext, c.cext, c.kext};
+  {
+    constexpr bool one_type = (MM == Mma::F32 && std::is_same<TA, float>::value && std::is_same<TB, float>::value &&
+                               std::is_same<TC, float>::value) ||
+                              (MM == Mma::F64 && std::is_same<TA, double>::value &&
+                               std::is_same<TB, double>::value && std::is_same<TC, double>::value);
+    if (c.tiles && c.tile != 64 && !(one_type && c.tile == P128_T && !c.nn && n % P128_T == 0))
+      return hipErrorInvalidValue;  // a list of 128-tiles is walked by the persistent kernel only
+  }
   int T = (n % 128 == 0 && !ext) ? 128 : 64;
   if constexpr ((MM == Mma::F32 && std::is_same<TA, float>::value && std::is_same<TB, float>::value &&
                  std::is_same<TC, float>::value) ||
@@ -210,6 +219,16 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
   constexpr bool same64 = MM == Mma::F64 && std::is_same<TA, double>::value && std::is_same<TB, double>::value &&
                           std::is_same<TC, double>::value;
   if constexpr (same32 || same64) {
+    // extents with a list of 128-tiles: the persistent kernel walks the list
+    if (c.tiles && c.tile == P128_T && !c.nn && n % P128_T == 0) {
+      using E = typename std::conditional<same32, float, double>::type;
+      int cus = 0;
+      HIP_TRY_ERR(cu_count(&cus));
+      const int64_t wgs = (int64_t)std::max(8, (cus / 8) * 8) * 2;
+      hipLaunchKernelGGL((gemm_p128_kernel<E, false, true>), dim3((unsigned)wgs), dim3(256), 0, st, g,
+                         TileList{c.tiles, c.cut}, c.kext);
+      return hipGetLastError();
+    }
     if (T == P128_T && (!c.nn || (!c.sym && !c.transC))) {
       using E = typename std::conditional<same32, float, double>::type;
       int cus = 0;
@@ -223,9 +242,9 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
       // persistent grid: two workgroups per CU, a multiple of the 8 XCDs
       const int64_t wgs = std::min<int64_t>(((h.total + 7) / 8) * 8, std::max(8, (cus / 8) * 8) * 2);
       if (c.nn)
-        hipLaunchKernelGGL((gemm_p128_kernel<E, true>), dim3((unsigned)wgs), dim3(256), 0, st, h);
+        hipLaunchKernelGGL((gemm_p128_kernel<E, true, false>), dim3((unsigned)wgs), dim3(256), 0, st, h, TileList{nullptr, nullptr}, nullptr);
       else
-        hipLaunchKernelGGL((gemm_p128_kernel<E, false>), dim3((unsigned)wgs), dim3(256), 0, st, h);
+        hipLaunchKernelGGL((gemm_p128_kernel<E, false, false>), dim3((unsigned)wgs), dim3(256), 0, st, h, TileList{nullptr, nullptr}, nullptr);
       return hipGetLastError();
     }
   }
@@ -237,7 +256,7 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
       int cus = 0;
       HIP_TRY_ERR(cu_count(&cus));
       const int64_t wgs = std::min<int64_t>(((g.total + 7) / 8) * 8, std::max(8, (cus / 8) * 8) * 2);
-      hipLaunchKernelGGL((gemm_p128_kernel<__bf16, false>), dim3((unsigned)wgs), dim3(256), 0, st, g);
+      hipLaunchKernelGGL((gemm_p128_kernel<__bf16, false, false>), dim3((unsigned)wgs), dim3(256), 0, st, g, TileList{nullptr, nullptr}, nullptr);
       return hipGetLastError();
     }
   }
@@ -281,7 +300,7 @@ hipError_t gemm(const GemmCall& c, int n, int64_t batch, hipStream_t st) {
       int cus = 0;
       HIP_TRY_ERR(cu_count(&cus));
       const int64_t wgs = std::min<int64_t>(((g.total + 7) / 8) * 8, std::max(8, (cus / 8) * 8) * 2);
-      hipLaunchKernelGGL((gemm_p128_kernel<_Float16, false>), dim3((unsigned)wgs), dim3(256), 0, st, g);
+      hipLaunchKernelGGL((gemm_p128_kernel<_Float16, false, false>), dim3((unsigned)wgs), dim3(256), 0, st, g, TileList{nullptr, nullptr}, nullptr);
       return hipGetLastError();
     }
   }
@@ -1314,6 +1333,7 @@ shampoo_status pack_impl(const shampoo_matrix* mats, int32_t nparams, const sham
 struct ProductTiles {
   const int32_t* tiles[4] = {nullptr, nullptr, nullptr, nullptr};
   const int32_t* cut[4] = {nullptr, nullptr, nullptr, nullptr};
+  int T = 64;  // tile side of the lists
 };
 
 shampoo_status stats_impl(const void* g, const void* gt, shampoo_dtype gdt, int64_t nblk, int32_t B, void* LR,
@@ -1349,6 +1369,7 @@ shampoo_status stats_impl(const void* g, const void* gt, shampoo_dtype gdt, int6
       cl.cut = pt->cut[0];
       cr.tiles = pt->tiles[1];
       cr.cut = pt->cut[1];
+      cl.tile = cr.tile = pt->T;
     }
   }
   if (sdt == SHAMPOO_F64) {
@@ -1402,6 +1423,7 @@ shampoo_status precond_impl(const void* roots, shampoo_dtype rdt, const void* g,
       c1.cut = pt->cut[2];
       c2.tiles = pt->tiles[3];
       c2.cut = pt->cut[3];
+      c1.tile = c2.tile = pt->T;
     }
   }
   if (rdt == SHAMPOO_F64) {
@@ -1720,9 +1742,13 @@ shampoo_status step_impl(const shampoo_step_args* a, hipStream_t st) {
       pt.tiles[q] = sp.tiles;
       pt.cut[q] = sp.cut;
     }
+    // float32 gradients, statistics and roots, B a multiple of 128: all four
+    // products run on the persistent 128-tile kernel (lists of 128-tiles);
+    // otherwise on the tiled kernel (lists of 64-tiles)
+    pt.T = (a->g_dt == SHAMPOO_F32 && a->stats_dt == SHAMPOO_F32 && B % 128 == 0) ? 128 : 64;
     ta.nmat = nblk;
     ta.n = B;
-    ta.T = 64;
+    ta.T = pt.T;
     ta.BK = 32;
     hipLaunchKernelGGL(tile_list_kernel, dim3(4), dim3(1024), 0, st, ta);
     LAUNCH_CHECK("tile_list");
