@@ -469,6 +469,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, Extents ext, T
 // the 1024 chunk sums in LDS, chunk walks) give each matrix's first list
 // slot and cost offset; cut[x] is the first tile whose cost offset reaches
 // x C / 8 (C the total cost), found by binary search over the matrices.
+// Within each range the tiles are then put in order of decreasing cost (a
+// counting sort on the k-stage count): the range's workgroups take its
+// tiles round-robin, so the costly tiles are spread over them first
+// (longest-processing-time order) instead of falling to a few workgroups
+// where blocks of one shape sit together.  Every tile is computed the same
+// way in any order.
 struct TileListSpec {
   const int32_t* r;
   const int32_t* c;
@@ -478,6 +484,7 @@ struct TileListSpec {
   int32_t* cut;    // [9]
   int32_t* tpre;   // [matrices] scratch: first list slot of each matrix
   int64_t* cpre;   // [matrices] scratch: cost before each matrix
+  int32_t* tmp;    // [matrices * (n/T)^2] scratch: the reordered ranges
 };
 struct TileListArgs {
   TileListSpec s[4];
@@ -489,6 +496,8 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(TileListArgs a) {
   const TileListSpec sp = a.s[blockIdx.x];
   __shared__ int32_t tsum[1024];
   __shared__ int64_t csum[1024];
+  __shared__ int32_t lcut[9];
+  __shared__ int32_t hist[256];
   const int tid = threadIdx.x;
   const int nt = a.n / a.T, nsmax = a.n / a.BK;
   const int64_t ch = (a.nmat + 1023) / 1024;
@@ -556,6 +565,39 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(TileListArgs a) {
       cut = (int32_t)(sp.tpre[lo] + j);
     }
     sp.cut[tid] = cut;
+    lcut[tid] = cut;
+  }
+  __syncthreads();  // the list (global) and the cuts (LDS) are complete
+  // per range: counting sort on key nsmax - (k-stages), bins in LDS
+  constexpr int NB = 256;
+  for (int x = 0; x < 8; ++x) {
+    const int lo = lcut[x], hi = lcut[x + 1];
+    if (hi - lo < 2) continue;
+    if (tid < NB) hist[tid] = 0;
+    __syncthreads();
+    auto key = [&](int32_t pk) {
+      int cnt, rt, ct, nst;
+      info(pk >> 16, cnt, rt, ct, nst);
+      return min(NB - 1, max(0, nsmax - nst));
+    };
+    for (int i = lo + tid; i < hi; i += 1024) atomicAdd(&hist[key(sp.tiles[i])], 1);
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      for (int q = 0; q < NB; ++q) {
+        const int h = hist[q];
+        hist[q] = acc;
+        acc += h;
+      }
+    }
+    __syncthreads();
+    for (int i = lo + tid; i < hi; i += 1024) {
+      const int32_t pk = sp.tiles[i];
+      sp.tmp[lo + atomicAdd(&hist[key(pk)], 1)] = pk;
+    }
+    __syncthreads();
+    for (int i = lo + tid; i < hi; i += 1024) sp.tiles[i] = sp.tmp[i];
+    __syncthreads();
   }
 }
 

@@ -1518,7 +1518,7 @@ shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
   L->tl = L->tl_each = 0;
   if (L->ragged) {
     const int64_t nt = a->B / 64;
-    L->tl_each = align_up((size_t)a->nblk * nt * nt * 4) + align_up((size_t)a->nblk * 4) +
+    L->tl_each = 2 * align_up((size_t)a->nblk * nt * nt * 4) + align_up((size_t)a->nblk * 4) +
                  align_up((size_t)a->nblk * 8) + ALIGN;
     L->tl = off;
     off += 4 * L->tl_each;
@@ -1739,6 +1739,7 @@ shampoo_status step_impl(const shampoo_step_args* a, hipStream_t st) {
       sp.tpre = (int32_t*)(base + tb);
       sp.cpre = (int64_t*)(base + tb + align_up((size_t)nblk * 4));
       sp.cut = (int32_t*)(base + tb + align_up((size_t)nblk * 4) + align_up((size_t)nblk * 8));
+      sp.tmp = (int32_t*)(base + tb + align_up((size_t)nblk * 4) + align_up((size_t)nblk * 8) + ALIGN);
       pt.tiles[q] = sp.tiles;
       pt.cut[q] = sp.cut;
     }
