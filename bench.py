@@ -532,7 +532,7 @@ def main():
     achieved = flops_alg / mean_gemm / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP64_MFMA, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP64_MFMA, 4), "traffic": traffic_from_profiles("gemm_f64_b512"),
-            "kernel": "gemm_p128_kernel<double, true>", "launches_timed": len(gemm_ms),
+            "kernel": "gemm_p128_kernel<double, true, false>", "launches_timed": len(gemm_ms),
             "mean_launch_ms": round(mean_gemm * 1e3, 4), "flop_per_launch": flops_alg,
             "algorithmic_bytes_per_launch": 3 * N_BLOCKS * B * B * 8}
     gemm_share = float(np.sum(gemm_ms)) * 1e-3 / (dt * K) if gemm_ms else None
