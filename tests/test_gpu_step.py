@@ -568,3 +568,47 @@ def test_zero_gradient_parameter(mir, eps):
             log(f"eps {eps} step {t + 1}: worst rel err {e:.2e}")
             assert e < 1e-4
     assert np.isfinite(W[0].cpu().numpy()).all() and np.isfinite(W[1].cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("stats_dtype", ["f32", "f64"])
+def test_ragged_step_statistics_bit_exact(mir, stats_dtype):
+    """Statistics of ragged blocks inside a full step, where they run as
+    products with extents walking device-built tile lists: 128-tile lists on
+    the persistent kernel for float32 gradients and statistics at B = 256
+    and 1024, 64-tile lists on the tiled kernel at B = 192 and for float64
+    statistics.  Small integer gradients make every sum exact, so L and R of
+    every block (valid region and zero padding) equal the integer sums of
+    G G^T and G^T G over two steps bit for bit."""
+    import torch
+    shapes = [(300, 700), (130, 1000), (1024, 2100), (64, 100), (250, 390)]
+    bsz = {(300, 700): 256, (130, 1000): 256, (1024, 2100): 1024, (64, 100): 1024, (250, 390): 192}
+    gen = np.random.default_rng(11)
+    grads = [[gen.integers(-3, 4, size=s).astype(np.float32) for s in shapes] for _ in range(2)]
+    W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    sdt = torch.float32 if stats_dtype == "f32" else torch.float64
+    opt = mir.Shampoo(W, block_size=lambda m, n: bsz[(m, n)], beta2=1.0, eps=1e-3, stats_dtype=sdt,
+                      root=mir.RootOpts(method="cn", iters=4, compute="f32" if stats_dtype == "f32" else "f64"),
+                      graft="none", lr=0.0, group_factors=True)
+    for g in grads:
+        opt.step([to_dev(x) for x in g])
+    torch.cuda.synchronize()
+    checked = 0
+    for st, idx in zip(opt.stacks, opt.members):
+        LR = st.LR.cpu().numpy()
+        nb = st.nblk
+        assert any(int(r[5]) < st.B or int(r[6]) < st.B for r in st.table), "stack without ragged blocks"
+        for b, row in enumerate(st.table):
+            p, r0, c0, rows, cols = int(row[0]), int(row[3]), int(row[4]), int(row[5]), int(row[6])
+            L = np.zeros((rows, rows), dtype=np.int64)
+            R = np.zeros((cols, cols), dtype=np.int64)
+            for g in grads:
+                gb = g[idx[p]][r0:r0 + rows, c0:c0 + cols].astype(np.int64)
+                L += gb @ gb.T
+                R += gb.T @ gb
+            Lg, Rg = LR[b], LR[nb + b]
+            assert np.array_equal(Lg[:rows, :rows], L.astype(Lg.dtype))
+            assert np.array_equal(Rg[:cols, :cols], R.astype(Rg.dtype))
+            assert not Lg[rows:, :].any() and not Lg[:, rows:].any()
+            assert not Rg[cols:, :].any() and not Rg[:, cols:].any()
+            checked += 1
+    assert checked == sum(st.nblk for st in opt.stacks)
