@@ -881,8 +881,8 @@ template <typename TG> __device__ __forceinline__ bool graft_vec(const shampoo_p
 // 16-byte aligned and a multiple of 4 wide take the vector path (GRAFT_U
 // chunks loaded before any is used); the others one chunk at a time with
 // scalar accesses.  The scalar path is kept out of the unrolled loop so that
-// it does not set the register count: the vector kernels then run 4 (norms)
-// and 6 (update) waves per SIMD instead of 3 and 2.  Both paths visit the
+// it does not set the register count: the kernels then run 4 (norms) and 7
+// (update) waves per SIMD instead of 3 and 2.  Both paths visit the
 // same chunks in the same order, so the sums are the same bit for bit.
 constexpr int GRAFT_U = 4;
 
