@@ -46,9 +46,10 @@ namespace shampoo {
 // Stores that leave partial segments (8-byte pieces of 16 rows per
 // instruction, the earlier in-place form) were written back to memory
 // before the segments were complete: 1.33-1.45x the output bytes for one
-// output and 2.2x for two, and about a quarter of the kernel's time.  With
-// the swap the writes are 1.05x (one output) and the squaring of 288 x 1024^2
-// takes 485 us instead of 623 (measured in isolation).  A block on the
+// output and 2.2x for two.  With the swap the writes are 1.05x and 1.21x,
+// and on 288 x 1024^2 (measured in isolation, steady state) a squaring takes
+// 464 us instead of 486 and a product with two outputs 569 instead of 670;
+// without any stores it would take 340.  A block on the
 // diagonal is written 4 x 4 sub-block by sub-block: its upper sub-blocks in
 // place (8-byte rows) and mirrored, the diagonal sub-blocks element by
 // element; blocks below the diagonal store nothing.
