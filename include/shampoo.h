@@ -178,7 +178,7 @@ typedef struct shampoo_param {
  *   shampoo_cheb_eval, how the series is summed.
  * eps: added to the diagonal of each matrix's valid region before scaling
  *   ([DASH] "2. Preliminaries on Shampoo"; added once, see [DASH] "B.1").
- * tol: the Newton iterations (CN, NDB), compute F32 or F64; 0 runs
+ * tol: the Newton iterations (CN, NDB), any compute type; 0 runs
  *   exactly `iters` (and `iters2`) iterations (the fixed count of [3DS]
  *   "Hyperparameters", fix_iter).  tol > 0 stops early once every matrix is
  *   within tol over its valid region: coupled Newton ||M - I||_F <= tol
@@ -187,9 +187,12 @@ typedef struct shampoo_param {
  *   each call, checked after each T product, the call then ending with that
  *   iteration as its last (the chain is planned again with that count).
  *   Matrices that cannot converge are not waited for: an iterate turned
- *   NaN, or a scale that is zero or not finite (the final pass flags them).  Rounding keeps ||M - I||_F near u sqrt(v) .. u v (u the unit
- *   roundoff, v the valid size), so tol must lie above that: 1e-4 suits
- *   float32 up to v = 1024.  Each check synchronises the stream with the
+ *   NaN, or a scale that is zero or not finite (the final pass flags them).
+ *   Rounding keeps ||M - I||_F near u sqrt(v) .. u v (u the unit roundoff,
+ *   v the valid size), so tol must lie above that: 1e-4 suits float32 up
+ *   to v = 1024.  F16 chains check the half copy of the iterate, the one
+ *   the next products read; it settles near 2.6e-2 at v = 1024, where
+ *   0.1 suits.  Each check synchronises the stream with the
  *   host (one flag read), so work queued after it on other streams is not
  *   enqueued until the solve ends; `iters` stays the upper bound; the
  *   float64 recomputation of shampoo_step's fallback runs the full count.

@@ -200,7 +200,7 @@ class RootOpts:
     eps: float = 0.0
     cheb_eps: Optional[float] = None   # defaults to eps
     pi_start: object = None       # device float32 [pi_vectors, B]
-    tol: float = 0.0              # CN / NDB, f32 or f64: stop once ||M - I||_F <= tol (0: run iters)
+    tol: float = 0.0              # CN / NDB: stop once ||M - I||_F <= tol (0: run iters; f16 checks the half copy)
     residual_out: object = None   # device float32 [n]: ||X^p A_s - I||_F / sqrt(v) per matrix
     residual_bound: float = 0.0   # > 0: FLAG_RESIDUAL where the residual exceeds it
 

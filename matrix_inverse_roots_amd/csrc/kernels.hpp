@@ -175,6 +175,16 @@ template <> struct Quad<float> {
     *reinterpret_cast<floatx4*>(p) = floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
   }
 };
+template <> struct Quad<_Float16> {
+  static __device__ __forceinline__ void load(const _Float16* p, double* o) {
+    const halfx4 t = *reinterpret_cast<const halfx4*>(p);
+    o[0] = (double)t[0]; o[1] = (double)t[1]; o[2] = (double)t[2]; o[3] = (double)t[3];
+  }
+  static __device__ __forceinline__ void load_nt(const _Float16* p, double* o) {
+    const halfx4 t = __builtin_nontemporal_load(reinterpret_cast<const halfx4*>(p));
+    o[0] = (double)t[0]; o[1] = (double)t[1]; o[2] = (double)t[2]; o[3] = (double)t[3];
+  }
+};
 template <> struct Quad<double> {
   static __device__ __forceinline__ void load(const double* p, double* o) {
     const doublex2 t0 = *reinterpret_cast<const doublex2*>(p), t1 = *reinterpret_cast<const doublex2*>(p + 2);

@@ -815,9 +815,6 @@ shampoo_status check_root_args(int64_t n, int32_t B, int32_t p, const shampoo_ro
     return fail(SHAMPOO_E_INVALID, "residual_bound must be finite and >= 0");
   if (o->tol > 0.0 && o->method == SHAMPOO_CHEBYSHEV)
     return fail(SHAMPOO_E_INVALID, "tol applies to the Newton iterations (CN, NDB), not to Chebyshev");
-  if (o->tol > 0.0 && o->compute == SHAMPOO_F16)
-    return fail(SHAMPOO_E_UNSUPPORTED, "tol needs float32 or float64 iterates: half products leave ||M - I||_F near "
-                "half resolution times the matrix size");
   switch (o->method) {
     case SHAMPOO_CN:
       if (!pow2_in(p, 8)) return fail(SHAMPOO_E_UNSUPPORTED, "coupled Newton supports p in {1, 2, 4, 8}, got %d", p);
@@ -856,7 +853,10 @@ shampoo_status check_root_args(int64_t n, int32_t B, int32_t p, const shampoo_ro
 // reads its operands as half (in half-operand chains) and its addend D in
 // float32; the final pass reads float32.  A buffer written by an op holds a
 // new value, so the needs gathered after it belong to that op's output.
-void mark_needs(Plan& P) {
+// half: a half-operand chain, whose convergence checks read the half copy of
+// the checked iterate (the copy later products read), so that a check does
+// not add a float32 output to the product before it.
+void mark_needs(Plan& P, bool half) {
   std::vector<int> need(P.peak > 0 ? P.peak : 1, 0);
   auto take = [&](int b) {
     const int v = need[b];
@@ -881,7 +881,7 @@ void mark_needs(Plan& P) {
       for (size_t j = 0; j < op.mout.size(); ++j) op.mneed[j] = take(op.mout[j]);
       for (int b : op.min) need[b] |= NEED_F32;
     } else if (op.kind == OP_CHECK) {
-      need[op.a] |= NEED_F32;
+      need[op.a] |= half ? NEED_HALF : NEED_F32;
     } else {
       need[op.a] |= NEED_F32;
     }
@@ -908,7 +908,7 @@ Plan build_plan(int32_t p, const shampoo_root_opts* o) {
         plan_cheb(P, cheb_coeffs(p, d, N, o->cheb_eps));
     }
   }
-  mark_needs(P);
+  mark_needs(P, o->compute == SHAMPOO_F16);
   if (want_residual(o)) {
     // the residual products run after the chain, in any three buffers other
     // than the result, with the Frobenius scratch of the checks
@@ -1178,9 +1178,14 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
       if (op.kind == OP_GEMM) ++gemms;
       continue;
     }
-    // ||M - I||_F: the Frobenius sums of M + eps I with eps = -1
-    hipLaunchKernelGGL((frob_partial_kernel<TS>), dim3((unsigned)parts, (unsigned)n), dim3(256), 0, st,
-                       (const TS*)buf(op.a), B, valid, -1.0, parts, cpart);
+    // ||M - I||_F: the Frobenius sums of M + eps I with eps = -1 (half
+    // chains: of the half copy that the next products read)
+    if constexpr (HALF)
+      hipLaunchKernelGGL((frob_partial_kernel<_Float16>), dim3((unsigned)parts, (unsigned)n), dim3(256), 0, st,
+                         (const _Float16*)hbuf(op.a), B, valid, -1.0, parts, cpart);
+    else
+      hipLaunchKernelGGL((frob_partial_kernel<TS>), dim3((unsigned)parts, (unsigned)n), dim3(256), 0, st,
+                         (const TS*)buf(op.a), B, valid, -1.0, parts, cpart);
     LAUNCH_CHECK("frob_partial");
     hipLaunchKernelGGL(frob_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (const double*)cpart,
                        parts, n, cnorm);
@@ -1198,7 +1203,11 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
       // coupled Newton has converged: the next op (X T) is X's last update
       if (oi + 1 >= cur->ops.size() || cur->ops[oi + 1].kind != OP_GEMM || cur->ops.back().kind != OP_FINAL)
         return fail(SHAMPOO_E_INVALID, "internal: convergence check placement");
-      shampoo_status r = exec(cur->ops[oi + 1]);
+      // it was planned with the outputs a later iteration reads: in a half
+      // chain only the half copy; the final pass reads the float32 result
+      Op last = cur->ops[oi + 1];
+      last.need_c = NEED_F32;
+      shampoo_status r = exec(last);
       if (r != SHAMPOO_OK) return r;
       Op fin = cur->ops.back();
       fin.a = cur->ops[oi + 1].c;
@@ -1210,7 +1219,7 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
     if (op.b == 1) used1 = op.c;
     Plan next;
     plan_ndb(next, p, it1, it2, true);
-    mark_needs(next);
+    mark_needs(next, HALF);
     if (next.peak > P.peak) return fail(SHAMPOO_E_INVALID, "internal: re-planned chain needs more buffers");
     size_t j = 0;
     for (int g = 0; j < next.ops.size(); ++j)

@@ -149,18 +149,19 @@ def test_chebyshev_split_workspace_and_validation(mir):
 def test_newton_tolerance_workspace_and_validation(mir):
     """A Newton tolerance adds the check's scratch to the workspace
     (Frobenius partial sums, 32 per matrix for 64 matrices; the norms; a
-    flag slot); it is rejected for Chebyshev, for half-precision chains and
-    when negative."""
+    flag slot), for half-precision chains too (their checks read the half
+    copies); it is rejected for Chebyshev and when negative."""
     a = mir.shampoo_inverse_root_workspace(64, 256, 4, mir.RootOpts(method="cn", iters=20))
     b = mir.shampoo_inverse_root_workspace(64, 256, 4, mir.RootOpts(method="cn", iters=20, tol=1e-6))
     assert b - a == 32 * 64 * 8 + 64 * 8 + 256
     c = mir.shampoo_inverse_root_workspace(64, 256, 4, mir.RootOpts(method="ndb", iters=9, iters2=7))
     d = mir.shampoo_inverse_root_workspace(64, 256, 4, mir.RootOpts(method="ndb", iters=9, iters2=7, tol=1e-6))
     assert d - c == b - a
+    e = mir.shampoo_inverse_root_workspace(64, 256, 4, mir.RootOpts(method="cn", iters=20, compute="f16"))
+    f = mir.shampoo_inverse_root_workspace(64, 256, 4, mir.RootOpts(method="cn", iters=20, compute="f16", tol=0.1))
+    assert f - e == b - a
     for opts, status in [(mir.RootOpts(method="chebyshev", tol=1e-6), mir.E_INVALID),
-                         (mir.RootOpts(method="ndb", iters=5, iters2=5, tol=1e-4, compute="f16"), mir.E_UNSUPPORTED),
-                         (mir.RootOpts(method="cn", iters=5, tol=-1.0), mir.E_INVALID),
-                         (mir.RootOpts(method="cn", iters=5, tol=1e-4, compute="f16"), mir.E_UNSUPPORTED)]:
+                         (mir.RootOpts(method="cn", iters=5, tol=-1.0), mir.E_INVALID)]:
         with pytest.raises(mir.ShampooError) as e:
             mir.shampoo_inverse_root_workspace(4, 128, 4, opts)
         assert e.value.status == status, opts

@@ -296,6 +296,30 @@ def test_newton_tolerance(mir, method, p, compute, lo, tol, bar):
     assert not fl.any() and worst < bar and len(ms) < fixed
 
 
+@pytest.mark.parametrize("B", [128, 256])
+def test_newton_tolerance_half_products(mir, B):
+    """Coupled Newton on half products with a tolerance: the check reads the
+    half copy of M that the next products read (its rounding floor at these
+    sizes is about 1e-2, so 0.05 is reached at convergence); fewer products
+    than the fixed count, and the root within the half-precision bar 2e-2
+    against the oracle, as close to it as the fixed count's.  B = 256 runs
+    on the 256-tile symmetric kernel, B = 128 on the 128-tile one."""
+    A = synthetic.spd_stack(B + 3, 6, B, 1e-2, 1.0).astype(np.float32)
+    kw = dict(method="cn", iters=40, compute="f16")
+    mir.shampoo_timing_enable(512)
+    try:
+        X, _, fl = run_root(mir, A, 4, tol=0.05, **kw)
+        ms = mir.shampoo_timing_read(512)
+    finally:
+        mir.shampoo_timing_enable(0)
+    Xf, _, flf = run_root(mir, A, 4, **kw)
+    worst, _ = worst_vs_eigh(X, A, 4)
+    worst_f, _ = worst_vs_eigh(Xf, A, 4)
+    log(f"cn f16 B={B} tol 0.05: {len(ms)} products (fixed 156), worst {worst:.2e} (fixed count {worst_f:.2e})")
+    assert not fl.any() and not flf.any()
+    assert worst < 2e-2 and len(ms) < 80 and worst < 2 * worst_f + 1e-3
+
+
 @pytest.mark.parametrize("bad", ["nan", "zero"])
 def test_newton_tolerance_does_not_wait_for_failures(mir, bad):
     """A matrix with a NaN entry, or all zero (zero scale without eps),
