@@ -115,3 +115,38 @@ def test_replay_after_many_eager_gradient_sets(mir):
         torch.cuda.synchronize()
         assert all(torch.equal(a, b) for a, b in zip(Wa, Wb)), t
     assert all(len(st._desc_cache) <= 8 for st in opt_b.stacks)
+
+
+@pytest.mark.parametrize("compute", ["f64", "f32"])
+def test_captured_inverse_root_replays_match_eager(mir, compute):
+    """One shampoo_inverse_root call on the 64 x 128^2 stack (lambda in
+    [1e-6, 1], coupled Newton 20) captured as a graph, as the benchmark
+    times it: every replay, with an eager call on other data and a
+    synchronisation between replays, gives the eager call's bits."""
+    import torch
+    A = synthetic.spd_stack(2, 64, 128, 1e-6, 1.0)
+    A2 = synthetic.spd_stack(3, 64, 128, 1e-3, 1.0)
+    dt = np.float64 if compute == "f64" else np.float32
+    inp, other = to_dev(A.astype(dt)), to_dev(A2.astype(dt))
+    opts = mir.RootOpts(method="cn", iters=20, compute=compute)
+    ws = torch.empty(mir.shampoo_inverse_root_workspace(64, 128, 4, opts), dtype=torch.uint8, device="cuda")
+    ref = torch.empty_like(inp)
+    mir.shampoo_inverse_root(inp, ref, 4, opts, ws=ws)
+    out, scratch = torch.empty_like(inp), torch.empty_like(inp)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mir.shampoo_inverse_root(inp, out, 4, opts, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mir.shampoo_inverse_root(inp, out, 4, opts, ws=ws)
+    for r in range(4):
+        out.zero_()
+        mir.shampoo_inverse_root(other, scratch, 4, opts, ws=ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(out, ref)
+        log(f"{compute} solve replay {r}: identical {same}")
+        assert same
