@@ -322,18 +322,20 @@ def flagged(opt):
     return sum(int((f != 0).sum().item()) for f in opt.flags())
 
 
-def decoder_step_ms(mir, steps, warmup, compute="f32", stats64=False, fallback="none", tol=0.0, bound=0.0):
+def decoder_step_ms(mir, steps, warmup, compute="f32", stats64=False, fallback="none", tol=0.0, bound=0.0,
+                    scaling="frobenius"):
     """Full step on the 12-layer decoder set (151 M parameters, block 1024,
     bfloat16 gradients N(0, 0.02^2), beta2 0.999, eps 1e-12, Adam grafting,
-    coupled Newton 34 iterations (or stopping at ||M - I||_F <= tol), roots
-    every step).  Returns the median step time and the number of factors
+    coupled Newton 34 iterations (or stopping at ||M - I||_F <= tol) after
+    Frobenius (or power-iteration) scaling, roots every step).  Returns the median step time and the number of factors
     flagged during the timed steps."""
     import torch
     import synthetic
     shapes = synthetic.decoder_shapes()
     W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
     opt = mir.Shampoo(W, block_size=1024, beta2=0.999, eps=1e-12,
-                      root=mir.RootOpts(method="cn", iters=34, compute=compute, tol=tol, residual_bound=bound),
+                      root=mir.RootOpts(method="cn", iters=34, compute=compute, tol=tol, residual_bound=bound,
+                                        scaling=scaling),
                       graft="adam", lr=1e-3, grad_dtype=torch.bfloat16, fallback=fallback,
                       stats_dtype=torch.float64 if stats64 else torch.float32)
     gen = torch.Generator(device="cuda")
@@ -468,7 +470,7 @@ def main():
                     help="with --only roots*: solve only the first this-many blocks (counter runs whose "
                          "per-dispatch counts would otherwise overflow 32 bits)")
     ap.add_argument("--only", choices=["roots", "roots_f32", "roots_f16", "copy", "spd128", "step", "step_f16",
-                                       "step_f16_tol", "step_tol", "step_res", "step_tol_res", "step_f64", "step5", "step5_ps",
+                                       "step_f16_tol", "step_f16_tol_pi", "step_tol_res_pi", "step_tol", "step_res", "step_tol_res", "step_f64", "step5", "step5_ps",
                                        "step1", "step1_f64", "cheb_sweep"],
                     default=None,
                     help="profiling runs: only the float64 solve (roots) or its float32 / half-product "
@@ -500,6 +502,9 @@ def main():
         "step": dict(compute="f32"),
         "step_f16": dict(compute="f16", fallback="f64"),
         "step_f16_tol": dict(compute="f16", fallback="f64", tol=HALF_TOL),
+        "step_f16_tol_pi": dict(compute="f16", fallback="f64", tol=HALF_TOL, scaling="power"),
+        "step_tol_res_pi": dict(compute="f32", stats64=True, fallback="f64", tol=1e-4, bound=RESIDUAL_BOUND,
+                                scaling="power"),
         "step_tol": dict(compute="f32", tol=1e-4),
         "step_res": dict(compute="f32", stats64=True, fallback="f64", bound=RESIDUAL_BOUND),
         "step_tol_res": dict(compute="f32", stats64=True, fallback="f64", tol=1e-4, bound=RESIDUAL_BOUND),
@@ -629,10 +634,15 @@ def main():
         # decoder set
         ks = max(3, K)
         dec = {"parity_bar": 1e-4, "parity_paths": ["f64", "f32_chain_residual_checked",
-                                                    "f32_chain_tol1e-4_residual_checked"]}
+                                                    "f32_chain_tol1e-4_residual_checked",
+                                                    "f32_chain_tol1e-4_power_scaling_residual_checked"]}
         ms, nf = decoder_step_ms(mir, ks, 1, compute="f32", stats64=True, fallback="f64", tol=1e-4,
                                  bound=RESIDUAL_BOUND)
         dec["f32_chain_tol1e-4_residual_checked_ms"], dec["f32_chain_tol1e-4_residual_checked_flagged"] = round(ms, 2), nf
+        ms, nf = decoder_step_ms(mir, ks, 1, compute="f32", stats64=True, fallback="f64", tol=1e-4,
+                                 bound=RESIDUAL_BOUND, scaling="power")
+        dec["f32_chain_tol1e-4_power_scaling_residual_checked_ms"] = round(ms, 2)
+        dec["f32_chain_tol1e-4_power_scaling_residual_checked_flagged"] = nf
         ms, nf = decoder_step_ms(mir, ks, 1, compute="f32", stats64=True, fallback="f64", bound=RESIDUAL_BOUND)
         dec["f32_chain_residual_checked_ms"], dec["f32_chain_residual_checked_flagged"] = round(ms, 2), nf
         ms, nf = decoder_step_ms(mir, 2, 1, compute="f64", stats64=True)
@@ -642,6 +652,9 @@ def main():
         dec["cn_f16_products_parity_bar"] = 2e-2
         ms, nf = decoder_step_ms(mir, ks, 1, compute="f16", fallback="f64", tol=HALF_TOL)
         dec["cn_f16_products_tol0.1_ms"], dec["cn_f16_products_tol0.1_flagged"] = round(ms, 2), nf
+        ms, nf = decoder_step_ms(mir, ks, 1, compute="f16", fallback="f64", tol=HALF_TOL, scaling="power")
+        dec["cn_f16_products_tol0.1_power_scaling_ms"] = round(ms, 2)
+        dec["cn_f16_products_tol0.1_power_scaling_flagged"] = nf
         ms, nf = decoder_step_ms(mir, ks, 1, compute="f32")
         dec["f32_diagnostic_ms"] = round(ms, 2)
         cfg[DECODER + "_cn34"] = dec

@@ -140,13 +140,14 @@ def test_decoder_set_full_size_f64(mir):
     assert all(e < 1e-4 for e in errs)
 
 
-def test_decoder_set_full_size_f32_chain_residual_checked(mir):
-    """Float64 statistics, a float32 coupled Newton chain stopping at
-    ||M - I||_F <= 1e-4, its device residual checked against 1e-4 and the
-    float64 recomputation as fallback (step 1's factors fail the check):
-    the stated 1e-4."""
+@pytest.mark.parametrize("scaling", ["frobenius", "power"])
+def test_decoder_set_full_size_f32_chain_residual_checked(mir, scaling):
+    """Float64 statistics, a float32 coupled Newton chain (after Frobenius or
+    power-iteration scaling) stopping at ||M - I||_F <= 1e-4, its device
+    residual checked against 1e-4 and the float64 recomputation as fallback
+    (step 1's factors fail the check): the stated 1e-4."""
     errs = _decoder_run(mir, "f32", True, sample=[0, 1, 2, 3, 46, 47], fallback="f64", tol=1e-4,
-                        residual_bound=1e-4)
+                        residual_bound=1e-4, scaling=scaling)
     assert all(e < 1e-4 for e in errs)
 
 
@@ -158,12 +159,13 @@ def test_decoder_set_full_size_f32_diagnostic(mir):
     assert all(e < 5e-2 for e in errs)
 
 
-@pytest.mark.parametrize("tol", [0.0, 0.1])
-def test_decoder_set_full_size_cn_half_products(mir, tol):
+@pytest.mark.parametrize("tol,scaling", [(0.0, "frobenius"), (0.1, "frobenius"), (0.1, "power")])
+def test_decoder_set_full_size_cn_half_products(mir, tol, scaling):
     """The decoder set with coupled Newton on half-precision products and the
     float64 fallback, as the benchmark's half-product steps run it (34
     iterations, or stopping once the half copy of M is within 0.1 of I in
-    Frobenius norm): step 1's single-Gram factors diverge in half precision
+    Frobenius norm; Frobenius or power-iteration scaling): step 1's
+    single-Gram factors diverge in half precision
     and are recomputed in float64; steps 2 and 3 converge in half precision
     on every factor; sampled parameters within the half-precision bar."""
     import torch
@@ -171,7 +173,7 @@ def test_decoder_set_full_size_cn_half_products(mir, tol):
     grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
     W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
     opt = mir.Shampoo(W, block_size=1024, beta2=0.999, eps=1e-12,
-                      root=mir.RootOpts(method="cn", iters=34, compute="f16", tol=tol),
+                      root=mir.RootOpts(method="cn", iters=34, compute="f16", tol=tol, scaling=scaling),
                       graft="adam", lr=1e-3, grad_dtype=torch.bfloat16, fallback="f64")
     sample = [0, 1, 2, 3, 46, 47]
     sshapes = [shapes[i] for i in sample]
@@ -185,7 +187,7 @@ def test_decoder_set_full_size_cn_half_products(mir, tol):
         torch.cuda.synchronize()
         fl = torch.cat(opt.flags()).cpu().numpy()
         e = max(rel_fro(W[i].cpu().numpy(), Wo[k]) for k, i in enumerate(sample))
-        log(f"decoder set (half products, tol {tol}) step {t + 1}: sampled rel err {e:.2e}, "
+        log(f"decoder set (half products, tol {tol}, {scaling}) step {t + 1}: sampled rel err {e:.2e}, "
             f"flags {np.unique(fl).tolist()}")
         if t == 0:
             assert (fl == (mir.FLAG_NONFINITE | mir.FLAG_RECOMPUTED_F64)).all()
