@@ -320,6 +320,30 @@ def test_newton_tolerance_half_products(mir, B):
     assert worst < 2e-2 and len(ms) < 80 and worst < 2 * worst_f + 1e-3
 
 
+@pytest.mark.parametrize("p", [2, 4])
+def test_newton_db_tolerance_half_products(mir, p):
+    """Newton-DB on half products with a tolerance (each call checks the half
+    copy of T, ||ZY - I||_F = 2 ||T - I||_F; at convergence the chain is
+    planned again with the half copies and float32 results the shorter
+    chain needs): fewer products than the fixed counts and the fixed
+    count's error within 2e-2 on a well-conditioned 256^2 stack."""
+    A = synthetic.spd_stack(37, 6, 256, 1e-2, 1.0).astype(np.float32)
+    kw = dict(method="ndb", iters=30, iters2=20, compute="f16")
+    fixed = (3 * 30 - 3) + (3 * 20 - 3 if p == 4 else 0)
+    mir.shampoo_timing_enable(512)
+    try:
+        X, _, fl = run_root(mir, A, p, tol=0.2, **kw)
+        ms = mir.shampoo_timing_read(512)
+    finally:
+        mir.shampoo_timing_enable(0)
+    Xf, _, flf = run_root(mir, A, p, **kw)
+    worst, _ = worst_vs_eigh(X, A, p)
+    worst_f, _ = worst_vs_eigh(Xf, A, p)
+    log(f"ndb f16 p={p} tol 0.2: {len(ms)} products (fixed {fixed}), worst {worst:.2e} (fixed count {worst_f:.2e})")
+    assert not fl.any() and not flf.any()
+    assert worst < 2e-2 and len(ms) < fixed and worst < 2 * worst_f + 1e-3
+
+
 @pytest.mark.parametrize("bad", ["nan", "zero"])
 def test_newton_tolerance_does_not_wait_for_failures(mir, bad):
     """A matrix with a NaN entry, or all zero (zero scale without eps),
