@@ -461,6 +461,30 @@ __global__ void above_tol_kernel(const double* __restrict__ norms, const double*
   if (b < n && scale[b] > 0.0 && scale[b] < 1.0e300 && norms[b] > tol) atomicOr(notdone, 1);
 }
 
+// A necessary condition read from the diagonal alone, one workgroup per
+// matrix: ||M - I||_F >= |tr(M) - v| / sqrt(v) (Cauchy-Schwarz on the v
+// diagonal entries of M - I).  A matrix whose trace puts it beyond tol
+// (with a 1e-12 relative margin over the rounding of the two double sums)
+// is not converged whatever its other entries, and the Frobenius pass that
+// would say so too is skipped; NaN traces and unusable scales decide
+// nothing, as above.
+template <typename T>
+__global__ __launch_bounds__(256) void trace_gap_kernel(const T* __restrict__ in, int B,
+                                                        const int32_t* __restrict__ valid,
+                                                        const double* __restrict__ scale, double tol,
+                                                        int32_t* __restrict__ notdone) {
+  __shared__ double red[4];
+  const int64_t b = blockIdx.x;
+  const int v = valid ? min(max(valid[b], 0), B) : B;
+  const T* M = in + b * (int64_t)B * B;
+  double t = 0.0;
+  for (int i = (int)threadIdx.x; i < v; i += 256) t += (double)M[(int64_t)i * B + i] - 1.0;
+  t = block_sum256(t, red);
+  if (threadIdx.x == 0 && v > 0 && scale[b] > 0.0 && scale[b] < 1.0e300 &&
+      fabs(t) / sqrt((double)v) > tol * (1.0 + 1e-12))
+    atomicOr(notdone, 1);
+}
+
 // ---------------------------------------------------------------------------
 // Solver residual ||X^p A_s - I||_F / sqrt(v) per matrix, from the Frobenius
 // norm of the product X^p A_s - I over the valid region (frob kernels with

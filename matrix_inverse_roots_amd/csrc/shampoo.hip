@@ -1178,6 +1178,23 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
       if (op.kind == OP_GEMM) ++gemms;
       continue;
     }
+    // first the diagonal alone: a trace beyond tol settles "not converged"
+    // without the Frobenius pass (same decision, a B-th of the reads)
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, notdone, (int64_t)1, 0);
+    LAUNCH_CHECK("fill");
+    if constexpr (HALF)
+      hipLaunchKernelGGL((trace_gap_kernel<_Float16>), dim3((unsigned)n), dim3(256), 0, st,
+                         (const _Float16*)hbuf(op.a), B, valid, sc, o->tol * op.alpha, notdone);
+    else
+      hipLaunchKernelGGL((trace_gap_kernel<TS>), dim3((unsigned)n), dim3(256), 0, st, (const TS*)buf(op.a), B,
+                         valid, sc, o->tol * op.alpha, notdone);
+    LAUNCH_CHECK("trace_gap");
+    {
+      int32_t h = 0;
+      HIP_TRY(hipMemcpyAsync(&h, notdone, 4, hipMemcpyDeviceToHost, st));
+      HIP_TRY(hipStreamSynchronize(st));
+      if (h != 0) continue;
+    }
     // ||M - I||_F: the Frobenius sums of M + eps I with eps = -1 (half
     // chains: of the half copy that the next products read)
     if constexpr (HALF)
