@@ -323,7 +323,7 @@ def flagged(opt):
 
 
 def decoder_step_ms(mir, steps, warmup, compute="f32", stats64=False, fallback="none", tol=0.0, bound=0.0,
-                    scaling="frobenius"):
+                    scaling="frobenius", precond_bf16=False):
     """Full step on the 12-layer decoder set (151 M parameters, block 1024,
     bfloat16 gradients N(0, 0.02^2), beta2 0.999, eps 1e-12, Adam grafting,
     coupled Newton 34 iterations (or stopping at ||M - I||_F <= tol) after
@@ -337,7 +337,8 @@ def decoder_step_ms(mir, steps, warmup, compute="f32", stats64=False, fallback="
                       root=mir.RootOpts(method="cn", iters=34, compute=compute, tol=tol, residual_bound=bound,
                                         scaling=scaling),
                       graft="adam", lr=1e-3, grad_dtype=torch.bfloat16, fallback=fallback,
-                      stats_dtype=torch.float64 if stats64 else torch.float32)
+                      stats_dtype=torch.float64 if stats64 else torch.float32,
+                      precondition_dtype=torch.bfloat16 if precond_bf16 else None)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(4)
     grads = [[(torch.randn(s, generator=gen, device="cuda") * 0.02).to(torch.bfloat16) for s in shapes]
@@ -470,7 +471,7 @@ def main():
                     help="with --only roots*: solve only the first this-many blocks (counter runs whose "
                          "per-dispatch counts would otherwise overflow 32 bits)")
     ap.add_argument("--only", choices=["roots", "roots_f32", "roots_f16", "copy", "spd128", "step", "step_f16",
-                                       "step_f16_tol", "step_f16_tol_pi", "step_tol_res_pi", "step_tol", "step_res", "step_tol_res", "step_f64", "step5", "step5_ps",
+                                       "step_f16_tol", "step_f16_tol_pi", "step_f16_tol_pi_pbf16", "step_tol_res_pi", "step_tol", "step_res", "step_tol_res", "step_f64", "step5", "step5_ps",
                                        "step1", "step1_f64", "cheb_sweep"],
                     default=None,
                     help="profiling runs: only the float64 solve (roots) or its float32 / half-product "
@@ -503,6 +504,7 @@ def main():
         "step_f16": dict(compute="f16", fallback="f64"),
         "step_f16_tol": dict(compute="f16", fallback="f64", tol=HALF_TOL),
         "step_f16_tol_pi": dict(compute="f16", fallback="f64", tol=HALF_TOL, scaling="power"),
+        "step_f16_tol_pi_pbf16": dict(compute="f16", fallback="f64", tol=HALF_TOL, scaling="power", precond_bf16=True),
         "step_tol_res_pi": dict(compute="f32", stats64=True, fallback="f64", tol=1e-4, bound=RESIDUAL_BOUND,
                                 scaling="power"),
         "step_tol": dict(compute="f32", tol=1e-4),
@@ -655,6 +657,10 @@ def main():
         ms, nf = decoder_step_ms(mir, ks, 1, compute="f16", fallback="f64", tol=HALF_TOL, scaling="power")
         dec["cn_f16_products_tol0.1_power_scaling_ms"] = round(ms, 2)
         dec["cn_f16_products_tol0.1_power_scaling_flagged"] = nf
+        ms, nf = decoder_step_ms(mir, ks, 1, compute="f16", fallback="f64", tol=HALF_TOL, scaling="power",
+                                 precond_bf16=True)
+        dec["cn_f16_products_tol0.1_power_scaling_bf16_precondition_ms"] = round(ms, 2)
+        dec["cn_f16_products_tol0.1_power_scaling_bf16_precondition_flagged"] = nf
         ms, nf = decoder_step_ms(mir, ks, 1, compute="f32")
         dec["f32_diagnostic_ms"] = round(ms, 2)
         cfg[DECODER + "_cn34"] = dec

@@ -270,6 +270,15 @@ typedef struct shampoo_step_args {
                                        rows x rows and cols x cols regions (their padding stays as it
                                        was, zero from the caller's initialisation), and D on the valid
                                        rows x cols region, in 64 x 64 tiles. */
+  shampoo_dtype precond_dt;         /* SHAMPOO_F32 (0, the default): D = Lr G Rr in the roots'
+                                       precision.  SHAMPOO_BF16 (bfloat16 gradients and float32
+                                       statistics only): both roots and E = G Rr are rounded to
+                                       bfloat16 and the two products run on bfloat16 matrix cores
+                                       with float32 accumulation; D stays float32.  The half-precision
+                                       products of [DASH] "A.3 Numerical Precision" (float32
+                                       accumulation) carried over to the preconditioning products:
+                                       the search direction then carries bfloat16 rounding (about
+                                       3e-3 relative on the decoder set after step 1). */
 } shampoo_step_args;
 
 /* Version string of the library. */

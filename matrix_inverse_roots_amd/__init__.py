@@ -85,7 +85,8 @@ class StepArgsC(ctypes.Structure):
                 ("lr", ctypes.c_float), ("momentum", ctypes.c_float),
                 ("beta1", ctypes.c_float), ("graft_beta2", ctypes.c_float), ("graft_eps", ctypes.c_float),
                 ("t", ctypes.c_int32), ("flags_dev", ctypes.c_void_p), ("dstack", ctypes.c_void_p),
-                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("table_host", ctypes.c_void_p)]
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("table_host", ctypes.c_void_p),
+                ("precond_dt", ctypes.c_int32)]
 
 
 EXPORTS = [

@@ -705,6 +705,18 @@ __global__ __launch_bounds__(256) void finalize_kernel(const TS* __restrict__ X,
 // ---------------------------------------------------------------------------
 // step fallback helpers
 // ---------------------------------------------------------------------------
+// float32 -> bfloat16, rounded to nearest even; n4 four-element chunks
+// (16-byte aligned input, 8-byte aligned output), grid-stride.
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ in, __bf16* __restrict__ out,
+                                                          int64_t n4) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(in) + i);
+    const bf16x4_t o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    __builtin_nontemporal_store(o, reinterpret_cast<bf16x4_t*>(out) + i);
+  }
+}
+
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;

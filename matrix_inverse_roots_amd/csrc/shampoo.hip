@@ -1464,6 +1464,57 @@ shampoo_status precond_impl(const void* roots, shampoo_dtype rdt, const void* g,
   return SHAMPOO_OK;
 }
 
+// Preconditioning on bfloat16 matrix cores (step option precond_dt = BF16,
+// bfloat16 gradients, float32 roots): both roots are rounded to bfloat16, E =
+// G Rr is formed (float32 accumulation, stored transposed) and rounded to
+// bfloat16, and D = Lr E is accumulated and stored in float32.  ws holds
+// E^T in float32, then in bfloat16, then the bfloat16 roots
+// (precond_bf16_bytes).  Extents and tile lists as in precond_impl.
+size_t precond_bf16_bytes(int64_t nblk, int32_t B) {
+  const size_t BB = (size_t)B * B;
+  return align_up((size_t)nblk * BB * 4) + align_up((size_t)nblk * BB * 2) + align_up((size_t)nblk * 2 * BB * 2);
+}
+
+shampoo_status precond_bf16_impl(const float* roots, const void* g, int64_t nblk, int32_t B, float* dstack,
+                                 unsigned char* ws, hipStream_t st, const int32_t* valid, const ProductTiles* pt) {
+  if (nblk == 0) return SHAMPOO_OK;
+  const size_t BB = (size_t)B * B;
+  float* Et = (float*)ws;
+  __bf16* Etb = (__bf16*)(ws + align_up((size_t)nblk * BB * 4));
+  __bf16* rb = (__bf16*)(ws + align_up((size_t)nblk * BB * 4) + align_up((size_t)nblk * BB * 2));
+  auto to_bf16 = [&](const float* in, __bf16* out, int64_t count) -> shampoo_status {
+    const int64_t n4 = count / 4;  // B is a multiple of 64
+    const int64_t wgs = std::min<int64_t>((n4 + 255) / 256, 8192);
+    hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)std::max<int64_t>(wgs, 1)), dim3(256), 0, st, in, out, n4);
+    LAUNCH_CHECK("f32_to_bf16");
+    return SHAMPOO_OK;
+  };
+  shampoo_status r = to_bf16(roots, rb, 2 * nblk * (int64_t)BB);
+  if (r != SHAMPOO_OK) return r;
+  GemmCall c1;
+  c1.A = g; c1.B = rb + nblk * BB; c1.D = nullptr; c1.C = Et; c1.C2 = nullptr; c1.sym = false; c1.transC = true;
+  GemmCall c2;
+  c2.A = rb; c2.B = Etb; c2.D = nullptr; c2.C = dstack; c2.C2 = nullptr; c2.sym = false;
+  if (valid) {
+    c1.rext = c2.rext = valid;
+    c1.cext = c2.cext = valid + nblk;
+    c1.kext = valid + nblk;
+    c2.kext = valid;
+    if (pt && pt->T == 64) {
+      c1.tiles = pt->tiles[2];
+      c1.cut = pt->cut[2];
+      c2.tiles = pt->tiles[3];
+      c2.cut = pt->cut[3];
+      c1.tile = c2.tile = 64;
+    }
+  }
+  HIP_TRY((gemm<Mma::BF16, __bf16, __bf16, float>(c1, B, nblk, st)));
+  r = to_bf16(Et, Etb, nblk * (int64_t)BB);
+  if (r != SHAMPOO_OK) return r;
+  HIP_TRY((gemm<Mma::BF16, __bf16, __bf16, float>(c2, B, nblk, st)));
+  return SHAMPOO_OK;
+}
+
 // ---------------------------------------------------------------------------
 // step
 // ---------------------------------------------------------------------------
@@ -1501,6 +1552,10 @@ shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
     return fail(SHAMPOO_E_UNSUPPORTED, "statistics dtype %d (F32, F64)", (int)a->stats_dt);
   if (a->fallback < SHAMPOO_FALLBACK_NONE || a->fallback > SHAMPOO_FALLBACK_F64)
     return fail(SHAMPOO_E_INVALID, "unknown fallback %d", a->fallback);
+  if (a->precond_dt != SHAMPOO_F32 && a->precond_dt != SHAMPOO_BF16)
+    return fail(SHAMPOO_E_UNSUPPORTED, "precondition dtype %d (F32, BF16)", (int)a->precond_dt);
+  if (a->precond_dt == SHAMPOO_BF16 && (a->g_dt != SHAMPOO_BF16 || a->stats_dt != SHAMPOO_F32))
+    return fail(SHAMPOO_E_UNSUPPORTED, "bfloat16 preconditioning needs bfloat16 gradients and float32 statistics");
   shampoo_status r = check_root_args(2 * a->nblk, a->B, a->p, &a->root);
   if (r != SHAMPOO_OK) return r;
   const Plan P = build_plan(a->p, &a->root);
@@ -1510,7 +1565,9 @@ shampoo_status step_layout(const shampoo_step_args* a, StepLayout* L) {
   L->root_bytes = root_ws_bytes(2 * a->nblk, a->B, P, a->root.compute);
   size_t root = L->root_bytes;
   // E^T (in the roots' precision) and D (f32) reuse the root workspace
-  const size_t ed = align_up((size_t)a->nblk * BB * dtype_size(a->stats_dt)) + align_up((size_t)a->nblk * BB * 4);
+  const size_t ed = (a->precond_dt == SHAMPOO_BF16 ? precond_bf16_bytes(a->nblk, a->B)
+                                                    : align_up((size_t)a->nblk * BB * dtype_size(a->stats_dt))) +
+                    align_up((size_t)a->nblk * BB * 4);
   if (root < ed) root = ed;
   size_t off = 0;
   L->g = off; off += align_up((size_t)a->nblk * BB * es);
@@ -1790,11 +1847,16 @@ shampoo_status step_impl(const shampoo_step_args* a, hipStream_t st) {
     if (r != SHAMPOO_OK) return r;
   }
   // 4. D = Lr G Rr
-  const size_t ebytes = align_up((size_t)nblk * BB * dtype_size(a->stats_dt));
+  const bool pbf = a->precond_dt == SHAMPOO_BF16;
+  const size_t ebytes = pbf ? precond_bf16_bytes(nblk, B) : align_up((size_t)nblk * BB * dtype_size(a->stats_dt));
   void* Et = root;
   float* D = a->dstack ? a->dstack : (float*)(root + ebytes);
-  r = precond_impl(a->roots, a->stats_dt, g, a->g_dt, nblk, B, D, Et, ebytes, st, L.ragged ? valid : nullptr,
-                   L.ragged ? &pt : nullptr);
+  if (pbf)
+    r = precond_bf16_impl((const float*)a->roots, g, nblk, B, D, (unsigned char*)Et, st, L.ragged ? valid : nullptr,
+                          L.ragged ? &pt : nullptr);
+  else
+    r = precond_impl(a->roots, a->stats_dt, g, a->g_dt, nblk, B, D, Et, ebytes, st, L.ragged ? valid : nullptr,
+                     L.ragged ? &pt : nullptr);
   if (r != SHAMPOO_OK) return r;
   // 5. grafting and update
   GraftArgs ga;

@@ -94,6 +94,7 @@ class ShampooStack:
         a.graft_beta2 = hp["graft_beta2"]
         a.graft_eps = hp["graft_eps"]
         a.flags_dev = self.flags.data_ptr()
+        a.precond_dt = BF16 if hp["precond_dtype"] == torch.bfloat16 else F32
         a.dstack = None
         # host copy of the table: roots grouped by each factor's own side
         self.table_host = np.ascontiguousarray(self.table, dtype=np.int32)
@@ -173,12 +174,16 @@ class Shampoo:
     ||X^p A_s - I||_F / sqrt(v) of its latest root (``residuals()``); with
     ``root.residual_bound`` > 0 a root above the bound is flagged RESIDUAL
     and handled by ``fallback`` like a non-finite one.
+    precondition_dtype: None (the products of D = L^{-1/4} G R^{-1/4} in the
+    roots' precision) or torch.bfloat16 (bfloat16 operands, float32
+    accumulation and D; bfloat16 gradients and float32 statistics only).
     """
 
     def __init__(self, params, block_size=1024, beta2=1.0, eps=1e-12, p=4, root=None, graft="sgd",
                  lr=0.1, momentum=0.9, beta1=0.9, graft_beta2=0.999, graft_eps=1e-8,
                  graft_blockwise=False, precondition_frequency=1, grad_dtype=None, stats_dtype=None,
-                 pi_seed=0, fallback="none", group_factors=True, concurrent_stacks=True, residuals=False):
+                 pi_seed=0, fallback="none", group_factors=True, concurrent_stacks=True, residuals=False,
+                 precondition_dtype=None):
         import torch
         params = list(params)
         if not params:
@@ -197,7 +202,9 @@ class Shampoo:
                        grad_dtype=grad_dtype if grad_dtype is not None else torch.float32,
                        stats_dtype=stats_dtype if stats_dtype is not None else torch.float32,
                        pi_seed=int(pi_seed), fallback=str(fallback), group_factors=bool(group_factors),
-                       residuals=bool(residuals))
+                       residuals=bool(residuals), precond_dtype=precondition_dtype)
+        if precondition_dtype not in (None, torch.float32, torch.bfloat16):
+            raise ValueError("precondition_dtype must be None, torch.float32 or torch.bfloat16")
         if fallback not in FALLBACKS:
             raise ValueError("fallback must be one of %s" % sorted(FALLBACKS))
         bs_of = block_size if callable(block_size) else (lambda m, n, b=int(block_size): b)

@@ -207,6 +207,24 @@ def test_step_workspace_and_validation(mir):
     a.B = 96
     with pytest.raises(mir.ShampooError):
         mir.shampoo_step_workspace(a)
+    # bfloat16 preconditioning: bfloat16 gradients and float32 statistics only
+    a.B = 128
+    a.precond_dt = mir.BF16
+    with pytest.raises(mir.ShampooError) as e:
+        mir.shampoo_step_workspace(a)          # float32 gradients
+    assert e.value.status == mir.E_UNSUPPORTED
+    a.g_dt = mir.BF16
+    c = mir.shampoo_step_workspace(a)
+    a.precond_dt = mir.F32
+    assert c >= mir.shampoo_step_workspace(a)
+    a.precond_dt = mir.BF16
+    a.stats_dt = mir.F64
+    with pytest.raises(mir.ShampooError) as e:
+        mir.shampoo_step_workspace(a)
+    assert e.value.status == mir.E_UNSUPPORTED
+    a.stats_dt, a.precond_dt = mir.F32, 7
+    with pytest.raises(mir.ShampooError):
+        mir.shampoo_step_workspace(a)
 
 
 def test_no_cpu_fallback_in_product():

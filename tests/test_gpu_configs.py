@@ -159,13 +159,15 @@ def test_decoder_set_full_size_f32_diagnostic(mir):
     assert all(e < 5e-2 for e in errs)
 
 
-@pytest.mark.parametrize("tol,scaling", [(0.0, "frobenius"), (0.1, "frobenius"), (0.1, "power")])
-def test_decoder_set_full_size_cn_half_products(mir, tol, scaling):
+@pytest.mark.parametrize("tol,scaling,pdt", [(0.0, "frobenius", None), (0.1, "frobenius", None), (0.1, "power", None),
+                                             (0.1, "power", "bf16")])
+def test_decoder_set_full_size_cn_half_products(mir, tol, scaling, pdt):
     """The decoder set with coupled Newton on half-precision products and the
     float64 fallback, as the benchmark's half-product steps run it (34
     iterations, or stopping once the half copy of M is within 0.1 of I in
-    Frobenius norm; Frobenius or power-iteration scaling): step 1's
-    single-Gram factors diverge in half precision
+    Frobenius norm; Frobenius or power-iteration scaling; preconditioning
+    products in float32 or bfloat16): step 1's single-Gram factors diverge
+    in half precision
     and are recomputed in float64; steps 2 and 3 converge in half precision
     on every factor; sampled parameters within the half-precision bar."""
     import torch
@@ -174,7 +176,8 @@ def test_decoder_set_full_size_cn_half_products(mir, tol, scaling):
     W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
     opt = mir.Shampoo(W, block_size=1024, beta2=0.999, eps=1e-12,
                       root=mir.RootOpts(method="cn", iters=34, compute="f16", tol=tol, scaling=scaling),
-                      graft="adam", lr=1e-3, grad_dtype=torch.bfloat16, fallback="f64")
+                      graft="adam", lr=1e-3, grad_dtype=torch.bfloat16, fallback="f64",
+                      precondition_dtype=torch.bfloat16 if pdt == "bf16" else None)
     sample = [0, 1, 2, 3, 46, 47]
     sshapes = [shapes[i] for i in sample]
     orc = oracle.ShampooOracle(sshapes, [1024] * len(sample), beta2=0.999, eps=1e-12, graft="adam", lr=1e-3)
@@ -187,7 +190,8 @@ def test_decoder_set_full_size_cn_half_products(mir, tol, scaling):
         torch.cuda.synchronize()
         fl = torch.cat(opt.flags()).cpu().numpy()
         e = max(rel_fro(W[i].cpu().numpy(), Wo[k]) for k, i in enumerate(sample))
-        log(f"decoder set (half products, tol {tol}, {scaling}) step {t + 1}: sampled rel err {e:.2e}, "
+        log(f"decoder set (half products, tol {tol}, {scaling}, precondition {pdt or 'f32'}) step {t + 1}: "
+            f"sampled rel err {e:.2e}, "
             f"flags {np.unique(fl).tolist()}")
         if t == 0:
             assert (fl == (mir.FLAG_NONFINITE | mir.FLAG_RECOMPUTED_F64)).all()

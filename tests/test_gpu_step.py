@@ -278,6 +278,22 @@ def test_ragged_blocks_momentum_and_ndb(mir, tol):
     assert all(e < 1e-4 for e in errs)
 
 
+@pytest.mark.parametrize("shapes,B", [([(300, 130), (64, 64), (5, 200)], 128), ([(512, 256), (256, 768)], 256)])
+def test_bfloat16_preconditioning(mir, shapes, B):
+    """Preconditioning on bfloat16 matrix cores (roots and G R^{-1/4} rounded
+    to bfloat16, float32 accumulation) within the bfloat16 bar 2e-2 of the
+    oracle, on ragged blocks (extents, tile lists of 64-tiles) and on full
+    blocks (the persistent 128-tile kernel); eps = 1e-3 bounds the factors'
+    condition numbers, gradients bfloat16 N(0, 0.1^2), Adam grafting."""
+    import torch
+    grads = synthetic.gaussian_grads(23, shapes, 3, 0.1, dtype="bf16")
+    errs = run_steps(mir, shapes, B, grads, 3,
+                     dict(beta2=0.999, eps=1e-3, graft="adam", lr=0.01, precondition_dtype=torch.bfloat16),
+                     dict(method="cn", iters=30), grad_bf16=True)
+    log(f"bfloat16 preconditioning, B {B}: error per step {errs}")
+    assert all(e < 2e-2 for e in errs)
+
+
 def test_decoder_layer_adam_bf16(mir):
     """One decoder layer of the d_model 1024 / MLP 4096 set (QKV, out, MLP up,
     MLP down), bfloat16 gradients N(0, 0.02^2), beta2 = 0.999, eps = 1e-12,
