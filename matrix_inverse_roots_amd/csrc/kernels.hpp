@@ -521,11 +521,17 @@ constexpr int32_t FAILED_ROOT = SHAMPOO_FLAG_NONFINITE | SHAMPOO_FLAG_ZERO_SCALE
 // Pass 0 computes A_s from `in` (in double, rounded once to half)
 // and stores the half matrix in `hcopy`; later passes read that copy, half
 // the bytes of a float32 matrix.  Each lane reads back exactly the 16 bytes
-// it wrote.  Two workgroups per CU keep few matrices in flight.
+// it wrote.  Workgroups of PI_THREADS (16 waves): a matrix's passes are
+// streams of its half copy through L2, bound by the loads each workgroup
+// keeps in flight, so a workgroup holds as many waves as a CU takes; a
+// row block of 16 rows and a vector's norm are each one wave's work, the
+// same instructions whichever wave runs them (the result does not depend
+// on the number of waves).
 // Dynamic LDS: Vh half [k16][B + 8], Wf float [k16][B + 4], k16 floats.
 // ---------------------------------------------------------------------------
+constexpr int PI_THREADS = 1024;
 template <typename TI, int NVB>
-__global__ __launch_bounds__(256) void power_iter_fused_kernel(const TI* __restrict__ in, int B, int64_t n,
+__global__ __launch_bounds__(PI_THREADS) void power_iter_fused_kernel(const TI* __restrict__ in, int B, int64_t n,
                                                                const int32_t* __restrict__ valid, double eps,
                                                                const double* __restrict__ sf, int k, int iters,
                                                                const float* __restrict__ v0,
@@ -540,6 +546,7 @@ __global__ __launch_bounds__(256) void power_iter_fused_kernel(const TI* __restr
   float* Wf = reinterpret_cast<float*>(smem + (size_t)k16 * VP * 2);
   float* rq = Wf + (size_t)k16 * WP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = (int)(blockDim.x >> 6);
   const int i16 = lane & 15, grp = lane >> 4;
   for (int64_t b = blockIdx.x; b < n; b += gridDim.x) {
     const TI* A = in + b * (int64_t)B * B;
@@ -548,13 +555,13 @@ __global__ __launch_bounds__(256) void power_iter_fused_kernel(const TI* __restr
     const double sfb = sf[b];
     const double inv = (sfb > 0.0 && sfb < 1.0e300) ? 1.0 / sfb : 0.0;
     __syncthreads();  // the previous matrix's last reads of Wf / Vh are done
-    for (int e = tid; e < k16 * B; e += 256) {
+    for (int e = tid; e < k16 * B; e += (int)blockDim.x) {
       const int vv = e / B, i = e - vv * B;
       Wf[vv * WP + i] = vv < k ? v0[(int64_t)vv * B + i] : 0.0f;
     }
     for (int it = 0; it <= iters; ++it) {
       __syncthreads();
-      for (int vv = wave; vv < k16; vv += 4) {
+      for (int vv = wave; vv < k16; vv += nw) {
         float ss = 0.0f;
         for (int i = lane; i < B; i += 64) {
           const float x = Wf[vv * WP + i];
@@ -566,7 +573,7 @@ __global__ __launch_bounds__(256) void power_iter_fused_kernel(const TI* __restr
         for (int i = lane; i < B; i += 64) Vh[vv * VP + i] = (_Float16)(Wf[vv * WP + i] * rn);
       }
       __syncthreads();
-      for (int rb = wave; rb < B / 16; rb += 4) {
+      for (int rb = wave; rb < B / 16; rb += nw) {
         floatx4 acc[NVB];
 #pragma unroll
         for (int vb = 0; vb < NVB; ++vb) acc[vb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -607,7 +614,7 @@ __global__ __launch_bounds__(256) void power_iter_fused_kernel(const TI* __restr
       }
     }
     __syncthreads();
-    for (int vv = wave; vv < k16; vv += 4) {
+    for (int vv = wave; vv < k16; vv += nw) {
       float num = 0.0f, den = 0.0f;
       for (int i = lane; i < B; i += 64) {
         const float x = (float)Vh[vv * VP + i];

@@ -1013,13 +1013,14 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
     HIP_TRY(hipFuncSetAttribute(pk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     int cus = 0;
     HIP_TRY(cu_count(&cus));
+    // two workgroups per CU where LDS allows (B <= 512 with 16 vectors)
     const unsigned pgrid = (unsigned)std::min<int64_t>(n, (int64_t)std::max(1, cus) * 2);
     _Float16* hcopy = (_Float16*)buf(0);
     if (k16 == 16)
-      hipLaunchKernelGGL((power_iter_fused_kernel<TI, 1>), dim3(pgrid), dim3(256), lds, st, (const TI*)in, B, n, valid,
+      hipLaunchKernelGGL((power_iter_fused_kernel<TI, 1>), dim3(pgrid), dim3(PI_THREADS), lds, st, (const TI*)in, B, n, valid,
                          o->eps, sf, o->pi_vectors, o->pi_iters, o->pi_start_dev, hcopy, s, flags);
     else
-      hipLaunchKernelGGL((power_iter_fused_kernel<TI, 2>), dim3(pgrid), dim3(256), lds, st, (const TI*)in, B, n, valid,
+      hipLaunchKernelGGL((power_iter_fused_kernel<TI, 2>), dim3(pgrid), dim3(PI_THREADS), lds, st, (const TI*)in, B, n, valid,
                          o->eps, sf, o->pi_vectors, o->pi_iters, o->pi_start_dev, hcopy, s, flags);
     LAUNCH_CHECK("power_iter");
     sc = s;
