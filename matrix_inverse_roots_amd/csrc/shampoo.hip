@@ -1055,12 +1055,28 @@ shampoo_status run_root(const void* in, void* out, int64_t n, int32_t B, int32_t
       g.gamma = gamma;
       return gemm<RM, TS, TS, TS>(g, B, n, st);
     };
+    // squarings of an exactly symmetric X (every chain but Newton-DB's,
+    // whose products are full and whose result is symmetrised only by the
+    // final pass) run as symmetric products: (X X)_ij and (X X)_ji then sum
+    // the same terms in the same order, so the mirrored upper triangle has
+    // the bits the full product would give, at 10 / 16 or 36 / 64 of its
+    // work
+    auto square = [&](int a, int c) -> hipError_t {
+      if (P.sym_out) return mul(a, a, c, 0.0);
+      GemmCall g;
+      g.A = buf(a);
+      g.B = buf(a);
+      g.C = buf(c);
+      g.sym = true;
+      g.nn = false;
+      return gemm<RM, TS, TS, TS>(g, B, n, st);
+    };
     int cur = x;
     auto other = [&]() { return cur == t0 ? t1 : t0; };
     if ((p & (p - 1)) == 0) {
       for (int q = 1; q < p; q *= 2) {
         const int t = other();
-        HIP_TRY(mul(cur, cur, t, 0.0));
+        HIP_TRY(square(cur, t));
         cur = t;
       }
     } else {
