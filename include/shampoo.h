@@ -192,14 +192,19 @@ typedef struct shampoo_param {
  *   v the valid size), so tol must lie above that: 1e-4 suits float32 up
  *   to v = 1024.  F16 chains check the half copy of the iterate, the one
  *   the next products read; it settles near 2.6e-2 at v = 1024, where
- *   0.1 suits.  Each check synchronises the stream with the
- *   host (one flag read), so work queued after it on other streams is not
- *   enqueued until the solve ends; `iters` stays the upper bound; the
- *   float64 recomputation of shampoo_step's fallback runs the full count.
+ *   0.1 suits.  A check first reads the diagonals: |tr M - v| / sqrt(v), a
+ *   lower bound of ||M - I||_F, above tol settles "not converged" without
+ *   the Frobenius pass (the same decision).  Each check synchronises the
+ *   stream with the host (one flag read, two when the diagonals pass), so
+ *   work queued after it on other streams is not enqueued until the solve
+ *   ends; `iters` stays the upper bound; the float64 recomputation of
+ *   shampoo_step's fallback runs the full count.
  * residual_out_dev, residual_bound: the solver residual ||X^p A_s - I||_F /
  *   sqrt(v) of each matrix's chain result X (before unscaling; equal to
  *   ||out^p (in + eps I) - I||_F / sqrt(v)), v the valid size, from p - 1
- *   or log2(p) full products and one with the regenerated A_s, all in the
+ *   products or log2(p) squarings (symmetric products when X is exactly
+ *   symmetric, every method but NDB) and a full product with the
+ *   regenerated A_s, all in the
  *   chain's iterate precision (float32 for F32 and F16 chains, float64 for
  *   F64), and one Frobenius pass.  It is computed when residual_out_dev
  *   (device float32 [n]) is non-NULL or residual_bound > 0; residual_bound > 0
