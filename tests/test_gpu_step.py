@@ -278,6 +278,19 @@ def test_ragged_blocks_momentum_and_ndb(mir, tol):
     assert all(e < 1e-4 for e in errs)
 
 
+def test_ragged_blocks_half_products_tolerance(mir):
+    """Ragged blocks rooted in groups by factor side (64 to 512), coupled
+    Newton on half products stopping at ||M - I||_F <= 0.05 (the half copy
+    of M), Adam grafting: within the half-precision bar 2e-2 of the oracle
+    at every step (eps = 1e-3 bounds the factors' condition numbers)."""
+    shapes = [(600, 300), (64, 200), (300, 130), (5, 40)]
+    grads = synthetic.gaussian_grads(29, shapes, 3, 0.1)
+    errs = run_steps(mir, shapes, 512, grads, 3, dict(beta2=0.999, eps=1e-3, graft="adam", lr=0.01),
+                     dict(method="cn", iters=34, compute="f16", tol=0.05))
+    log(f"ragged blocks, half products with a tolerance: error per step {errs}")
+    assert all(e < 2e-2 for e in errs)
+
+
 @pytest.mark.parametrize("shapes,B", [([(300, 130), (64, 64), (5, 200)], 128), ([(512, 256), (256, 768)], 256)])
 def test_bfloat16_preconditioning(mir, shapes, B):
     """Preconditioning on bfloat16 matrix cores (roots and G R^{-1/4} rounded
