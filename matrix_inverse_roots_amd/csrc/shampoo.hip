@@ -931,7 +931,9 @@ size_t root_slot_bytes(int64_t n, int32_t B, int compute) {
 // Frobenius partial sums per matrix: about 9216 workgroups in all, at most 32
 // per matrix (288 float32 matrices of 1024^2: 15 parts 5.6 TB/s, 32 parts
 // 6.3 TB/s on MI355X).
-int frob_parts(int64_t n) { return (int)std::max<int64_t>(1, std::min<int64_t>(32, (9216 + n - 1) / n)); }
+int frob_parts(int64_t n) {
+  return n < 1 ? 1 : (int)std::max<int64_t>(1, std::min<int64_t>(32, (9216 + n - 1) / n));
+}
 
 // Convergence checks: partial sums, per-matrix norms and the flag, after the
 // iterate buffers.

@@ -167,6 +167,22 @@ def test_newton_tolerance_workspace_and_validation(mir):
         assert e.value.status == status, opts
 
 
+def test_empty_stack_workspace(mir):
+    """Workspace queries for a stack of no matrices succeed for every method
+    and precision (the Frobenius partial-sum count once divided by the
+    batch size)."""
+    for kw in (dict(method="cn", iters=10), dict(method="ndb", iters=5, iters2=4),
+               dict(method="cn", iters=10, tol=1e-4), dict(method="chebyshev", cheb_degree=8),
+               dict(method="cn", iters=10, compute="f16"), dict(method="ndb", iters=5, iters2=4, compute="f64"),
+               dict(method="cn", iters=10, residual_bound=1e-4)):
+        assert mir.shampoo_inverse_root_workspace(0, 128, 4, mir.RootOpts(**kw)) >= 0
+    a = mir.StepArgsC()
+    a.nparams, a.B, a.nblk = 0, 128, 0
+    a.g_dt, a.p = mir.F32, 4
+    a.root = mir.RootOpts(method="cn", iters=10).c()
+    assert mir.shampoo_step_workspace(a) >= 0
+
+
 def test_invalid_calls_fail_before_launch(mir):
     oc = mir.RootOpts(method="cn", iters=5).c()
     # null input

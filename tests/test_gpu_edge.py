@@ -1,6 +1,7 @@
-"""Edge cases of shampoo_inverse_root: the largest batch one call accepts,
-a large block side, identity inputs (whose root is exactly I), and a
-rank-one statistic regularised by eps (condition number 1 + ||g||^2 / eps)."""
+"""Edge cases: the largest batch one call accepts, an empty stack,
+a large block side, identity inputs (whose root is exactly I), a rank-one
+statistic regularised by eps (condition number 1 + ||g||^2 / eps), and
+parameters of one element, one row or one column."""
 
 import numpy as np
 import pytest
@@ -91,3 +92,40 @@ def test_rank_one_statistic_with_eps(mir):
         r = oracle.residual(X[i], A[i] + eps * np.eye(B), 4)
         log(f"rank one + eps, factor {i}: rel err {e:.2e}, residual {r:.2e}")
         assert e < 1e-9
+
+
+def test_empty_stack(mir):
+    """A stack of no matrices: every call succeeds and writes nothing (the
+    output tensor next to it keeps its bytes)."""
+    import torch
+    inp = torch.empty((0, 128, 128), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(inp)
+    for kw in (dict(method="cn", iters=10), dict(method="ndb", iters=5, iters2=4), dict(method="cn", iters=10, tol=1e-4),
+               dict(method="chebyshev", cheb_degree=8), dict(method="cn", iters=10, compute="f16")):
+        mir.shampoo_inverse_root(inp, out, 4, mir.RootOpts(**kw))
+    guard = torch.full((4,), 7.0, device="cuda")
+    torch.cuda.synchronize()
+    assert torch.equal(guard, torch.full((4,), 7.0, device="cuda"))
+
+
+def test_degenerate_parameter_shapes(mir):
+    """Parameters of one element, one row and one column (blocks of side 64
+    with a single valid row or column; rank-one factors regularised by eps),
+    on the float64 path: within 1e-4 of the oracle over two steps."""
+    import torch
+    shapes = [(1, 1), (1, 300), (300, 1), (2, 3)]
+    grads = synthetic.gaussian_grads(43, shapes, 2, 0.1)
+    W = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    opt = mir.Shampoo(W, block_size=256, beta2=0.999, eps=1e-3,
+                      root=mir.RootOpts(method="cn", iters=30, compute="f64"), graft="sgd", lr=0.1,
+                      stats_dtype=torch.float64)
+    orc = oracle.ShampooOracle(shapes, [256] * len(shapes), beta2=0.999, eps=1e-3, graft="sgd", lr=0.1)
+    Wo = [np.zeros(s) for s in shapes]
+    for t in range(2):
+        opt.step([to_dev(g) for g in grads[t]])
+        orc.step(Wo, [g.astype(np.float64) for g in grads[t]])
+        torch.cuda.synchronize()
+        errs = [rel_fro(w.cpu().numpy(), wo) for w, wo in zip(W, Wo)]
+        log(f"degenerate shapes step {t + 1}: {['%.1e' % e for e in errs]}")
+        assert max(errs) < 1e-4
+    assert sum(int(f.sum().item()) for f in opt.flags()) == 0
