@@ -336,7 +336,8 @@ shampoo_status shampoo_update_stats(const void* gstack, const void* gstack_t, sh
                                     int64_t nblk, int32_t B, void* LR, shampoo_dtype stats_dt,
                                     double beta2, hipStream_t stream);
 
-/* Workspace bytes for shampoo_inverse_root with these arguments. */
+/* Workspace bytes for shampoo_inverse_root with these arguments (0 for
+ * n = 0); the call's limits apply (E_UNSUPPORTED for n > 65535). */
 shampoo_status shampoo_inverse_root_workspace(int64_t n, int32_t B, int32_t p,
                                               const shampoo_root_opts* opts, size_t* bytes);
 
@@ -353,7 +354,8 @@ shampoo_status shampoo_inverse_root_workspace(int64_t n, int32_t B, int32_t p,
  * the identity; X = solver(A_s); out = X s^(-1/p).
  * Supported: CN with p in {1, 2, 4, 8}; NDB with p in {2, 4}; Chebyshev with
  * p >= 1; compute F32, F16 or F64; power scaling with B <= 1024.  B must be a
- * multiple of 64.  Errors: E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP. */
+ * multiple of 64; n at most 65535 (n = 0 returns at once).  Errors:
+ * E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP. */
 shampoo_status shampoo_inverse_root(const void* in, void* out, shampoo_dtype io_dt, int64_t n,
                                     int32_t B, int32_t p, const shampoo_root_opts* opts,
                                     const int32_t* valid_dev, float* scale_out_dev,

@@ -806,6 +806,9 @@ shampoo_status check_root_args(int64_t n, int32_t B, int32_t p, const shampoo_ro
   if (!o) return fail(SHAMPOO_E_INVALID, "opts is NULL");
   if (n < 0) return fail(SHAMPOO_E_INVALID, "n = %lld < 0", (long long)n);
   if (B < 64 || B % 64 != 0) return fail(SHAMPOO_E_UNSUPPORTED, "B = %d: must be a positive multiple of 64", B);
+  // the launch limits of the call, here too so that a workspace query never
+  // sizes (and overflows on) a batch the call would refuse
+  if (n > 65535) return fail(SHAMPOO_E_UNSUPPORTED, "n = %lld > 65535: batch too large for one launch", (long long)n);
   if (p < 1) return fail(SHAMPOO_E_INVALID, "p = %d < 1", p);
   if (o->compute != SHAMPOO_F32 && o->compute != SHAMPOO_F16 && o->compute != SHAMPOO_F64)
     return fail(SHAMPOO_E_UNSUPPORTED, "compute dtype %d not supported (F32, F16, F64)", o->compute);

@@ -261,6 +261,11 @@ def test_size_limits_are_rejected(mir):
     st = mir.lib.shampoo_inverse_root(fake, fake, mir.F32, 65536, 64, 4, ctypes.byref(oc), None, None, None, fake,
                                       1 << 40, None)
     assert st == mir.E_UNSUPPORTED
+    # the workspace query applies the same batch limit (no size that would overflow)
+    with pytest.raises(mir.ShampooError) as e:
+        mir.shampoo_inverse_root_workspace(1 << 40, 1024, 4, mir.RootOpts(method="cn", iters=5))
+    assert e.value.status == mir.E_UNSUPPORTED
+    assert mir.shampoo_inverse_root_workspace(65535, 64, 4, mir.RootOpts(method="cn", iters=5)) > 0
     with pytest.raises(mir.ShampooError) as e:
         mir.shampoo_inverse_root_workspace(4, 2048, 4, mir.RootOpts(method="cn", iters=5, scaling="power"))
     assert e.value.status == mir.E_UNSUPPORTED
