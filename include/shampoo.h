@@ -382,7 +382,9 @@ shampoo_status shampoo_inverse_root_noalloc(const void* in, void* out, shampoo_d
                                             const int32_t* valid_dev, float* scale_out_dev,
                                             int32_t* flags_dev, hipStream_t stream);
 
-/* Workspace bytes for shampoo_precondition: nblk * B * B * sizeof(roots_dt). */
+/* Workspace bytes for shampoo_precondition: nblk * B * B * sizeof(roots_dt);
+ * E_UNSUPPORTED for a B that is not a multiple of 64 or a batch the call
+ * refuses (more than 65535 blocks). */
 shampoo_status shampoo_precondition_workspace(int64_t nblk, int32_t B, shampoo_dtype roots_dt,
                                               size_t* bytes);
 

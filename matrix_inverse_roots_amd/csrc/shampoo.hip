@@ -1394,7 +1394,7 @@ shampoo_status stats_impl(const void* g, const void* gt, shampoo_dtype gdt, int6
   if (sdt != SHAMPOO_F32 && sdt != SHAMPOO_F64) return fail(SHAMPOO_E_UNSUPPORTED, "statistics dtype %d (F32, F64)", (int)sdt);
   if (nblk == 0) return SHAMPOO_OK;
   if (!g || !gt || !LR) return fail(SHAMPOO_E_INVALID, "null pointer argument");
-  if (gemm_wgs(B, nblk, true) >= (int64_t)1 << 31) return fail(SHAMPOO_E_UNSUPPORTED, "batch too large");
+  if (nblk > 65535 || gemm_wgs(B, nblk, true) >= (int64_t)1 << 31) return fail(SHAMPOO_E_UNSUPPORTED, "batch too large");
   const double a = beta2 == 1.0 ? 1.0 : 1.0 - beta2;
   const double b = beta2;
   const size_t half = (size_t)nblk * B * B * (sdt == SHAMPOO_F64 ? 8 : 4);
@@ -1450,7 +1450,8 @@ shampoo_status precond_impl(const void* roots, shampoo_dtype rdt, const void* g,
   const size_t es = rdt == SHAMPOO_F64 ? 8 : 4;
   const size_t need = (size_t)nblk * B * B * es;
   if (!ws || ws_bytes < need) return fail(SHAMPOO_E_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
-  if (gemm_wgs(B, nblk, false) >= (int64_t)1 << 31) return fail(SHAMPOO_E_UNSUPPORTED, "batch too large");
+  if (nblk > 65535 || gemm_wgs(B, nblk, false) >= (int64_t)1 << 31)
+    return fail(SHAMPOO_E_UNSUPPORTED, "batch too large");
   const void* Lr = roots;
   const void* Rr = (const unsigned char*)roots + (size_t)nblk * B * B * es;
   // E = G Rr, stored transposed; D = Lr E = Lr (E^T)^T.
@@ -2017,6 +2018,10 @@ shampoo_status shampoo_inverse_root_noalloc(const void* in, void* out, shampoo_d
 shampoo_status shampoo_precondition_workspace(int64_t nblk, int32_t B, shampoo_dtype roots_dt, size_t* bytes) {
   if (!bytes || nblk < 0 || B < 1) return fail(SHAMPOO_E_INVALID, "bad arguments");
   if (roots_dt != SHAMPOO_F32 && roots_dt != SHAMPOO_F64) return fail(SHAMPOO_E_UNSUPPORTED, "roots dtype %d", (int)roots_dt);
+  if (B % 64 != 0) return fail(SHAMPOO_E_UNSUPPORTED, "B = %d: must be a positive multiple of 64", B);
+  // the call's launch limits, so that no size is computed for a batch it refuses
+  if (nblk > 65535 || gemm_wgs(B, nblk, false) >= (int64_t)1 << 31)
+    return fail(SHAMPOO_E_UNSUPPORTED, "batch too large");
   *bytes = (size_t)nblk * B * B * dtype_size(roots_dt);
   return SHAMPOO_OK;
 }

@@ -254,8 +254,9 @@ def test_no_cpu_fallback_in_product():
 
 def test_size_limits_are_rejected(mir):
     """Documented limits fail before any launch: more than 65535 matrices in
-    one root call, power scaling beyond B = 1024 with 16 vectors, more than
-    32767 blocks in a step, and an unknown fallback."""
+    one root call (its workspace query too), statistics or preconditioning of
+    more than 65535 blocks, power scaling beyond B = 1024 with 16 vectors,
+    more than 32767 blocks in a step, and an unknown fallback."""
     oc = mir.RootOpts(method="cn", iters=5).c()
     fake = ctypes.c_void_p(0x1000)
     st = mir.lib.shampoo_inverse_root(fake, fake, mir.F32, 65536, 64, 4, ctypes.byref(oc), None, None, None, fake,
@@ -266,6 +267,13 @@ def test_size_limits_are_rejected(mir):
         mir.shampoo_inverse_root_workspace(1 << 40, 1024, 4, mir.RootOpts(method="cn", iters=5))
     assert e.value.status == mir.E_UNSUPPORTED
     assert mir.shampoo_inverse_root_workspace(65535, 64, 4, mir.RootOpts(method="cn", iters=5)) > 0
+    # statistics and preconditioning: the batch limits hold before any size arithmetic
+    sz = ctypes.c_size_t(0)
+    assert mir.lib.shampoo_precondition_workspace(1 << 40, 1 << 20, mir.F32, ctypes.byref(sz)) == mir.E_UNSUPPORTED
+    assert mir.lib.shampoo_update_stats(fake, fake, mir.F32, 1 << 40, 1 << 20, fake, mir.F32, 0.9,
+                                        None) == mir.E_UNSUPPORTED
+    assert mir.lib.shampoo_precondition(fake, mir.F32, fake, mir.F32, 1 << 40, 1 << 20, fake, fake, 1 << 62,
+                                        None) == mir.E_UNSUPPORTED
     with pytest.raises(mir.ShampooError) as e:
         mir.shampoo_inverse_root_workspace(4, 2048, 4, mir.RootOpts(method="cn", iters=5, scaling="power"))
     assert e.value.status == mir.E_UNSUPPORTED
