@@ -203,6 +203,10 @@ def test_decoder_set_full_size_cn_half_products(mir, tol, scaling, pdt):
 
 @pytest.mark.parametrize("cheb_eval", ["clenshaw", "ps"])
 def test_bottleneck_set_full_size_chebyshev(mir, cheb_eval):
+    """The bottleneck-50 set (53 parameters, blocks of 256 and 1024 with
+    ragged edges, Chebyshev degree 16 summed by Clenshaw's recurrence or the
+    Paterson-Stockmeyer split, momentum grafting): every parameter within
+    the stated 1e-4 of the oracle's exact polynomial at each of 3 steps."""
     import torch
     shapes = synthetic.bottleneck50_shapes()
     bsz = synthetic.bottleneck50_block_sizes(shapes)
@@ -211,7 +215,7 @@ def test_bottleneck_set_full_size_chebyshev(mir, cheb_eval):
     opt = mir.Shampoo(W, block_size=lambda m, n: 1024 if max(m, n) >= 2048 else 256, beta2=0.999, eps=1e-12,
                       root=mir.RootOpts(method="chebyshev", cheb_degree=16, cheb_eval=cheb_eval), graft="momentum",
                       lr=0.1, momentum=0.9)
-    sample = [0, 1, 2, 3, 14, 24, 40, 41, 48, 51, 52]
+    sample = list(range(len(shapes)))   # all 53 parameters
     sshapes = [shapes[i] for i in sample]
     orc = oracle.ShampooOracle(sshapes, [bsz[i] for i in sample], beta2=0.999, eps=1e-12, root="chebyshev",
                                cheb_degree=16, graft="momentum", lr=0.1, momentum=0.9)
