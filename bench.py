@@ -207,6 +207,49 @@ def oracle_full_steps():
     return res
 
 
+def oracle_decoder_parity(mir):
+    """Parity of the decoder set's two fastest timed step forms against the
+    oracle: 3 steps on the whole set (bfloat16 gradients N(0, 0.02^2), seed
+    4), the oracle run on the first 4 parameters (one layer); the largest
+    relative Frobenius error of those parameters over the 3 steps."""
+    import numpy as np
+    import torch
+    import oracle
+    import synthetic
+    shapes = synthetic.decoder_shapes()
+    grads = synthetic.gaussian_grads(4, shapes, 3, 0.02, dtype="bf16")
+    sample = [0, 1, 2, 3]
+    forms = {
+        "cn_f16_products_tol0.1_power_scaling_bf16_precondition":
+            (dict(compute="f16", tol=HALF_TOL, scaling="power"), dict(fallback="f64", precondition_dtype=torch.bfloat16),
+             2e-2),
+        "f32_chain_tol1e-4_power_scaling_residual_checked":
+            (dict(compute="f32", tol=1e-4, scaling="power", residual_bound=RESIDUAL_BOUND),
+             dict(fallback="f64", stats_dtype=torch.float64), 1e-4),
+    }
+    res = {}
+    for name, (root_kw, kw, bar) in forms.items():
+        W = [torch.zeros(sh, dtype=torch.float32, device="cuda") for sh in shapes]
+        opt = mir.Shampoo(W, block_size=1024, beta2=0.999, eps=1e-12, root=mir.RootOpts(method="cn", iters=34, **root_kw),
+                          graft="adam", lr=1e-3, grad_dtype=torch.bfloat16, **kw)
+        orc = oracle.ShampooOracle([shapes[i] for i in sample], [1024] * len(sample), beta2=0.999, eps=1e-12,
+                                   graft="adam", lr=1e-3)
+        Wo = [np.zeros(shapes[i]) for i in sample]
+        worst = 0.0
+        for t in range(3):
+            bits = [torch.from_numpy(np.ascontiguousarray(g).view(np.int16)).view(torch.bfloat16).cuda()
+                    for g in grads[t]]
+            opt.step(bits)
+            orc.step(Wo, [synthetic.bf16_bits_to_f32(grads[t][i]).astype(np.float64) for i in sample])
+            torch.cuda.synchronize()
+            for k, i in enumerate(sample):
+                w = W[i].cpu().numpy().astype(np.float64)
+                worst = max(worst, float(np.linalg.norm(w - Wo[k]) / np.linalg.norm(Wo[k])))
+        res[name] = {"rel_err_max": worst, "bar": bar, "parameters_checked": len(sample), "steps": 3}
+        del opt, W
+    return res
+
+
 def oracle_spd128(X64_dev):
     """Parity of the float64 coupled-Newton roots of the 64 x 128^2 stack
     against the oracle (all 64 blocks)."""
@@ -685,6 +728,7 @@ def main():
         if not args.no_full_step:
             result["cpu_baseline"]["full_steps"] = oracle_full_steps()
             par["spd_stack_64x128_cn20_f64"] = oracle_spd128(x128)
+            par["decoder12_fastest_step_forms"] = oracle_decoder_parity(mir)
         log(f"cpu baseline: {result['cpu_baseline']}")
         result["parity_sample"] = par
         log(f"parity sample: {par}")
